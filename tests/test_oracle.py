@@ -1,0 +1,366 @@
+"""Pins for the fp64 CPU oracle: worked values, closed forms, invariants, library routines and
+brute force on tiny inputs.  None of these re-derives a value through the oracle itself."""
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from oracle import exl3_oracle as O
+from moe_exl3_pre_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ------------------------------------------------------------------------------------------ codebook
+
+def test_codebook_worked_values():
+    for s, bits, val in _rows("codebook_values.txt"):
+        v = O.codebook_value(np.array([int(s, 16)]))[0]
+        assert v == float(val), (s, v, val)
+        assert np.float16(v).view(np.uint16) == int(bits, 16)
+
+
+def test_codebook_distribution_closed_form():
+    # 0x9E37 is odd, so s -> s*0x9E37 mod 2^16 is a bijection and the 6 masked bits are uniform:
+    # 64 values +-2^e (1 + m/8), e in -3..0, m in 0..7, each taken by exactly 1024 states.
+    v = O.codebook_value(np.arange(1 << 16))
+    expect = sorted(s * 2.0 ** e * (1 + m / 8) for s in (-1, 1) for e in range(-3, 1) for m in range(8))
+    vals, counts = np.unique(v, return_counts=True)
+    assert list(vals) == expect
+    assert np.all(counts == 1024)
+    assert v.sum() == 0.0
+    # E[v^2] = (1/4 sum_e 4^e) (1/8 sum_m (1+m/8)^2) = (85/256) (1100/512)
+    assert np.mean(v * v) == (85 / 256) * (1100 / 512)
+    # exact as int8 * 2^-6
+    assert np.all(np.abs(v * 64) <= 120) and np.all(v * 64 == np.rint(v * 64))
+
+
+# ------------------------------------------------------------------------------------------ stream
+
+def _bigint_states(words16, K):
+    """Independent reader: the tile's words as one little-endian big integer, doubled for the wrap."""
+    n = 256 * K
+    stream = 0
+    for j, w in enumerate(words16):
+        stream |= (int(w) & 0xFFFF) << (16 * j)
+    ring = stream | (stream << n)
+    return [(ring >> (i * K)) & 0xFFFF for i in range(256)]
+
+
+def _bit_definition_states(words16, K):
+    """The definition as stated: bit j of the stream is bit (j mod 16) of word j // 16."""
+    w = np.asarray(words16).astype(np.int64) & 0xFFFF
+    n = 256 * K
+    bits = [(int(w[j >> 4]) >> (j & 15)) & 1 for j in range(n)]
+    return [sum(bits[(i * K + t) % n] << t for t in range(16)) for i in range(256)]
+
+
+def test_impulse_tail_biting():
+    table = {}
+    for K, i, s in _rows("impulse_states.txt"):
+        table.setdefault(int(K), {})[int(i)] = int(s, 16)
+    for K, nz in table.items():
+        words = np.zeros(16 * K, dtype=np.int16)
+        words[0] = 1
+        st = O.tile_states(words, K)
+        expect = np.zeros(256, dtype=np.int64)
+        for i, s in nz.items():
+            expect[i] = s
+        assert np.array_equal(st.astype(np.int64), expect), K
+
+
+def test_all_ones_words():
+    for K in range(1, 9):
+        words = np.full(16 * K, -1, dtype=np.int16)
+        assert np.all(O.tile_states(words, K) == 0xFFFF)
+        assert np.all(O.codebook_value(O.tile_states(words, K)) == 0.171875)
+
+
+@pytest.mark.parametrize("K", range(1, 9))
+def test_states_vs_independent_readers(K):
+    rng = np.random.default_rng(100 + K)
+    tiles = rng.integers(0, 1 << 16, size=(3, 16 * K), dtype=np.uint16).view(np.int16)
+    st = O.tile_states(tiles, K)
+    for t in range(3):
+        assert list(st[t]) == _bigint_states(tiles[t], K)
+    assert list(st[0]) == _bit_definition_states(tiles[0], K)
+
+
+def test_pattern_tile_k3():
+    vals = {k: float(v) for k, v in _rows("pattern_tile_k3.txt")}
+    words = ((0x1111 * (np.arange(48) + 1)) & 0xFFFF).astype(np.uint16).view(np.int16)
+    W = O.decode_weight(words.reshape(1, 1, 48), 3)
+    assert W[0, 0] == vals["W00"] and W[15, 0] == vals["W15_0"]
+    assert W[0, 1] == vals["W0_1"] and W[15, 15] == vals["W15_15"]
+    assert W.sum() == vals["sum"] and (W * W).sum() == vals["sumsq"]
+
+
+def test_placement_brute_force():
+    """W[16a + r, 16b + c] = D(state r + 16c of tile (a, b)), states from the big-int reader and
+    values from the fp16 bit pattern read with numpy's own half type."""
+    rng = np.random.default_rng(7)
+    for K in (2, 3, 5):
+        code = synth.random_code(rng, 32, 48, K)
+        W = O.decode_weight(code, K)
+        for a in range(2):
+            for b in range(3):
+                st = _bigint_states(code[a, b], K)
+                for i in range(256):
+                    r, c = i % 16, i // 16
+                    p = ((st[i] * 0x9E37) & 0xFFFF) & 0x8F80 | 0x3000
+                    v = float(np.array([p], dtype=np.uint16).view(np.float16)[0])
+                    assert W[16 * a + r, 16 * b + c] == v
+
+
+# ------------------------------------------------------------------------------------------ Hadamard
+
+def test_had128_matrix_properties():
+    H = O.had128_matrix()
+    assert np.max(np.abs(H @ H - np.eye(128))) <= 1e-15
+    assert np.array_equal(H, H.T)
+    assert np.allclose(H, scipy.linalg.hadamard(128) / np.sqrt(128), atol=0, rtol=0)
+    e0 = np.zeros(128); e0[0] = 1
+    assert np.allclose(O.had128(e0), np.full(128, 1 / np.sqrt(128)), rtol=1e-15, atol=0)
+    assert np.allclose(O.had128(np.ones(128)), np.sqrt(128) * e0, rtol=0, atol=1e-13)
+
+
+def _fwht(v):
+    """In-place radix-2 fast Walsh-Hadamard transform (natural / Sylvester order), normalised."""
+    v = np.array(v, dtype=np.float64)
+    h = 1
+    while h < len(v):
+        for i in range(0, len(v), 2 * h):
+            a, b = v[i:i + h].copy(), v[i + h:i + 2 * h].copy()
+            v[i:i + h], v[i + h:i + 2 * h] = a + b, a - b
+        h *= 2
+    return v / np.sqrt(len(v))
+
+
+def test_had128_blockwise_vs_fwht_and_norm():
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((3, 512))
+    y = O.had128(v)
+    for r in range(3):
+        for q in range(4):
+            assert np.allclose(y[r, 128 * q:128 * q + 128], _fwht(v[r, 128 * q:128 * q + 128]), rtol=0, atol=1e-13)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(v, axis=1), rtol=1e-14)
+    assert np.allclose(O.had128(y), v, rtol=0, atol=1e-13)
+    with pytest.raises(ValueError):
+        O.had128(np.ones(100))
+
+
+# ------------------------------------------------------------------------------------------ linear
+
+def _ones(n):
+    return np.ones(n)
+
+
+@pytest.mark.parametrize("fill,val", [(0, 0.125), (-1, 0.171875)])
+def test_linear_constant_code_closed_form(fill, val):
+    """Constant states make W = v * ones; the output is v * 128 * sum_q t[m, 128q] in column 128p of
+    every block and exactly 0 elsewhere (t = x * s_in * rin), times rout * s_out."""
+    rng = np.random.default_rng(11)
+    M, IC, OC, K = 3, 384, 256, 2
+    code = np.full((IC // 16, OC // 16, 16 * K), fill, dtype=np.int16)
+    x = rng.standard_normal((M, IC))
+    s_in, rin = rng.choice([-1.0, 1.0], IC), rng.uniform(0.5, 1.5, IC)
+    rout, s_out = rng.uniform(0.5, 1.5, OC), rng.choice([-1.0, 1.0], OC)
+    y = O.linear(x, code, K, s_in, rin, rout, s_out)
+    t = x * s_in * rin
+    head = val * 128 * t[:, ::128].sum(axis=1)
+    expect = np.zeros((M, OC))
+    for p in range(OC // 128):
+        expect[:, 128 * p] = head * rout[128 * p] * s_out[128 * p]
+    assert np.allclose(y, expect, rtol=1e-12, atol=1e-12)
+    assert np.all(y[:, 1:128] == 0.0) or np.max(np.abs(y[:, 1:128])) < 1e-12
+
+
+def test_linear_basis_probe_recovers_rows():
+    """x = Had128(e_k) with unit vectors gives xh = e_k, so Had128 of the output is row k of W."""
+    rng = np.random.default_rng(5)
+    IC, OC, K = 256, 128, 3
+    code = synth.random_code(rng, IC, OC, K)
+    ks = [0, 17, 130, 255]
+    x = np.stack([O.had128(np.eye(IC)[k]) for k in ks])
+    y = O.linear(x, code, K, _ones(IC), _ones(IC), _ones(OC), _ones(OC))
+    rows = O.had128(y)
+    for j, k in enumerate(ks):
+        a, r = divmod(k, 16)
+        for b in range(OC // 16):
+            st = _bigint_states(code[a, b], K)
+            for c in range(16):
+                p = ((st[r + 16 * c] * 0x9E37) & 0xFFFF) & 0x8F80 | 0x3000
+                v = float(np.array([p], dtype=np.uint16).view(np.float16)[0])
+                assert abs(rows[j, 16 * b + c] - v) < 1e-12
+
+
+def test_linear_tiny_brute_force():
+    """IC = OC = 128: explicit loops with the explicit Hadamard matrix and the big-int decoder."""
+    rng = np.random.default_rng(9)
+    M, IC, OC, K = 2, 128, 128, 4
+    case = synth.linear_case(9, M, IC, OC, K)
+    H = scipy.linalg.hadamard(128) / np.sqrt(128)
+    W = np.zeros((IC, OC))
+    for a in range(IC // 16):
+        for b in range(OC // 16):
+            st = _bigint_states(case["code"][a, b], K)
+            for i in range(256):
+                p = ((st[i] * 0x9E37) & 0xFFFF) & 0x8F80 | 0x3000
+                W[16 * a + i % 16, 16 * b + i // 16] = float(np.array([p], dtype=np.uint16).view(np.float16)[0])
+    x = case["x"].astype(np.float64)
+    s_in, rin = case["s_in"].astype(np.float64), case["rin"].astype(np.float64)
+    rout, s_out = case["rout"].astype(np.float64), case["s_out"].astype(np.float64)
+    expect = np.zeros((M, OC))
+    for m in range(M):
+        t = [x[m, k] * s_in[k] * rin[k] for k in range(IC)]
+        xh = [sum(H[a, b] * t[b] for b in range(IC)) for a in range(IC)]
+        yv = [sum(xh[k] * W[k, n] for k in range(IC)) for n in range(OC)]
+        z = [sum(H[a, b] * yv[b] for b in range(OC)) for a in range(OC)]
+        expect[m] = [z[n] * rout[n] * s_out[n] for n in range(OC)]
+    y = O.linear(case["x"], case["code"], K, case["s_in"], case["rin"], case["rout"], case["s_out"])
+    assert np.allclose(y, expect, rtol=1e-12, atol=1e-10)
+
+
+def test_linear_invariants():
+    c = synth.linear_case(21, 4, 256, 384, 3)
+    args = (c["code"], 3, c["s_in"], c["rin"], c["rout"], c["s_out"])
+    y = O.linear(c["x"], *args)
+    # linearity and exact doubling
+    assert np.array_equal(O.linear(2 * c["x"].astype(np.float64), *args), 2 * y)
+    # s_in -> -s_in negates exactly
+    neg = (c["code"], 3, -c["s_in"].astype(np.float64), c["rin"], c["rout"], c["s_out"])
+    assert np.array_equal(O.linear(c["x"], *neg), -y)
+    # no bias: zero input gives exactly zero
+    assert np.all(O.linear(np.zeros_like(c["x"]), *args) == 0.0)
+    # rin (pre-scale) and rout (post-scale) are not interchangeable
+    IC = 256
+    rin2 = np.resize(c["rout"], IC)
+    rout2 = np.resize(c["rin"], 384)
+    y2 = O.linear(c["x"], c["code"], 3, c["s_in"], rin2, rout2, c["s_out"])
+    assert np.max(np.abs(y2 - y)) > 1e-3 * np.max(np.abs(y))
+    # rows are independent
+    assert np.allclose(O.linear_rows([1, 3], c["x"], *args), y[[1, 3]], rtol=1e-14, atol=1e-12)
+
+
+def test_merged_equals_concatenation():
+    case = synth.merged_case(31, 3, 256, [(128, 2), (256, 3)], shared_input_vectors=False)
+    out = np.full((3, case["ldo"]), np.nan)
+    pieces = []
+    for s in case["shards"]:
+        O.linear_into(out, s["col0"], case["x"], s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"])
+        pieces.append(O.linear(case["x"], s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"]))
+    assert np.array_equal(out, np.concatenate(pieces, axis=1))
+    # a slice write leaves the other columns untouched
+    out2 = np.full((3, 600), 7.0)
+    s = case["shards"][0]
+    O.linear_into(out2, 100, case["x"], s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"])
+    assert np.all(out2[:, :100] == 7.0) and np.all(out2[:, 228:] == 7.0)
+
+
+def test_fp16_activation_mode_error():
+    c = synth.linear_case(41, 8, 1024, 256, 2)
+    args = (c["code"], 2, c["s_in"], c["rin"], c["rout"], c["s_out"])
+    y = O.linear(c["x"], *args)
+    y16 = O.linear(c["x"], *args, act="f16")
+    rel = np.linalg.norm(y16 - y) / np.linalg.norm(y)
+    assert 1e-5 < rel < 2 ** -11
+
+
+# ------------------------------------------------------------------------------------------ 8-bit path
+
+def test_int8_quantisation_properties():
+    rng = np.random.default_rng(13)
+    xh = rng.standard_normal((6, 1024)) * np.array([1, 10, 0.01, 3, 1, 1])[:, None]
+    xh[4] = 0.0
+    q, sc = O.quantize_rows_int8(xh)
+    assert q.dtype == np.int8 and np.all(np.abs(q.astype(int)) <= 127)
+    assert sc[4] == 0 and np.all(q[4] == 0)
+    for r in (0, 1, 2, 3, 5):
+        assert np.max(np.abs(q[r].astype(int))) == 127
+        assert np.max(np.abs(q[r] * sc[r] - xh[r])) <= sc[r] / 2 * (1 + 1e-12)
+    q2, sc2 = O.quantize_rows_int8(2 * xh)
+    assert np.array_equal(q2, q) and np.array_equal(sc2, 2 * sc)
+
+
+def test_int8_linear_scale_invariance_and_error():
+    c = synth.linear_case(51, 8, 5120 // 4, 256, 3)
+    args = (c["code"], 3, c["s_in"], c["rin"], c["rout"], c["s_out"])
+    y = O.linear(c["x"], *args)
+    y8 = O.linear(c["x"], *args, act="int8")
+    assert np.array_equal(O.linear(2 * c["x"].astype(np.float64), *args, act="int8"), 2 * y8)
+    rel = np.linalg.norm(y8 - y) / np.linalg.norm(y)
+    assert 1e-3 < rel < 3e-2
+    zero = O.linear(np.zeros_like(c["x"]), *args, act="int8")
+    assert np.all(zero == 0.0)
+
+
+# ------------------------------------------------------------------------------------------ MoE
+
+def _small_moe(seed=61, T=12, E=6, topk=2, H=256, I=256):
+    return synth.moe_case(seed, T=T, E=E, topk=topk, H=H, I=I)
+
+
+def test_moe_top1_reduces_to_linears():
+    m = _small_moe()
+    e = m["experts"][3]
+    T = m["T"]
+    ids = np.full((T, 1), 3, dtype=np.int32)
+    w = np.ones((T, 1), dtype=np.float32)
+    out = O.moe_forward(m["x"], ids, w, m["experts"])
+    one = np.ones(m["H"])
+    h1 = O.linear(m["x"], e["w1"], e["k_gu"], e["w1_suh"], 1.0, 1.0, e["w1_svh"])
+    h3 = O.linear(m["x"], e["w3"], e["k_gu"], e["w3_suh"], 1.0, 1.0, e["w3_svh"])
+    a = h1 / (1 + np.exp(-h1)) * h3
+    y = O.linear(a, e["w2"], e["k_d"], e["w2_suh"], one[:m["I"]], 1.0, e["w2_svh"])
+    assert np.allclose(out, y, rtol=1e-13, atol=1e-9)
+
+
+def test_moe_weighted_sum_and_relabel_invariance():
+    m = _small_moe()
+    out = O.moe_forward(m["x"], m["topk_ids"], m["topk_w"], m["experts"])
+    # explicit weighted sum, token by token
+    for t in (0, 5):
+        acc = np.zeros(m["H"])
+        for j in range(m["topk"]):
+            acc += float(m["topk_w"][t, j]) * O.expert_forward(m["x"][t:t + 1], m["experts"][m["topk_ids"][t, j]])[0]
+        assert np.allclose(out[t], acc, rtol=1e-12, atol=1e-9)
+    # relabel experts with a permutation: same output
+    perm = np.random.default_rng(1).permutation(m["E"])
+    experts2 = [None] * m["E"]
+    for e in range(m["E"]):
+        experts2[perm[e]] = m["experts"][e]
+    out2 = O.moe_forward(m["x"], perm[m["topk_ids"]], m["topk_w"], experts2)
+    assert np.allclose(out2, out, rtol=1e-12, atol=1e-9)
+
+
+def test_moe_unrouted_expert_contributes_nothing():
+    m = _small_moe()
+    ids = np.where(m["topk_ids"] == 0, 1, m["topk_ids"])
+    experts = list(m["experts"])
+    experts[0] = dict(experts[0], w1_suh=np.full(m["H"], np.nan))
+    out = O.moe_forward(m["x"], ids, m["topk_w"], experts)
+    assert np.all(np.isfinite(out))
+
+
+def test_moe_128_aligned_intermediate_cut_is_exact():
+    """Splitting every expert's intermediate dim at a multiple of 128 and summing the two halves
+    reproduces the full output (the bank page's rank cut is exact because it is 128-aligned)."""
+    m = _small_moe(H=256, I=384)
+    cut = 256
+    full = O.moe_forward(m["x"], m["topk_ids"], m["topk_w"], m["experts"])
+    halves = []
+    for lo, hi in ((0, cut), (cut, m["I"])):
+        ex = []
+        for e in m["experts"]:
+            ex.append(dict(e, w1=e["w1"][:, lo // 16:hi // 16], w3=e["w3"][:, lo // 16:hi // 16],
+                           w2=e["w2"][lo // 16:hi // 16], w1_svh=e["w1_svh"][lo:hi], w3_svh=e["w3_svh"][lo:hi],
+                           w2_suh=e["w2_suh"][lo:hi]))
+        halves.append(O.moe_forward(m["x"], m["topk_ids"], m["topk_w"], ex))
+    rel = np.linalg.norm(halves[0] + halves[1] - full) / np.linalg.norm(full)
+    assert rel <= 1e-12
