@@ -1,0 +1,180 @@
+/*
+ * exl3.h -- C ABI of the MI355X (gfx950) EXL3 trellis-quantized linear layer.
+ *
+ * Pages cited by title:
+ *   "radiance_escha.py"      -- vLLM quantization method for escha (EXL3 trellis) W2 checkpoints on gfx1201.
+ *                               Module docstring (forward formula), `_TILE`/`_HAD` constants,
+ *                               `escha_linear_into`, `_ensure_scratch`, `EschaLinearMethod.apply`,
+ *                               `process_weights_after_loading`.
+ *   "vllm-quantpack 0.1.0"   -- wheel diff, exl3/linear.py: module docstring and `Exl3LinearMethod._forward`.
+ *   "dspark/worker/exl3/bank.py" -- class `Exl3Bank` (expert bank layout, `allocate`, `views`, `tables`).
+ *   "vLLM PR #190: [GG] Add EXL3 Trellis backend for rank-sliced MoE checkpoints" -- commit messages.
+ *
+ * The layer ("radiance_escha.py", module docstring):
+ *     out[:, col0 : col0+OC] = bf16( Had128( Had128((x * s_in) * rin) @ W ) * rout * s_out )
+ * where W = decode(code) is [IC, OC] and Had128 is the orthonormal Sylvester Walsh-Hadamard transform of
+ * every consecutive 128-block (input side along IC, output side along OC).  rin is a pre-scale and rout a
+ * post-scale; no bias is applied.
+ *
+ * Trellis layout (`_TILE = 16`, "code tensor is [IC//16, OC//16, 16*K]"): code[a][b][0 .. 16K) holds the
+ * 16x16 tile W[16a .. 16a+16, 16b .. 16b+16) as a tail-biting 256K-bit stream (bit j = bit j%16 of word
+ * j/16).  State i of a tile is the 16-bit window at stream bit i*K (circular, least significant bit
+ * first); it sets W[16a + i%16][16b + i/16] to the fp16 number with bit pattern
+ * ((state * 0x9E37) mod 2^16) & 0x8F80 | 0x3000.  The pages do not print EXL3's own codebooks; this one
+ * is fixed here and checkpoints coded with another codebook decode to different values.
+ *
+ * Conventions (all entry points):
+ *   - Every pointer is a device pointer unless stated otherwise; the caller owns every buffer.  The
+ *     library never allocates, frees or synchronises, so each call is legal inside stream capture
+ *     ("radiance_escha.py", `_ensure_scratch`: a lazy allocation inside the launch would land in graph
+ *     capture).  `stream` is a hipStream_t (NULL = the legacy default stream).
+ *   - Workspace: `ws` must hold at least the bytes the matching *_workspace_bytes() function returns,
+ *     be 256-byte aligned, and be zero-filled once before its first use.  Kernels leave their counters
+ *     zero again on exit, so later calls need no clearing.  One workspace serves one stream at a time:
+ *     calls that may overlap (different streams) need different workspaces.
+ *   - Host-side validation happens before any launch; a rejected call launches nothing and returns a
+ *     negative status.  exl3_last_error() then names the offending argument (thread-local text).
+ *   - M == 0 (or T == 0) is a valid no-op returning EXL3_OK ("radiance_escha.py", `escha_linear_into`).
+ */
+#ifndef EXL3_H
+#define EXL3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EXL3_OK = 0,
+  EXL3_EINVAL = -1,      /* bad shape, K, alignment, null pointer or flag */
+  EXL3_EWORKSPACE = -2,  /* workspace missing or smaller than required */
+  EXL3_EUNSUPPORTED = -3,/* valid request outside what this build implements */
+  EXL3_ELAUNCH = -4      /* a kernel launch failed (message carries the HIP error) */
+} exl3_status;
+
+/* flags */
+enum {
+  EXL3_ACT_INT8 = 1u << 0,   /* per-row 8-bit activations: sc = max|xh| / 127, q = clamp(rne(xh / sc), +-127) */
+  EXL3_FORCE_GEMV = 1u << 1, /* force the decode-phase (streaming split-K) kernel whatever M is */
+  EXL3_FORCE_MFMA = 1u << 2  /* force the prefill-phase (tiled MFMA GEMM) kernel whatever M is */
+};
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char* exl3_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int exl3_version(void);
+
+/* Largest M served by the decode-phase kernel when no FORCE flag is given. */
+int64_t exl3_gemv_max_rows(void);
+
+/* --------------------------------------------------------------------------------------------------
+ * One projection written into its column slice ("radiance_escha.py", `escha_linear_into`: one escha
+ * projection written into out[:, col0:col0+OC]; merged modules run one call per source tensor,
+ * `EschaLinearMethod.apply`).
+ *
+ *   out    bf16 [M, ldo] row-major.  Only columns [col0, col0 + OC) are written; others are untouched.
+ *   x      bf16 [M, IC] row-major, contiguous.
+ *   code   int16 [IC/16, OC/16, 16K], contiguous, 16-byte aligned.
+ *   s_in, rin    fp16 [IC];  rout, s_out   fp16 [OC].
+ *   K      bits per weight, 1..8.
+ * Requirements: IC % 128 == 0 and OC % 128 == 0 (the transform is blocked at 128, `create_weights`),
+ * OC / 128 <= 4096, col0 >= 0, col0 + OC <= ldo, out/x/code 16-byte aligned, ldo even.
+ * Returns EXL3_OK, EXL3_EINVAL, EXL3_EWORKSPACE, EXL3_ELAUNCH.
+ * ------------------------------------------------------------------------------------------------ */
+size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned flags);
+
+int exl3_linear_into(void* out, int64_t ldo, int64_t col0,
+                     const void* x, int64_t M, int64_t IC,
+                     const int16_t* code, int64_t OC, int K,
+                     const void* s_in, const void* rin,
+                     const void* rout, const void* s_out,
+                     unsigned flags, void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------------------
+ * Several shards of one merged projection in one call: every shard reads the same x and writes its own
+ * column slice [col0_i, col0_i + OC_i) ("radiance_escha.py", module docstring: gate K=2 and up K=3 cannot
+ * be one GEMM, each keeps its own code/rout/s_out; `apply`: one output buffer, each shard writes its own
+ * columns).  The result is bitwise identical to one exl3_linear_into call per shard.
+ *   shards    host array of n_shards descriptors (read during the call only); 1 <= n_shards <= 16.
+ * Workspace: exl3_linear_multi_workspace_bytes with the same shard list.
+ * ------------------------------------------------------------------------------------------------ */
+typedef struct {
+  const int16_t* code;   /* int16 [IC/16, OC/16, 16K] */
+  int64_t OC;
+  int32_t K;
+  int32_t reserved;
+  int64_t col0;
+  const void* s_in;      /* fp16 [IC] */
+  const void* rin;       /* fp16 [IC] */
+  const void* rout;      /* fp16 [OC] */
+  const void* s_out;     /* fp16 [OC] */
+} exl3_shard;
+
+size_t exl3_linear_multi_workspace_bytes(int64_t M, int64_t IC, int n_shards, const exl3_shard* shards,
+                                         unsigned flags);
+
+int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int64_t IC,
+                           int n_shards, const exl3_shard* shards,
+                           unsigned flags, void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------------------
+ * MoE expert bank ("dspark/worker/exl3/bank.py", `Exl3Bank` docstring and `allocate`): experts sit in
+ * K-sorted physical slots; the trellis words of all experts share two flat int16 banks (w13 = [w1 | w3]
+ * per slot, and w2); sign/scale vectors are fp16 [E, ...].
+ *
+ *   out[t] = bf16( sum_j topk_w[t, j] * E_{topk_ids[t, j]}(x[t]) )          (j in top-k order)
+ *   E_e(v) = L_w2( silu(L_w1(v)) * L_w3(v) ),   silu(h) = h / (1 + exp(-h)),
+ *   L_P(v) = svh * Had128( Had128(v * suh) @ W_P )      (suh plays s_in*rin, svh plays rout*s_out)
+ *
+ * Slot p (= perm[logical id]) holds w1 at w13 + off_w1[p] as [H/16, I/16, 16 k_gu], w3 at w13 + off_w3[p]
+ * (same shape), w2 at w2 + off_w2[p] as [I/16, H/16, 16 k_d]; offsets count int16 elements and each
+ * must make the address 16-byte aligned.  Groups are contiguous slot ranges [lo, hi) sharing (k_gu, k_d)
+ * ("bank.py", `tables`: one GroupTables per K group).
+ * ------------------------------------------------------------------------------------------------ */
+typedef struct { int32_t k_gu, k_d, lo, hi; } exl3_group;
+
+typedef struct {
+  int32_t E, H, I;                     /* experts, hidden, intermediate (multiples of 128) */
+  int32_t n_groups;                    /* 1 .. 64 */
+  const int16_t* w13;                  /* flat int16 bank of w1 | w3 */
+  const int16_t* w2;                   /* flat int16 bank of w2 */
+  const void* w13_suh;                 /* fp16 [E, 2, H]  (slot order) */
+  const void* w13_svh;                 /* fp16 [E, 2, I] */
+  const void* w2_suh;                  /* fp16 [E, I] */
+  const void* w2_svh;                  /* fp16 [E, H] */
+  const int64_t* off_w1;               /* device int64 [E], slot order */
+  const int64_t* off_w3;               /* device int64 [E] */
+  const int64_t* off_w2;               /* device int64 [E] */
+  const int32_t* perm;                 /* device int32 [E]: logical expert -> slot */
+  const exl3_group* groups;            /* HOST array [n_groups], covering slots 0 .. E-1 in order */
+} exl3_bank;
+
+size_t exl3_moe_workspace_bytes(const exl3_bank* bank, int64_t T, int topk, unsigned flags);
+
+/*   out      bf16 [T, H];  x  bf16 [T, H]
+ *   topk_ids int32 [T, topk] logical expert ids in [0, E) (device);  topk_w float32 [T, topk] (device).
+ * An id outside [0, E) is ignored (contributes nothing).  Returns EXL3_OK / EXL3_EINVAL / EXL3_EWORKSPACE /
+ * EXL3_ELAUNCH. */
+int exl3_moe_bank_forward(void* out, const void* x, int64_t T,
+                          const int32_t* topk_ids, const float* topk_w, int topk,
+                          const exl3_bank* bank, unsigned flags, void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------------------
+ * Test hook: the decoded weight, fp16 [IC, OC] row-major, produced by the same device decode routine
+ * the GEMM kernels use.  IC, OC multiples of 16; K in 1..8.
+ * ------------------------------------------------------------------------------------------------ */
+int exl3_decode_tiles(void* w_out, const int16_t* code, int64_t IC, int64_t OC, int K, void* stream);
+
+/* Test hook: the rotated activations the GEMM kernels consume for x [M, IC] (fp16 [M, IC], natural
+ * feature order) or, with EXL3_ACT_INT8, int8 codes [M, IC] into q_out and float32 row scales [M] into
+ * scale_out.  Same kernels as exl3_linear_into. */
+int exl3_rotate_activations(void* q_out, float* scale_out, const void* x, int64_t M, int64_t IC,
+                            const void* s_in, const void* rin, unsigned flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EXL3_H */

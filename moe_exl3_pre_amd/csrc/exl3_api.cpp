@@ -1,0 +1,283 @@
+// C ABI of the EXL3 layer: argument validation, workspace layout, path choice and launches.
+// Host work only; every step of the layer runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/exl3.h"
+#include "exl3_internal.hpp"
+
+using namespace exl3;
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return EXL3_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(EXL3_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return EXL3_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr unsigned kKnownFlags = EXL3_ACT_INT8 | EXL3_FORCE_GEMV | EXL3_FORCE_MFMA;
+constexpr int64_t kGemvMaxRows = 16;
+
+int check_flags(unsigned flags) {
+  if (flags & ~kKnownFlags) return fail(EXL3_EINVAL, "flags: unknown bits 0x%x", flags & ~kKnownFlags);
+  if ((flags & EXL3_FORCE_GEMV) && (flags & EXL3_FORCE_MFMA))
+    return fail(EXL3_EINVAL, "flags: EXL3_FORCE_GEMV and EXL3_FORCE_MFMA are exclusive");
+  if (flags & EXL3_ACT_INT8) return fail(EXL3_EUNSUPPORTED, "flags: EXL3_ACT_INT8 is not available in this build");
+  if (flags & EXL3_FORCE_MFMA) return fail(EXL3_EUNSUPPORTED, "flags: EXL3_FORCE_MFMA is not available in this build");
+  return EXL3_OK;
+}
+
+int check_dims(int64_t M, int64_t IC) {
+  if (M < 0) return fail(EXL3_EINVAL, "M: %lld is negative", (long long)M);
+  if (M > (int64_t(1) << 30)) return fail(EXL3_EINVAL, "M: %lld is too large", (long long)M);
+  if (IC <= 0 || IC % 128) return fail(EXL3_EINVAL, "IC: %lld is not a positive multiple of 128", (long long)IC);
+  if (IC > (int64_t(1) << 20)) return fail(EXL3_EINVAL, "IC: %lld is too large", (long long)IC);
+  return EXL3_OK;
+}
+
+int check_shard(const char* who, int64_t IC, const int16_t* code, int64_t OC, int K, int64_t col0, int64_t ldo,
+                const void* s_in, const void* rin, const void* rout, const void* s_out) {
+  if (OC <= 0 || OC % 128) return fail(EXL3_EINVAL, "%sOC: %lld is not a positive multiple of 128", who, (long long)OC);
+  if (OC / 128 > kCounterSlots) return fail(EXL3_EINVAL, "%sOC: %lld exceeds %d blocks of 128", who, (long long)OC, kCounterSlots);
+  if (K < 1 || K > 8) return fail(EXL3_EINVAL, "%sK: %d is outside 1..8", who, K);
+  if (col0 < 0 || col0 + OC > ldo)
+    return fail(EXL3_EINVAL, "%scol0: slice [%lld, %lld) does not fit ldo %lld", who, (long long)col0,
+                (long long)(col0 + OC), (long long)ldo);
+  if (IC / 16 * (OC / 16) * 32 * int64_t(K) >= (int64_t(1) << 31))
+    return fail(EXL3_EUNSUPPORTED, "%scode: %lld x %lld at K=%d exceeds 2 GiB of trellis words per shard", who,
+                (long long)IC, (long long)OC, K);
+  if (!code) return fail(EXL3_EINVAL, "%scode: null", who);
+  if (!aligned(code, 16)) return fail(EXL3_EINVAL, "%scode: not 16-byte aligned", who);
+  if (!s_in || !rin) return fail(EXL3_EINVAL, "%ss_in/rin: null", who);
+  if (!aligned(s_in, 4) || !aligned(rin, 4)) return fail(EXL3_EINVAL, "%ss_in/rin: not 4-byte aligned", who);
+  if (!rout || !s_out) return fail(EXL3_EINVAL, "%srout/s_out: null", who);
+  if (!aligned(rout, 2) || !aligned(s_out, 2)) return fail(EXL3_EINVAL, "%srout/s_out: not 2-byte aligned", who);
+  (void)IC;
+  return EXL3_OK;
+}
+
+bool use_gemv(int64_t M, unsigned flags) {
+  if (flags & EXL3_FORCE_GEMV) return true;
+  if (flags & EXL3_FORCE_MFMA) return false;
+  (void)M;
+  return true;   // the decode-phase kernel serves every M until the prefill kernel takes over large M
+}
+
+struct Layout {
+  size_t xh_off, xh_bytes;   // rotated activations (one region per distinct s_in/rin pair)
+  size_t slab_off, slab_bytes;
+  size_t total;
+};
+
+// Split-K slab a shard needs: the largest S * rows * OC over the row chunks run_gemv_shard launches
+// (a short last chunk may use more splits than a full one).
+size_t slab_bytes_for(int64_t M, int64_t IC, int64_t OC) {
+  if (M <= 0) return 0;
+  const int64_t chunk = gemv_chunk_rows(M, OC);
+  const int64_t first = M < chunk ? M : chunk;                 // every full chunk has this plan
+  const int64_t last = M - (M - 1) / chunk * chunk;            // rows of the final chunk (1 .. chunk)
+  size_t need = 0;
+  for (int64_t rows : {first, last}) {
+    const GemvPlan pl = plan_gemv(rows, IC, OC);
+    const size_t b = size_t(pl.S) * size_t(rows) * size_t(OC) * sizeof(float);
+    need = b > need ? b : need;
+  }
+  return need;
+}
+
+Layout layout_for(int64_t M, int64_t IC, size_t slab_bytes, int n_xh, unsigned flags) {
+  Layout L;
+  L.xh_off = align_up(kCounterBytes);
+  L.xh_bytes = align_up(size_t((M + 15) / 16 * 16) * size_t(IC) * 2);   // padded to whole 16-row blocks
+  L.slab_off = L.xh_off + L.xh_bytes * n_xh;
+  L.slab_bytes = use_gemv(M, flags) ? align_up(slab_bytes) : 0;
+  L.total = L.slab_off + L.slab_bytes;
+  return L;
+}
+
+size_t multi_slab_bytes(int64_t M, int64_t IC, int n_shards, const exl3_shard* shards) {
+  size_t need = 0;
+  for (int i = 0; i < n_shards; ++i) {
+    const size_t b = shards[i].OC > 0 ? slab_bytes_for(M, IC, shards[i].OC) : 0;
+    need = b > need ? b : need;
+  }
+  return need;
+}
+
+int check_workspace(const Layout& L, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(EXL3_EWORKSPACE, "ws: null (need %zu bytes)", L.total);
+  if (!aligned(ws, kAlign)) return fail(EXL3_EINVAL, "ws: not %zu-byte aligned", kAlign);
+  if (ws_bytes < L.total) return fail(EXL3_EWORKSPACE, "ws_bytes: %zu < required %zu", ws_bytes, L.total);
+  return EXL3_OK;
+}
+
+// One shard through the decode-phase kernel, in row chunks bounded by the counter slots.
+int run_gemv_shard(void* out, int64_t ldo, int64_t col0, const uint16_t* xh, int64_t M, int64_t IC,
+                   const int16_t* code, int64_t OC, int K, const void* rout, const void* s_out, char* ws,
+                   const Layout& L, hipStream_t stream) {
+  const int64_t chunk = gemv_chunk_rows(M, OC);
+  for (int64_t r0 = 0; r0 < M; r0 += chunk) {
+    const int64_t rows = (M - r0) < chunk ? (M - r0) : chunk;
+    const GemvPlan pl = plan_gemv(rows, IC, OC);
+    hipError_t e = launch_gemv(pl, xh + r0 * IC, code, K, rout, s_out, reinterpret_cast<float*>(ws + L.slab_off),
+                               reinterpret_cast<int*>(ws), static_cast<uint16_t*>(out) + r0 * ldo, ldo, col0, rows,
+                               IC, OC, stream);
+    if (int rc = launch_status(e, "exl3_linear_into")) return rc;
+  }
+  return EXL3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* exl3_last_error(void) { return g_error.c_str(); }
+
+int exl3_version(void) { return 100; }
+
+int64_t exl3_gemv_max_rows(void) { return kGemvMaxRows; }
+
+size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned flags) {
+  if (M <= 0 || IC <= 0 || OC <= 0) return align_up(kCounterBytes);
+  return layout_for(M, IC, slab_bytes_for(M, IC, OC), 1, flags).total;
+}
+
+int exl3_linear_into(void* out, int64_t ldo, int64_t col0, const void* x, int64_t M, int64_t IC,
+                     const int16_t* code, int64_t OC, int K, const void* s_in, const void* rin, const void* rout,
+                     const void* s_out, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+  if (int rc = check_flags(flags)) return rc;
+  if (int rc = check_dims(M, IC)) return rc;
+  if (int rc = check_shard("", IC, code, OC, K, col0, ldo, s_in, rin, rout, s_out)) return rc;
+  if (M == 0) return ok();
+  if (!out || !aligned(out, 16)) return fail(EXL3_EINVAL, "out: null or not 16-byte aligned");
+  if (!x || !aligned(x, 16)) return fail(EXL3_EINVAL, "x: null or not 16-byte aligned");
+  const Layout L = layout_for(M, IC, slab_bytes_for(M, IC, OC), 1, flags);
+  if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  uint16_t* xh = reinterpret_cast<uint16_t*>(w + L.xh_off);
+  if (int rc = launch_status(launch_prepass_f16(x, s_in, rin, xh, M, IC, true, st, (M + 15) / 16 * 16), "exl3_linear_into")) return rc;
+  if (int rc = run_gemv_shard(out, ldo, col0, xh, M, IC, code, OC, K, rout, s_out, w, L, st)) return rc;
+  return ok();
+}
+
+size_t exl3_linear_multi_workspace_bytes(int64_t M, int64_t IC, int n_shards, const exl3_shard* shards,
+                                         unsigned flags) {
+  if (M <= 0 || IC <= 0 || n_shards <= 0 || !shards) return align_up(kCounterBytes);
+  return layout_for(M, IC, multi_slab_bytes(M, IC, n_shards, shards), n_shards, flags).total;
+}
+
+int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n_shards,
+                           const exl3_shard* shards, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+  if (int rc = check_flags(flags)) return rc;
+  if (int rc = check_dims(M, IC)) return rc;
+  if (n_shards < 1 || n_shards > 16) return fail(EXL3_EINVAL, "n_shards: %d is outside 1..16", n_shards);
+  if (!shards) return fail(EXL3_EINVAL, "shards: null");
+  for (int i = 0; i < n_shards; ++i) {
+    const exl3_shard& s = shards[i];
+    char who[32];
+    snprintf(who, sizeof who, "shards[%d].", i);
+    if (int rc = check_shard(who, IC, s.code, s.OC, s.K, s.col0, ldo, s.s_in, s.rin, s.rout, s.s_out)) return rc;
+  }
+  if (M == 0) return ok();
+  if (!out || !aligned(out, 16)) return fail(EXL3_EINVAL, "out: null or not 16-byte aligned");
+  if (!x || !aligned(x, 16)) return fail(EXL3_EINVAL, "x: null or not 16-byte aligned");
+  const Layout L = layout_for(M, IC, multi_slab_bytes(M, IC, n_shards, shards), n_shards, flags);
+  if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  // one rotated copy of x per distinct (s_in, rin) pair
+  const void* seen_s[16];
+  const void* seen_r[16];
+  int n_seen = 0;
+  for (int i = 0; i < n_shards; ++i) {
+    const exl3_shard& s = shards[i];
+    int slot = -1;
+    for (int j = 0; j < n_seen; ++j)
+      if (seen_s[j] == s.s_in && seen_r[j] == s.rin) slot = j;
+    uint16_t* xh;
+    if (slot < 0) {
+      slot = n_seen++;
+      seen_s[slot] = s.s_in;
+      seen_r[slot] = s.rin;
+      xh = reinterpret_cast<uint16_t*>(w + L.xh_off + L.xh_bytes * slot);
+      if (int rc = launch_status(launch_prepass_f16(x, s.s_in, s.rin, xh, M, IC, true, st, (M + 15) / 16 * 16),
+                                   "exl3_linear_multi_into"))
+        return rc;
+    } else {
+      xh = reinterpret_cast<uint16_t*>(w + L.xh_off + L.xh_bytes * slot);
+    }
+    if (int rc = run_gemv_shard(out, ldo, s.col0, xh, M, IC, s.code, s.OC, s.K, s.rout, s.s_out, w, L, st)) return rc;
+  }
+  return ok();
+}
+
+size_t exl3_moe_workspace_bytes(const exl3_bank* bank, int64_t T, int topk, unsigned flags) {
+  (void)bank; (void)T; (void)topk; (void)flags;
+  return align_up(kCounterBytes);
+}
+
+int exl3_moe_bank_forward(void* out, const void* x, int64_t T, const int32_t* topk_ids, const float* topk_w, int topk,
+                          const exl3_bank* bank, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+  (void)out; (void)x; (void)T; (void)topk_ids; (void)topk_w; (void)topk; (void)bank; (void)flags; (void)ws;
+  (void)ws_bytes; (void)stream;
+  return fail(EXL3_EUNSUPPORTED, "exl3_moe_bank_forward: not available in this build");
+}
+
+int exl3_decode_tiles(void* w_out, const int16_t* code, int64_t IC, int64_t OC, int K, void* stream) {
+  if (IC <= 0 || IC % 16 || OC <= 0 || OC % 16)
+    return fail(EXL3_EINVAL, "IC/OC: %lld x %lld are not positive multiples of 16", (long long)IC, (long long)OC);
+  if (K < 1 || K > 8) return fail(EXL3_EINVAL, "K: %d is outside 1..8", K);
+  if (!w_out || !code) return fail(EXL3_EINVAL, "w_out/code: null");
+  if (!aligned(code, 16)) return fail(EXL3_EINVAL, "code: not 16-byte aligned");
+  if (!aligned(w_out, 2)) return fail(EXL3_EINVAL, "w_out: not 2-byte aligned");
+  if (int rc = launch_status(launch_decode_tiles(w_out, code, IC, OC, K, static_cast<hipStream_t>(stream)),
+                             "exl3_decode_tiles"))
+    return rc;
+  return ok();
+}
+
+int exl3_rotate_activations(void* q_out, float* scale_out, const void* x, int64_t M, int64_t IC, const void* s_in,
+                            const void* rin, unsigned flags, void* stream) {
+  if (flags & ~unsigned(EXL3_ACT_INT8)) return fail(EXL3_EINVAL, "flags: only EXL3_ACT_INT8 is meaningful here");
+  if (int rc = check_dims(M, IC)) return rc;
+  if (M == 0) return ok();
+  if (!q_out || !x || !s_in || !rin) return fail(EXL3_EINVAL, "q_out/x/s_in/rin: null");
+  if (!aligned(x, 16) || !aligned(q_out, 16)) return fail(EXL3_EINVAL, "x/q_out: not 16-byte aligned");
+  if (!aligned(s_in, 4) || !aligned(rin, 4)) return fail(EXL3_EINVAL, "s_in/rin: not 4-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (flags & EXL3_ACT_INT8) {
+    if (!scale_out) return fail(EXL3_EINVAL, "scale_out: null");
+    e = launch_prepass_i8(x, s_in, rin, q_out, scale_out, M, IC, false, st);
+  } else {
+    e = launch_prepass_f16(x, s_in, rin, q_out, M, IC, false, st);
+  }
+  if (int rc = launch_status(e, "exl3_rotate_activations")) return rc;
+  return ok();
+}
+
+}  // extern "C"

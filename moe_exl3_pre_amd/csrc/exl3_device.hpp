@@ -1,0 +1,181 @@
+// Device-side building blocks shared by every EXL3 kernel on gfx950 (CDNA4, wave64).
+//
+//  * the trellis column decode: one lane turns the words of one 16x16 tile column into the 16 fp16
+//    weights of that column, packed two per register in the MFMA operand order used everywhere;
+//  * the wave-wide Hadamard-128 (two features per lane);
+//  * small conversions (bf16/fp16) and the MFMA wrappers.
+//
+// Trellis layout ("radiance_escha.py", `_TILE = 16`: code is [IC/16, OC/16, 16K]; the kernels see the
+// words as little-endian uint32, `process_weights_after_loading`).  In a tile, state i is the 16-bit
+// window at stream bit i*K (circular), and lands on in-tile row i % 16 (input feature) and column i / 16
+// (output feature).  Column c therefore owns states 16c .. 16c+15, i.e. stream bits [16cK, 16cK + 15K + 16).
+//
+// Operand order.  A 16x16x32 fp16 MFMA takes 8 k-values per lane.  A lane that decodes tile column c
+// produces the 16 k-values (tile rows 0..15) of that column as 8 registers; register p holds
+// (row p, row p + 8) in its (low, high) halves.  Registers 0..3 feed one MFMA and 4..7 the next, so the
+// k-slots of the two MFMAs visit the tile rows in the order
+//     PERM16 = [0, 8, 1, 9, 2, 10, 3, 11 | 4, 12, 5, 13, 6, 14, 7, 15].
+// The activation pre-pass stores the rotated activations in that order inside every 16-feature group,
+// so A fragments are plain 16-byte loads.  A reduction over k does not care about the order, and the
+// same order is used for every K.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exl3 {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHad = 128;    // "radiance_escha.py" `_HAD`
+constexpr int kTile = 16;    // "radiance_escha.py" `_TILE`
+constexpr float kInvSqrt128 = 0.08838834764831845f;
+// Buffer resource word 3 for raw (untyped) dword loads on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
+
+// Position of tile row r inside the permuted 16-group (inverse of PERM16).
+__host__ __device__ constexpr int perm16_pos(int r) { return r < 8 ? 2 * r : 2 * (r - 8) + 1; }
+
+template <int K>
+struct Geom {
+  static_assert(K >= 1 && K <= 8, "K must be 1..8");
+  static constexpr int kWords = 8 * K;                                   // uint32 words per tile
+  static constexpr int kSpan = 15 * K + 16;                              // bits a column needs
+  static constexpr int kNW = (((K & 1) ? 16 : 0) + kSpan + 31) / 32;      // words loaded per column
+  static constexpr int kNR = (kSpan + 31) / 32;                          // words after realignment
+};
+
+// Word offsets (within a tile) a lane must load for tile column c, and the column's bit shift in the
+// first of them (0, or 16 for odd c when K is odd).
+template <int K>
+__device__ __forceinline__ void column_word_offsets(int c, int (&woff)[Geom<K>::kNW], int& shift) {
+  const int w0 = (c * K) >> 1;
+  shift = (K & 1) ? ((c & 1) << 4) : 0;
+#pragma unroll
+  for (int j = 0; j < Geom<K>::kNW; ++j) {
+    int w = w0 + j;
+    woff[j] = w >= Geom<K>::kWords ? w - Geom<K>::kWords : w;   // tail-biting wrap
+  }
+}
+
+// Bits [o, o+16) of the realigned column stream r (valid in the low 16 bits of the result).
+template <int K, int O>
+__device__ __forceinline__ uint32_t window16(const uint32_t (&r)[Geom<K>::kNR]) {
+  constexpr int q = O >> 5, sh = O & 31;
+  if constexpr (sh == 0) {
+    return r[q];
+  } else if constexpr (sh <= 16) {
+    return r[q] >> sh;
+  } else {
+    return __builtin_amdgcn_alignbit(r[q + 1], r[q], sh);
+  }
+}
+
+// Constants of the codebook held in registers.  gfx9 VOP3 encodings cannot carry literals, so with
+// literal operands the compiler splits the mask-and-or into two instructions; opaque register values
+// let it select a single v_and_or_b32.
+struct CodebookRegs {
+  uint32_t mask;   // 0x8F808F80 (scalar register)
+  uint32_t bias;   // 0x30003000 (vector register)
+};
+
+__device__ __forceinline__ CodebookRegs codebook_regs() {
+  CodebookRegs c;
+  asm("s_mov_b32 %0, 0x8f808f80" : "=s"(c.mask));
+  asm("v_mov_b32 %0, 0x30003000" : "=v"(c.bias));
+  return c;
+}
+
+// State -> fp16 bit pattern for two states at once:  ((s * 0x9E37) mod 2^16) & 0x8F80 | 0x3000.
+__device__ __forceinline__ uint32_t codebook2(uint32_t states, const CodebookRegs& c) {
+  u16x2 s = __builtin_bit_cast(u16x2, states);
+  s = s * (u16x2){0x9E37, 0x9E37};
+  return (__builtin_bit_cast(uint32_t, s) & c.mask) | c.bias;
+}
+
+template <int K, int P>
+__device__ __forceinline__ uint32_t decode_pair(const uint32_t (&r)[Geom<K>::kNR], const CodebookRegs& c) {
+  if constexpr (K == 2) {
+    // state p at bit 2p, state p+8 at bit 2p+16: one 32-bit window holds both.
+    return codebook2(P == 0 ? r[0] : __builtin_amdgcn_alignbit(r[1], r[0], 2 * P), c);
+  } else {
+    const uint32_t lo = window16<K, P * K>(r);
+    const uint32_t hi = window16<K, (P + 8) * K>(r);
+    return codebook2((lo & 0xFFFFu) | (hi << 16), c);
+  }
+}
+
+// Decode one tile column from the words loaded at column_word_offsets: out[p] = (row p, row p+8).
+template <int K>
+__device__ __forceinline__ void decode_column(const uint32_t (&w)[Geom<K>::kNW], int shift, uint32_t (&out)[8],
+                                              const CodebookRegs& c) {
+  uint32_t r[Geom<K>::kNR];
+  if constexpr (K & 1) {
+#pragma unroll
+    for (int j = 0; j < Geom<K>::kNR; ++j) r[j] = __builtin_amdgcn_alignbit(w[j + 1], w[j], shift);
+  } else {
+#pragma unroll
+    for (int j = 0; j < Geom<K>::kNR; ++j) r[j] = w[j];
+  }
+  out[0] = decode_pair<K, 0>(r, c);
+  out[1] = decode_pair<K, 1>(r, c);
+  out[2] = decode_pair<K, 2>(r, c);
+  out[3] = decode_pair<K, 3>(r, c);
+  out[4] = decode_pair<K, 4>(r, c);
+  out[5] = decode_pair<K, 5>(r, c);
+  out[6] = decode_pair<K, 6>(r, c);
+  out[7] = decode_pair<K, 7>(r, c);
+}
+
+__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(half8, v);
+}
+
+__device__ __forceinline__ float4v mfma16(half8 a, half8 b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Conversions
+// ---------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {   // round to nearest even; NaN stays NaN
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {   // round to nearest even
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Wave-wide orthonormal Hadamard-128: lane l holds features 2l (v0) and 2l+1 (v1) of one 128-block.
+// Radix-2 butterflies in natural (Sylvester) order; the lower index of each pair takes a + b, the upper
+// a - b.  The 1/sqrt(128) normalisation is applied by the caller.
+// ---------------------------------------------------------------------------------------------------
+__device__ __forceinline__ void had128_wave(float& v0, float& v1, int lane) {
+  float a = v0 + v1, b = v0 - v1;
+  v0 = a;
+  v1 = b;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float p0 = __shfl_xor(v0, d, 64);
+    const float p1 = __shfl_xor(v1, d, 64);
+    const bool upper = (lane & d) != 0;
+    v0 = upper ? p0 - v0 : v0 + p0;
+    v1 = upper ? p1 - v1 : v1 + p1;
+  }
+}
+
+}  // namespace exl3

@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and rejects bad
+arguments before launching anything.  No call here reaches a kernel (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_exl3_pre_amd import exl3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "exl3.h")
+
+FAKE = 0x10000           # 64 KiB-aligned fake device address: never dereferenced by host validation
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(exl3_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = exl3.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(declared) == sorted(exl3.exported_symbols())
+
+
+def test_version_and_limits():
+    L = exl3.lib()
+    assert L.exl3_version() >= 100
+    assert L.exl3_gemv_max_rows() >= 8
+
+
+def _linear(**kw):
+    a = dict(out=FAKE, ldo=512, col0=0, x=FAKE, M=4, IC=512, code=FAKE, OC=512, K=3, s_in=FAKE, rin=FAKE, rout=FAKE,
+             s_out=FAKE, flags=0, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return exl3.lib().exl3_linear_into(a["out"], a["ldo"], a["col0"], a["x"], a["M"], a["IC"], a["code"], a["OC"],
+                                       a["K"], a["s_in"], a["rin"], a["rout"], a["s_out"], a["flags"], a["ws"],
+                                       a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(IC=500), exl3.EINVAL, "IC"),
+    (dict(IC=0), exl3.EINVAL, "IC"),
+    (dict(OC=300), exl3.EINVAL, "OC"),
+    (dict(K=0), exl3.EINVAL, "K"),
+    (dict(K=9), exl3.EINVAL, "K"),
+    (dict(col0=100), exl3.EINVAL, "col0"),
+    (dict(col0=-1), exl3.EINVAL, "col0"),
+    (dict(M=-1), exl3.EINVAL, "M"),
+    (dict(code=None), exl3.EINVAL, "code"),
+    (dict(code=FAKE + 2), exl3.EINVAL, "code"),
+    (dict(s_in=None), exl3.EINVAL, "s_in"),
+    (dict(rin=FAKE + 2), exl3.EINVAL, "rin"),
+    (dict(rout=None), exl3.EINVAL, "rout"),
+    (dict(x=None), exl3.EINVAL, "x"),
+    (dict(x=FAKE + 4), exl3.EINVAL, "x"),
+    (dict(out=None), exl3.EINVAL, "out"),
+    (dict(flags=1 << 7), exl3.EINVAL, "flags"),
+    (dict(flags=exl3.FORCE_GEMV | exl3.FORCE_MFMA), exl3.EINVAL, "flags"),
+    (dict(ws=None), exl3.EWORKSPACE, "ws"),
+    (dict(ws=FAKE, ws_bytes=1024), exl3.EWORKSPACE, "ws_bytes"),
+    (dict(ws=FAKE + 16, ws_bytes=1 << 30), exl3.EINVAL, "ws"),
+])
+def test_linear_rejects_before_launch(kw, code, needle):
+    rc = _linear(**kw)
+    assert rc == code, (rc, exl3.last_error())
+    assert needle in exl3.last_error()
+
+
+def test_linear_zero_rows_is_a_noop():
+    assert _linear(M=0, out=None, x=None) == exl3.OK
+    assert exl3.last_error() == ""
+
+
+def test_workspace_sizes_are_monotone_in_m():
+    sizes = [exl3.linear_workspace_bytes(M, 4096, 14336) for M in (1, 8, 16, 64)]
+    assert all(s % 256 == 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    assert exl3.linear_workspace_bytes(0, 4096, 14336) >= 16384
+
+
+def test_multi_rejects_bad_shard():
+    sh = (exl3.Shard * 2)()
+    sh[0] = exl3.Shard(FAKE, 256, 2, 0, 0, FAKE, FAKE, FAKE, FAKE)
+    sh[1] = exl3.Shard(FAKE, 256, 3, 0, 200, FAKE, FAKE, FAKE, FAKE)      # overlaps past ldo=400
+    rc = exl3.lib().exl3_linear_multi_into(FAKE, 400, FAKE, 4, 512, 2, sh, 0, None, 0, None)
+    assert rc == exl3.EINVAL and "shards[1].col0" in exl3.last_error()
+    rc = exl3.lib().exl3_linear_multi_into(FAKE, 512, FAKE, 4, 512, 0, sh, 0, None, 0, None)
+    assert rc == exl3.EINVAL and "n_shards" in exl3.last_error()
+
+
+def test_decode_tiles_rejects():
+    L = exl3.lib()
+    assert L.exl3_decode_tiles(FAKE, FAKE, 100, 32, 2, None) == exl3.EINVAL
+    assert L.exl3_decode_tiles(FAKE, FAKE, 32, 32, 0, None) == exl3.EINVAL
+    assert L.exl3_decode_tiles(FAKE, FAKE + 8, 32, 32, 2, None) == exl3.EINVAL
+
+
+def test_rotate_rejects():
+    L = exl3.lib()
+    assert L.exl3_rotate_activations(FAKE, None, FAKE, 4, 100, FAKE, FAKE, 0, None) == exl3.EINVAL
+    assert L.exl3_rotate_activations(FAKE, None, FAKE, 4, 128, FAKE, FAKE, exl3.ACT_INT8, None) == exl3.EINVAL
+    assert L.exl3_rotate_activations(FAKE, None, FAKE, 0, 128, FAKE, FAKE, 0, None) == exl3.OK
