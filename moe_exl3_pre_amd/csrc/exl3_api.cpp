@@ -39,7 +39,7 @@ int launch_status(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr unsigned kKnownFlags = EXL3_ACT_INT8 | EXL3_FORCE_GEMV | EXL3_FORCE_MFMA;
-constexpr int64_t kGemvMaxRows = 16;
+constexpr int64_t kGemvMaxRows = kDecodeMaxRows;
 
 int check_flags(unsigned flags) {
   if (flags & ~kKnownFlags) return fail(EXL3_EINVAL, "flags: unknown bits 0x%x", flags & ~kKnownFlags);
@@ -79,52 +79,48 @@ int check_shard(const char* who, int64_t IC, const int16_t* code, int64_t OC, in
   return EXL3_OK;
 }
 
-bool use_gemv(int64_t M, unsigned flags) {
+bool use_decode_path(int64_t M, unsigned flags) {
   if (flags & EXL3_FORCE_GEMV) return true;
   if (flags & EXL3_FORCE_MFMA) return false;
   (void)M;
   return true;   // the decode-phase kernel serves every M until the prefill kernel takes over large M
 }
 
+// Row chunks the decode-phase path launches: full chunks of kDecodeMaxRows rows, then the remainder.
+int64_t first_chunk(int64_t M) { return M < kDecodeMaxRows ? M : kDecodeMaxRows; }
+int64_t last_chunk(int64_t M) { return M - (M - 1) / kDecodeMaxRows * kDecodeMaxRows; }
+
+// Slab bytes the decode-phase path needs for these shards (mixes the kernels do not cover run one
+// launch per shard); false if some chunk cannot be planned.
+bool decode_slab_bytes(int64_t M, int64_t IC, int n, const DecShardIn* in, size_t* need) {
+  *need = 0;
+  for (int64_t rows : {first_chunk(M), last_chunk(M)}) {
+    DecPlan pl;
+    if (!plan_decode(rows, IC, n, in, &pl)) return false;
+    if (pl.kset < 0) {
+      for (int i = 0; i < n; ++i) {
+        DecPlan p1;
+        if (!plan_decode(rows, IC, 1, in + i, &p1)) return false;
+        *need = p1.slab_bytes > *need ? p1.slab_bytes : *need;
+      }
+    } else {
+      *need = pl.slab_bytes > *need ? pl.slab_bytes : *need;
+    }
+  }
+  return true;
+}
+
 struct Layout {
-  size_t xh_off, xh_bytes;   // rotated activations (one region per distinct s_in/rin pair)
   size_t slab_off, slab_bytes;
   size_t total;
 };
 
-// Split-K slab a shard needs: the largest S * rows * OC over the row chunks run_gemv_shard launches
-// (a short last chunk may use more splits than a full one).
-size_t slab_bytes_for(int64_t M, int64_t IC, int64_t OC) {
-  if (M <= 0) return 0;
-  const int64_t chunk = gemv_chunk_rows(M, OC);
-  const int64_t first = M < chunk ? M : chunk;                 // every full chunk has this plan
-  const int64_t last = M - (M - 1) / chunk * chunk;            // rows of the final chunk (1 .. chunk)
-  size_t need = 0;
-  for (int64_t rows : {first, last}) {
-    const GemvPlan pl = plan_gemv(rows, IC, OC);
-    const size_t b = size_t(pl.S) * size_t(rows) * size_t(OC) * sizeof(float);
-    need = b > need ? b : need;
-  }
-  return need;
-}
-
-Layout layout_for(int64_t M, int64_t IC, size_t slab_bytes, int n_xh, unsigned flags) {
+Layout layout_for(size_t slab_bytes) {
   Layout L;
-  L.xh_off = align_up(kCounterBytes);
-  L.xh_bytes = align_up(size_t((M + 15) / 16 * 16) * size_t(IC) * 2);   // padded to whole 16-row blocks
-  L.slab_off = L.xh_off + L.xh_bytes * n_xh;
-  L.slab_bytes = use_gemv(M, flags) ? align_up(slab_bytes) : 0;
+  L.slab_off = align_up(kCounterBytes);
+  L.slab_bytes = align_up(slab_bytes);
   L.total = L.slab_off + L.slab_bytes;
   return L;
-}
-
-size_t multi_slab_bytes(int64_t M, int64_t IC, int n_shards, const exl3_shard* shards) {
-  size_t need = 0;
-  for (int i = 0; i < n_shards; ++i) {
-    const size_t b = shards[i].OC > 0 ? slab_bytes_for(M, IC, shards[i].OC) : 0;
-    need = b > need ? b : need;
-  }
-  return need;
 }
 
 int check_workspace(const Layout& L, void* ws, size_t ws_bytes) {
@@ -134,20 +130,44 @@ int check_workspace(const Layout& L, void* ws, size_t ws_bytes) {
   return EXL3_OK;
 }
 
-// One shard through the decode-phase kernel, in row chunks bounded by the counter slots.
-int run_gemv_shard(void* out, int64_t ldo, int64_t col0, const uint16_t* xh, int64_t M, int64_t IC,
-                   const int16_t* code, int64_t OC, int K, const void* rout, const void* s_out, char* ws,
-                   const Layout& L, hipStream_t stream) {
-  const int64_t chunk = gemv_chunk_rows(M, OC);
-  for (int64_t r0 = 0; r0 < M; r0 += chunk) {
-    const int64_t rows = (M - r0) < chunk ? (M - r0) : chunk;
-    const GemvPlan pl = plan_gemv(rows, IC, OC);
-    hipError_t e = launch_gemv(pl, xh + r0 * IC, code, K, rout, s_out, reinterpret_cast<float*>(ws + L.slab_off),
-                               reinterpret_cast<int*>(ws), static_cast<uint16_t*>(out) + r0 * ldo, ldo, col0, rows,
-                               IC, OC, stream);
-    if (int rc = launch_status(e, "exl3_linear_into")) return rc;
+// The decode-phase path: one launch per chunk of <= 16 rows covering every shard.
+int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n,
+               const DecShardIn* in, char* ws, const Layout& L, hipStream_t stream) {
+  for (int64_t r0 = 0; r0 < M; r0 += kDecodeMaxRows) {
+    const int64_t rows = (M - r0) < kDecodeMaxRows ? (M - r0) : kDecodeMaxRows;
+    const void* xr = static_cast<const uint16_t*>(x) + r0 * IC;
+    void* orow = static_cast<uint16_t*>(out) + r0 * ldo;
+    DecPlan pl;
+    if (!plan_decode(rows, IC, n, in, &pl)) return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
+    if (pl.kset >= 0) {
+      hipError_t e = launch_decode(pl, xr, rows, IC, n, in, orow, ldo, reinterpret_cast<float*>(ws + L.slab_off),
+                                   reinterpret_cast<int*>(ws), stream);
+      if (int rc = launch_status(e, who)) return rc;
+    } else {
+      for (int i = 0; i < n; ++i) {
+        DecPlan p1;
+        if (!plan_decode(rows, IC, 1, in + i, &p1)) return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
+        hipError_t e = launch_decode(p1, xr, rows, IC, 1, in + i, orow, ldo,
+                                     reinterpret_cast<float*>(ws + L.slab_off), reinterpret_cast<int*>(ws), stream);
+        if (int rc = launch_status(e, who)) return rc;
+      }
+    }
   }
   return EXL3_OK;
+}
+
+DecShardIn shard_in(const int16_t* code, int64_t OC, int K, int64_t col0, const void* s_in, const void* rin,
+                    const void* rout, const void* s_out) {
+  DecShardIn d;
+  d.code = code;
+  d.OC = OC;
+  d.K = K;
+  d.col0 = col0;
+  d.s_in = s_in;
+  d.rin = rin;
+  d.rout = rout;
+  d.s_out = s_out;
+  return d;
 }
 
 }  // namespace
@@ -161,8 +181,13 @@ int exl3_version(void) { return 100; }
 int64_t exl3_gemv_max_rows(void) { return kGemvMaxRows; }
 
 size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned flags) {
-  if (M <= 0 || IC <= 0 || OC <= 0) return align_up(kCounterBytes);
-  return layout_for(M, IC, slab_bytes_for(M, IC, OC), 1, flags).total;
+  if (M <= 0 || IC <= 0 || OC <= 0 || IC % 128 || OC % 128) return align_up(kCounterBytes);
+  size_t slab = 0;
+  if (use_decode_path(M, flags)) {
+    const DecShardIn in = shard_in(nullptr, OC, 2, 0, nullptr, nullptr, nullptr, nullptr);
+    if (!decode_slab_bytes(M, IC, 1, &in, &slab)) slab = 0;
+  }
+  return layout_for(slab).total;
 }
 
 int exl3_linear_into(void* out, int64_t ldo, int64_t col0, const void* x, int64_t M, int64_t IC,
@@ -174,64 +199,54 @@ int exl3_linear_into(void* out, int64_t ldo, int64_t col0, const void* x, int64_
   if (M == 0) return ok();
   if (!out || !aligned(out, 16)) return fail(EXL3_EINVAL, "out: null or not 16-byte aligned");
   if (!x || !aligned(x, 16)) return fail(EXL3_EINVAL, "x: null or not 16-byte aligned");
-  const Layout L = layout_for(M, IC, slab_bytes_for(M, IC, OC), 1, flags);
+  const DecShardIn in = shard_in(code, OC, K, col0, s_in, rin, rout, s_out);
+  size_t slab = 0;
+  if (!decode_slab_bytes(M, IC, 1, &in, &slab)) return fail(EXL3_EUNSUPPORTED, "exl3_linear_into: no plan");
+  const Layout L = layout_for(slab);
   if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-  uint16_t* xh = reinterpret_cast<uint16_t*>(w + L.xh_off);
-  if (int rc = launch_status(launch_prepass_f16(x, s_in, rin, xh, M, IC, true, st, (M + 15) / 16 * 16), "exl3_linear_into")) return rc;
-  if (int rc = run_gemv_shard(out, ldo, col0, xh, M, IC, code, OC, K, rout, s_out, w, L, st)) return rc;
+  if (int rc = run_decode("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L,
+                          static_cast<hipStream_t>(stream)))
+    return rc;
   return ok();
 }
 
 size_t exl3_linear_multi_workspace_bytes(int64_t M, int64_t IC, int n_shards, const exl3_shard* shards,
                                          unsigned flags) {
-  if (M <= 0 || IC <= 0 || n_shards <= 0 || !shards) return align_up(kCounterBytes);
-  return layout_for(M, IC, multi_slab_bytes(M, IC, n_shards, shards), n_shards, flags).total;
+  if (M <= 0 || IC <= 0 || IC % 128 || n_shards <= 0 || n_shards > kMaxShards || !shards) return align_up(kCounterBytes);
+  DecShardIn in[kMaxShards];
+  for (int i = 0; i < n_shards; ++i) {
+    if (shards[i].OC <= 0 || shards[i].OC % 128) return align_up(kCounterBytes);
+    in[i] = shard_in(nullptr, shards[i].OC, shards[i].K, 0, nullptr, nullptr, nullptr, nullptr);
+  }
+  size_t slab = 0;
+  if (use_decode_path(M, flags) && !decode_slab_bytes(M, IC, n_shards, in, &slab)) slab = 0;
+  return layout_for(slab).total;
 }
 
 int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n_shards,
                            const exl3_shard* shards, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
   if (int rc = check_flags(flags)) return rc;
   if (int rc = check_dims(M, IC)) return rc;
-  if (n_shards < 1 || n_shards > 16) return fail(EXL3_EINVAL, "n_shards: %d is outside 1..16", n_shards);
+  if (n_shards < 1 || n_shards > kMaxShards) return fail(EXL3_EINVAL, "n_shards: %d is outside 1..16", n_shards);
   if (!shards) return fail(EXL3_EINVAL, "shards: null");
+  DecShardIn in[kMaxShards];
   for (int i = 0; i < n_shards; ++i) {
     const exl3_shard& s = shards[i];
     char who[32];
     snprintf(who, sizeof who, "shards[%d].", i);
     if (int rc = check_shard(who, IC, s.code, s.OC, s.K, s.col0, ldo, s.s_in, s.rin, s.rout, s.s_out)) return rc;
+    in[i] = shard_in(s.code, s.OC, s.K, s.col0, s.s_in, s.rin, s.rout, s.s_out);
   }
   if (M == 0) return ok();
   if (!out || !aligned(out, 16)) return fail(EXL3_EINVAL, "out: null or not 16-byte aligned");
   if (!x || !aligned(x, 16)) return fail(EXL3_EINVAL, "x: null or not 16-byte aligned");
-  const Layout L = layout_for(M, IC, multi_slab_bytes(M, IC, n_shards, shards), n_shards, flags);
+  size_t slab = 0;
+  if (!decode_slab_bytes(M, IC, n_shards, in, &slab)) return fail(EXL3_EUNSUPPORTED, "exl3_linear_multi_into: no plan");
+  const Layout L = layout_for(slab);
   if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-  // one rotated copy of x per distinct (s_in, rin) pair
-  const void* seen_s[16];
-  const void* seen_r[16];
-  int n_seen = 0;
-  for (int i = 0; i < n_shards; ++i) {
-    const exl3_shard& s = shards[i];
-    int slot = -1;
-    for (int j = 0; j < n_seen; ++j)
-      if (seen_s[j] == s.s_in && seen_r[j] == s.rin) slot = j;
-    uint16_t* xh;
-    if (slot < 0) {
-      slot = n_seen++;
-      seen_s[slot] = s.s_in;
-      seen_r[slot] = s.rin;
-      xh = reinterpret_cast<uint16_t*>(w + L.xh_off + L.xh_bytes * slot);
-      if (int rc = launch_status(launch_prepass_f16(x, s.s_in, s.rin, xh, M, IC, true, st, (M + 15) / 16 * 16),
-                                   "exl3_linear_multi_into"))
-        return rc;
-    } else {
-      xh = reinterpret_cast<uint16_t*>(w + L.xh_off + L.xh_bytes * slot);
-    }
-    if (int rc = run_gemv_shard(out, ldo, s.col0, xh, M, IC, s.code, s.OC, s.K, s.rout, s.s_out, w, L, st)) return rc;
-  }
+  if (int rc = run_decode("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L,
+                          static_cast<hipStream_t>(stream)))
+    return rc;
   return ok();
 }
 

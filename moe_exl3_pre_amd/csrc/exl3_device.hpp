@@ -107,7 +107,7 @@ __device__ __forceinline__ uint32_t decode_pair(const uint32_t (&r)[Geom<K>::kNR
   } else {
     const uint32_t lo = window16<K, P * K>(r);
     const uint32_t hi = window16<K, (P + 8) * K>(r);
-    return codebook2((lo & 0xFFFFu) | (hi << 16), c);
+    return codebook2(__builtin_amdgcn_perm(hi, lo, 0x05040100u), c);   // lo[15:0] | hi[15:0] << 16
   }
 }
 
@@ -161,21 +161,48 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {   // round to nearest 
 
 // ---------------------------------------------------------------------------------------------------
 // Wave-wide orthonormal Hadamard-128: lane l holds features 2l (v0) and 2l+1 (v1) of one 128-block.
-// Radix-2 butterflies in natural (Sylvester) order; the lower index of each pair takes a + b, the upper
-// a - b.  The 1/sqrt(128) normalisation is applied by the caller.
+// Radix-2 butterflies in natural (Sylvester) order; of each pair the lower feature index takes a + b,
+// the upper a - b.  The 1/sqrt(128) normalisation is applied by the caller.
+// Partners across lanes come from DPP where the row patterns allow it (lane xor 1, 2 directly; xor 4
+// and xor 8 as two mirrors), from ds_swizzle for xor 16 and from ds_bpermute for xor 32.
 // ---------------------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kQuadXor3 = 0x1B;       // quad_perm [3,2,1,0]
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15 - i within each row of 16
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7 - i within each half-row of 8
+
+__device__ __forceinline__ float lane_xor4(float v) { return dpp<kRowHalfMirror>(dpp<kQuadXor3>(v)); }   // ^3 ^7
+__device__ __forceinline__ float lane_xor8(float v) { return dpp<kRowMirror>(dpp<kRowHalfMirror>(v)); }  // ^7 ^15
+__device__ __forceinline__ float lane_xor16(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));  // xor 16 in 32
+}
+
+// butterfly with the partner value p: lower lanes keep v + p, upper lanes p - v
+__device__ __forceinline__ float bfly(float v, float p, bool upper) {
+  return p + __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) ^ (upper ? 0x80000000u : 0u));
+}
+
 __device__ __forceinline__ void had128_wave(float& v0, float& v1, int lane) {
   float a = v0 + v1, b = v0 - v1;
+  v0 = bfly(a, dpp<kQuadXor1>(a), lane & 1);
+  v1 = bfly(b, dpp<kQuadXor1>(b), lane & 1);
+  a = bfly(v0, dpp<kQuadXor2>(v0), lane & 2);
+  b = bfly(v1, dpp<kQuadXor2>(v1), lane & 2);
+  v0 = bfly(a, lane_xor4(a), lane & 4);
+  v1 = bfly(b, lane_xor4(b), lane & 4);
+  a = bfly(v0, lane_xor8(v0), lane & 8);
+  b = bfly(v1, lane_xor8(v1), lane & 8);
+  v0 = bfly(a, lane_xor16(a), lane & 16);
+  v1 = bfly(b, lane_xor16(b), lane & 16);
+  a = bfly(v0, __shfl_xor(v0, 32, 64), lane & 32);
+  b = bfly(v1, __shfl_xor(v1, 32, 64), lane & 32);
   v0 = a;
   v1 = b;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float p0 = __shfl_xor(v0, d, 64);
-    const float p1 = __shfl_xor(v1, d, 64);
-    const bool upper = (lane & d) != 0;
-    v0 = upper ? p0 - v0 : v0 + p0;
-    v1 = upper ? p1 - v1 : v1 + p1;
-  }
 }
 
 }  // namespace exl3

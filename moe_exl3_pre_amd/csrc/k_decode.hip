@@ -1,0 +1,446 @@
+// Decode-phase kernel (M <= 16): the whole layer -- activation pre-pass, trellis decode, contraction,
+// reduction, output Hadamard-128, rout/s_out scales and the bf16 slice write -- in ONE launch that can
+// cover several shards of a merged projection ("radiance_escha.py", `escha_linear_into`: the
+// prefill/decode choice is made inside the op; `apply`: each shard writes its own column slice).
+//
+// At decode M the trellis words are the whole cost, so the kernel is shaped around streaming them once:
+//   * a block of 16 waves owns one 128-column output block of one shard (one Hadamard-128 block, so the
+//     output transform needs no other block) over a range of the input features (usually all of IC);
+//   * the 16 waves split that feature range; every lane streams the words of one tile column through a
+//     small register pipeline (buffer loads, kPipe units in flight), decodes them in registers
+//     (exl3_device.hpp) straight into MFMA B fragments and accumulates [16 rows x 128 cols] in fp32;
+//   * while the first words are in flight the block computes its own slice of the rotated activations
+//     (x * s_in * rin, Hadamard-128, fp16, permuted order) into LDS -- no separate pre-pass launch and no
+//     round trip of the activations through HBM;
+//   * the 16 partial accumulators are summed in LDS in a fixed order (deterministic), then one wave per
+//     row applies the output Hadamard, rout and s_out and writes bf16;
+//   * only when a shard has too few 128-column blocks to fill the chip is its feature range split over
+//     several blocks (S > 1): each writes its partial rows to the split-K slab with agent-coherent
+//     stores, bumps the block counter (agent-scope atomic, no L2-wide fences), and the last one to arrive
+//     finishes the block and resets the counter for the next launch or graph replay.  The slab and the
+//     counters live in the caller's workspace ("radiance_escha.py", `_ensure_scratch`: split-K partial
+//     slab plus block counter, allocated once, never inside the launch).
+#include <utility>
+
+#include "exl3_device.hpp"
+#include "exl3_internal.hpp"
+
+namespace exl3 {
+
+constexpr int kWaves = 16;       // waves per block
+constexpr int kNB = 8;           // tile columns per wave = one 128-column block
+
+struct DecShard {
+  const uint32_t* code;
+  const uint16_t* s_in;
+  const uint16_t* rin;
+  const uint16_t* rout;
+  const uint16_t* s_out;
+  float* slab;                   // [S, M, OC] fp32 (S > 1 only)
+  int* counters;                 // [OC / 128] (S > 1 only)
+  int64_t col0;
+  uint32_t code_bytes;
+  int OC, K, S, wg_begin;
+};
+
+struct DecArgs {
+  const uint16_t* x;             // bf16 [M, IC]
+  uint16_t* out;                 // bf16 [M, ldo]
+  int64_t ldo;
+  int M, IC, n_shards, lds_row;  // lds_row: halves per activation row in LDS (padded)
+  DecShard sh[kMaxShards];
+};
+
+template <int K, int SPW, int MR>
+__device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& sh, int local, char* lds) {
+  using G = Geom<K>;
+  constexpr int kPipe = G::kNW <= 2 ? 16 : (36 / G::kNW);            // units in flight per wave
+  constexpr int kUnits = SPW * kNB;                                 // (step, tile column) units per wave
+  constexpr int kPB = SPW > 1 ? SPW / 2 : 1;                        // Hadamard blocks per wave (pre-pass)
+  static_assert(SPW % 2 == 0, "steps come in Hadamard-block pairs");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int M = a.M;
+  const int nblk = sh.OC / kHad;
+  const int blk = local % nblk, s = local / nblk;
+  const int B = a.IC / kHad;
+  const int ba = s * B / sh.S, bb = (s + 1) * B / sh.S;     // Hadamard blocks of this block's k-range
+  const int nb = bb - ba;
+  // Each wave owns whole Hadamard blocks [hb0, hb1) of that range (two 64-feature steps each): it
+  // rotates their activations itself, so no wave waits for another before its main loop.
+  const int hb0 = (nb * wave) / kWaves, hb1 = (nb * (wave + 1)) / kWaves;
+  const int w_s0 = 2 * hb0, cnt = 2 * (hb1 - hb0);         // cnt <= SPW (planner)
+  const uint32_t tpr = uint32_t(sh.OC / kTile);
+
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);          // [(M + 1) rows][lds_row] fp16
+  const int lrow = a.lds_row;
+
+  // ---- 1. pre-pass inputs of this wave's Hadamard blocks (issued first: they are needed first).
+  // Unconditional loads with clamped rows and blocks: a load under a branch would make the compiler
+  // wait for the weight stream behind it before the pre-pass can start.
+  uint32_t xv[kPB][MR], sv[kPB], rv[kPB];
+#pragma unroll
+  for (int pb = 0; pb < kPB; ++pb) {
+    const int hb = hb0 + pb < hb1 ? hb0 + pb : (hb1 > hb0 ? hb1 - 1 : 0);
+    const int64_t k = int64_t(ba + hb) * kHad + 2 * lane;
+    sv[pb] = *reinterpret_cast<const uint32_t*>(sh.s_in + k);
+    rv[pb] = *reinterpret_cast<const uint32_t*>(sh.rin + k);
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      xv[pb][m] = *reinterpret_cast<const uint32_t*>(a.x + int64_t(m < M ? m : M - 1) * a.IC + k);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the weight stream
+
+  // ---- 2. the first kPipe units of the weight stream
+  int woff[G::kNW], shift;
+  column_word_offsets<K>(n, woff, shift);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(sh.code), (short)0, (int)sh.code_bytes, kBufferFlags);
+  uint32_t lane_off[G::kNW];
+#pragma unroll
+  for (int w = 0; w < G::kNW; ++w) lane_off[w] = (uint32_t(g) * tpr * G::kWords + uint32_t(woff[w])) * 4u;
+  const uint32_t step_stride = 4u * tpr * G::kWords * 4u;
+  const uint32_t base_blk = uint32_t(blk) * kNB * G::kWords * 4u;
+  uint32_t buf[kPipe][G::kNW];
+  auto load_unit = [&](int u, uint32_t (&dst)[G::kNW]) {
+    const int st = u / kNB, j = u % kNB;
+    // Steps past this wave's count (their results are never used) re-read a step of this block's own
+    // range, so every address stays inside the tensor: the buffer range check covers only the vector
+    // offset, not the scalar one used here.
+    const int step = 2 * ba + (cnt > 0 ? w_s0 + (st < cnt ? st : cnt - 1) : 0);
+    const uint32_t soff = uint32_t(step) * step_stride + base_blk;
+#pragma unroll
+    for (int w = 0; w < G::kNW; ++w)
+      dst[w] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off[w] + uint32_t(j * G::kWords * 4), soff, 0);
+  };
+#pragma unroll
+  for (int u = 0; u < kPipe && u < kUnits; ++u) load_unit(u, buf[u]);
+
+  // ---- 3. this wave's rotated activations into LDS (PERM16 order); its part of row M stays zero
+#pragma unroll
+  for (int pb = 0; pb < kPB; ++pb) {
+    if (hb0 + pb < hb1) {
+      const float s0 = f16_to_f32(sv[pb] & 0xFFFFu), s1 = f16_to_f32(sv[pb] >> 16);
+      const float r0 = f16_to_f32(rv[pb] & 0xFFFFu), r1 = f16_to_f32(rv[pb] >> 16);
+      const int kl = (hb0 + pb) * kHad + 2 * lane;
+      const int p0 = (kl & ~15) | perm16_pos(kl & 15), p1 = (kl & ~15) | perm16_pos((kl + 1) & 15);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        if (m < M) {
+          float v0 = bf16_to_f32(xv[pb][m] & 0xFFFFu) * s0 * r0;
+          float v1 = bf16_to_f32(xv[pb][m] >> 16) * s1 * r1;
+          had128_wave(v0, v1, lane);
+          xs[m * lrow + p0] = f32_to_f16(v0 * kInvSqrt128);
+          xs[m * lrow + p1] = f32_to_f16(v1 * kInvSqrt128);
+        }
+      }
+      *reinterpret_cast<uint32_t*>(xs + M * lrow + kl) = 0u;
+    }
+  }
+
+  // ---- 4. stream, decode, multiply (reads only this wave's own LDS slice: no barrier needed)
+  const CodebookRegs cb = codebook_regs();
+  float4v acc[kNB];
+#pragma unroll
+  for (int j = 0; j < kNB; ++j) acc[j] = (float4v){0.f, 0.f, 0.f, 0.f};
+  const uint16_t* xa = xs + (n < M ? n : M) * lrow + 64 * w_s0 + 16 * g;   // row n, or the zero row
+  half8 a0 = {}, a1 = {};
+#pragma unroll
+  for (int u = 0; u < kUnits; ++u) {
+    const int st = u / kNB, j = u % kNB;
+    if (st < cnt) {
+      if (j == 0) {
+        a0 = *reinterpret_cast<const half8*>(xa + 64 * st);
+        a1 = *reinterpret_cast<const half8*>(xa + 64 * st + 8);
+      }
+      uint32_t b[8];
+      decode_column<K>(buf[u % kPipe], shift, b, cb);
+      acc[j] = mfma16(a0, as_half8(b[0], b[1], b[2], b[3]), acc[j]);
+      acc[j] = mfma16(a1, as_half8(b[4], b[5], b[6], b[7]), acc[j]);
+    }
+    if (u + kPipe < kUnits) load_unit(u + kPipe, buf[u % kPipe]);
+  }
+
+  // ---- 5. sum the 16 waves' partials in LDS (fixed order), one wave per output row
+  __syncthreads();                                          // everyone is done reading xs
+  float* red = reinterpret_cast<float*>(lds);               // [kWaves][M][128]
+#pragma unroll
+  for (int j = 0; j < kNB; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      if (row < M) red[(wave * M + row) * kHad + 16 * j + n] = acc[j][r];
+    }
+  __syncthreads();
+
+  const int64_t c0 = int64_t(blk) * kHad + 2 * lane;        // shard-local column of (v0, v1)
+  float v0 = 0.f, v1 = 0.f;
+  if (wave < M) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* p = red + (w * M + wave) * kHad + 2 * lane;
+      v0 += p[0];
+      v1 += p[1];
+    }
+  }
+
+  if (sh.S > 1) {
+    // ---- 6a. split-K hand-off: coherent partial stores, then one counter bump per block
+    const int64_t OC = sh.OC;
+    if (wave < M) {
+      float* dst = sh.slab + (int64_t(s) * M + wave) * OC + c0;
+      __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);                          // this wave's partial stores have completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();                                        // ... and every other wave's
+    int* flag = reinterpret_cast<int*>(lds);
+    if (threadIdx.x == 0)
+      *flag = __hip_atomic_fetch_add(sh.counters + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int old = *flag;
+    if (old != sh.S - 1) return;                            // not the last split of this block
+    if (wave < M) {
+      v0 = v1 = 0.f;
+      for (int sp = 0; sp < sh.S; ++sp) {
+        float* src = sh.slab + (int64_t(sp) * M + wave) * OC + c0;
+        v0 += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v1 += __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(sh.counters + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- 6. output Hadamard-128, rout * s_out, bf16 into the slice
+  if (wave < M) {
+    had128_wave(v0, v1, lane);
+    v0 = v0 * kInvSqrt128 * f16_to_f32(sh.rout[c0]) * f16_to_f32(sh.s_out[c0]);
+    v1 = v1 * kInvSqrt128 * f16_to_f32(sh.rout[c0 + 1]) * f16_to_f32(sh.s_out[c0 + 1]);
+    uint16_t* dst = a.out + int64_t(wave) * a.ldo + sh.col0 + c0;
+    if (((a.ldo | sh.col0) & 1) == 0) {
+      *reinterpret_cast<uint32_t*>(dst) = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
+    } else {
+      dst[0] = (uint16_t)f32_to_bf16(v0);
+      dst[1] = (uint16_t)f32_to_bf16(v1);
+    }
+  }
+}
+
+template <int KSET, int SPW, int MR>
+__global__ __launch_bounds__(1024) void decode_kernel(DecArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int wg = blockIdx.x;
+  int i = 0;
+  while (i + 1 < a.n_shards && wg >= a.sh[i + 1].wg_begin) ++i;     // shards are in wg_begin order
+  const DecShard& sh = a.sh[i];
+  const int local = wg - sh.wg_begin;
+  if constexpr (KSET >= 1 && KSET <= 8) {
+    decode_block<KSET, SPW, MR>(a, sh, local, lds);
+  } else {   // KSET 0: the mixed set {2, 3, 4}
+    switch (sh.K) {
+      case 2: decode_block<2, SPW, MR>(a, sh, local, lds); break;
+      case 3: decode_block<3, SPW, MR>(a, sh, local, lds); break;
+      default: decode_block<4, SPW, MR>(a, sh, local, lds); break;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Host side: plan and launch
+// ---------------------------------------------------------------------------------------------------
+namespace {
+
+int spw_variant(int need) { return need <= 2 ? 2 : 4; }
+constexpr int kMaxSpw = 4;     // wider variants exceed the 128 registers a 1024-thread block allows
+
+size_t lds_bytes_for(int M, int lds_row) {
+  const size_t xs = size_t(M + 1) * lds_row * 2;
+  const size_t red = size_t(kWaves) * M * kHad * 4;
+  return xs > red ? xs : red;
+}
+
+}  // namespace
+
+// Splits of one shard's feature range.  A function of (M, IC, OC) alone -- never of the other shards in
+// the call -- so a merged call reduces every shard in the same order as a call of that shard by itself
+// and the two agree bit for bit.  Split only as far as needed: until the shard has kFillBlocks blocks
+// (C1's 14336-column shards already do, and together fill 224 of the 256 CUs), a wave's steps fit the
+// largest unrolled variant, and the activation slice fits in LDS.
+constexpr int kFillBlocks = 112;
+
+int shard_splits(int64_t M, int B, int nblk) {
+  for (int S = 1;; ++S) {
+    if (S >= B) return B;
+    const int nb_max = (B + S - 1) / S;
+    const int spw_need = 2 * ((nb_max + kWaves - 1) / kWaves);   // whole Hadamard blocks per wave
+    const bool lds_ok = lds_bytes_for(int(M), kHad * nb_max + 8) <= kMaxLds;
+    if (spw_need <= kMaxSpw && lds_ok && (nblk * S >= kFillBlocks || nb_max <= kWaves)) return S;
+  }
+}
+
+bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl) {
+  if (M < 1 || M > 16 || n < 1 || n > kMaxShards) return false;
+  const int B = int(IC / kHad);
+  int nb_max = 1;
+  for (int i = 0; i < n; ++i) {
+    pl->S[i] = shard_splits(M, B, int(in[i].OC / kHad));
+    const int nb = (B + pl->S[i] - 1) / pl->S[i];
+    nb_max = nb > nb_max ? nb : nb_max;
+  }
+  pl->spw = spw_variant(2 * ((nb_max + kWaves - 1) / kWaves));
+  pl->lds_row = kHad * nb_max + 8;
+  pl->lds_bytes = lds_bytes_for(int(M), pl->lds_row);
+  if (pl->lds_bytes > kMaxLds) return false;
+  // heavier shards (larger K) first: blocks are dispatched in index order
+  int order[kMaxShards];
+  for (int i = 0; i < n; ++i) order[i] = i;
+  for (int i = 1; i < n; ++i)
+    for (int j = i; j > 0 && in[order[j]].K > in[order[j - 1]].K; --j) std::swap(order[j], order[j - 1]);
+  int wg = 0;
+  size_t slab = 0;
+  int counters = 0;
+  for (int r = 0; r < n; ++r) {
+    const int i = order[r];
+    const int S = pl->S[i];
+    pl->order[r] = i;
+    pl->wg_begin[r] = wg;
+    wg += int(in[i].OC / kHad) * S;
+    if (S > 1) {
+      pl->slab_off[r] = slab;
+      slab += size_t(S) * size_t(M) * size_t(in[i].OC) * sizeof(float);
+      pl->counter_off[r] = counters;
+      counters += int(in[i].OC / kHad);
+    } else {
+      pl->slab_off[r] = 0;
+      pl->counter_off[r] = 0;
+    }
+  }
+  pl->wg_total = wg;
+  pl->slab_bytes = slab;
+  pl->counters = counters;
+  bool all_same = true;
+  for (int i = 1; i < n; ++i) all_same &= in[i].K == in[0].K;
+  bool mixed234 = true;
+  for (int i = 0; i < n; ++i) mixed234 &= in[i].K >= 2 && in[i].K <= 4;
+  pl->kset = all_same ? in[0].K : (mixed234 ? 0 : -1);
+  return counters <= kCounterSlots;
+}
+
+template <int KSET, int MR>
+static void launch_kset_mr(const DecPlan& pl, const DecArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)pl.wg_total), block(kWaves * 64);
+  const size_t lds = pl.lds_bytes;
+  if (pl.spw <= 2)
+    hipLaunchKernelGGL((decode_kernel<KSET, 2, MR>), grid, block, lds, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<KSET, 4, MR>), grid, block, lds, stream, a);
+}
+
+template <int KSET>
+static hipError_t launch_kset(const DecPlan& pl, const DecArgs& a, hipStream_t stream) {
+  // activation rows the pre-pass loads unconditionally: 1, 4 or 16
+  if (a.M <= 1)
+    launch_kset_mr<KSET, 1>(pl, a, stream);
+  else if (a.M <= 4)
+    launch_kset_mr<KSET, 4>(pl, a, stream);
+  else
+    launch_kset_mr<KSET, 16>(pl, a, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,
+                         void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream) {
+  if (pl.kset < 0) return hipErrorInvalidValue;
+  DecArgs a;
+  a.x = (const uint16_t*)x;
+  a.out = (uint16_t*)out;
+  a.ldo = ldo;
+  a.M = (int)M;
+  a.IC = (int)IC;
+  a.n_shards = n;
+  a.lds_row = pl.lds_row;
+  for (int r = 0; r < n; ++r) {
+    const DecShardIn& s = in[pl.order[r]];
+    DecShard& d = a.sh[r];
+    d.code = (const uint32_t*)s.code;
+    d.s_in = (const uint16_t*)s.s_in;
+    d.rin = (const uint16_t*)s.rin;
+    d.rout = (const uint16_t*)s.rout;
+    d.s_out = (const uint16_t*)s.s_out;
+    d.slab = slab + pl.slab_off[r] / sizeof(float);
+    d.counters = counters + pl.counter_off[r];
+    d.col0 = s.col0;
+    d.code_bytes = uint32_t(IC / 16 * (s.OC / 16) * 32 * s.K);
+    d.OC = (int)s.OC;
+    d.K = s.K;
+    d.S = pl.S[pl.order[r]];
+    d.wg_begin = pl.wg_begin[r];
+  }
+  switch (pl.kset) {
+    case 0: return launch_kset<0>(pl, a, stream);
+    case 1: return launch_kset<1>(pl, a, stream);
+    case 2: return launch_kset<2>(pl, a, stream);
+    case 3: return launch_kset<3>(pl, a, stream);
+    case 4: return launch_kset<4>(pl, a, stream);
+    case 5: return launch_kset<5>(pl, a, stream);
+    case 6: return launch_kset<6>(pl, a, stream);
+    case 7: return launch_kset<7>(pl, a, stream);
+    case 8: return launch_kset<8>(pl, a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Test hook: the decoded weight as fp16 [IC, OC], through decode_column.  One wave per 4 tiles of a
+// tile row; lane (n, g) decodes column n of tile 4*wave_tile + g.
+// ---------------------------------------------------------------------------------------------------
+template <int K>
+__global__ __launch_bounds__(256) void decode_tiles_kernel(uint16_t* __restrict__ w, const uint32_t* __restrict__ code,
+                                                           int64_t IC, int64_t OC) {
+  using G = Geom<K>;
+  const int lane = threadIdx.x & 63;
+  const int64_t ntiles = (IC / 16) * (OC / 16);
+  const int64_t t = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  if (t >= ntiles) return;
+  const int n = lane & 15;
+  const int64_t a = t / (OC / 16), b = t % (OC / 16);
+  int woff[G::kNW], shift;
+  column_word_offsets<K>(n, woff, shift);
+  uint32_t words[G::kNW];
+  const uint32_t* tile = code + t * G::kWords;
+#pragma unroll
+  for (int j = 0; j < G::kNW; ++j) words[j] = tile[woff[j]];
+  uint32_t v[8];
+  decode_column<K>(words, shift, v, codebook_regs());
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    w[(16 * a + p) * OC + 16 * b + n] = uint16_t(v[p] & 0xFFFFu);
+    w[(16 * a + p + 8) * OC + 16 * b + n] = uint16_t(v[p] >> 16);
+  }
+}
+
+hipError_t launch_decode_tiles(void* w, const int16_t* code, int64_t IC, int64_t OC, int K, hipStream_t stream) {
+  const int64_t ntiles = (IC / 16) * (OC / 16);
+  if (ntiles == 0) return hipSuccess;
+  dim3 block(256), grid((unsigned)((ntiles + 15) / 16));
+  const uint32_t* c = (const uint32_t*)code;
+  uint16_t* o = (uint16_t*)w;
+  switch (K) {
+    case 1: hipLaunchKernelGGL(decode_tiles_kernel<1>, grid, block, 0, stream, o, c, IC, OC); break;
+    case 2: hipLaunchKernelGGL(decode_tiles_kernel<2>, grid, block, 0, stream, o, c, IC, OC); break;
+    case 3: hipLaunchKernelGGL(decode_tiles_kernel<3>, grid, block, 0, stream, o, c, IC, OC); break;
+    case 4: hipLaunchKernelGGL(decode_tiles_kernel<4>, grid, block, 0, stream, o, c, IC, OC); break;
+    case 5: hipLaunchKernelGGL(decode_tiles_kernel<5>, grid, block, 0, stream, o, c, IC, OC); break;
+    case 6: hipLaunchKernelGGL(decode_tiles_kernel<6>, grid, block, 0, stream, o, c, IC, OC); break;
+    case 7: hipLaunchKernelGGL(decode_tiles_kernel<7>, grid, block, 0, stream, o, c, IC, OC); break;
+    case 8: hipLaunchKernelGGL(decode_tiles_kernel<8>, grid, block, 0, stream, o, c, IC, OC); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace exl3

@@ -30,33 +30,32 @@ __device__ __forceinline__ int64_t dest_index(int64_t k, bool permuted) {
   return permuted ? ((k & ~int64_t(15)) | perm16_pos(int(k & 15))) : k;
 }
 
-// Rows M .. gridDim.x-1 are padding: they are written as zeros (the decode-phase kernel reads whole
-// 16-row blocks).
+// One wave per (row, 128-block): blockIdx.x * 4 + wave enumerates rows-major pairs.  Rows M .. M_pad-1
+// are padding and are written as zeros (the decode-phase kernel reads whole 16-row blocks).
 template <bool PERMUTED>
 __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ s_in,
                                                           const uint16_t* __restrict__ rin,
-                                                          uint16_t* __restrict__ xh, int64_t M, int64_t IC) {
-  const int64_t m = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                                          uint16_t* __restrict__ xh, int64_t M, int64_t M_pad,
+                                                          int64_t IC) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nblk = IC / kHad;
+  const int64_t pair = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (pair >= M_pad * nblk) return;
+  const int64_t m = pair / nblk, q = pair % nblk;
+  const int64_t k = q * kHad + 2 * lane;
   uint16_t* dst = xh + m * IC;
   if (m >= M) {
-    for (int64_t k = 8 * int64_t(threadIdx.x); k < IC; k += 8 * 256)
-      *reinterpret_cast<u32x4*>(dst + k) = (u32x4){0u, 0u, 0u, 0u};
+    *reinterpret_cast<uint32_t*>(dst + k) = 0u;
     return;
   }
-  const uint16_t* xr = x + m * IC;
-  for (int64_t q = wave; q < IC / kHad; q += 4) {
-    float v0, v1;
-    rotate_block(xr, s_in, rin, q * kHad, lane, v0, v1);
-    const int64_t k = q * kHad + 2 * lane;
-    if (PERMUTED) {
-      dst[dest_index(k, true)] = f32_to_f16(v0);
-      dst[dest_index(k + 1, true)] = f32_to_f16(v1);
-    } else {
-      const uint32_t packed = uint32_t(f32_to_f16(v0)) | (uint32_t(f32_to_f16(v1)) << 16);
-      *reinterpret_cast<uint32_t*>(dst + k) = packed;
-    }
+  float v0, v1;
+  rotate_block(x + m * IC, s_in, rin, q * kHad, lane, v0, v1);
+  if (PERMUTED) {
+    dst[dest_index(k, true)] = f32_to_f16(v0);
+    dst[dest_index(k + 1, true)] = f32_to_f16(v1);
+  } else {
+    *reinterpret_cast<uint32_t*>(dst + k) = uint32_t(f32_to_f16(v0)) | (uint32_t(f32_to_f16(v1)) << 16);
   }
 }
 
@@ -108,13 +107,14 @@ __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restr
 hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, void* xh, int64_t M, int64_t IC,
                               bool permuted, hipStream_t stream, int64_t M_pad) {
   if (M <= 0) return hipSuccess;
-  dim3 grid((unsigned)(M_pad > M ? M_pad : M)), block(256);
+  const int64_t rows = M_pad > M ? M_pad : M;
+  dim3 grid((unsigned)((rows * (IC / kHad) + 3) / 4)), block(256);
   if (permuted)
     hipLaunchKernelGGL(prepass_f16_kernel<true>, grid, block, 0, stream, (const uint16_t*)x, (const uint16_t*)s_in,
-                       (const uint16_t*)rin, (uint16_t*)xh, M, IC);
+                       (const uint16_t*)rin, (uint16_t*)xh, M, rows, IC);
   else
     hipLaunchKernelGGL(prepass_f16_kernel<false>, grid, block, 0, stream, (const uint16_t*)x, (const uint16_t*)s_in,
-                       (const uint16_t*)rin, (uint16_t*)xh, M, IC);
+                       (const uint16_t*)rin, (uint16_t*)xh, M, rows, IC);
   return hipGetLastError();
 }
 
