@@ -34,6 +34,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extra-m", default="2,4,8", help="additional decode M values reported under 'extra'")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 prefill measurements")
     return ap.parse_args()
 
 
@@ -86,6 +87,44 @@ def time_decode(torch, exl3, dev, x, out, sets, steps, warmup):
     return t0.elapsed_time(t1) / 1e3 / steps
 
 
+def time_prefill(torch, exl3, synth, dev, reps=5):
+    """M=8192 prefill projections: gate_up (IC=5120 -> 2 x 17408, K=2 | K=3) and down (17408 -> 5120, K=3).
+    Returns {name: (seconds per call, FLOP per call)}; FLOP = 2*M*IC*OC (decode and transforms not counted)."""
+    p = synth.PREFILL
+    M = p["M"]
+    res = {}
+    rng = np.random.default_rng(4242)
+    gu, dn = p["gate_up"], p["down"]
+    for name, IC, shards in (("gate_up", gu["IC"], [(gu["OC"], gu["K_gate"]), (gu["OC"], gu["K_up"])]),
+                             ("down", dn["IC"], [(dn["OC"], dn["K"])])):
+        _, xb = synth.random_activations(rng, M, IC)
+        x = torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        s_in = torch.from_numpy(synth.random_signs(rng, IC)).to(dev)
+        rin = torch.from_numpy(synth.random_scales(rng, IC)).to(dev)
+        sh, col = [], 0
+        for OC, K in shards:
+            d = synth.shard(rng, IC, OC, K)
+            sh.append(dict(code=torch.from_numpy(d["code"]).to(dev), K=K, col0=col, s_in=s_in, rin=rin,
+                           rout=torch.from_numpy(d["rout"]).to(dev), s_out=torch.from_numpy(d["s_out"]).to(dev)))
+            col += OC
+        out = torch.empty((M, col), dtype=torch.bfloat16, device=dev)
+        ws = exl3.alloc_workspace(exl3.linear_multi_workspace_bytes(M, IC, sh), dev)
+        exl3.linear_multi_into(out, x, sh, ws=ws)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            exl3.linear_multi_into(out, x, sh, ws=ws)
+        t1.record()
+        torch.cuda.synchronize()
+        sec = t0.elapsed_time(t1) / 1e3 / reps
+        res[name] = (sec, 2.0 * M * IC * col)
+        print(f"# prefill {name} M={M}: {sec * 1e3:.3f} ms/call, {res[name][1] / sec / 1e12:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        del x, out, ws, sh
+    return res
+
+
 def cpu_baseline(synth, O):
     """The fp64 oracle on one M=1 step of the same workload (both shards), single-threaded."""
     from threadpoolctl import threadpool_limits
@@ -126,6 +165,8 @@ def main():
         print(f"# decode gate_up M={M}: {sec * 1e6:.2f} us/step, {trellis_bytes / sec / 1e9:.1f} GB/s trellis",
               file=sys.stderr, flush=True)
 
+    prefill = {} if a.no_prefill else time_prefill(torch, exl3, synth, dev)
+
     sec = results[1]
     gbs = trellis_bytes / sec / 1e9
     line = {
@@ -141,6 +182,9 @@ def main():
         "extra": {f"decode_M{M}": {"us_per_step": round(s * 1e6, 3), "trellis_GBps": round(trellis_bytes / s / 1e9, 1)}
                   for M, s in results.items()},
     }
+    for name, (s, flop) in prefill.items():
+        line["extra"][f"prefill_{name}_M8192"] = {"ms_per_call": round(s * 1e3, 4), "TFLOPs": round(flop / s / 1e12, 1),
+                                                  "frac_of_fp16_peak": round(flop / s / 2.5e15, 4)}
     if not a.no_cpu:
         from oracle import exl3_oracle as O
         line["cpu_baseline"] = cpu_baseline(synth, O)

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libexl3.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["exl3_api.cpp", "k_prepass.hip", "k_decode.hip"]
+SOURCES = ["exl3_api.cpp", "k_prepass.hip", "k_decode.hip", "k_gemm.hip"]
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
@@ -32,9 +32,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the EXL3 library)")
 
 
+# Per-file code generation options.  The GEMM keeps its 128 fp32 accumulators per wave in ordinary
+# VGPRs: with the accumulator-register form the compiler retargets every MFMA result and copies the
+# accumulators around the loop.
+EXTRA = {"k_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {src}\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

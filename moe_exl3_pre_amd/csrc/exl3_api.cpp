@@ -46,7 +46,6 @@ int check_flags(unsigned flags) {
   if ((flags & EXL3_FORCE_GEMV) && (flags & EXL3_FORCE_MFMA))
     return fail(EXL3_EINVAL, "flags: EXL3_FORCE_GEMV and EXL3_FORCE_MFMA are exclusive");
   if (flags & EXL3_ACT_INT8) return fail(EXL3_EUNSUPPORTED, "flags: EXL3_ACT_INT8 is not available in this build");
-  if (flags & EXL3_FORCE_MFMA) return fail(EXL3_EUNSUPPORTED, "flags: EXL3_FORCE_MFMA is not available in this build");
   return EXL3_OK;
 }
 
@@ -79,11 +78,11 @@ int check_shard(const char* who, int64_t IC, const int16_t* code, int64_t OC, in
   return EXL3_OK;
 }
 
+// The prefill/decode choice is made here, inside the op, by M ("radiance_escha.py", `escha_linear_into`).
 bool use_decode_path(int64_t M, unsigned flags) {
   if (flags & EXL3_FORCE_GEMV) return true;
   if (flags & EXL3_FORCE_MFMA) return false;
-  (void)M;
-  return true;   // the decode-phase kernel serves every M until the prefill kernel takes over large M
+  return M <= kGemvMaxRows;
 }
 
 // Row chunks the decode-phase path launches: full chunks of kDecodeMaxRows rows, then the remainder.
@@ -111,16 +110,31 @@ bool decode_slab_bytes(int64_t M, int64_t IC, int n, const DecShardIn* in, size_
 }
 
 struct Layout {
-  size_t slab_off, slab_bytes;
+  size_t slab_off, slab_bytes;   // decode-phase split-K slab
+  size_t xh_off, xh_bytes;       // prefill-phase rotated activations, one region per distinct (s_in, rin)
   size_t total;
 };
 
-Layout layout_for(size_t slab_bytes) {
+Layout layout_for(size_t slab_bytes, int64_t M = 0, int64_t IC = 0, int n_xh = 0) {
   Layout L;
   L.slab_off = align_up(kCounterBytes);
   L.slab_bytes = align_up(slab_bytes);
-  L.total = L.slab_off + L.slab_bytes;
+  L.xh_off = L.slab_off + L.slab_bytes;
+  L.xh_bytes = align_up(size_t(M) * size_t(IC) * 2);
+  L.total = L.xh_off + L.xh_bytes * size_t(n_xh);
   return L;
+}
+
+// Distinct (s_in, rin) pairs among the shards, in first-use order; slot[i] = region of shard i.
+int distinct_inputs(int n, const DecShardIn* in, int* slot) {
+  int k = 0;
+  for (int i = 0; i < n; ++i) {
+    slot[i] = -1;
+    for (int j = 0; j < i; ++j)
+      if (in[j].s_in == in[i].s_in && in[j].rin == in[i].rin) { slot[i] = slot[j]; break; }
+    if (slot[i] < 0) slot[i] = k++;
+  }
+  return k;
 }
 
 int check_workspace(const Layout& L, void* ws, size_t ws_bytes) {
@@ -156,6 +170,25 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
   return EXL3_OK;
 }
 
+// The prefill-phase path: one pre-pass per distinct (s_in, rin), then one GEMM per shard.
+int run_gemm(const char* who, void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,
+             char* ws, const Layout& L, hipStream_t stream) {
+  int slot[kMaxShards];
+  distinct_inputs(n, in, slot);
+  int done = -1;
+  for (int i = 0; i < n; ++i) {
+    void* xh = ws + L.xh_off + L.xh_bytes * size_t(slot[i]);
+    if (slot[i] > done) {
+      if (int rc = launch_status(launch_prepass_f16(x, in[i].s_in, in[i].rin, xh, M, IC, true, stream), who)) return rc;
+      done = slot[i];
+    }
+    hipError_t e = launch_gemm(xh, in[i].code, in[i].K, in[i].rout, in[i].s_out, out, ldo, in[i].col0, M, IC, in[i].OC,
+                               stream);
+    if (int rc = launch_status(e, who)) return rc;
+  }
+  return EXL3_OK;
+}
+
 DecShardIn shard_in(const int16_t* code, int64_t OC, int K, int64_t col0, const void* s_in, const void* rin,
                     const void* rout, const void* s_out) {
   DecShardIn d;
@@ -180,14 +213,25 @@ int exl3_version(void) { return 100; }
 
 int64_t exl3_gemv_max_rows(void) { return kGemvMaxRows; }
 
+// Workspace of either path for these shards (host descriptors; only OC, K and the s_in/rin pointers are read).
+bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsigned flags, Layout* L) {
+  if (use_decode_path(M, flags)) {
+    size_t slab = 0;
+    if (!decode_slab_bytes(M, IC, n, in, &slab)) return false;
+    *L = layout_for(slab);
+  } else {
+    int slot[kMaxShards];
+    *L = layout_for(0, M, IC, distinct_inputs(n, in, slot));
+  }
+  return true;
+}
+
 size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned flags) {
   if (M <= 0 || IC <= 0 || OC <= 0 || IC % 128 || OC % 128) return align_up(kCounterBytes);
-  size_t slab = 0;
-  if (use_decode_path(M, flags)) {
-    const DecShardIn in = shard_in(nullptr, OC, 2, 0, nullptr, nullptr, nullptr, nullptr);
-    if (!decode_slab_bytes(M, IC, 1, &in, &slab)) slab = 0;
-  }
-  return layout_for(slab).total;
+  const DecShardIn in = shard_in(nullptr, OC, 2, 0, nullptr, nullptr, nullptr, nullptr);
+  Layout L;
+  if (!workspace_layout(M, IC, 1, &in, flags, &L)) return align_up(kCounterBytes);
+  return L.total;
 }
 
 int exl3_linear_into(void* out, int64_t ldo, int64_t col0, const void* x, int64_t M, int64_t IC,
@@ -200,13 +244,14 @@ int exl3_linear_into(void* out, int64_t ldo, int64_t col0, const void* x, int64_
   if (!out || !aligned(out, 16)) return fail(EXL3_EINVAL, "out: null or not 16-byte aligned");
   if (!x || !aligned(x, 16)) return fail(EXL3_EINVAL, "x: null or not 16-byte aligned");
   const DecShardIn in = shard_in(code, OC, K, col0, s_in, rin, rout, s_out);
-  size_t slab = 0;
-  if (!decode_slab_bytes(M, IC, 1, &in, &slab)) return fail(EXL3_EUNSUPPORTED, "exl3_linear_into: no plan");
-  const Layout L = layout_for(slab);
+  Layout L;
+  if (!workspace_layout(M, IC, 1, &in, flags, &L)) return fail(EXL3_EUNSUPPORTED, "exl3_linear_into: no plan");
   if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
-  if (int rc = run_decode("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L,
-                          static_cast<hipStream_t>(stream)))
-    return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int rc = use_decode_path(M, flags)
+                     ? run_decode("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, st)
+                     : run_gemm("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, st);
+  if (rc) return rc;
   return ok();
 }
 
@@ -216,11 +261,11 @@ size_t exl3_linear_multi_workspace_bytes(int64_t M, int64_t IC, int n_shards, co
   DecShardIn in[kMaxShards];
   for (int i = 0; i < n_shards; ++i) {
     if (shards[i].OC <= 0 || shards[i].OC % 128) return align_up(kCounterBytes);
-    in[i] = shard_in(nullptr, shards[i].OC, shards[i].K, 0, nullptr, nullptr, nullptr, nullptr);
+    in[i] = shard_in(nullptr, shards[i].OC, shards[i].K, 0, shards[i].s_in, shards[i].rin, nullptr, nullptr);
   }
-  size_t slab = 0;
-  if (use_decode_path(M, flags) && !decode_slab_bytes(M, IC, n_shards, in, &slab)) slab = 0;
-  return layout_for(slab).total;
+  Layout L;
+  if (!workspace_layout(M, IC, n_shards, in, flags, &L)) return align_up(kCounterBytes);
+  return L.total;
 }
 
 int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n_shards,
@@ -240,13 +285,14 @@ int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int
   if (M == 0) return ok();
   if (!out || !aligned(out, 16)) return fail(EXL3_EINVAL, "out: null or not 16-byte aligned");
   if (!x || !aligned(x, 16)) return fail(EXL3_EINVAL, "x: null or not 16-byte aligned");
-  size_t slab = 0;
-  if (!decode_slab_bytes(M, IC, n_shards, in, &slab)) return fail(EXL3_EUNSUPPORTED, "exl3_linear_multi_into: no plan");
-  const Layout L = layout_for(slab);
+  Layout L;
+  if (!workspace_layout(M, IC, n_shards, in, flags, &L)) return fail(EXL3_EUNSUPPORTED, "exl3_linear_multi_into: no plan");
   if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
-  if (int rc = run_decode("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L,
-                          static_cast<hipStream_t>(stream)))
-    return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int rc = use_decode_path(M, flags)
+                     ? run_decode("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L, st)
+                     : run_gemm("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L, st);
+  if (rc) return rc;
   return ok();
 }
 

@@ -51,5 +51,8 @@ hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, 
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
                              int64_t IC, bool permuted, hipStream_t stream);
 hipError_t launch_decode_tiles(void* w, const int16_t* code, int64_t IC, int64_t OC, int K, hipStream_t stream);
+// Prefill-phase GEMM of one shard; xh is the pre-pass output (fp16 [M, IC], PERM16 order).
+hipError_t launch_gemm(const void* xh, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
+                       int64_t ldo, int64_t col0, int64_t M, int64_t IC, int64_t OC, hipStream_t stream);
 
 }  // namespace exl3

@@ -62,6 +62,7 @@ def _linear(**kw):
     (dict(x=FAKE + 4), exl3.EINVAL, "x"),
     (dict(out=None), exl3.EINVAL, "out"),
     (dict(flags=1 << 7), exl3.EINVAL, "flags"),
+    (dict(flags=exl3.ACT_INT8), exl3.EUNSUPPORTED, "flags"),
     (dict(flags=exl3.FORCE_GEMV | exl3.FORCE_MFMA), exl3.EINVAL, "flags"),
     (dict(ws=None), exl3.EWORKSPACE, "ws"),
     (dict(ws=FAKE, ws_bytes=1024), exl3.EWORKSPACE, "ws_bytes"),

@@ -1,0 +1,136 @@
+"""GPU parity of the prefill-phase (MFMA GEMM) path against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import exl3_oracle as O
+from moe_exl3_pre_amd import exl3, synth
+from tests.helpers import (assert_close_linear, bf16_to_f64, dev, log, oracle_block_columns, rel_fro, shard_to_dev,
+                           to_dev, to_dev_x)
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -1000.0
+
+
+def _dev_case(c):
+    return dict(x=to_dev_x(c["x_bits"]), code=to_dev(c["code"]), s_in=to_dev(c["s_in"]), rin=to_dev(c["rin"]),
+                rout=to_dev(c["rout"]), s_out=to_dev(c["s_out"]))
+
+
+def _run(c, d, flags, ldo=None, col0=0):
+    out = torch.full((c["M"], ldo or c["OC"]), SENTINEL, dtype=torch.bfloat16, device=dev())
+    exl3.linear_into(out, d["x"], d["code"], c["K"], d["s_in"], d["rin"], d["rout"], d["s_out"], col0=col0, flags=flags)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("M", [1, 3, 17, 64, 255, 300])
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_mfma_path_ragged(M, K):
+    log(f"mfma ragged M={M} K={K}")
+    c = synth.linear_case(5000 + 7 * M + K, M, 384, 384, K)      # 3 column blocks: one odd 128-column tile
+    out = _run(c, _dev_case(c), exl3.FORCE_MFMA)
+    args = (c["code"], K, c["s_in"], c["rin"], c["rout"], c["s_out"])
+    assert_close_linear(bf16_to_f64(out), O.linear(c["x"], *args, act="f16"), O.linear(c["x"], *args))
+
+
+@pytest.mark.parametrize("K", [1, 5, 6, 7, 8])
+def test_mfma_path_other_k(K):
+    c = synth.linear_case(5100 + K, 40, 256, 256, K)
+    out = _run(c, _dev_case(c), exl3.FORCE_MFMA)
+    args = (c["code"], K, c["s_in"], c["rin"], c["rout"], c["s_out"])
+    assert_close_linear(bf16_to_f64(out), O.linear(c["x"], *args, act="f16"), O.linear(c["x"], *args))
+
+
+def test_default_dispatch_uses_mfma_above_threshold():
+    """Above exl3_gemv_max_rows() the default call equals the forced MFMA call bit for bit; at or below
+    it equals the forced decode-phase call."""
+    thr = exl3.lib().exl3_gemv_max_rows()
+    for M, force in ((thr, exl3.FORCE_GEMV), (thr + 1, exl3.FORCE_MFMA), (200, exl3.FORCE_MFMA)):
+        c = synth.linear_case(5200 + M, M, 512, 256, 3)
+        d = _dev_case(c)
+        assert torch.equal(_run(c, d, 0), _run(c, d, force)), M
+
+
+def test_decode_and_mfma_paths_agree():
+    c = synth.linear_case(5300, 48, 1024, 512, 3)
+    d = _dev_case(c)
+    a = bf16_to_f64(_run(c, d, exl3.FORCE_GEMV))
+    b = bf16_to_f64(_run(c, d, exl3.FORCE_MFMA))
+    assert rel_fro(a, b) < 4e-3
+    args = (c["code"], 3, c["s_in"], c["rin"], c["rout"], c["s_out"])
+    ref16 = O.linear(c["x"], *args, act="f16")
+    ref = O.linear(c["x"], *args)
+    assert_close_linear(a, ref16, ref)
+    assert_close_linear(b, ref16, ref)
+
+
+def test_mfma_slice_and_sentinel():
+    c = synth.linear_case(5400, 70, 256, 256, 2)
+    out = _run(c, _dev_case(c), exl3.FORCE_MFMA, ldo=640, col0=256)
+    o = out.float().cpu().numpy()
+    assert np.all(o[:, :256] == SENTINEL) and np.all(o[:, 512:] == SENTINEL)
+    args = (c["code"], 2, c["s_in"], c["rin"], c["rout"], c["s_out"])
+    assert_close_linear(o[:, 256:512].astype(np.float64), O.linear(c["x"], *args, act="f16"), O.linear(c["x"], *args))
+
+
+def test_mfma_exact_symmetries_and_determinism():
+    c = synth.linear_case(5500, 130, 512, 384, 3)
+    d = _dev_case(c)
+    base = _run(c, d, exl3.FORCE_MFMA)
+    assert torch.equal(_run(c, d, exl3.FORCE_MFMA), base)
+    assert torch.equal(_run(c, dict(d, s_in=-d["s_in"]), exl3.FORCE_MFMA), -base)
+
+
+def test_mfma_batch_invariance():
+    """A row's output does not depend on the other rows (each output element is one fixed-order
+    reduction), so a prefix of the batch reproduces the same rows."""
+    c = synth.linear_case(5600, 300, 512, 256, 2)
+    d = _dev_case(c)
+    full = _run(c, d, exl3.FORCE_MFMA)
+    for M in (1, 77, 256):
+        part = _run(dict(c, M=M), dict(d, x=d["x"][:M].contiguous()), exl3.FORCE_MFMA)
+        assert torch.equal(part, full[:M]), M
+
+
+def _sampled_check(case_x, shards, out, rows, blocks_per_shard=3, seed=0):
+    got = bf16_to_f64(out)[rows]
+    rng = np.random.default_rng(seed)
+    x = case_x[rows]
+    for s in shards:
+        nblk = s["OC"] // 128
+        blocks = sorted(set([0, nblk - 1] + list(rng.choice(nblk, blocks_per_shard, replace=False))))
+        cols, y64 = oracle_block_columns(x, s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"], blocks)
+        _, y16 = oracle_block_columns(x, s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"], blocks,
+                                      act="f16")
+        e = assert_close_linear(got[:, s["col0"] + cols], y16, y64)
+        log(f"  shard K={s['K']} OC={s['OC']}: rel err {e:.3e} on {len(rows)} rows x {len(cols)} cols")
+
+
+def test_prefill_gate_up_full_size_sampled():
+    """M=8192, IC=5120, gate (K=2) | up (K=3) of 17408 columns each: full-size run, sampled check."""
+    p = synth.PREFILL
+    cfg = p["gate_up"]
+    M = p["M"]
+    case = synth.merged_case(2000, M, cfg["IC"], [(cfg["OC"], cfg["K_gate"]), (cfg["OC"], cfg["K_up"])])
+    log("prefill gate_up 8192 x 5120 -> 2 x 17408")
+    x = to_dev_x(case["x_bits"])
+    s_in, rin = to_dev(case["shards"][0]["s_in"]), to_dev(case["shards"][0]["rin"])
+    shards = [shard_to_dev(s, s_in, rin) for s in case["shards"]]
+    out = torch.full((M, case["ldo"]), SENTINEL, dtype=torch.bfloat16, device=dev())
+    exl3.linear_multi_into(out, x, shards)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(1).choice(M, 12, replace=False)]))
+    _sampled_check(case["x"], case["shards"], out, rows)
+
+
+def test_prefill_down_full_size_sampled():
+    p = synth.PREFILL
+    cfg = p["down"]
+    M = p["M"]
+    c = synth.linear_case(2001, M, cfg["IC"], cfg["OC"], cfg["K"])
+    log("prefill down 8192 x 17408 -> 5120")
+    out = _run(c, _dev_case(c), 0)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(2).choice(M, 10, replace=False)]))
+    _sampled_check(c["x"], [dict(c, col0=0)], out, rows)
