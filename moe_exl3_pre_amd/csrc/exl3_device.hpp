@@ -42,6 +42,13 @@ constexpr int kBufferFlags = 0x00020000;
 // Position of tile row r inside the permuted 16-group (inverse of PERM16).
 __host__ __device__ constexpr int perm16_pos(int r) { return r < 8 ? 2 * r : 2 * (r - 8) + 1; }
 
+// Feature pair a lane transforms when the rotated activations are written in PERM16 order: lane l takes
+// features f = 16*(l/8) + l%8 and f + 8 of its 128-block.  PERM16 puts exactly that pair at positions
+// 2l, 2l+1, so each lane writes one contiguous 4-byte word.  The Hadamard is unchanged: lane bits 0..2
+// are feature bits 0..2, lane bits 3..5 are feature bits 4..6 (monotone), and the in-lane pair is
+// feature bit 3 with the lower feature in v0.
+__device__ __forceinline__ int perm_pair_feature(int lane) { return 16 * (lane >> 3) + (lane & 7); }
+
 template <int K>
 struct Geom {
   static_assert(K >= 1 && K <= 8, "K must be 1..8");

@@ -84,12 +84,15 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
 #pragma unroll
   for (int pb = 0; pb < kPB; ++pb) {
     const int hb = hb0 + pb < hb1 ? hb0 + pb : (hb1 > hb0 ? hb1 - 1 : 0);
-    const int64_t k = int64_t(ba + hb) * kHad + 2 * lane;
-    sv[pb] = *reinterpret_cast<const uint32_t*>(sh.s_in + k);
-    rv[pb] = *reinterpret_cast<const uint32_t*>(sh.rin + k);
+    // lane transforms features f and f + 8 (perm_pair_feature), stored at PERM16 positions 2l, 2l+1
+    const int64_t f = int64_t(ba + hb) * kHad + perm_pair_feature(lane);
+    sv[pb] = uint32_t(sh.s_in[f]) | (uint32_t(sh.s_in[f + 8]) << 16);
+    rv[pb] = uint32_t(sh.rin[f]) | (uint32_t(sh.rin[f + 8]) << 16);
 #pragma unroll
-    for (int m = 0; m < MR; ++m)
-      xv[pb][m] = *reinterpret_cast<const uint32_t*>(a.x + int64_t(m < M ? m : M - 1) * a.IC + k);
+    for (int m = 0; m < MR; ++m) {
+      const uint16_t* xr = a.x + int64_t(m < M ? m : M - 1) * a.IC + f;
+      xv[pb][m] = uint32_t(xr[0]) | (uint32_t(xr[8]) << 16);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the weight stream
 
@@ -124,16 +127,15 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
     if (hb0 + pb < hb1) {
       const float s0 = f16_to_f32(sv[pb] & 0xFFFFu), s1 = f16_to_f32(sv[pb] >> 16);
       const float r0 = f16_to_f32(rv[pb] & 0xFFFFu), r1 = f16_to_f32(rv[pb] >> 16);
-      const int kl = (hb0 + pb) * kHad + 2 * lane;
-      const int p0 = (kl & ~15) | perm16_pos(kl & 15), p1 = (kl & ~15) | perm16_pos((kl + 1) & 15);
+      const int kl = (hb0 + pb) * kHad + 2 * lane;          // PERM16 positions 2l, 2l+1 of the block
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         if (m < M) {
           float v0 = bf16_to_f32(xv[pb][m] & 0xFFFFu) * s0 * r0;
           float v1 = bf16_to_f32(xv[pb][m] >> 16) * s1 * r1;
           had128_wave(v0, v1, lane);
-          xs[m * lrow + p0] = f32_to_f16(v0 * kInvSqrt128);
-          xs[m * lrow + p1] = f32_to_f16(v1 * kInvSqrt128);
+          *reinterpret_cast<uint32_t*>(xs + m * lrow + kl) =
+              uint32_t(f32_to_f16(v0 * kInvSqrt128)) | (uint32_t(f32_to_f16(v1 * kInvSqrt128)) << 16);
         }
       }
       *reinterpret_cast<uint32_t*>(xs + M * lrow + kl) = 0u;

@@ -74,20 +74,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   const int col0 = ntile * kBN + wn * kWN;                  // first shard column of this wave
   const uint32_t tpr = uint32_t(p.OC / kTile);
 
-  // ---- A tile of the block: rows mtile*256 .. +256, one 64-feature step per LDS buffer.  Row stride
-  //      padded by 16 bytes so the 16 rows one fragment read touches fall in different banks.
-  constexpr int kArow = 64 + 8;                             // halves per LDS row
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kArow];
+  // ---- A tile of the block: rows mtile*256 .. +256, one 64-feature step per LDS buffer, stored in
+  //      MFMA fragment order: fragment (wm, mb, h) is 64 slots of 16 bytes; lane (n, g) of it is row
+  //      wm*128 + 16*mb + n, PERM16 features 16g + 8h .. +8 of the step, kept in slot
+  //      (16g + n) ^ (4g + 2h).  The XOR keeps each 16-lane read group on one contiguous 256-byte span
+  //      (the conflict-free ds_read_b128 pattern) and sends the 8 chunks of a row, which 8 consecutive
+  //      threads write after a coalesced global load, to 8 different bank groups.
+  constexpr int kAFrag = 64 * 8;                            // halves per fragment
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][2 * 8 * 2 * kAFrag];
   const int steps = p.IC / 64;
-  // staging: thread t copies 8 chunks of 16 bytes (row (t + 256 q) / 8, chunk (t + 256 q) % 8)
+  // staging: thread t copies row (t + 256 q) / 8, chunk (t + 256 q) % 8 of the step (coalesced rows)
   const uint16_t* asrc[8];
   int adst[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const int c = threadIdx.x + 256 * q, r = c >> 3, ch = c & 7;
+    const int cidx = threadIdx.x + 256 * q, r = cidx >> 3, c = cidx & 7;
     const int grow = mtile * kBM + r;
-    asrc[q] = p.xh + int64_t(grow < p.M ? grow : p.M - 1) * p.IC + 8 * ch;
-    adst[q] = r * kArow + 8 * ch;
+    asrc[q] = p.xh + int64_t(grow < p.M ? grow : p.M - 1) * p.IC + 8 * c;
+    const int fwm = r >> 7, fmb = (r >> 4) & 7, fn = r & 15, fg = c >> 1, fh = c & 1;
+    const int frag = (fwm * 8 + fmb) * 2 + fh;
+    adst[q] = (frag * 64 + ((16 * fg + fn) ^ (4 * fg + 2 * fh))) * 8;
   }
   u32x4 astage[8];
   auto load_a = [&](int st) {
@@ -132,8 +138,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   load_w(0, wcur);
   store_a(0);
   __syncthreads();
-  // A fragment of row group mb: row wm*128 + 16*mb + n, PERM16 features 16g .. 16g+15 of the step
-  const int afrag = (wm * kWM + n) * kArow + 16 * g;
+  const int aslot0 = wm * 16 * kAFrag + (lane ^ (4 * g)) * 8;       // fragment (wm, mb, 0)
+  const int aslot1 = wm * 16 * kAFrag + (lane ^ (4 * g + 2)) * 8;   // fragment (wm, mb, 1), less kAFrag
   // One step per iteration (no unrolled pair: that makes the compiler move the accumulators between
   // register files at the back edge); the double buffers rotate by value instead.
   for (int st = 0; st < steps; ++st) {
@@ -143,8 +149,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     half8 a[8][2];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-      a[mb][0] = *reinterpret_cast<const half8*>(&As[buf][afrag + 16 * mb * kArow]);
-      a[mb][1] = *reinterpret_cast<const half8*>(&As[buf][afrag + 16 * mb * kArow + 8]);
+      a[mb][0] = *reinterpret_cast<const half8*>(&As[buf][aslot0 + (2 * mb) * kAFrag]);
+      a[mb][1] = *reinterpret_cast<const half8*>(&As[buf][aslot1 + (2 * mb + 1) * kAFrag]);
     }
 #pragma unroll
     for (int nb = 0; nb < kNBW; ++nb) {

@@ -10,28 +10,35 @@
 
 namespace exl3 {
 
-// Transform one 128-block: returns the normalised features 2*lane and 2*lane+1 in fp32.
+// Transform one 128-block.  Natural order: lane l holds features 2l, 2l+1.  PERMUTED order: lane l holds
+// features perm_pair_feature(l) and +8, which the PERM16 layout stores at positions 2l, 2l+1.
+template <bool PERMUTED>
 __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ x, const uint16_t* __restrict__ s_in,
                                              const uint16_t* __restrict__ rin, int64_t k0, int lane,
                                              float& v0, float& v1) {
-  const int64_t k = k0 + 2 * lane;
-  const uint32_t xb = *reinterpret_cast<const uint32_t*>(x + k);
-  const uint32_t sb = *reinterpret_cast<const uint32_t*>(s_in + k);
-  const uint32_t rb = *reinterpret_cast<const uint32_t*>(rin + k);
-  v0 = bf16_to_f32(xb & 0xFFFFu) * f16_to_f32(sb & 0xFFFFu) * f16_to_f32(rb & 0xFFFFu);
-  v1 = bf16_to_f32(xb >> 16) * f16_to_f32(sb >> 16) * f16_to_f32(rb >> 16);
+  if (PERMUTED) {
+    const int64_t f = k0 + perm_pair_feature(lane);
+    v0 = bf16_to_f32(x[f]) * f16_to_f32(s_in[f]) * f16_to_f32(rin[f]);
+    v1 = bf16_to_f32(x[f + 8]) * f16_to_f32(s_in[f + 8]) * f16_to_f32(rin[f + 8]);
+  } else {
+    const int64_t k = k0 + 2 * lane;
+    const uint32_t xb = *reinterpret_cast<const uint32_t*>(x + k);
+    const uint32_t sb = *reinterpret_cast<const uint32_t*>(s_in + k);
+    const uint32_t rb = *reinterpret_cast<const uint32_t*>(rin + k);
+    v0 = bf16_to_f32(xb & 0xFFFFu) * f16_to_f32(sb & 0xFFFFu) * f16_to_f32(rb & 0xFFFFu);
+    v1 = bf16_to_f32(xb >> 16) * f16_to_f32(sb >> 16) * f16_to_f32(rb >> 16);
+  }
   had128_wave(v0, v1, lane);
   v0 *= kInvSqrt128;
   v1 *= kInvSqrt128;
 }
 
-// Destination index of feature k inside its 16-group for the permuted layout.
-__device__ __forceinline__ int64_t dest_index(int64_t k, bool permuted) {
-  return permuted ? ((k & ~int64_t(15)) | perm16_pos(int(k & 15))) : k;
-}
+// One wave per 8 rows of one 128-block: the block's s_in / rin are loaded once, every input load is
+// issued before any arithmetic (the kernel is latency-bound otherwise), and each row's result is one
+// coalesced 256-byte store.  Rows M .. M_pad-1 are padding and are written as zeros (the decode-phase
+// kernel reads whole 16-row blocks).
+constexpr int kPrepassRows = 8;
 
-// One wave per (row, 128-block): blockIdx.x * 4 + wave enumerates rows-major pairs.  Rows M .. M_pad-1
-// are padding and are written as zeros (the decode-phase kernel reads whole 16-row blocks).
 template <bool PERMUTED>
 __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ s_in,
@@ -40,22 +47,35 @@ __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __rest
                                                           int64_t IC) {
   const int lane = threadIdx.x & 63;
   const int64_t nblk = IC / kHad;
-  const int64_t pair = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (pair >= M_pad * nblk) return;
-  const int64_t m = pair / nblk, q = pair % nblk;
-  const int64_t k = q * kHad + 2 * lane;
-  uint16_t* dst = xh + m * IC;
-  if (m >= M) {
-    *reinterpret_cast<uint32_t*>(dst + k) = 0u;
-    return;
+  const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);   // (row group, block) pairs
+  const int64_t ngroups = (M_pad + kPrepassRows - 1) / kPrepassRows;
+  if (unit >= ngroups * nblk) return;
+  const int64_t m0 = (unit / nblk) * kPrepassRows, q = unit % nblk;
+  const int64_t k0 = q * kHad;
+  // this lane's two features: natural (2l, 2l+1) or PERM16 pair (f, f+8) stored at (2l, 2l+1)
+  const int64_t f0 = PERMUTED ? k0 + perm_pair_feature(lane) : k0 + 2 * lane;
+  const int64_t f1 = PERMUTED ? f0 + 8 : f0 + 1;
+  const float si0 = f16_to_f32(s_in[f0]), ri0 = f16_to_f32(rin[f0]);
+  const float si1 = f16_to_f32(s_in[f1]), ri1 = f16_to_f32(rin[f1]);
+  uint32_t xv[kPrepassRows];
+#pragma unroll
+  for (int r = 0; r < kPrepassRows; ++r) {
+    const int64_t m = m0 + r < M ? m0 + r : M - 1;
+    xv[r] = uint32_t(x[m * IC + f0]) | (uint32_t(x[m * IC + f1]) << 16);
   }
-  float v0, v1;
-  rotate_block(x + m * IC, s_in, rin, q * kHad, lane, v0, v1);
-  if (PERMUTED) {
-    dst[dest_index(k, true)] = f32_to_f16(v0);
-    dst[dest_index(k + 1, true)] = f32_to_f16(v1);
-  } else {
-    *reinterpret_cast<uint32_t*>(dst + k) = uint32_t(f32_to_f16(v0)) | (uint32_t(f32_to_f16(v1)) << 16);
+#pragma unroll
+  for (int r = 0; r < kPrepassRows; ++r) {
+    const int64_t m = m0 + r;
+    if (m >= M_pad) break;
+    uint32_t packed = 0u;
+    if (m < M) {
+      // (x * s_in) * rin, in the order the layer defines
+      float v0 = bf16_to_f32(xv[r] & 0xFFFFu) * si0 * ri0;
+      float v1 = bf16_to_f32(xv[r] >> 16) * si1 * ri1;
+      had128_wave(v0, v1, lane);
+      packed = uint32_t(f32_to_f16(v0 * kInvSqrt128)) | (uint32_t(f32_to_f16(v1 * kInvSqrt128)) << 16);
+    }
+    *reinterpret_cast<uint32_t*>(xh + m * IC + k0 + 2 * lane) = packed;
   }
 }
 
@@ -74,7 +94,7 @@ __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restr
   float amax = 0.f;
   for (int64_t q = wave; q < IC / kHad; q += 4) {
     float v0, v1;
-    rotate_block(xr, s_in, rin, q * kHad, lane, v0, v1);
+    rotate_block<PERMUTED>(xr, s_in, rin, q * kHad, lane, v0, v1);
     amax = fmaxf(amax, fmaxf(fabsf(v0), fabsf(v1)));
   }
 #pragma unroll
@@ -87,20 +107,14 @@ __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restr
   int8_t* dst = q_out + m * IC;
   for (int64_t q = wave; q < IC / kHad; q += 4) {
     float v0, v1;
-    rotate_block(xr, s_in, rin, q * kHad, lane, v0, v1);
+    rotate_block<PERMUTED>(xr, s_in, rin, q * kHad, lane, v0, v1);
     int q0 = 0, q1 = 0;
     if (sc > 0.f) {
       q0 = (int)fminf(fmaxf(rintf(__fdiv_rn(v0, sc)), -127.f), 127.f);
       q1 = (int)fminf(fmaxf(rintf(__fdiv_rn(v1, sc)), -127.f), 127.f);
     }
-    const int64_t k = q * kHad + 2 * lane;
-    if (PERMUTED) {
-      dst[dest_index(k, true)] = (int8_t)q0;
-      dst[dest_index(k + 1, true)] = (int8_t)q1;
-    } else {
-      const uint16_t packed = uint16_t(uint8_t(q0)) | uint16_t(uint16_t(uint8_t(q1)) << 8);
-      *reinterpret_cast<uint16_t*>(dst + k) = packed;
-    }
+    const int64_t k = q * kHad + 2 * lane;             // natural: features k, k+1; permuted: positions k, k+1
+    *reinterpret_cast<uint16_t*>(dst + k) = uint16_t(uint8_t(q0)) | uint16_t(uint16_t(uint8_t(q1)) << 8);
   }
 }
 
@@ -108,7 +122,8 @@ hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, 
                               bool permuted, hipStream_t stream, int64_t M_pad) {
   if (M <= 0) return hipSuccess;
   const int64_t rows = M_pad > M ? M_pad : M;
-  dim3 grid((unsigned)((rows * (IC / kHad) + 3) / 4)), block(256);
+  const int64_t units = (rows + kPrepassRows - 1) / kPrepassRows * (IC / kHad);
+  dim3 grid((unsigned)((units + 3) / 4)), block(256);
   if (permuted)
     hipLaunchKernelGGL(prepass_f16_kernel<true>, grid, block, 0, stream, (const uint16_t*)x, (const uint16_t*)s_in,
                        (const uint16_t*)rin, (uint16_t*)xh, M, rows, IC);
