@@ -225,37 +225,46 @@ def silu(h: np.ndarray) -> np.ndarray:
     return h / (1.0 + np.exp(-h))
 
 
-def expert_forward(v, e) -> np.ndarray:
+def expert_forward(v, e, act: str = "f64") -> np.ndarray:
     """One expert's MLP on rows v [n, H]: w2( silu(w1 v) * (w3 v) ), each an EXL3 projection whose
     input sign/scale vector is its suh and whose output vector is its svh ([bank] docstring: w13_suh,
     w13_svh, w2_suh, w2_svh; [pr190]: input suh + Hadamard-128, output svh + Hadamard-128).
 
     `e` is a dict with keys w1, w3 (int16 [H/16, I/16, 16 k_gu]), w2 (int16 [I/16, H/16, 16 k_d]),
     k_gu, k_d, w1_suh, w3_suh [H], w1_svh, w3_svh [I], w2_suh [I], w2_svh [H].  Optional pre-decoded
-    dense weights may be given as W1, W3, W2.
+    dense weights may be given as W1, W3, W2.  `act` is passed to each of the three projections
+    ("f16": every projection's rotated input is rounded once to fp16; h1, h3 and the silu product are
+    not rounded).
     """
     ones_h = 1.0
-    h1 = linear(v, e["w1"], e["k_gu"], e["w1_suh"], ones_h, ones_h, e["w1_svh"], W=e.get("W1"))
-    h3 = linear(v, e["w3"], e["k_gu"], e["w3_suh"], ones_h, ones_h, e["w3_svh"], W=e.get("W3"))
+    h1 = linear(v, e["w1"], e["k_gu"], e["w1_suh"], ones_h, ones_h, e["w1_svh"], act=act, W=e.get("W1"))
+    h3 = linear(v, e["w3"], e["k_gu"], e["w3_suh"], ones_h, ones_h, e["w3_svh"], act=act, W=e.get("W3"))
     a = silu(h1) * h3
-    return linear(a, e["w2"], e["k_d"], e["w2_suh"], ones_h, ones_h, e["w2_svh"], W=e.get("W2"))
+    return linear(a, e["w2"], e["k_d"], e["w2_suh"], ones_h, ones_h, e["w2_svh"], act=act, W=e.get("W2"))
 
 
-def moe_forward(x, topk_ids, topk_w, experts) -> np.ndarray:
+def moe_forward(x, topk_ids, topk_w, experts, act: str = "f64", tokens=None) -> np.ndarray:
     """Dense per-expert loop over logical expert ids:
        out[t] = sum_j topk_w[t, j] * E_{topk_ids[t, j]}(x[t])            (float64 [T, H]).
 
     `experts[e]` is the dict of `expert_forward` for logical expert e.  Experts that receive no
-    token are never evaluated and contribute nothing.
+    token are never evaluated and contribute nothing; ids outside [0, E) contribute nothing.  With
+    `tokens` given, only those rows are computed (the others stay zero).
     """
     x = np.asarray(x, dtype=np.float64)
     ids = np.asarray(topk_ids)
     w = np.asarray(topk_w, dtype=np.float64)
     T = x.shape[0]
     out = np.zeros_like(x)
+    keep = np.zeros(T, dtype=bool)
+    keep[np.arange(T) if tokens is None else np.asarray(tokens)] = True
     for ex in np.unique(ids):
-        tok, slot = np.nonzero(ids == ex)
-        y = expert_forward(x[tok], experts[int(ex)])
+        if ex < 0 or ex >= len(experts):
+            continue
+        tok, slot = np.nonzero((ids == ex) & keep[:, None])
+        if tok.size == 0:
+            continue
+        y = expert_forward(x[tok], experts[int(ex)], act=act)
         np.add.at(out, tok, w[tok, slot][:, None] * y)
     assert out.shape[0] == T
     return out

@@ -364,3 +364,38 @@ def test_moe_128_aligned_intermediate_cut_is_exact():
         halves.append(O.moe_forward(m["x"], m["topk_ids"], m["topk_w"], ex))
     rel = np.linalg.norm(halves[0] + halves[1] - full) / np.linalg.norm(full)
     assert rel <= 1e-12
+
+
+def test_moe_out_of_range_id_equals_zero_weight():
+    """An id outside [0, E) drops its (token, j) term: same result as routing that term to a real expert
+    with weight 0 (two different code paths of the dense loop)."""
+    m = _small_moe()
+    ids = m["topk_ids"].copy()
+    w = m["topk_w"].copy()
+    ids_bad = ids.copy()
+    ids_bad[2, 1] = -1
+    ids_bad[7, 0] = m["E"]
+    w0 = w.copy()
+    w0[2, 1] = 0.0
+    w0[7, 0] = 0.0
+    a = O.moe_forward(m["x"], ids_bad, w, m["experts"])
+    b = O.moe_forward(m["x"], ids, w0, m["experts"])
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-9)
+
+
+def test_moe_token_subset_matches_full():
+    m = _small_moe()
+    full = O.moe_forward(m["x"], m["topk_ids"], m["topk_w"], m["experts"])
+    sub = O.moe_forward(m["x"], m["topk_ids"], m["topk_w"], m["experts"], tokens=[1, 4])
+    assert np.allclose(sub[[1, 4]], full[[1, 4]], rtol=1e-12, atol=1e-9)   # BLAS blocking may differ
+    assert not np.any(np.delete(sub, [1, 4], axis=0))
+
+
+def test_moe_f16_operands_close_to_exact():
+    """Rounding each projection's rotated input to fp16 perturbs the output by about the fp16 unit
+    roundoff (2^-11 relative), far inside the 16-bit path tolerance."""
+    m = _small_moe()
+    a = O.moe_forward(m["x"], m["topk_ids"], m["topk_w"], m["experts"])
+    b = O.moe_forward(m["x"], m["topk_ids"], m["topk_w"], m["experts"], act="f16")
+    rel = np.linalg.norm(a - b) / np.linalg.norm(a)
+    assert 1e-6 < rel < 2e-3
