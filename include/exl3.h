@@ -56,7 +56,8 @@ typedef enum {
 
 /* flags */
 enum {
-  EXL3_ACT_INT8 = 1u << 0,   /* per-row 8-bit activations: sc = max|xh| / 127, q = clamp(rne(xh / sc), +-127) */
+  EXL3_ACT_INT8 = 1u << 0,   /* per-row 8-bit activations: sc = max|xh| / 127, q = clamp(rne(xh / sc), +-127);
+                                 the linear entry points answer EXL3_EUNSUPPORTED for now */
   EXL3_FORCE_GEMV = 1u << 1, /* force the decode-phase (streaming split-K) kernel whatever M is */
   EXL3_FORCE_MFMA = 1u << 2  /* force the prefill-phase (tiled MFMA GEMM) kernel whatever M is */
 };
@@ -81,8 +82,14 @@ int64_t exl3_gemv_max_rows(void);
  *   s_in, rin    fp16 [IC];  rout, s_out   fp16 [OC].
  *   K      bits per weight, 1..8.
  * Requirements: IC % 128 == 0 and OC % 128 == 0 (the transform is blocked at 128, `create_weights`),
- * OC / 128 <= 4096, col0 >= 0, col0 + OC <= ldo, out/x/code 16-byte aligned, ldo even.
- * Returns EXL3_OK, EXL3_EINVAL, EXL3_EWORKSPACE, EXL3_ELAUNCH.
+ * OC / 128 <= 4096, col0 >= 0, col0 + OC <= ldo, out/x/code 16-byte aligned, s_in/rin 4-byte aligned,
+ * rout/s_out 2-byte aligned, IC*OC*K/8 < 2 GiB.
+ * Precision: x * s_in * rin and the Hadamard in fp32, the rotated activations rounded once to fp16, fp16 x
+ * fp16 products accumulated in fp32, output transform and scales in fp32, one round-to-nearest-even to
+ * bf16.  Row results do not depend on the other rows; M <= exl3_gemv_max_rows() runs the decode-phase
+ * kernel, larger M the MFMA GEMM (the two agree to rounding, not bitwise).
+ * Returns EXL3_OK, EXL3_EINVAL, EXL3_EWORKSPACE, EXL3_EUNSUPPORTED (EXL3_ACT_INT8, not provided yet),
+ * EXL3_ELAUNCH.
  * ------------------------------------------------------------------------------------------------ */
 size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned flags);
 
@@ -132,7 +139,17 @@ int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int
  * Slot p (= perm[logical id]) holds w1 at w13 + off_w1[p] as [H/16, I/16, 16 k_gu], w3 at w13 + off_w3[p]
  * (same shape), w2 at w2 + off_w2[p] as [I/16, H/16, 16 k_d]; offsets count int16 elements and each
  * must make the address 16-byte aligned.  Groups are contiguous slot ranges [lo, hi) sharing (k_gu, k_d)
- * ("bank.py", `tables`: one GroupTables per K group).
+ * ("bank.py", `tables`: one GroupTables per K group); they must cover slots 0 .. E-1 in order.
+ * The device tables (perm, off_w*) are trusted: the host cannot read them without synchronising.  A perm
+ * entry outside [0, E) drops the expert like an out-of-range id; offsets must address the banks.
+ * Limits: 1 <= E <= 1024, H and I multiples of 128 up to 65536, 1 <= n_groups <= 64, k_gu, k_d in 1..8,
+ * 1 <= topk <= E, T * topk <= 2^24; w13/w2, x and out 16-byte aligned, vectors 2-byte aligned, offset
+ * tables 8-byte and perm/topk arrays 4-byte aligned.
+ * Precision: each projection as in exl3_linear_into (fp16 operands, fp32 accumulation); h1, h3 and
+ * silu(h1) * h3 stay in fp32 until w2's rotation rounds them to fp16; the top-k sum is taken in fp32 in
+ * top-k order with one bf16 rounding.  Deterministic: every reduction has a fixed order.
+ * Workspace: exl3_moe_workspace_bytes(bank, T, topk, flags); it holds the per-(token, expert) rotated
+ * activations, w2 operands and expert outputs, so it grows linearly with T * topk.
  * ------------------------------------------------------------------------------------------------ */
 typedef struct { int32_t k_gu, k_d, lo, hi; } exl3_group;
 
@@ -156,8 +173,8 @@ size_t exl3_moe_workspace_bytes(const exl3_bank* bank, int64_t T, int topk, unsi
 
 /*   out      bf16 [T, H];  x  bf16 [T, H]
  *   topk_ids int32 [T, topk] logical expert ids in [0, E) (device);  topk_w float32 [T, topk] (device).
- * An id outside [0, E) is ignored (contributes nothing).  Returns EXL3_OK / EXL3_EINVAL / EXL3_EWORKSPACE /
- * EXL3_ELAUNCH. */
+ * An id outside [0, E) is ignored (contributes nothing).  flags must be 0 (EXL3_ACT_INT8 answers
+ * EXL3_EUNSUPPORTED).  Returns EXL3_OK / EXL3_EINVAL / EXL3_EWORKSPACE / EXL3_EUNSUPPORTED / EXL3_ELAUNCH. */
 int exl3_moe_bank_forward(void* out, const void* x, int64_t T,
                           const int32_t* topk_ids, const float* topk_w, int topk,
                           const exl3_bank* bank, unsigned flags, void* ws, size_t ws_bytes, void* stream);

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libexl3.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["exl3_api.cpp", "k_prepass.hip", "k_decode.hip", "k_gemm.hip"]
+SOURCES = ["exl3_api.cpp", "k_prepass.hip", "k_decode.hip", "k_gemm.hip", "k_moe.hip"]
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
@@ -32,10 +32,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the EXL3 library)")
 
 
-# Per-file code generation options.  The GEMM keeps its 128 fp32 accumulators per wave in ordinary
-# VGPRs: with the accumulator-register form the compiler retargets every MFMA result and copies the
-# accumulators around the loop.
-EXTRA = {"k_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file code generation options.  The GEMM and the MoE kernels keep their MFMA accumulators in
+# ordinary VGPRs: with the accumulator-register form the compiler retargets every MFMA result and copies
+# the accumulators around the loop (GEMM), or splits the budget between the two files (MoE).
+EXTRA = {"k_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "k_moe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

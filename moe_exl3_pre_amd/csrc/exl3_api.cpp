@@ -203,6 +203,69 @@ DecShardIn shard_in(const int16_t* code, int64_t OC, int K, int64_t col0, const 
   return d;
 }
 
+
+// Workspace of the MoE bank forward: the route tables, then the per-pair rotated activations of w1 and
+// w3, w2's rotated operand and the fp32 expert outputs.  The counter area at the head is kept for
+// uniformity with the linear calls (unused here).
+struct MoeLayout {
+  size_t offs, pslot, rows, chunks, n_chunks, xh13, ah, o, total;
+};
+
+void moe_layout(int E, int H, int I, int64_t T, int topk, MoeLayout* L) {
+  const size_t P = size_t(T) * size_t(topk);
+  size_t at = align_up(kCounterBytes);
+  auto take = [&](size_t bytes) {
+    const size_t r = at;
+    at += align_up(bytes ? bytes : 1);
+    return r;
+  };
+  L->offs = take(size_t(E + 1) * 4);
+  L->pslot = take(P * 4);
+  L->rows = take(P * 4);
+  L->chunks = take(size_t(moe_max_chunks(int64_t(P), E)) * 16);
+  L->n_chunks = take(16);
+  L->xh13 = take(2 * P * size_t(H) * 2);
+  L->ah = take(P * size_t(I) * 2);
+  L->o = take(P * size_t(H) * 4);
+  L->total = at;
+}
+
+int check_bank(const exl3_bank* b) {
+  if (!b) return fail(EXL3_EINVAL, "bank: null");
+  if (b->E < 1 || b->E > kMoeMaxExperts) return fail(EXL3_EINVAL, "bank.E: %d is outside 1..%d", b->E, kMoeMaxExperts);
+  if (b->H <= 0 || b->H % 128 || b->H > (1 << 16))
+    return fail(EXL3_EINVAL, "bank.H: %d is not a positive multiple of 128 (at most 65536)", b->H);
+  if (b->I <= 0 || b->I % 128 || b->I > (1 << 16))
+    return fail(EXL3_EINVAL, "bank.I: %d is not a positive multiple of 128 (at most 65536)", b->I);
+  if (b->n_groups < 1 || b->n_groups > kMoeMaxGroups)
+    return fail(EXL3_EINVAL, "bank.n_groups: %d is outside 1..%d", b->n_groups, kMoeMaxGroups);
+  if (!b->groups) return fail(EXL3_EINVAL, "bank.groups: null");
+  int lo = 0;
+  for (int g = 0; g < b->n_groups; ++g) {
+    const exl3_group& G = b->groups[g];
+    if (G.lo != lo || G.hi <= G.lo)
+      return fail(EXL3_EINVAL, "bank.groups[%d]: [%d, %d) does not continue the slot ranges at %d", g, G.lo, G.hi, lo);
+    if (G.k_gu < 1 || G.k_gu > 8 || G.k_d < 1 || G.k_d > 8)
+      return fail(EXL3_EINVAL, "bank.groups[%d]: k_gu %d / k_d %d outside 1..8", g, G.k_gu, G.k_d);
+    lo = G.hi;
+  }
+  if (lo != b->E) return fail(EXL3_EINVAL, "bank.groups: cover slots [0, %d), not [0, E=%d)", lo, b->E);
+  if (!b->w13 || !b->w2 || !aligned(b->w13, 16) || !aligned(b->w2, 16))
+    return fail(EXL3_EINVAL, "bank.w13/w2: null or not 16-byte aligned");
+  if (!b->w13_suh || !b->w13_svh || !b->w2_suh || !b->w2_svh)
+    return fail(EXL3_EINVAL, "bank.w13_suh/w13_svh/w2_suh/w2_svh: null");
+  if (!aligned(b->w13_suh, 2) || !aligned(b->w13_svh, 2) || !aligned(b->w2_suh, 2) || !aligned(b->w2_svh, 2))
+    return fail(EXL3_EINVAL, "bank.w13_suh/w13_svh/w2_suh/w2_svh: not 2-byte aligned");
+  if (!b->off_w1 || !b->off_w3 || !b->off_w2 || !aligned(b->off_w1, 8) || !aligned(b->off_w3, 8) ||
+      !aligned(b->off_w2, 8))
+    return fail(EXL3_EINVAL, "bank.off_w1/off_w3/off_w2: null or not 8-byte aligned");
+  if (!b->perm || !aligned(b->perm, 4)) return fail(EXL3_EINVAL, "bank.perm: null or not 4-byte aligned");
+  if (int64_t(b->H) * b->I >= (int64_t(1) << 31))
+    return fail(EXL3_EUNSUPPORTED, "bank: H x I = %lld x %lld exceeds 2 GiB of trellis words per matrix",
+                (long long)b->H, (long long)b->I);
+  return EXL3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -297,15 +360,67 @@ int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int
 }
 
 size_t exl3_moe_workspace_bytes(const exl3_bank* bank, int64_t T, int topk, unsigned flags) {
-  (void)bank; (void)T; (void)topk; (void)flags;
-  return align_up(kCounterBytes);
+  (void)flags;
+  MoeLayout L;
+  if (!bank || T < 0 || topk < 1 || bank->E < 1 || bank->H <= 0 || bank->I <= 0) return align_up(kCounterBytes);
+  moe_layout(bank->E, bank->H, bank->I, T, topk, &L);
+  return L.total;
 }
 
 int exl3_moe_bank_forward(void* out, const void* x, int64_t T, const int32_t* topk_ids, const float* topk_w, int topk,
                           const exl3_bank* bank, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
-  (void)out; (void)x; (void)T; (void)topk_ids; (void)topk_w; (void)topk; (void)bank; (void)flags; (void)ws;
-  (void)ws_bytes; (void)stream;
-  return fail(EXL3_EUNSUPPORTED, "exl3_moe_bank_forward: not available in this build");
+  if (flags & EXL3_ACT_INT8) return fail(EXL3_EUNSUPPORTED, "flags: EXL3_ACT_INT8 is not available for the MoE bank");
+  if (flags) return fail(EXL3_EINVAL, "flags: 0x%x has no meaning for the MoE bank", flags);
+  if (int rc = check_bank(bank)) return rc;
+  if (topk < 1 || topk > bank->E) return fail(EXL3_EINVAL, "topk: %d is outside 1..E (%d)", topk, bank->E);
+  if (T < 0) return fail(EXL3_EINVAL, "T: %lld is negative", (long long)T);
+  if (T * topk > (int64_t(1) << 24)) return fail(EXL3_EINVAL, "T: %lld x topk %d exceeds 2^24 pairs", (long long)T, topk);
+  if (T == 0) return ok();
+  if (!out || !aligned(out, 16)) return fail(EXL3_EINVAL, "out: null or not 16-byte aligned");
+  if (!x || !aligned(x, 16)) return fail(EXL3_EINVAL, "x: null or not 16-byte aligned");
+  if (!topk_ids || !aligned(topk_ids, 4)) return fail(EXL3_EINVAL, "topk_ids: null or not 4-byte aligned");
+  if (!topk_w || !aligned(topk_w, 4)) return fail(EXL3_EINVAL, "topk_w: null or not 4-byte aligned");
+  MoeLayout L;
+  moe_layout(bank->E, bank->H, bank->I, T, topk, &L);
+  if (!ws) return fail(EXL3_EWORKSPACE, "ws: null (need %zu bytes)", L.total);
+  if (!aligned(ws, kAlign)) return fail(EXL3_EINVAL, "ws: not %zu-byte aligned", kAlign);
+  if (ws_bytes < L.total) return fail(EXL3_EWORKSPACE, "ws_bytes: %zu < required %zu", ws_bytes, L.total);
+  char* w = static_cast<char*>(ws);
+  MoeLaunch m;
+  m.x = x;
+  m.ids = topk_ids;
+  m.wts = topk_w;
+  m.perm = bank->perm;
+  m.w13 = bank->w13;
+  m.w2 = bank->w2;
+  m.w13_suh = bank->w13_suh;
+  m.w13_svh = bank->w13_svh;
+  m.w2_suh = bank->w2_suh;
+  m.w2_svh = bank->w2_svh;
+  m.off_w1 = bank->off_w1;
+  m.off_w3 = bank->off_w3;
+  m.off_w2 = bank->off_w2;
+  m.out = out;
+  m.offs = reinterpret_cast<int32_t*>(w + L.offs);
+  m.pslot = reinterpret_cast<int32_t*>(w + L.pslot);
+  m.rows = reinterpret_cast<int32_t*>(w + L.rows);
+  m.chunks = reinterpret_cast<int32_t*>(w + L.chunks);
+  m.n_chunks = reinterpret_cast<int32_t*>(w + L.n_chunks);
+  m.xh13 = w + L.xh13;
+  m.ah = w + L.ah;
+  m.o = reinterpret_cast<float*>(w + L.o);
+  m.T = T;
+  m.topk = topk;
+  m.E = bank->E;
+  m.H = bank->H;
+  m.I = bank->I;
+  m.n_groups = bank->n_groups;
+  for (int g = 0; g < kMoeMaxGroups; ++g) {
+    m.g_hi[g] = g < bank->n_groups ? bank->groups[g].hi : 0;
+    m.g_k[g] = g < bank->n_groups ? (bank->groups[g].k_gu | (bank->groups[g].k_d << 8)) : 0;
+  }
+  if (int rc = launch_status(launch_moe(m, static_cast<hipStream_t>(stream)), "exl3_moe_bank_forward")) return rc;
+  return ok();
 }
 
 int exl3_decode_tiles(void* w_out, const int16_t* code, int64_t IC, int64_t OC, int K, void* stream) {

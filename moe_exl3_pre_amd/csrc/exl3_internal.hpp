@@ -55,4 +55,34 @@ hipError_t launch_decode_tiles(void* w, const int16_t* code, int64_t IC, int64_t
 hipError_t launch_gemm(const void* xh, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
                        int64_t ldo, int64_t col0, int64_t M, int64_t IC, int64_t OC, hipStream_t stream);
 
+// ---- MoE expert bank
+constexpr int kMoeMaxGroups = 64;
+constexpr int kMoeMaxExperts = 1024;    // the route sort keeps one slot per thread of one workgroup
+
+struct MoeLaunch {
+  const void* x;
+  const int32_t* ids;
+  const float* wts;
+  const int32_t* perm;
+  const void *w13, *w2, *w13_suh, *w13_svh, *w2_suh, *w2_svh;
+  const int64_t *off_w1, *off_w3, *off_w2;
+  void* out;
+  // workspace regions
+  int32_t* offs;
+  int32_t* pslot;
+  int32_t* rows;
+  int32_t* chunks;          // int32 x 4 per chunk
+  int32_t* n_chunks;
+  void* xh13;
+  void* ah;
+  float* o;
+  int64_t T;
+  int topk, E, H, I, n_groups;
+  int g_hi[kMoeMaxGroups];  // exclusive end slot of each group
+  int g_k[kMoeMaxGroups];   // k_gu | k_d << 8
+};
+
+int64_t moe_max_chunks(int64_t P, int E);
+hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream);
+
 }  // namespace exl3

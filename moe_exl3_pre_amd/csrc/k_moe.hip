@@ -1,0 +1,593 @@
+// MoE expert-bank forward ("dspark/worker/exl3/bank.py", `Exl3Bank`: one layer's experts in K-sorted
+// physical slots, trellis words in two flat int16 banks, w13 = [w1 | w3] per slot; "vLLM PR #190":
+// every expert projection is an EXL3 linear with input suh + Hadamard-128 and output Hadamard-128 + svh).
+//
+//   out[t] = bf16( sum_j topk_w[t, j] * E_{topk_ids[t, j]}(x[t]) ),   E(v) = L_w2( silu(L_w1 v) * L_w3 v )
+//
+// Four launches, all sized from host-known quantities so the call is graph-capturable:
+//   1. route + rotate.  Workgroup 0 sorts the (token, slot) pairs by slot with a stable counting sort
+//      (pair ids ascending inside a slot) and cuts every slot's list into chunks of at most 32 rows.
+//      Every other workgroup rotates gathered activations for w1 and w3 of each pair
+//      (x[t] * suh, Hadamard-128, fp16, PERM16 order) -- that needs only the pair's slot, not the sort.
+//   2. w13.  One workgroup per (chunk, 128-column block of I): two waves stream w1's trellis words and
+//      two stream w3's, each decoding tile columns in registers straight into MFMA operands against up
+//      to 32 gathered rows.  The epilogue has h1 and h3 of the same 128 intermediate features, so it
+//      applies both output Hadamards and svh, forms a = silu(h1) * h3, applies w2's suh and w2's input
+//      Hadamard (the same 128-feature block) and writes w2's fp16 operand: the intermediate never goes
+//      to HBM in fp32 and needs no pre-pass of its own.
+//   3. w2.  One workgroup per (chunk, pair of 128-column blocks of H): same streaming core; output
+//      Hadamard and svh; fp32 result per pair.
+//   4. combine.  out[t] = sum over j in top-k order, one bf16 rounding.
+// Every intermediate is indexed by pair id q = t * topk + j, so only the w13/w2 row lists depend on the
+// sort.  Reductions run in a fixed order, so results are deterministic.
+#include <type_traits>
+
+#include "exl3_device.hpp"
+#include "exl3_internal.hpp"
+
+namespace exl3 {
+
+constexpr int kMoeRows = 32;          // rows of one chunk: two 16-row MFMA groups per decoded operand
+constexpr int kMoeWaves = 4;          // waves per w13 / w2 workgroup: two per half
+constexpr int kRedStride = kHad + 4;  // padded fp32 row of the reduction buffers (spreads LDS banks)
+constexpr int kRouteThreads = 1024;
+
+struct MoeArgs {
+  const uint16_t* x;        // bf16 [T, H]
+  const int32_t* ids;       // [T * topk] logical expert ids
+  const float* wts;         // [T * topk]
+  const int32_t* perm;      // [E] logical -> slot
+  const uint16_t* w13;      // flat int16 banks
+  const uint16_t* w2;
+  const uint16_t* w13_suh;  // fp16 [E, 2, H]
+  const uint16_t* w13_svh;  // fp16 [E, 2, I]
+  const uint16_t* w2_suh;   // fp16 [E, I]
+  const uint16_t* w2_svh;   // fp16 [E, H]
+  const int64_t* off_w1;    // int16-element offsets per slot
+  const int64_t* off_w3;
+  const int64_t* off_w2;
+  uint16_t* out;            // bf16 [T, H]
+  // workspace
+  int32_t* offs;            // [E + 1] first row of each slot's list
+  int32_t* pslot;           // [P] slot of each pair, -1 if dropped (written by the route)
+  int32_t* rows;            // [P] pair ids sorted by slot
+  int4v* chunks;            // [max_chunks] {slot, first row, rows, k_gu | k_d << 8}
+  int32_t* n_chunks;        // [1]
+  uint16_t* xh13;           // fp16 [2, P, H] rotated activations of w1 (0) and w3 (1), PERM16 order
+  uint16_t* ah;             // fp16 [P, I] w2's rotated operand, PERM16 order
+  float* o;                 // fp32 [P, H] expert outputs
+  int T, topk, P, E, H, I, max_chunks;
+  int n_groups;
+  int g_hi[kMoeMaxGroups];  // group g covers slots [g_hi[g-1], g_hi[g])
+  int g_k[kMoeMaxGroups];   // k_gu | k_d << 8
+};
+
+// Slot of pair q, or -1 when its id is outside [0, E) or the permutation entry is.
+__device__ __forceinline__ int pair_slot(const MoeArgs& a, int q) {
+  const int e = a.ids[q];
+  if (e < 0 || e >= a.E) return -1;
+  const int s = a.perm[e];
+  return (s >= 0 && s < a.E) ? s : -1;
+}
+
+// ---------------------------------------------------------------------------------------------------
+// 1a. Route: stable counting sort of the pairs by slot, done by one workgroup of 1024 threads.
+// ---------------------------------------------------------------------------------------------------
+// Exclusive scan of v over the block's 1024 threads; returns the prefix and leaves the total in *total.
+// tmp holds 48 ints of LDS.
+__device__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += u;
+  }
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kRouteThreads / 64 ? tmp[lane] : 0;
+    int winc = w;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int u = __shfl_up(winc, d, 64);
+      if (lane >= d) winc += u;
+    }
+    if (lane < kRouteThreads / 64) tmp[16 + lane] = winc - w;   // exclusive wave offsets
+    if (lane == 15) tmp[32] = winc;
+  }
+  __syncthreads();
+  const int r = tmp[16 + wave] + inc - v;
+  *total = tmp[32];
+  __syncthreads();
+  return r;
+}
+
+constexpr int kSlotCache = 16384;   // pairs whose slots the route keeps in LDS between its two passes
+
+__device__ void moe_route(const MoeArgs& a, int* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kW = kRouteThreads / 64;
+  const int E = a.E;
+  int* cnt = lds;                 // [E]
+  int* next = cnt + E;            // [E] next free row of each slot
+  int* wcnt = next + E;           // [kW][E]
+  int* tmp = wcnt + kW * E;       // [48]
+  int* cache = a.P <= kSlotCache ? tmp + 48 : nullptr;   // [P] slot per pair
+  for (int s = tid; s < E; s += kRouteThreads) cnt[s] = 0;
+  __syncthreads();
+  for (int q = tid; q < a.P; q += kRouteThreads) {
+    const int s = pair_slot(a, q);
+    a.pslot[q] = s;
+    if (cache) cache[q] = s;
+    if (s >= 0) atomicAdd(&cnt[s], 1);
+  }
+  __syncthreads();
+  // slot offsets and chunk offsets (E <= 1024: one slot per thread)
+  const int s = tid;
+  const int c = s < E ? cnt[s] : 0;
+  int total = 0, chunk_total = 0;
+  const int off = block_excl_scan(c, tmp, &total);
+  const int nch = (c + kMoeRows - 1) / kMoeRows;
+  const int coff = block_excl_scan(nch, tmp, &chunk_total);
+  if (s < E) {
+    a.offs[s] = off;
+    next[s] = off;
+    int gk = 0;
+    for (int g = 0; g < a.n_groups; ++g)
+      if (s < a.g_hi[g]) {
+        gk = a.g_k[g];
+        break;
+      }
+    for (int i = 0; i < nch; ++i) {
+      const int r0 = off + i * kMoeRows;
+      const int nr = c - i * kMoeRows < kMoeRows ? c - i * kMoeRows : kMoeRows;
+      a.chunks[coff + i] = (int4v){s, r0, nr, gk};
+    }
+  }
+  if (s == 0) {
+    a.offs[E] = total;
+    a.n_chunks[0] = chunk_total;
+  }
+  // stable placement, 1024 pairs at a time: rank inside the wave by ballots, then per-slot prefix over
+  // the waves in wave order
+  for (int q0 = 0; q0 < a.P; q0 += kRouteThreads) {
+    for (int i = tid; i < kW * E; i += kRouteThreads) wcnt[i] = 0;
+    __syncthreads();
+    const int q = q0 + tid;
+    const int sl = q < a.P ? (cache ? cache[q] : pair_slot(a, q)) : -1;
+    uint64_t remaining = __ballot(sl >= 0);
+    int rank = 0;
+    while (remaining) {
+      const int leader = __builtin_ctzll(remaining);
+      const int ls = __builtin_amdgcn_readlane(sl, leader);
+      const uint64_t m = __ballot(sl == ls);
+      if (sl == ls) rank = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == leader) wcnt[wave * E + ls] = __popcll(m);
+      remaining &= ~m;
+    }
+    __syncthreads();
+    for (int t = tid; t < E; t += kRouteThreads) {
+      int b = next[t];
+      for (int w = 0; w < kW; ++w) {
+        const int v = wcnt[w * E + t];
+        wcnt[w * E + t] = b;
+        b += v;
+      }
+      next[t] = b;
+    }
+    __syncthreads();
+    if (sl >= 0) a.rows[wcnt[wave * E + sl] + rank] = q;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------
+// 1b. Rotation of gathered activations for w1 and w3: one wave per (token, 128-block).  The token's x
+// block is loaded once and rotated for each of its top-k pairs and both projections; the pair slots and
+// every sign/scale load are issued before the first Hadamard.
+// ---------------------------------------------------------------------------------------------------
+constexpr int kRotBatch = 8;    // pairs whose loads are in flight together
+
+__device__ void moe_rotate(const MoeArgs& a, int64_t unit) {
+  const int lane = threadIdx.x & 63;
+  const int nblk = a.H / kHad;
+  const int t = int(unit / nblk), hb = int(unit % nblk);
+  if (t >= a.T) return;
+  const int f = hb * kHad + perm_pair_feature(lane);
+  const uint16_t* xr = a.x + int64_t(t) * a.H + f;
+  const uint32_t xv = uint32_t(xr[0]) | (uint32_t(xr[8]) << 16);
+  const float x0 = bf16_to_f32(xv & 0xFFFFu), x1 = bf16_to_f32(xv >> 16);
+  for (int j0 = 0; j0 < a.topk; j0 += kRotBatch) {
+    int sl[kRotBatch];
+    uint32_t sv[kRotBatch][2];
+#pragma unroll
+    for (int r = 0; r < kRotBatch; ++r) {
+      const int j = j0 + r < a.topk ? j0 + r : a.topk - 1;
+      sl[r] = pair_slot(a, t * a.topk + j);
+      const int sc = sl[r] < 0 ? 0 : sl[r];
+#pragma unroll
+      for (int proj = 0; proj < 2; ++proj) {
+        const uint16_t* su = a.w13_suh + (int64_t(sc) * 2 + proj) * a.H + f;
+        sv[r][proj] = uint32_t(su[0]) | (uint32_t(su[8]) << 16);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRotBatch; ++r) {
+      if (j0 + r >= a.topk || sl[r] < 0) continue;   // wave-uniform
+      const int64_t q = int64_t(t) * a.topk + j0 + r;
+#pragma unroll
+      for (int proj = 0; proj < 2; ++proj) {
+        float v0 = x0 * f16_to_f32(sv[r][proj] & 0xFFFFu);
+        float v1 = x1 * f16_to_f32(sv[r][proj] >> 16);
+        had128_wave(v0, v1, lane);
+        uint16_t* dst = a.xh13 + (int64_t(proj) * a.P + q) * a.H + hb * kHad + 2 * lane;
+        *reinterpret_cast<uint32_t*>(dst) =
+            uint32_t(f32_to_f16(v0 * kInvSqrt128)) | (uint32_t(f32_to_f16(v1 * kInvSqrt128)) << 16);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_rotate_kernel(MoeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) int route_lds[];
+  if (blockIdx.x == 0) {
+    moe_route(a, route_lds);
+    return;
+  }
+  const int64_t unit = int64_t(blockIdx.x - 1) * (kRouteThreads / 64) + (threadIdx.x >> 6);
+  moe_rotate(a, unit);
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Streaming core: one wave accumulates rows x [128 columns] over its 64-feature steps [st0, st0 + nst)
+// of one expert projection.  Trellis words of PD steps are in flight; the A fragments of the next step
+// are loaded one step ahead.  Loads are unconditional with clamped steps (every address stays inside the
+// tensor); only the arithmetic is predicated.
+// ---------------------------------------------------------------------------------------------------
+template <int K>
+__device__ __forceinline__ void moe_accumulate(const uint16_t* code, uint32_t code_bytes, int tpr, int blk,
+                                               const uint16_t* arow0, const uint16_t* arow1, int st0, int nst,
+                                               bool two, float4v (&acc0)[8], float4v (&acc1)[8]) {
+  using G = Geom<K>;
+  constexpr int PD = G::kNW <= 2 ? 2 : 1;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  int woff[G::kNW], shift;
+  column_word_offsets<K>(n, woff, shift);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(code), (short)0, (int)code_bytes, kBufferFlags);
+  uint32_t lane_off[G::kNW];
+#pragma unroll
+  for (int w = 0; w < G::kNW; ++w) lane_off[w] = (uint32_t(g) * uint32_t(tpr) * G::kWords + uint32_t(woff[w])) * 4u;
+  const uint32_t step_stride = 4u * uint32_t(tpr) * G::kWords * 4u;
+  const uint32_t base_blk = uint32_t(blk) * 8u * G::kWords * 4u;
+  const int last = st0 + (nst > 0 ? nst - 1 : 0);
+
+  uint32_t buf[PD][8][G::kNW];
+  half8 A[2][2][2];   // [ring][row group][k half]
+  auto load_step = [&](int st, uint32_t (&dst)[8][G::kNW]) {
+    const uint32_t soff = uint32_t(st < last ? st : last) * step_stride + base_blk;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int w = 0; w < G::kNW; ++w)
+        dst[j][w] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off[w] + uint32_t(j * G::kWords * 4), soff, 0);
+  };
+  auto load_a = [&](int st, half8 (&dst)[2][2]) {
+    const int o = 64 * (st < last ? st : last);
+    dst[0][0] = *reinterpret_cast<const half8*>(arow0 + o);
+    dst[0][1] = *reinterpret_cast<const half8*>(arow0 + o + 8);
+    dst[1][0] = *reinterpret_cast<const half8*>(arow1 + o);
+    dst[1][1] = *reinterpret_cast<const half8*>(arow1 + o + 8);
+  };
+  load_a(st0, A[0]);
+#pragma unroll
+  for (int p = 0; p < PD; ++p) load_step(st0 + p, buf[p]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const CodebookRegs cb = codebook_regs();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    acc0[j] = (float4v){0.f, 0.f, 0.f, 0.f};
+    acc1[j] = (float4v){0.f, 0.f, 0.f, 0.f};
+  }
+  for (int s = 0; s < nst; s += 2) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int st = s + p;
+      load_a(st0 + st + 1, A[(p + 1) & 1]);
+      const bool live = st < nst;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (live) {
+          uint32_t b[8];
+          decode_column<K>(buf[p % PD][j], shift, b, cb);
+          const half8 b0 = as_half8(b[0], b[1], b[2], b[3]);
+          const half8 b1 = as_half8(b[4], b[5], b[6], b[7]);
+          acc0[j] = mfma16(A[p][0][0], b0, acc0[j]);
+          acc0[j] = mfma16(A[p][0][1], b1, acc0[j]);
+          if (two) {
+            acc1[j] = mfma16(A[p][1][0], b0, acc1[j]);
+            acc1[j] = mfma16(A[p][1][1], b1, acc1[j]);
+          }
+        }
+        // refill this slot with the same column of step st + PD
+        const uint32_t soff =
+            uint32_t(st0 + st + PD < last ? st0 + st + PD : last) * step_stride + base_blk;
+#pragma unroll
+        for (int w = 0; w < G::kNW; ++w)
+          buf[p % PD][j][w] =
+              __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off[w] + uint32_t(j * G::kWords * 4), soff, 0);
+      }
+    }
+  }
+}
+
+// Fixed-order sum of the two waves of one half into red [32][kRedStride]: wave 0 stores, wave 1 adds.
+__device__ __forceinline__ void moe_reduce(float* red, int wq, bool two, const float4v (&acc0)[8],
+                                           const float4v (&acc1)[8]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  for (int turn = 0; turn < 2; ++turn) {
+    if (wq == turn) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* p0 = red + (4 * g + r) * kRedStride + 16 * j + n;
+          float* p1 = red + (16 + 4 * g + r) * kRedStride + 16 * j + n;
+          if (turn == 0) {
+            *p0 = acc0[j][r];
+            if (two) *p1 = acc1[j][r];
+          } else {
+            *p0 += acc0[j][r];
+            if (two) *p1 += acc1[j][r];
+          }
+        }
+    }
+    __syncthreads();
+  }
+}
+
+// Chunk c of the launch (heavier K groups sit at the end of the slot order, so they go first).
+__device__ __forceinline__ bool moe_chunk(const MoeArgs& a, int c, int4v& ch) {
+  const int n = a.n_chunks[0];
+  if (c >= n) return false;
+  ch = a.chunks[n - 1 - c];
+  return true;
+}
+
+// Workgroup -> (chunk, column group).  The column groups of one chunk land on one XCD (workgroups are
+// dealt to the 8 XCDs round-robin), so the chunk's gathered activations are fetched into one L2.
+__device__ __forceinline__ void moe_tile(int ncg, int& c, int& cg) {
+  const int id = blockIdx.x, x = id & 7, y = id >> 3;
+  cg = y % ncg;
+  c = (y / ncg) * 8 + x;
+}
+
+template <int K>
+__device__ __forceinline__ void moe_w13_block(const MoeArgs& a, const int4v ch, int cb, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = wave >> 1, wq = wave & 1, n = lane & 15, g = lane >> 4;
+  const int slot = ch[0], row0 = ch[1], nrows = ch[2];
+  const bool two = nrows > 16;
+  const int NS = a.H / 64;
+  const int st0 = NS * wq / 2, st1 = NS * (wq + 1) / 2;
+  const int64_t off = h == 0 ? a.off_w1[slot] : a.off_w3[slot];
+  const uint16_t* A = a.xh13 + int64_t(h) * a.P * a.H;
+  const int r0 = a.rows[row0 + (n < nrows ? n : nrows - 1)];
+  const int r1 = a.rows[row0 + (16 + n < nrows ? 16 + n : nrows - 1)];
+  float4v acc0[8], acc1[8];
+  moe_accumulate<K>(a.w13 + off, uint32_t(int64_t(a.H) * a.I * K / 8), a.I / 16, cb, A + int64_t(r0) * a.H + 16 * g,
+                    A + int64_t(r1) * a.H + 16 * g, st0, st1 - st0, two, acc0, acc1);
+  moe_reduce(red + h * kMoeRows * kRedStride, wq, two, acc0, acc1);
+
+  // epilogue: lane l owns intermediate features f, f + 8 of this block (PERM16 positions 2l, 2l+1)
+  const int f = perm_pair_feature(lane);
+  const int64_t col = int64_t(cb) * kHad + f;
+  const uint16_t* svh1 = a.w13_svh + (int64_t(slot) * 2 + 0) * a.I + col;
+  const uint16_t* svh3 = a.w13_svh + (int64_t(slot) * 2 + 1) * a.I + col;
+  const uint16_t* suh2 = a.w2_suh + int64_t(slot) * a.I + col;
+  const float s1a = f16_to_f32(svh1[0]), s1b = f16_to_f32(svh1[8]);
+  const float s3a = f16_to_f32(svh3[0]), s3b = f16_to_f32(svh3[8]);
+  const float u2a = f16_to_f32(suh2[0]), u2b = f16_to_f32(suh2[8]);
+  for (int r = wave; r < nrows; r += kMoeWaves) {
+    const float* p1 = red + r * kRedStride;
+    const float* p3 = red + (kMoeRows + r) * kRedStride;
+    float h1a = p1[f], h1b = p1[f + 8], h3a = p3[f], h3b = p3[f + 8];
+    had128_wave(h1a, h1b, lane);
+    had128_wave(h3a, h3b, lane);
+    h1a *= kInvSqrt128 * s1a;
+    h1b *= kInvSqrt128 * s1b;
+    h3a *= kInvSqrt128 * s3a;
+    h3b *= kInvSqrt128 * s3b;
+    float va = h1a / (1.0f + __expf(-h1a)) * h3a * u2a;
+    float vb = h1b / (1.0f + __expf(-h1b)) * h3b * u2b;
+    had128_wave(va, vb, lane);
+    uint16_t* dst = a.ah + int64_t(a.rows[row0 + r]) * a.I + int64_t(cb) * kHad + 2 * lane;
+    *reinterpret_cast<uint32_t*>(dst) =
+        uint32_t(f32_to_f16(va * kInvSqrt128)) | (uint32_t(f32_to_f16(vb * kInvSqrt128)) << 16);
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void moe_w2_block(const MoeArgs& a, const int4v ch, int cbp, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = wave >> 1, wq = wave & 1, n = lane & 15, g = lane >> 4;
+  const int slot = ch[0], row0 = ch[1], nrows = ch[2];
+  const bool two = nrows > 16;
+  const int nblk = a.H / kHad;
+  const int cb = 2 * cbp + h;
+  const bool active = cb < nblk;                 // an odd last column block leaves half 1 idle
+  const int NS = a.I / 64;
+  const int st0 = NS * wq / 2, st1 = active ? NS * (wq + 1) / 2 : st0;
+  const int r0 = a.rows[row0 + (n < nrows ? n : nrows - 1)];
+  const int r1 = a.rows[row0 + (16 + n < nrows ? 16 + n : nrows - 1)];
+  float4v acc0[8], acc1[8];
+  moe_accumulate<K>(a.w2 + a.off_w2[slot], uint32_t(int64_t(a.I) * a.H * K / 8), a.H / 16, active ? cb : 0,
+                    a.ah + int64_t(r0) * a.I + 16 * g, a.ah + int64_t(r1) * a.I + 16 * g, st0, st1 - st0, two, acc0,
+                    acc1);
+  float* rh = red + h * kMoeRows * kRedStride;
+  moe_reduce(rh, wq, two, acc0, acc1);
+  if (!active) return;
+  const int64_t c0 = int64_t(cb) * kHad + 2 * lane;
+  const float sa = f16_to_f32(a.w2_svh[int64_t(slot) * a.H + c0]);
+  const float sb = f16_to_f32(a.w2_svh[int64_t(slot) * a.H + c0 + 1]);
+  for (int r = wq; r < nrows; r += 2) {
+    float v0 = rh[r * kRedStride + 2 * lane], v1 = rh[r * kRedStride + 2 * lane + 1];
+    had128_wave(v0, v1, lane);
+    float* dst = a.o + int64_t(a.rows[row0 + r]) * a.H + c0;
+    *reinterpret_cast<float2*>(dst) = make_float2(v0 * kInvSqrt128 * sa, v1 * kInvSqrt128 * sb);
+  }
+}
+
+// KSET 0 covers the mixed set {2, 3, 4} in one launch (one switch per workgroup); KSET k in 1..8 serves
+// the chunks of one K and skips the others, so any other mix runs as one launch per distinct K.
+template <int KSET, typename F>
+__device__ __forceinline__ void moe_dispatch(int k, F&& f) {
+  if constexpr (KSET == 0) {
+    switch (k) {
+      case 2: f(std::integral_constant<int, 2>{}); break;
+      case 3: f(std::integral_constant<int, 3>{}); break;
+      case 4: f(std::integral_constant<int, 4>{}); break;
+      default: break;
+    }
+  } else {
+    if (k == KSET) f(std::integral_constant<int, KSET>{});
+  }
+}
+
+template <int KSET>
+__global__ __launch_bounds__(kMoeWaves * 64, 3) void moe_w13_kernel(MoeArgs a) {
+  __shared__ float red[2 * kMoeRows * kRedStride];
+  int c, cb;
+  moe_tile(a.I / kHad, c, cb);
+  int4v ch;
+  if (!moe_chunk(a, c, ch)) return;
+  moe_dispatch<KSET>(ch[3] & 0xFF, [&](auto k) { moe_w13_block<decltype(k)::value>(a, ch, cb, red); });
+}
+
+template <int KSET>
+__global__ __launch_bounds__(kMoeWaves * 64) void moe_w2_kernel(MoeArgs a) {
+  __shared__ float red[2 * kMoeRows * kRedStride];
+  int c, cbp;
+  moe_tile((a.H / kHad + 1) / 2, c, cbp);
+  int4v ch;
+  if (!moe_chunk(a, c, ch)) return;
+  moe_dispatch<KSET>(ch[3] >> 8, [&](auto k) { moe_w2_block<decltype(k)::value>(a, ch, cbp, red); });
+}
+
+// ---------------------------------------------------------------------------------------------------
+// 4. Combine: one thread per (token, 4 columns); sum over j in top-k order in fp32, one bf16 rounding.
+// ---------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int per_row = a.H / 4;
+  if (i >= int64_t(a.T) * per_row) return;
+  const int t = int(i / per_row), c = int(i % per_row) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int kB = 8;   // terms whose loads are issued together
+  for (int j0 = 0; j0 < a.topk; j0 += kB) {
+    float w[kB];
+    float4 v[kB];
+#pragma unroll
+    for (int r = 0; r < kB; ++r) {
+      const int j = j0 + r < a.topk ? j0 + r : a.topk - 1;
+      const int q = t * a.topk + j;
+      const bool use = j0 + r < a.topk && a.pslot[q] >= 0;
+      w[r] = use ? a.wts[q] : 0.f;
+      v[r] = use ? *reinterpret_cast<const float4*>(a.o + int64_t(q) * a.H + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int r = 0; r < kB; ++r) {   // top-k order; a dropped term adds exactly zero
+      acc.x += w[r] * v[r].x;
+      acc.y += w[r] * v[r].y;
+      acc.z += w[r] * v[r].z;
+      acc.w += w[r] * v[r].w;
+    }
+  }
+  const uint32_t lo = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
+  const uint32_t hi = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
+  *reinterpret_cast<uint2*>(a.out + int64_t(t) * a.H + c) = make_uint2(lo, hi);
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------------------------------
+int64_t moe_max_chunks(int64_t P, int E) { return (P + kMoeRows - 1) / kMoeRows + E; }
+
+static size_t moe_route_lds_bytes(int E, int P) {
+  return size_t(2 * E + (kRouteThreads / 64) * E + 48 + (P <= kSlotCache ? P : 0)) * sizeof(int);
+}
+
+hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream) {
+  MoeArgs a;
+  a.x = (const uint16_t*)m.x;
+  a.ids = m.ids;
+  a.wts = m.wts;
+  a.perm = m.perm;
+  a.w13 = (const uint16_t*)m.w13;
+  a.w2 = (const uint16_t*)m.w2;
+  a.w13_suh = (const uint16_t*)m.w13_suh;
+  a.w13_svh = (const uint16_t*)m.w13_svh;
+  a.w2_suh = (const uint16_t*)m.w2_suh;
+  a.w2_svh = (const uint16_t*)m.w2_svh;
+  a.off_w1 = m.off_w1;
+  a.off_w3 = m.off_w3;
+  a.off_w2 = m.off_w2;
+  a.out = (uint16_t*)m.out;
+  a.offs = m.offs;
+  a.pslot = m.pslot;
+  a.rows = m.rows;
+  a.chunks = (int4v*)m.chunks;
+  a.n_chunks = m.n_chunks;
+  a.xh13 = (uint16_t*)m.xh13;
+  a.ah = (uint16_t*)m.ah;
+  a.o = m.o;
+  a.T = int(m.T);
+  a.topk = m.topk;
+  a.P = int(m.T * m.topk);
+  a.E = m.E;
+  a.H = m.H;
+  a.I = m.I;
+  a.max_chunks = int(moe_max_chunks(a.P, m.E));
+  a.n_groups = m.n_groups;
+  for (int g = 0; g < kMoeMaxGroups; ++g) {
+    a.g_hi[g] = g < m.n_groups ? m.g_hi[g] : 0;
+    a.g_k[g] = g < m.n_groups ? m.g_k[g] : 0;
+  }
+  const int64_t rot_units = int64_t(a.T) * (a.H / kHad);
+  const int64_t rot_blocks = (rot_units + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
+  hipLaunchKernelGGL(moe_route_rotate_kernel, dim3(unsigned(1 + rot_blocks)), dim3(kRouteThreads),
+                     moe_route_lds_bytes(a.E, a.P), stream, a);
+  const int64_t cgroups = (a.max_chunks + 7) / 8 * 8;
+  const dim3 g13(unsigned(cgroups * (a.I / kHad))), g2(unsigned(cgroups * ((a.H / kHad + 1) / 2)));
+  for (int pass = 0; pass < 2; ++pass) {
+    // the K values of this projection, as a bit set
+    unsigned ks = 0;
+    for (int g = 0; g < m.n_groups; ++g) ks |= 1u << (pass == 0 ? (m.g_k[g] & 0xFF) : (m.g_k[g] >> 8));
+    auto go = [&](auto kset) {
+      constexpr int KS = decltype(kset)::value;
+      if (pass == 0)
+        hipLaunchKernelGGL(moe_w13_kernel<KS>, g13, dim3(kMoeWaves * 64), 0, stream, a);
+      else
+        hipLaunchKernelGGL(moe_w2_kernel<KS>, g2, dim3(kMoeWaves * 64), 0, stream, a);
+    };
+    if ((ks & ~0x1Cu) == 0) {
+      go(std::integral_constant<int, 0>{});
+    } else {
+      if (ks & (1u << 1)) go(std::integral_constant<int, 1>{});
+      if (ks & (1u << 2)) go(std::integral_constant<int, 2>{});
+      if (ks & (1u << 3)) go(std::integral_constant<int, 3>{});
+      if (ks & (1u << 4)) go(std::integral_constant<int, 4>{});
+      if (ks & (1u << 5)) go(std::integral_constant<int, 5>{});
+      if (ks & (1u << 6)) go(std::integral_constant<int, 6>{});
+      if (ks & (1u << 7)) go(std::integral_constant<int, 7>{});
+      if (ks & (1u << 8)) go(std::integral_constant<int, 8>{});
+    }
+  }
+  const int64_t comb = (int64_t(a.T) * (a.H / 4) + 255) / 256;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(unsigned(comb)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace exl3

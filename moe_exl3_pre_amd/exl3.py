@@ -209,3 +209,29 @@ def rotate_activations(x, s_in, rin, int8: bool = False):
     _check(lib().exl3_rotate_activations(_ptr(q), _ptr(sc), _ptr(x), M, IC, _ptr(s_in), _ptr(rin),
                                          ACT_INT8 if int8 else 0, _stream(x.device)))
     return (q, sc) if int8 else q
+
+
+# ------------------------------------------------------------------------------------------ MoE bank
+
+def moe_workspace_bytes(bank, T: int, topk: int, flags: int = 0) -> int:
+    return int(lib().exl3_moe_workspace_bytes(ctypes.byref(bank.struct), T, topk, flags))
+
+
+def moe_bank_forward(out, x, topk_ids, topk_w, bank, flags: int = 0, ws=None):
+    """out = sum_j topk_w[:, j] * expert_{topk_ids[:, j]}(x) for a DeviceBank; see exl3_moe_bank_forward."""
+    dev = x.device
+    T, H = x.shape
+    if H != bank.H:
+        raise ValueError(f"x: hidden size {H} does not match the bank's {bank.H}")
+    _need(x, "x", torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != T:
+        raise ValueError(f"topk_ids: shape {tuple(topk_ids.shape)} does not have T={T} rows")
+    topk = topk_ids.shape[1]
+    _need(topk_ids, "topk_ids", torch.int32, (T, topk), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, topk), dev)
+    if ws is None:
+        ws = alloc_workspace(moe_workspace_bytes(bank, T, topk, flags), dev)
+    _check(lib().exl3_moe_bank_forward(_ptr(out), _ptr(x), T, _ptr(topk_ids), _ptr(topk_w), topk,
+                                       ctypes.byref(bank.struct), flags, _ptr(ws), ws.numel(), _stream(dev)))
+    return out
