@@ -3,17 +3,24 @@
 Headline workload: the decode-phase merged gate_up projection (IC=4096; gate OC=14336 at K=2 and up
 OC=14336 at K=3 written into column slices of one bf16 [M, 28672] output), M=1.  One step = one call
 of the whole layer (activation pre-pass, both shards' trellis decode + contraction, split-K reduce,
-output Hadamard and scales).  The metric is GB/s of trellis words (the method's algorithmic bytes,
-IC*OC*K/8 per shard).  Weights rotate over 16 seeded copies (587 MB) so the 256 MiB Infinity Cache
-cannot serve them.  Steps are captured once in a HIP graph and replayed between events.
+output Hadamard and scales), which is one kernel launch.  The metric is GB/s of trellis words (the
+method's algorithmic bytes, IC*OC*K/8 per shard).  Weights rotate over 16 seeded copies (587 MB) so the
+256 MiB Infinity Cache cannot serve them.  Steps are captured once in a HIP graph and replayed between
+events recorded on the stream the kernels run on.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Also reported (under "extra"): decode M = 2, 4, 8; prefill M=8192 gate_up and down (TFLOP/s); the MoE
+expert bank (T=256, E=128, top-8, H=2048, I=768; 3 rotated banks).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill] [--no-moe]
+    python bench.py --pmc-ref ...     # eager launches plus a 1 GiB copy, for counter runs
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,7 +31,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "EXL3 linear GB/s (trellis bytes) at M=1 & TFLOP/s at M=8192; % roofline"
 HBM_PEAK_GBS = 8000.0
+F16_PEAK_TFLOPS = 2500.0
 COPIES = 16
+MOE_COPIES = 3
+DECODE_KERNEL = "exl3::decode_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_gate_up_m1.md")
+# sources whose change invalidates the stored counter readings of the decode kernel
+TRAFFIC_SOURCES = ["moe_exl3_pre_amd/csrc/k_decode.hip", "moe_exl3_pre_amd/csrc/exl3_device.hpp",
+                   "moe_exl3_pre_amd/csrc/exl3_internal.hpp"]
 
 
 def parse():
@@ -35,7 +49,31 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extra-m", default="2,4,8", help="additional decode M values reported under 'extra'")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 prefill measurements")
+    ap.add_argument("--no-moe", action="store_true", help="skip the MoE bank measurement")
+    ap.add_argument("--pmc-ref", action="store_true",
+                    help="eager decode launches (no graph) plus a plain 1 GiB copy, for hardware-counter runs")
     return ap.parse_args()
+
+
+def sources_sha() -> str:
+    h = hashlib.sha256()
+    for p in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch of the decode kernel from the committed counter summary, or None when the
+    summary is missing or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_sha = re.search(r"sources_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != sources_sha():
+        return None
+    return float(m_b.group(1))
 
 
 def build_gate_up(torch, dev, synth, copies):
@@ -58,15 +96,14 @@ def build_gate_up(torch, dev, synth, copies):
     return IC, col, sets, trellis_bytes
 
 
-def time_decode(torch, exl3, dev, x, out, sets, steps, warmup):
-    """Capture `warmup` and `steps` rotated calls in two graphs; return seconds per step."""
-    M, IC = x.shape
-    ws = exl3.alloc_workspace(max(exl3.linear_multi_workspace_bytes(M, IC, s) for s in sets), dev)
+def graph_time(torch, step, steps, warmup):
+    """Capture `warmup` and `steps` calls of step(i) in two graphs; return seconds per step measured with
+    events on the current stream (the stream the kernels are launched on)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for s in sets:
-            exl3.linear_multi_into(out, x, s, ws=ws)
+        for i in range(3):
+            step(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graphs = []
@@ -74,17 +111,24 @@ def time_decode(torch, exl3, dev, x, out, sets, steps, warmup):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(n):
-                exl3.linear_multi_into(out, x, sets[i % len(sets)], ws=ws)
+                step(i)
         graphs.append(g)
     torch.cuda.synchronize()
     graphs[0].replay()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
+    t0.record(stream)
     graphs[1].replay()
-    t1.record()
+    t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / 1e3 / steps
+
+
+def time_decode(torch, exl3, dev, x, out, sets, steps, warmup):
+    M, IC = x.shape
+    ws = exl3.alloc_workspace(max(exl3.linear_multi_workspace_bytes(M, IC, s) for s in sets), dev)
+    return graph_time(torch, lambda i: exl3.linear_multi_into(out, x, sets[i % len(sets)], ws=ws), steps, warmup)
 
 
 def time_prefill(torch, exl3, synth, dev, reps=5):
@@ -111,11 +155,12 @@ def time_prefill(torch, exl3, synth, dev, reps=5):
         ws = exl3.alloc_workspace(exl3.linear_multi_workspace_bytes(M, IC, sh), dev)
         exl3.linear_multi_into(out, x, sh, ws=ws)
         torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
+        t0.record(stream)
         for _ in range(reps):
             exl3.linear_multi_into(out, x, sh, ws=ws)
-        t1.record()
+        t1.record(stream)
         torch.cuda.synchronize()
         sec = t0.elapsed_time(t1) / 1e3 / reps
         res[name] = (sec, 2.0 * M * IC * col)
@@ -123,6 +168,30 @@ def time_prefill(torch, exl3, synth, dev, reps=5):
               file=sys.stderr, flush=True)
         del x, out, ws, sh
     return res
+
+
+def time_moe(torch, exl3, synth, dev, steps=60):
+    """MoE bank T=256, E=128, top-8, H=2048, I=768, K in {2,3,4}: 3 banks rotated (~665 MB of trellis)."""
+    from moe_exl3_pre_amd.bank import DeviceBank, pack_bank
+    cfg = synth.MOE
+    banks = []
+    for r in range(MOE_COPIES):
+        m = synth.moe_case(1003 + r, T=cfg["T"], E=cfg["E"], topk=cfg["topk"], H=cfg["H"], I=cfg["I"], Ks=cfg["Ks"])
+        banks.append(DeviceBank(pack_bank(m["experts"], cfg["H"], cfg["I"]), dev))
+        if r == 0:
+            x = torch.from_numpy(m["x_bits"].view(np.int16).copy()).to(dev).view(torch.bfloat16)
+            ids = torch.from_numpy(m["topk_ids"].astype(np.int32)).to(dev)
+            w = torch.from_numpy(m["topk_w"].astype(np.float32)).to(dev)
+            used = np.unique(m["topk_ids"])
+    # trellis of the experts the routing touches, averaged over the rotated banks (their K draws differ)
+    tb = sum(b.packed.trellis_bytes([int(b.packed.perm[e]) for e in used]) for b in banks) / MOE_COPIES
+    out = torch.empty_like(x)
+    ws = exl3.alloc_workspace(exl3.moe_workspace_bytes(banks[0], cfg["T"], cfg["topk"]), dev)
+    sec = graph_time(torch, lambda i: exl3.moe_bank_forward(out, x, ids, w, banks[i % MOE_COPIES], ws=ws), steps,
+                     MOE_COPIES * 2)
+    print(f"# moe T={cfg['T']} E={cfg['E']} top{cfg['topk']}: {sec * 1e6:.1f} us/call, "
+          f"{tb / sec / 1e9:.1f} GB/s trellis ({tb / 1e6:.1f} MB touched)", file=sys.stderr, flush=True)
+    return sec, tb
 
 
 def cpu_baseline(synth, O):
@@ -141,6 +210,21 @@ def cpu_baseline(synth, O):
                        f"{dt:.1f} s")
 
 
+def pmc_reference(torch, exl3, dev, x, out, sets):
+    """Eager launches for counter runs: 1 GiB device copies (known bytes), then decode steps."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    M, IC = x.shape
+    ws = exl3.alloc_workspace(max(exl3.linear_multi_workspace_bytes(M, IC, s) for s in sets), dev)
+    for i in range(4 * len(sets)):
+        exl3.linear_multi_into(out, x, sets[i % len(sets)], ws=ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_reference": True, "copy_bytes": 1 << 30, "decode_launches": 4 * len(sets),
+                      "sources_sha256_16": sources_sha()}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -154,6 +238,11 @@ def main():
 
     IC, ldo, sets, trellis_bytes = build_gate_up(torch, dev, synth, COPIES)
     rng = np.random.default_rng(77)
+    if a.pmc_ref:
+        _, xb = synth.random_activations(rng, 1, IC)
+        x = torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        pmc_reference(torch, exl3, dev, x, torch.empty((1, ldo), dtype=torch.bfloat16, device=dev), sets)
+        return
     results = {}
     for M in [1] + [int(m) for m in a.extra_m.split(",") if m]:
         _, xb = synth.random_activations(rng, M, IC)
@@ -166,9 +255,11 @@ def main():
               file=sys.stderr, flush=True)
 
     prefill = {} if a.no_prefill else time_prefill(torch, exl3, synth, dev)
+    moe = None if a.no_moe else time_moe(torch, exl3, synth, dev)
 
     sec = results[1]
     gbs = trellis_bytes / sec / 1e9
+    traffic = stored_traffic()
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(sec * 1e3, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -176,15 +267,22 @@ def main():
         "config": {"workload": "decode gate_up: IC=4096, gate OC=14336 K=2 | up OC=14336 K=3, M=1, "
                                f"{COPIES} rotated weight copies", "M": 1, "IC": IC, "OC": [14336, 14336], "K": [2, 3],
                    "trellis_bytes_per_step": trellis_bytes},
+        # one step is one launch of the decode kernel, so the per-step event time is its launch duration
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "whole step (pre-pass + both shards' decode-phase kernels)"},
-        "extra": {f"decode_M{M}": {"us_per_step": round(s * 1e6, 3), "trellis_GBps": round(trellis_bytes / s / 1e9, 1)}
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": DECODE_KERNEL,
+                     "kernel_us": round(sec * 1e6, 3), "bytes_per_launch": trellis_bytes},
+        "extra": {f"decode_M{M}": {"us_per_step": round(s * 1e6, 3), "trellis_GBps": round(trellis_bytes / s / 1e9, 1),
+                                   "frac_hbm": round(trellis_bytes / s / 1e9 / HBM_PEAK_GBS, 4)}
                   for M, s in results.items()},
     }
     for name, (s, flop) in prefill.items():
         line["extra"][f"prefill_{name}_M8192"] = {"ms_per_call": round(s * 1e3, 4), "TFLOPs": round(flop / s / 1e12, 1),
-                                                  "frac_of_fp16_peak": round(flop / s / 2.5e15, 4)}
+                                                  "frac_of_f16_peak": round(flop / s / 1e12 / F16_PEAK_TFLOPS, 4)}
+    if moe is not None:
+        s, tb = moe
+        line["extra"]["moe_T256_E128_top8"] = {"us_per_call": round(s * 1e6, 2), "trellis_MB": round(tb / 1e6, 1),
+                                               "trellis_GBps": round(tb / s / 1e9, 1),
+                                               "frac_hbm": round(tb / s / 1e9 / HBM_PEAK_GBS, 4)}
     if not a.no_cpu:
         from oracle import exl3_oracle as O
         line["cpu_baseline"] = cpu_baseline(synth, O)
