@@ -29,6 +29,7 @@ struct DecPlan {
   int S[kMaxShards];        // per shard: blocks per 128-column output block along the input features
   int spw;                  // unrolled 64-feature steps per wave (1, 2, 4, 8)
   int lds_row;              // halves per activation row in LDS
+  int tr_off;               // LDS byte offset of the trellis staging slots
   size_t lds_bytes;         // dynamic LDS per block
   int kset;                 // kernel K set: 1..8 single K, 0 mixed {2,3,4}, -1 unsupported mix
   int order[kMaxShards];    // shard processed in grid position r

@@ -48,14 +48,22 @@ struct DecArgs {
   uint16_t* out;                 // bf16 [M, ldo]
   int64_t ldo;
   int M, IC, n_shards, lds_row;  // lds_row: halves per activation row in LDS (padded)
+  int tr_off;                    // byte offset of the per-wave trellis staging slots in LDS
   DecShard sh[kMaxShards];
+};
+
+// Per-wave LDS slot holding one 64-feature step of trellis words: 4 tile rows (g) x 8 tiles x 8K words,
+// each tile row padded by 16 words so the four groups of 16 lanes read different banks.
+template <int K>
+struct Slot {
+  static constexpr int kRowBytes = 256 * K + 64;
+  static constexpr int kBytes = 4 * kRowBytes;
 };
 
 template <int K, int SPW, int MR>
 __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& sh, int local, char* lds) {
   using G = Geom<K>;
-  constexpr int kPipe = G::kNW <= 2 ? 16 : (36 / G::kNW);            // units in flight per wave
-  constexpr int kUnits = SPW * kNB;                                 // (step, tile column) units per wave
+  constexpr int kD = K <= 3 ? 3 : 2;                                // steps of trellis words in flight per wave
   constexpr int kPB = SPW > 1 ? SPW / 2 : 1;                        // Hadamard blocks per wave (pre-pass)
   static_assert(SPW % 2 == 0, "steps come in Hadamard-block pairs");
 
@@ -96,30 +104,27 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   }
   __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the weight stream
 
-  // ---- 2. the first kPipe units of the weight stream
-  int woff[G::kNW], shift;
-  column_word_offsets<K>(n, woff, shift);
+  // ---- 2. the first kD steps of the weight stream, as coalesced 16-byte loads.  One step of this
+  // block is 4 tile rows (lane group g) x 8 tiles x 8K words: each lane group reads its tile row's
+  // 256K contiguous bytes with K loads of 16 bytes per lane.
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(sh.code), (short)0, (int)sh.code_bytes, kBufferFlags);
-  uint32_t lane_off[G::kNW];
-#pragma unroll
-  for (int w = 0; w < G::kNW; ++w) lane_off[w] = (uint32_t(g) * tpr * G::kWords + uint32_t(woff[w])) * 4u;
+  const uint32_t lane_off = uint32_t(g) * tpr * G::kWords * 4u + uint32_t(n) * 16u;
   const uint32_t step_stride = 4u * tpr * G::kWords * 4u;
   const uint32_t base_blk = uint32_t(blk) * kNB * G::kWords * 4u;
-  uint32_t buf[kPipe][G::kNW];
-  auto load_unit = [&](int u, uint32_t (&dst)[G::kNW]) {
-    const int st = u / kNB, j = u % kNB;
+  u32x4 tb[kD][K];
+  auto load_step = [&](int st, u32x4 (&dst)[K]) {
     // Steps past this wave's count (their results are never used) re-read a step of this block's own
     // range, so every address stays inside the tensor: the buffer range check covers only the vector
     // offset, not the scalar one used here.
     const int step = 2 * ba + (cnt > 0 ? w_s0 + (st < cnt ? st : cnt - 1) : 0);
     const uint32_t soff = uint32_t(step) * step_stride + base_blk;
 #pragma unroll
-    for (int w = 0; w < G::kNW; ++w)
-      dst[w] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off[w] + uint32_t(j * G::kWords * 4), soff, 0);
+    for (int i = 0; i < K; ++i)
+      dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off + uint32_t(i * 256), soff, 0));
   };
 #pragma unroll
-  for (int u = 0; u < kPipe && u < kUnits; ++u) load_unit(u, buf[u]);
+  for (int d = 0; d < kD; ++d) load_step(d, tb[d]);
 
   // ---- 3. this wave's rotated activations into LDS (PERM16 order); its part of row M stays zero
 #pragma unroll
@@ -142,27 +147,47 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
     }
   }
 
-  // ---- 4. stream, decode, multiply (reads only this wave's own LDS slice: no barrier needed)
+  // ---- 4. per step: stage the words in this wave's LDS slot, then every lane reads the words of its
+  // tile column (column n of tile row g), decodes them into MFMA B operands and accumulates.  Only
+  // this wave touches its slot and its slice of xs, so no barrier is needed; LDS operations of one wave
+  // complete in order, so the reads of a step see that step's writes and the next step's writes do
+  // not overtake this step's reads.
+  char* slot = lds + a.tr_off + wave * Slot<K>::kBytes;
+  char* my_row = slot + g * Slot<K>::kRowBytes;
+  int woff[G::kNW], shift;
+  column_word_offsets<K>(n, woff, shift);
   const CodebookRegs cb = codebook_regs();
   float4v acc[kNB];
 #pragma unroll
   for (int j = 0; j < kNB; ++j) acc[j] = (float4v){0.f, 0.f, 0.f, 0.f};
   const uint16_t* xa = xs + (n < M ? n : M) * lrow + 64 * w_s0 + 16 * g;   // row n, or the zero row
-  half8 a0 = {}, a1 = {};
 #pragma unroll
-  for (int u = 0; u < kUnits; ++u) {
-    const int st = u / kNB, j = u % kNB;
+  for (int st = 0; st < SPW; ++st) {
     if (st < cnt) {
-      if (j == 0) {
-        a0 = *reinterpret_cast<const half8*>(xa + 64 * st);
-        a1 = *reinterpret_cast<const half8*>(xa + 64 * st + 8);
-      }
-      uint32_t b[8];
-      decode_column<K>(buf[u % kPipe], shift, b, cb);
-      acc[j] = mfma16(a0, as_half8(b[0], b[1], b[2], b[3]), acc[j]);
-      acc[j] = mfma16(a1, as_half8(b[4], b[5], b[6], b[7]), acc[j]);
+#pragma unroll
+      for (int i = 0; i < K; ++i)
+        *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tb[st % kD][i];
     }
-    if (u + kPipe < kUnits) load_unit(u + kPipe, buf[u % kPipe]);
+    load_step(st + kD, tb[st % kD]);
+    if (st < cnt) {
+      const half8 a0 = *reinterpret_cast<const half8*>(xa + 64 * st);
+      const half8 a1 = *reinterpret_cast<const half8*>(xa + 64 * st + 8);
+      uint32_t wv[2][G::kNW];
+      auto read_col = [&](int j, uint32_t (&dst)[G::kNW]) {
+#pragma unroll
+        for (int w = 0; w < G::kNW; ++w)
+          dst[w] = *reinterpret_cast<const uint32_t*>(my_row + (j * G::kWords + woff[w]) * 4);
+      };
+      read_col(0, wv[0]);
+#pragma unroll
+      for (int j = 0; j < kNB; ++j) {
+        if (j + 1 < kNB) read_col(j + 1, wv[(j + 1) & 1]);
+        uint32_t b[8];
+        decode_column<K>(wv[j & 1], shift, b, cb);
+        acc[j] = mfma16(a0, as_half8(b[0], b[1], b[2], b[3]), acc[j]);
+        acc[j] = mfma16(a1, as_half8(b[4], b[5], b[6], b[7]), acc[j]);
+      }
+    }
   }
 
   // ---- 5. sum the 16 waves' partials in LDS (fixed order), one wave per output row
@@ -178,23 +203,33 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   __syncthreads();
 
   const int64_t c0 = int64_t(blk) * kHad + 2 * lane;        // shard-local column of (v0, v1)
-  float v0 = 0.f, v1 = 0.f;
-  if (wave < M) {
+  constexpr int kRW = (kDecodeMaxRows + kWaves - 1) / kWaves; // output rows per wave: wave + t * kWaves
+  float v0[kRW], v1[kRW];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* p = red + (w * M + wave) * kHad + 2 * lane;
-      v0 += p[0];
-      v1 += p[1];
+  for (int t = 0; t < kRW; ++t) {
+    const int row = wave + t * kWaves;
+    v0[t] = v1[t] = 0.f;
+    if (row < M) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* p = red + (w * M + row) * kHad + 2 * lane;
+        v0[t] += p[0];
+        v1[t] += p[1];
+      }
     }
   }
 
   if (sh.S > 1) {
     // ---- 6a. split-K hand-off: coherent partial stores, then one counter bump per block
     const int64_t OC = sh.OC;
-    if (wave < M) {
-      float* dst = sh.slab + (int64_t(s) * M + wave) * OC + c0;
-      __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(dst + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int t = 0; t < kRW; ++t) {
+      const int row = wave + t * kWaves;
+      if (row < M) {
+        float* dst = sh.slab + (int64_t(s) * M + row) * OC + c0;
+        __hip_atomic_store(dst, v0[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 1, v1[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);                          // this wave's partial stores have completed
@@ -206,28 +241,37 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
     __syncthreads();
     const int old = *flag;
     if (old != sh.S - 1) return;                            // not the last split of this block
-    if (wave < M) {
-      v0 = v1 = 0.f;
-      for (int sp = 0; sp < sh.S; ++sp) {
-        float* src = sh.slab + (int64_t(sp) * M + wave) * OC + c0;
-        v0 += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v1 += __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int t = 0; t < kRW; ++t) {
+      const int row = wave + t * kWaves;
+      if (row < M) {
+        v0[t] = v1[t] = 0.f;
+        for (int sp = 0; sp < sh.S; ++sp) {
+          float* src = sh.slab + (int64_t(sp) * M + row) * OC + c0;
+          v0[t] += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v1[t] += __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
     if (threadIdx.x == 0) __hip_atomic_store(sh.counters + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- 6. output Hadamard-128, rout * s_out, bf16 into the slice
-  if (wave < M) {
-    had128_wave(v0, v1, lane);
-    v0 = v0 * kInvSqrt128 * f16_to_f32(sh.rout[c0]) * f16_to_f32(sh.s_out[c0]);
-    v1 = v1 * kInvSqrt128 * f16_to_f32(sh.rout[c0 + 1]) * f16_to_f32(sh.s_out[c0 + 1]);
-    uint16_t* dst = a.out + int64_t(wave) * a.ldo + sh.col0 + c0;
-    if (((a.ldo | sh.col0) & 1) == 0) {
-      *reinterpret_cast<uint32_t*>(dst) = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
-    } else {
-      dst[0] = (uint16_t)f32_to_bf16(v0);
-      dst[1] = (uint16_t)f32_to_bf16(v1);
+#pragma unroll
+  for (int t = 0; t < kRW; ++t) {
+    const int row = wave + t * kWaves;
+    if (row < M) {
+      float x0 = v0[t], x1 = v1[t];
+      had128_wave(x0, x1, lane);
+      x0 = x0 * kInvSqrt128 * f16_to_f32(sh.rout[c0]) * f16_to_f32(sh.s_out[c0]);
+      x1 = x1 * kInvSqrt128 * f16_to_f32(sh.rout[c0 + 1]) * f16_to_f32(sh.s_out[c0 + 1]);
+      uint16_t* dst = a.out + int64_t(row) * a.ldo + sh.col0 + c0;
+      if (((a.ldo | sh.col0) & 1) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = f32_to_bf16(x0) | (f32_to_bf16(x1) << 16);
+      } else {
+        dst[0] = (uint16_t)f32_to_bf16(x0);
+        dst[1] = (uint16_t)f32_to_bf16(x1);
+      }
     }
   }
 }
@@ -259,27 +303,37 @@ namespace {
 int spw_variant(int need) { return need <= 2 ? 2 : 4; }
 constexpr int kMaxSpw = 4;     // wider variants exceed the 128 registers a 1024-thread block allows
 
-size_t lds_bytes_for(int M, int lds_row) {
-  const size_t xs = size_t(M + 1) * lds_row * 2;
+// K whose staging slots size the LDS: the mixed-K launch serves {2, 3, 4} with one layout, so any shard of
+// K <= 4 is planned with K = 4's slots (a shard's plan must not depend on the other shards of a call).
+int lds_k(int K) { return K <= 4 ? 4 : K; }
+
+size_t tr_offset(int M, int lds_row) { return (size_t(M + 1) * lds_row * 2 + 15) / 16 * 16; }
+
+size_t slot_bytes(int K) { return size_t(4) * (256 * K + 64); }
+
+// LDS of one block: rotated activations, then the waves' trellis staging slots; the reduction buffer
+// reuses the same space after the main loop.
+size_t lds_bytes_for(int M, int lds_row, int K) {
+  const size_t main = tr_offset(M, lds_row) + size_t(kWaves) * slot_bytes(lds_k(K));
   const size_t red = size_t(kWaves) * M * kHad * 4;
-  return xs > red ? xs : red;
+  return main > red ? main : red;
 }
 
 }  // namespace
 
-// Splits of one shard's feature range.  A function of (M, IC, OC) alone -- never of the other shards in
-// the call -- so a merged call reduces every shard in the same order as a call of that shard by itself
-// and the two agree bit for bit.  Split only as far as needed: until the shard has kFillBlocks blocks
+// Splits of one shard's feature range.  A function of (M, IC, OC, K) alone -- never of the other shards
+// in the call -- so a merged call reduces every shard in the same order as a call of that shard by
+// itself and the two agree bit for bit.  Split only as far as needed: until the shard has kFillBlocks blocks
 // (C1's 14336-column shards already do, and together fill 224 of the 256 CUs), a wave's steps fit the
 // largest unrolled variant, and the activation slice fits in LDS.
 constexpr int kFillBlocks = 112;
 
-int shard_splits(int64_t M, int B, int nblk) {
+int shard_splits(int64_t M, int B, int nblk, int K) {
   for (int S = 1;; ++S) {
     if (S >= B) return B;
     const int nb_max = (B + S - 1) / S;
     const int spw_need = 2 * ((nb_max + kWaves - 1) / kWaves);   // whole Hadamard blocks per wave
-    const bool lds_ok = lds_bytes_for(int(M), kHad * nb_max + 8) <= kMaxLds;
+    const bool lds_ok = lds_bytes_for(int(M), kHad * nb_max + 8, K) <= kMaxLds;
     if (spw_need <= kMaxSpw && lds_ok && (nblk * S >= kFillBlocks || nb_max <= kWaves)) return S;
   }
 }
@@ -289,13 +343,16 @@ bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl
   const int B = int(IC / kHad);
   int nb_max = 1;
   for (int i = 0; i < n; ++i) {
-    pl->S[i] = shard_splits(M, B, int(in[i].OC / kHad));
+    pl->S[i] = shard_splits(M, B, int(in[i].OC / kHad), in[i].K);
     const int nb = (B + pl->S[i] - 1) / pl->S[i];
     nb_max = nb > nb_max ? nb : nb_max;
   }
   pl->spw = spw_variant(2 * ((nb_max + kWaves - 1) / kWaves));
+  int kmax = 1;
+  for (int i = 0; i < n; ++i) kmax = in[i].K > kmax ? in[i].K : kmax;
   pl->lds_row = kHad * nb_max + 8;
-  pl->lds_bytes = lds_bytes_for(int(M), pl->lds_row);
+  pl->tr_off = int(tr_offset(int(M), pl->lds_row));
+  pl->lds_bytes = lds_bytes_for(int(M), pl->lds_row, kmax);
   if (pl->lds_bytes > kMaxLds) return false;
   // heavier shards (larger K) first: blocks are dispatched in index order
   int order[kMaxShards];
@@ -365,6 +422,7 @@ hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC
   a.IC = (int)IC;
   a.n_shards = n;
   a.lds_row = pl.lds_row;
+  a.tr_off = pl.tr_off;
   for (int r = 0; r < n; ++r) {
     const DecShardIn& s = in[pl.order[r]];
     DecShard& d = a.sh[r];
