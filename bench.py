@@ -132,8 +132,9 @@ def time_decode(torch, exl3, dev, x, out, sets, steps, warmup):
 
 
 def time_prefill(torch, exl3, synth, dev, reps=5):
-    """M=8192 prefill projections: gate_up (IC=5120 -> 2 x 17408, K=2 | K=3) and down (17408 -> 5120, K=3).
-    Returns {name: (seconds per call, FLOP per call)}; FLOP = 2*M*IC*OC (decode and transforms not counted)."""
+    """M=8192 prefill projections: gate_up (IC=5120 -> 2 x 17408, K=2 | K=3) and down (17408 -> 5120, K=3),
+    each on the 16-bit and on the 8-bit activation path.  Returns {name: (seconds per call, FLOP per call)};
+    FLOP = 2*M*IC*OC (decode and transforms not counted)."""
     p = synth.PREFILL
     M = p["M"]
     res = {}
@@ -152,21 +153,23 @@ def time_prefill(torch, exl3, synth, dev, reps=5):
                            rout=torch.from_numpy(d["rout"]).to(dev), s_out=torch.from_numpy(d["s_out"]).to(dev)))
             col += OC
         out = torch.empty((M, col), dtype=torch.bfloat16, device=dev)
-        ws = exl3.alloc_workspace(exl3.linear_multi_workspace_bytes(M, IC, sh), dev)
-        exl3.linear_multi_into(out, x, sh, ws=ws)
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(reps):
-            exl3.linear_multi_into(out, x, sh, ws=ws)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        sec = t0.elapsed_time(t1) / 1e3 / reps
-        res[name] = (sec, 2.0 * M * IC * col)
-        print(f"# prefill {name} M={M}: {sec * 1e3:.3f} ms/call, {res[name][1] / sec / 1e12:.1f} TFLOP/s",
-              file=sys.stderr, flush=True)
-        del x, out, ws, sh
+        for tag, flags in (("", 0), ("_int8", exl3.ACT_INT8)):
+            ws = exl3.alloc_workspace(exl3.linear_multi_workspace_bytes(M, IC, sh, flags), dev)
+            exl3.linear_multi_into(out, x, sh, flags=flags, ws=ws)
+            torch.cuda.synchronize()
+            stream = torch.cuda.current_stream()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(reps):
+                exl3.linear_multi_into(out, x, sh, flags=flags, ws=ws)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            sec = t0.elapsed_time(t1) / 1e3 / reps
+            res[name + tag] = (sec, 2.0 * M * IC * col)
+            print(f"# prefill {name}{tag} M={M}: {sec * 1e3:.3f} ms/call, {res[name + tag][1] / sec / 1e12:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+            del ws
+        del x, out, sh
     return res
 
 

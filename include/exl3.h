@@ -56,8 +56,8 @@ typedef enum {
 
 /* flags */
 enum {
-  EXL3_ACT_INT8 = 1u << 0,   /* per-row 8-bit activations: sc = max|xh| / 127, q = clamp(rne(xh / sc), +-127);
-                                 the linear entry points answer EXL3_EUNSUPPORTED for now */
+  EXL3_ACT_INT8 = 1u << 0,   /* per-row 8-bit activations: sc = max|xh| / 127, q = clamp(rne(xh / sc), +-127),
+                                 Y = sc * (q . W); runs on the MFMA GEMM at every M (not with FORCE_GEMV) */
   EXL3_FORCE_GEMV = 1u << 1, /* force the decode-phase (streaming split-K) kernel whatever M is */
   EXL3_FORCE_MFMA = 1u << 2  /* force the prefill-phase (tiled MFMA GEMM) kernel whatever M is */
 };
@@ -88,7 +88,10 @@ int64_t exl3_gemv_max_rows(void);
  * fp16 products accumulated in fp32, output transform and scales in fp32, one round-to-nearest-even to
  * bf16.  Row results do not depend on the other rows; M <= exl3_gemv_max_rows() runs the decode-phase
  * kernel, larger M the MFMA GEMM (the two agree to rounding, not bitwise).
- * Returns EXL3_OK, EXL3_EINVAL, EXL3_EWORKSPACE, EXL3_EUNSUPPORTED (EXL3_ACT_INT8, not provided yet),
+ * 8-bit path (EXL3_ACT_INT8): the codes q are exact in fp16 and every q * W product is exact in fp32,
+ * so the contraction is the integer dot product up to fp32 summation; the row scale is applied before
+ * the output transform.
+ * Returns EXL3_OK, EXL3_EINVAL, EXL3_EWORKSPACE, EXL3_EUNSUPPORTED (EXL3_ACT_INT8 with EXL3_FORCE_GEMV),
  * EXL3_ELAUNCH.
  * ------------------------------------------------------------------------------------------------ */
 size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned flags);

@@ -45,7 +45,8 @@ int check_flags(unsigned flags) {
   if (flags & ~kKnownFlags) return fail(EXL3_EINVAL, "flags: unknown bits 0x%x", flags & ~kKnownFlags);
   if ((flags & EXL3_FORCE_GEMV) && (flags & EXL3_FORCE_MFMA))
     return fail(EXL3_EINVAL, "flags: EXL3_FORCE_GEMV and EXL3_FORCE_MFMA are exclusive");
-  if (flags & EXL3_ACT_INT8) return fail(EXL3_EUNSUPPORTED, "flags: EXL3_ACT_INT8 is not available in this build");
+  if ((flags & EXL3_ACT_INT8) && (flags & EXL3_FORCE_GEMV))
+    return fail(EXL3_EUNSUPPORTED, "flags: the 8-bit path runs on the MFMA GEMM; EXL3_FORCE_GEMV cannot be combined with it");
   return EXL3_OK;
 }
 
@@ -80,6 +81,7 @@ int check_shard(const char* who, int64_t IC, const int16_t* code, int64_t OC, in
 
 // The prefill/decode choice is made here, inside the op, by M ("radiance_escha.py", `escha_linear_into`).
 bool use_decode_path(int64_t M, unsigned flags) {
+  if (flags & EXL3_ACT_INT8) return false;   // the row amax needs the whole row before any product
   if (flags & EXL3_FORCE_GEMV) return true;
   if (flags & EXL3_FORCE_MFMA) return false;
   return M <= kGemvMaxRows;
@@ -112,15 +114,17 @@ bool decode_slab_bytes(int64_t M, int64_t IC, int n, const DecShardIn* in, size_
 struct Layout {
   size_t slab_off, slab_bytes;   // decode-phase split-K slab
   size_t xh_off, xh_bytes;       // prefill-phase rotated activations, one region per distinct (s_in, rin)
+  size_t scale_off;              // 8-bit path: the row scales, at this offset inside each region
   size_t total;
 };
 
-Layout layout_for(size_t slab_bytes, int64_t M = 0, int64_t IC = 0, int n_xh = 0) {
+Layout layout_for(size_t slab_bytes, int64_t M = 0, int64_t IC = 0, int n_xh = 0, bool int8 = false) {
   Layout L;
   L.slab_off = align_up(kCounterBytes);
   L.slab_bytes = align_up(slab_bytes);
   L.xh_off = L.slab_off + L.slab_bytes;
-  L.xh_bytes = align_up(size_t(M) * size_t(IC) * 2);
+  L.scale_off = align_up(size_t(M) * size_t(IC) * 2);
+  L.xh_bytes = L.scale_off + (int8 ? align_up(size_t(M) * 4) : 0);
   L.total = L.xh_off + L.xh_bytes * size_t(n_xh);
   return L;
 }
@@ -170,20 +174,26 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
   return EXL3_OK;
 }
 
-// The prefill-phase path: one pre-pass per distinct (s_in, rin), then one GEMM per shard.
+// The prefill-phase path: one pre-pass per distinct (s_in, rin), then one GEMM per shard.  On the 8-bit
+// path the pre-pass writes the integer codes (as fp16 numbers, exact) and the row scales, and the GEMM
+// applies the row scale in its epilogue.
 int run_gemm(const char* who, void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,
-             char* ws, const Layout& L, hipStream_t stream) {
+             char* ws, const Layout& L, unsigned flags, hipStream_t stream) {
+  const bool int8 = (flags & EXL3_ACT_INT8) != 0;
   int slot[kMaxShards];
   distinct_inputs(n, in, slot);
   int done = -1;
   for (int i = 0; i < n; ++i) {
-    void* xh = ws + L.xh_off + L.xh_bytes * size_t(slot[i]);
+    char* region = ws + L.xh_off + L.xh_bytes * size_t(slot[i]);
+    float* scale = int8 ? reinterpret_cast<float*>(region + L.scale_off) : nullptr;
     if (slot[i] > done) {
-      if (int rc = launch_status(launch_prepass_f16(x, in[i].s_in, in[i].rin, xh, M, IC, true, stream), who)) return rc;
+      hipError_t e = int8 ? launch_prepass_i8(x, in[i].s_in, in[i].rin, region, scale, M, IC, true, stream, true)
+                          : launch_prepass_f16(x, in[i].s_in, in[i].rin, region, M, IC, true, stream);
+      if (int rc = launch_status(e, who)) return rc;
       done = slot[i];
     }
-    hipError_t e = launch_gemm(xh, in[i].code, in[i].K, in[i].rout, in[i].s_out, out, ldo, in[i].col0, M, IC, in[i].OC,
-                               stream);
+    hipError_t e = launch_gemm(region, in[i].code, in[i].K, in[i].rout, in[i].s_out, out, ldo, in[i].col0, M, IC,
+                               in[i].OC, stream, scale);
     if (int rc = launch_status(e, who)) return rc;
   }
   return EXL3_OK;
@@ -284,7 +294,7 @@ bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsign
     *L = layout_for(slab);
   } else {
     int slot[kMaxShards];
-    *L = layout_for(0, M, IC, distinct_inputs(n, in, slot));
+    *L = layout_for(0, M, IC, distinct_inputs(n, in, slot), (flags & EXL3_ACT_INT8) != 0);
   }
   return true;
 }
@@ -313,7 +323,7 @@ int exl3_linear_into(void* out, int64_t ldo, int64_t col0, const void* x, int64_
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rc = use_decode_path(M, flags)
                      ? run_decode("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, st)
-                     : run_gemm("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, st);
+                     : run_gemm("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, flags, st);
   if (rc) return rc;
   return ok();
 }
@@ -354,7 +364,8 @@ int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rc = use_decode_path(M, flags)
                      ? run_decode("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L, st)
-                     : run_gemm("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L, st);
+                     : run_gemm("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L, flags,
+                                st);
   if (rc) return rc;
   return ok();
 }

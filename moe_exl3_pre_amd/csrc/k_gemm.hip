@@ -32,6 +32,7 @@ struct GemmArgs {
   const uint32_t* code;
   const uint16_t* rout;
   const uint16_t* s_out;
+  const float* row_scale;   // 8-bit path: per-row scale of the integer codes in xh (else null)
   uint16_t* out;            // bf16 [M, ldo]
   int64_t ldo, col0;
   int M, IC, OC;
@@ -218,18 +219,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + 16 * mb + 4 * g + r;
       if (row < p.M) {
+        // the row scale commutes with the column transform; 1.0 on the 16-bit path (exact)
+        const float rs = p.row_scale ? p.row_scale[row] : 1.0f;
         uint16_t* dst = p.out + int64_t(row) * p.ldo + p.col0 + col0 + n;
 #pragma unroll
-        for (int nb = 0; nb < kNBW; ++nb) dst[16 * nb] = (uint16_t)f32_to_bf16(v[nb][r] * sc[nb]);
+        for (int nb = 0; nb < kNBW; ++nb) dst[16 * nb] = (uint16_t)f32_to_bf16(v[nb][r] * rs * sc[nb]);
       }
     }
   }
 }
 
 hipError_t launch_gemm(const void* xh, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
-                       int64_t ldo, int64_t col0, int64_t M, int64_t IC, int64_t OC, hipStream_t stream) {
+                       int64_t ldo, int64_t col0, int64_t M, int64_t IC, int64_t OC, hipStream_t stream,
+                       const float* row_scale) {
   GemmArgs a;
   a.xh = (const uint16_t*)xh;
+  a.row_scale = row_scale;
   a.code = (const uint32_t*)code;
   a.rout = (const uint16_t*)rout;
   a.s_out = (const uint16_t*)s_out;

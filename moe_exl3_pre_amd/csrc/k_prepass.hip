@@ -79,13 +79,17 @@ __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __rest
   }
 }
 
-// 8-bit variant.  Two passes over the row: the first finds the amax, the second recomputes the same
-// fp32 features (identical instruction sequence, so identical values) and quantises them.
-template <bool PERMUTED>
+// 8-bit variant ("radiance_escha.py", `escha_linear_into`: an 8-bit activation buffer plus one float
+// scale per row).  Two passes over the row: the first finds max |xh| over the row, the second recomputes
+// the same fp32 features (identical instruction sequence, so identical values) and quantises them:
+// sc = amax / 127, q = clamp(rne(xh / sc), -127, 127), and q = 0 for a row whose amax is 0.
+// F16OUT writes each code as the fp16 number q (exact: |q| <= 127), which the fp16 MFMA GEMM consumes;
+// otherwise the codes are written as int8.
+template <bool PERMUTED, bool F16OUT>
 __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ s_in,
                                                          const uint16_t* __restrict__ rin,
-                                                         int8_t* __restrict__ q_out, float* __restrict__ scale,
+                                                         void* __restrict__ q_out, float* __restrict__ scale,
                                                          int64_t M, int64_t IC) {
   __shared__ float red[4];
   const int64_t m = blockIdx.x;
@@ -104,7 +108,6 @@ __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restr
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float sc = __fdiv_rn(amax, 127.0f);
   if (threadIdx.x == 0) scale[m] = sc;
-  int8_t* dst = q_out + m * IC;
   for (int64_t q = wave; q < IC / kHad; q += 4) {
     float v0, v1;
     rotate_block<PERMUTED>(xr, s_in, rin, q * kHad, lane, v0, v1);
@@ -114,7 +117,13 @@ __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restr
       q1 = (int)fminf(fmaxf(rintf(__fdiv_rn(v1, sc)), -127.f), 127.f);
     }
     const int64_t k = q * kHad + 2 * lane;             // natural: features k, k+1; permuted: positions k, k+1
-    *reinterpret_cast<uint16_t*>(dst + k) = uint16_t(uint8_t(q0)) | uint16_t(uint16_t(uint8_t(q1)) << 8);
+    if constexpr (F16OUT) {
+      uint16_t* dst = static_cast<uint16_t*>(q_out) + m * IC;
+      *reinterpret_cast<uint32_t*>(dst + k) = uint32_t(f32_to_f16(float(q0))) | (uint32_t(f32_to_f16(float(q1))) << 16);
+    } else {
+      int8_t* dst = static_cast<int8_t*>(q_out) + m * IC;
+      *reinterpret_cast<uint16_t*>(dst + k) = uint16_t(uint8_t(q0)) | uint16_t(uint16_t(uint8_t(q1)) << 8);
+    }
   }
 }
 
@@ -134,15 +143,18 @@ hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, 
 }
 
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
-                             int64_t IC, bool permuted, hipStream_t stream) {
+                             int64_t IC, bool permuted, hipStream_t stream, bool f16_codes) {
   if (M <= 0) return hipSuccess;
   dim3 grid((unsigned)M), block(256);
-  if (permuted)
-    hipLaunchKernelGGL(prepass_i8_kernel<true>, grid, block, 0, stream, (const uint16_t*)x, (const uint16_t*)s_in,
-                       (const uint16_t*)rin, (int8_t*)q, scale, M, IC);
+  const uint16_t *xx = (const uint16_t*)x, *si = (const uint16_t*)s_in, *ri = (const uint16_t*)rin;
+  if (permuted && f16_codes)
+    hipLaunchKernelGGL((prepass_i8_kernel<true, true>), grid, block, 0, stream, xx, si, ri, q, scale, M, IC);
+  else if (permuted)
+    hipLaunchKernelGGL((prepass_i8_kernel<true, false>), grid, block, 0, stream, xx, si, ri, q, scale, M, IC);
+  else if (f16_codes)
+    hipLaunchKernelGGL((prepass_i8_kernel<false, true>), grid, block, 0, stream, xx, si, ri, q, scale, M, IC);
   else
-    hipLaunchKernelGGL(prepass_i8_kernel<false>, grid, block, 0, stream, (const uint16_t*)x, (const uint16_t*)s_in,
-                       (const uint16_t*)rin, (int8_t*)q, scale, M, IC);
+    hipLaunchKernelGGL((prepass_i8_kernel<false, false>), grid, block, 0, stream, xx, si, ri, q, scale, M, IC);
   return hipGetLastError();
 }
 

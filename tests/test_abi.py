@@ -62,7 +62,8 @@ def _linear(**kw):
     (dict(x=FAKE + 4), exl3.EINVAL, "x"),
     (dict(out=None), exl3.EINVAL, "out"),
     (dict(flags=1 << 7), exl3.EINVAL, "flags"),
-    (dict(flags=exl3.ACT_INT8), exl3.EUNSUPPORTED, "flags"),
+    (dict(flags=exl3.ACT_INT8 | exl3.FORCE_GEMV), exl3.EUNSUPPORTED, "flags"),
+    (dict(flags=exl3.ACT_INT8, ws=None), exl3.EWORKSPACE, "ws"),              # 8-bit path accepted
     (dict(flags=exl3.FORCE_GEMV | exl3.FORCE_MFMA), exl3.EINVAL, "flags"),
     (dict(ws=None), exl3.EWORKSPACE, "ws"),
     (dict(ws=FAKE, ws_bytes=1024), exl3.EWORKSPACE, "ws_bytes"),
@@ -77,6 +78,12 @@ def test_linear_rejects_before_launch(kw, code, needle):
 def test_linear_zero_rows_is_a_noop():
     assert _linear(M=0, out=None, x=None) == exl3.OK
     assert exl3.last_error() == ""
+
+
+def test_int8_workspace_holds_codes_and_scales():
+    """The 8-bit path runs on the GEMM at every M: its workspace holds M x IC fp16 codes plus M scales."""
+    for M in (1, 4, 300):
+        assert exl3.linear_workspace_bytes(M, 4096, 14336, exl3.ACT_INT8) >= 16384 + M * 4096 * 2 + M * 4
 
 
 def test_workspace_sizes():

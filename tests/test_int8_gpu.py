@@ -1,0 +1,153 @@
+"""GPU parity of the 8-bit activation path (EXL3_ACT_INT8) against the oracle's per-row int8 emulation
+and the exact fp64 result, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import exl3_oracle as O
+from moe_exl3_pre_amd import exl3, synth
+from tests.helpers import (assert_close_linear, bf16_to_f64, dev, log, oracle_block_columns, rel_fro, shard_to_dev,
+                           to_dev, to_dev_x)
+
+pytestmark = pytest.mark.gpu
+
+TOL_INT8 = 3e-2
+SENTINEL = -1000.0
+
+
+def _dev_case(c):
+    return dict(x=to_dev_x(c["x_bits"]), code=to_dev(c["code"]), s_in=to_dev(c["s_in"]), rin=to_dev(c["rin"]),
+                rout=to_dev(c["rout"]), s_out=to_dev(c["s_out"]))
+
+
+def _run(c, d, flags=exl3.ACT_INT8, ldo=None, col0=0, x=None):
+    x = d["x"] if x is None else x
+    out = torch.full((x.shape[0], ldo or c["OC"]), SENTINEL, dtype=torch.bfloat16, device=dev())
+    exl3.linear_into(out, x, d["code"], c["K"], d["s_in"], d["rin"], d["rout"], d["s_out"], col0=col0, flags=flags)
+    torch.cuda.synchronize()
+    return out
+
+
+def _refs(c, x=None):
+    x = c["x"] if x is None else x
+    args = (c["code"], c["K"], c["s_in"], c["rin"], c["rout"], c["s_out"])
+    return O.linear(x, *args, act="int8"), O.linear(x, *args)
+
+
+@pytest.mark.parametrize("M,IC", [(1, 512), (7, 1024), (64, 256), (333, 640)])
+def test_codes_and_scales_match_the_oracle(M, IC):
+    """q and the row scale from the rotate hook against quantize_rows_int8 of the oracle's rotation.  The
+    oracle rotates in fp64 and the kernel in fp32, so a code may differ by one only where xh/sc lies
+    within fp32 rounding of a rounding boundary; everywhere else the codes are identical."""
+    c = synth.linear_case(8100 + M, M, IC, 128, 2)
+    d = _dev_case(c)
+    q, sc = exl3.rotate_activations(d["x"], d["s_in"], d["rin"], int8=True)
+    torch.cuda.synchronize()
+    q = q.cpu().numpy().astype(np.int64)
+    sc = sc.cpu().numpy().astype(np.float64)
+    xh = O.rotate_input(c["x"], c["s_in"], c["rin"])
+    q_ref, sc_ref = O.quantize_rows_int8(xh)
+    assert np.allclose(sc, sc_ref, rtol=2e-6, atol=0)
+    assert np.abs(q).max() <= 127
+    diff = q != q_ref
+    if diff.any():
+        frac = (xh / np.where(sc_ref > 0, sc_ref, 1.0)[:, None]) % 1.0
+        near_tie = np.abs(frac - 0.5) < 1e-4
+        assert np.all(np.abs(q - q_ref)[diff] == 1) and np.all(near_tie[diff]), int(diff.sum())
+    log(f"  {int(diff.sum())} of {q.size} codes differ by one at near-ties")
+
+
+@pytest.mark.parametrize("M", [1, 4, 17, 200, 300])
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_int8_linear_ragged(M, K):
+    c = synth.linear_case(8200 + 7 * M + K, M, 384, 384, K)
+    out = _run(c, _dev_case(c))
+    ref8, ref = _refs(c)
+    e = assert_close_linear(bf16_to_f64(out), ref8, ref, tol=TOL_INT8)
+    # against the int8 emulation itself the only differences are code flips at ties, the fp32 sums and the
+    # bf16 rounding
+    assert rel_fro(bf16_to_f64(out), ref8) < 4e-3
+    log(f"  M={M} K={K}: rel err vs exact {e:.3e}")
+
+
+def test_int8_other_k_and_slice():
+    for K in (1, 5, 8):
+        c = synth.linear_case(8300 + K, 40, 256, 256, K)
+        out = _run(c, _dev_case(c), ldo=640, col0=128)
+        o = bf16_to_f64(out)
+        assert np.all(o[:, :128] == SENTINEL) and np.all(o[:, 384:] == SENTINEL)
+        ref8, ref = _refs(c)
+        assert_close_linear(o[:, 128:384], ref8, ref, tol=TOL_INT8)
+
+
+def test_int8_zero_rows_and_scale_invariance():
+    c = synth.linear_case(8400, 48, 512, 256, 3)
+    c["x"][5] = 0.0
+    c["x_bits"][5] = 0
+    d = _dev_case(c)
+    base = _run(c, d)
+    assert torch.all(base[5] == 0)
+    # x -> 2x: the codes are unchanged and the scale doubles exactly, so the output doubles bit for bit
+    twice = _run(c, d, x=(d["x"].float() * 2).to(torch.bfloat16))
+    assert torch.equal(twice, (base.float() * 2).to(torch.bfloat16))
+
+
+def test_int8_dispatch_and_merged():
+    """The 8-bit path runs on the MFMA GEMM at every M (bitwise equal to forcing it); merged shards equal
+    separate calls bit for bit."""
+    c = synth.linear_case(8500, 5, 512, 256, 2)
+    d = _dev_case(c)
+    assert torch.equal(_run(c, d), _run(c, d, flags=exl3.ACT_INT8 | exl3.FORCE_MFMA))
+    case = synth.merged_case(8501, 9, 512, [(256, 2), (384, 3)])
+    x = to_dev_x(case["x_bits"])
+    s_in, rin = to_dev(case["shards"][0]["s_in"]), to_dev(case["shards"][0]["rin"])
+    shards = [shard_to_dev(s, s_in, rin) for s in case["shards"]]
+    merged = torch.zeros((9, case["ldo"]), dtype=torch.bfloat16, device=dev())
+    exl3.linear_multi_into(merged, x, shards, flags=exl3.ACT_INT8)
+    sep = torch.zeros_like(merged)
+    for s in shards:
+        exl3.linear_into(sep, x, s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"], col0=s["col0"],
+                         flags=exl3.ACT_INT8)
+    torch.cuda.synchronize()
+    assert torch.equal(merged, sep)
+
+
+def _sampled(case_x, shards, out, rows, seed):
+    got = bf16_to_f64(out)[rows]
+    rng = np.random.default_rng(seed)
+    x = case_x[rows]
+    for s in shards:
+        nblk = s["OC"] // 128
+        blocks = sorted(set([0, nblk - 1] + list(rng.choice(nblk, 2, replace=False))))
+        cols, y64 = oracle_block_columns(x, s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"], blocks)
+        _, y8 = oracle_block_columns(x, s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"], blocks,
+                                     act="int8")
+        e = assert_close_linear(got[:, s["col0"] + cols], y8, y64, tol=TOL_INT8)
+        log(f"  shard K={s['K']}: rel err vs exact {e:.3e}")
+
+
+def test_int8_prefill_gate_up_full_size_sampled():
+    p = synth.PREFILL
+    cfg = p["gate_up"]
+    M = p["M"]
+    case = synth.merged_case(2100, M, cfg["IC"], [(cfg["OC"], cfg["K_gate"]), (cfg["OC"], cfg["K_up"])])
+    log("int8 prefill gate_up 8192 x 5120 -> 2 x 17408")
+    x = to_dev_x(case["x_bits"])
+    s_in, rin = to_dev(case["shards"][0]["s_in"]), to_dev(case["shards"][0]["rin"])
+    shards = [shard_to_dev(s, s_in, rin) for s in case["shards"]]
+    out = torch.full((M, case["ldo"]), SENTINEL, dtype=torch.bfloat16, device=dev())
+    exl3.linear_multi_into(out, x, shards, flags=exl3.ACT_INT8)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(3).choice(M, 8, replace=False)]))
+    _sampled(case["x"], case["shards"], out, rows, 4)
+
+
+def test_int8_prefill_down_full_size_sampled():
+    p = synth.PREFILL
+    cfg = p["down"]
+    M = p["M"]
+    c = synth.linear_case(2101, M, cfg["IC"], cfg["OC"], cfg["K"])
+    log("int8 prefill down 8192 x 17408 -> 5120")
+    out = _run(c, _dev_case(c))
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(5).choice(M, 6, replace=False)]))
+    _sampled(c["x"], [dict(c, col0=0)], out, rows, 6)
