@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--extra-m", default="2,4,8", help="additional decode M values reported under 'extra'")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 prefill measurements")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE bank measurement")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the M sweep over a 64-layer projection set on both paths (prints its own report)")
+    ap.add_argument("--sweep-ms", default="1,4,8,16,24,32,48,64,128,512,8192")
     ap.add_argument("--pmc-ref", action="store_true",
                     help="eager decode launches (no graph) plus a plain 1 GiB copy, for hardware-counter runs")
     return ap.parse_args()
@@ -213,6 +216,66 @@ def cpu_baseline(synth, O):
                        f"{dt:.1f} s")
 
 
+def run_sweep(torch, exl3, synth, dev, ms):
+    """M sweep over one 64-layer decoder's projections (hidden 5120, intermediate 17408): every layer has
+    its own seeded random trellis words and scales (generated on the GPU), so successive calls stream new
+    weights.  Each (projection, M) is timed on the decode-phase path (FORCE_GEMV, 16-row launches) and on
+    the MFMA path (FORCE_MFMA): one call per layer, all 64 layers, events around the whole pass."""
+    cfg = synth.SWEEP
+    L = cfg["layers"]
+    gen = torch.Generator(device=dev)
+    report = []
+    for pi, (name, IC, OC, K) in enumerate(cfg["projections"]):
+        gen.manual_seed(1004 * 100 + pi)
+        codes = [torch.randint(-32768, 32768, (IC // 16, OC // 16, 16 * K), dtype=torch.int16, device=dev,
+                               generator=gen) for _ in range(L)]
+        vec = lambda n: (torch.rand(n, device=dev, generator=gen) + 0.5).half()
+        sgn = lambda n: (torch.randint(0, 2, (n,), device=dev, generator=gen) * 2 - 1).half()
+        layers = [dict(code=c, s_in=sgn(IC), rin=vec(IC), rout=vec(OC), s_out=sgn(OC)) for c in codes]
+        trellis = IC * OC * K // 8
+        for M in ms:
+            x = (torch.randn((M, IC), device=dev, generator=gen)).to(torch.bfloat16)
+            out = torch.empty((M, OC), dtype=torch.bfloat16, device=dev)
+            row = {"projection": name, "IC": IC, "OC": OC, "K": K, "M": M}
+            for tag, flags in (("gemv", exl3.FORCE_GEMV), ("mfma", exl3.FORCE_MFMA)):
+                ws = exl3.alloc_workspace(exl3.linear_workspace_bytes(M, IC, OC, flags), dev)
+                step = lambda i: exl3.linear_into(out, x, layers[i % L]["code"], K, layers[i % L]["s_in"],
+                                                  layers[i % L]["rin"], layers[i % L]["rout"], layers[i % L]["s_out"],
+                                                  flags=flags, ws=ws)
+                if M <= 128:      # launch-bound sizes: replay a captured graph of the 64 calls
+                    sec = graph_time(torch, step, L, L)
+                else:
+                    for i in range(L):
+                        step(i)
+                    torch.cuda.synchronize()
+                    stream = torch.cuda.current_stream()
+                    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    t0.record(stream)
+                    for i in range(L):
+                        step(i)
+                    t1.record(stream)
+                    torch.cuda.synchronize()
+                    sec = t0.elapsed_time(t1) / 1e3 / L
+                row[f"{tag}_us"] = round(sec * 1e6, 2)
+                row[f"{tag}_trellis_GBps"] = round(trellis / sec / 1e9, 1)
+                row[f"{tag}_TFLOPs"] = round(2.0 * M * IC * OC / sec / 1e12, 2)
+                del ws
+            row["faster"] = "gemv" if row["gemv_us"] < row["mfma_us"] else "mfma"
+            print(json.dumps(row), flush=True)
+            report.append(row)
+            del x, out
+        del codes, layers
+        torch.cuda.empty_cache()
+    crossover = {}
+    for name, *_ in cfg["projections"]:
+        rows = [r for r in report if r["projection"] == name]
+        first = next((r["M"] for r in rows if r["faster"] == "mfma"), None)
+        last_gemv = max((r["M"] for r in rows if r["faster"] == "gemv"), default=None)
+        crossover[name] = {"last_M_gemv_faster": last_gemv, "first_M_mfma_faster": first}
+    thresholds = {name: exl3.lib().exl3_gemv_max_rows(OC) for name, IC, OC, K in cfg["projections"]}
+    print(json.dumps({"sweep_crossover": crossover, "dispatch_threshold_rows": thresholds}), flush=True)
+
+
 def pmc_reference(torch, exl3, dev, x, out, sets):
     """Eager launches for counter runs: 1 GiB device copies (known bytes), then decode steps."""
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -239,6 +302,9 @@ def main():
     dev = torch.device("cuda", 0)
     exl3.lib()
 
+    if a.sweep:
+        run_sweep(torch, exl3, synth, dev, [int(m) for m in a.sweep_ms.split(",") if m])
+        return
     IC, ldo, sets, trellis_bytes = build_gate_up(torch, dev, synth, COPIES)
     rng = np.random.default_rng(77)
     if a.pmc_ref:

@@ -68,8 +68,10 @@ const char* exl3_last_error(void);
 /* ABI version (major * 100 + minor). */
 int exl3_version(void);
 
-/* Largest M served by the decode-phase kernel when no FORCE flag is given. */
-int64_t exl3_gemv_max_rows(void);
+/* Largest M served by the decode-phase path (launches of up to 16 rows) when no FORCE flag is given,
+ * for a call whose widest shard has OC output columns: 16 * clamp(40960 / OC, 1, 8), the measured
+ * crossover against the MFMA GEMM over a 5120/17408 decoder's projections. */
+int64_t exl3_gemv_max_rows(int64_t OC);
 
 /* --------------------------------------------------------------------------------------------------
  * One projection written into its column slice ("radiance_escha.py", `escha_linear_into`: one escha
@@ -86,7 +88,7 @@ int64_t exl3_gemv_max_rows(void);
  * rout/s_out 2-byte aligned, IC*OC*K/8 < 2 GiB.
  * Precision: x * s_in * rin and the Hadamard in fp32, the rotated activations rounded once to fp16, fp16 x
  * fp16 products accumulated in fp32, output transform and scales in fp32, one round-to-nearest-even to
- * bf16.  Row results do not depend on the other rows; M <= exl3_gemv_max_rows() runs the decode-phase
+ * bf16.  Row results do not depend on the other rows; M <= exl3_gemv_max_rows(OC) runs the decode-phase
  * kernel, larger M the MFMA GEMM (the two agree to rounding, not bitwise).
  * 8-bit path (EXL3_ACT_INT8): the codes q are exact in fp16 and every q * W product is exact in fp32,
  * so the contraction is the integer dot product up to fp32 summation; the row scale is applied before

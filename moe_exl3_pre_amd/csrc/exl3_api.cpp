@@ -39,7 +39,16 @@ int launch_status(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr unsigned kKnownFlags = EXL3_ACT_INT8 | EXL3_FORCE_GEMV | EXL3_FORCE_MFMA;
-constexpr int64_t kGemvMaxRows = kDecodeMaxRows;
+// Dispatch threshold.  The decode-phase path streams every weight once per 16-row launch, so its time
+// grows with ceil(M/16) * OC; the MFMA GEMM keeps one 256-row tile per 128 output columns, so below
+// M = 256 it runs OC/128 workgroups whose time does not depend on OC.  Measured over the projections of
+// a 5120/17408 decoder (M sweep, 64 layers) the crossover sits at ceil(M/16) ~ 40960/OC (gate and up:
+// 32 rows, qkv: 64, o and down: 128); the threshold follows that, between one and eight launches.
+int64_t gemv_max_rows(int64_t OC) {
+  int64_t chunks = OC > 0 ? 40960 / OC : 1;
+  chunks = chunks < 1 ? 1 : (chunks > 8 ? 8 : chunks);
+  return chunks * kDecodeMaxRows;
+}
 
 int check_flags(unsigned flags) {
   if (flags & ~kKnownFlags) return fail(EXL3_EINVAL, "flags: unknown bits 0x%x", flags & ~kKnownFlags);
@@ -80,11 +89,11 @@ int check_shard(const char* who, int64_t IC, const int16_t* code, int64_t OC, in
 }
 
 // The prefill/decode choice is made here, inside the op, by M ("radiance_escha.py", `escha_linear_into`).
-bool use_decode_path(int64_t M, unsigned flags) {
+bool use_decode_path(int64_t M, unsigned flags, int64_t OC) {
   if (flags & EXL3_ACT_INT8) return false;   // the row amax needs the whole row before any product
   if (flags & EXL3_FORCE_GEMV) return true;
   if (flags & EXL3_FORCE_MFMA) return false;
-  return M <= kGemvMaxRows;
+  return M <= gemv_max_rows(OC);
 }
 
 // Row chunks the decode-phase path launches: full chunks of kDecodeMaxRows rows, then the remainder.
@@ -276,19 +285,16 @@ int check_bank(const exl3_bank* b) {
   return EXL3_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* exl3_last_error(void) { return g_error.c_str(); }
-
-int exl3_version(void) { return 100; }
-
-int64_t exl3_gemv_max_rows(void) { return kGemvMaxRows; }
+// Widest shard of a call: the GEMM runs one shard at a time, so its occupancy follows each shard's OC.
+int64_t max_oc(int n, const DecShardIn* in) {
+  int64_t m = 0;
+  for (int i = 0; i < n; ++i) m = in[i].OC > m ? in[i].OC : m;
+  return m;
+}
 
 // Workspace of either path for these shards (host descriptors; only OC, K and the s_in/rin pointers are read).
 bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsigned flags, Layout* L) {
-  if (use_decode_path(M, flags)) {
+  if (use_decode_path(M, flags, max_oc(n, in))) {
     size_t slab = 0;
     if (!decode_slab_bytes(M, IC, n, in, &slab)) return false;
     *L = layout_for(slab);
@@ -298,6 +304,16 @@ bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsign
   }
   return true;
 }
+
+}  // namespace
+
+extern "C" {
+
+const char* exl3_last_error(void) { return g_error.c_str(); }
+
+int exl3_version(void) { return 100; }
+
+int64_t exl3_gemv_max_rows(int64_t OC) { return gemv_max_rows(OC); }
 
 size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned flags) {
   if (M <= 0 || IC <= 0 || OC <= 0 || IC % 128 || OC % 128) return align_up(kCounterBytes);
@@ -321,7 +337,7 @@ int exl3_linear_into(void* out, int64_t ldo, int64_t col0, const void* x, int64_
   if (!workspace_layout(M, IC, 1, &in, flags, &L)) return fail(EXL3_EUNSUPPORTED, "exl3_linear_into: no plan");
   if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int rc = use_decode_path(M, flags)
+  const int rc = use_decode_path(M, flags, OC)
                      ? run_decode("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, st)
                      : run_gemm("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, flags, st);
   if (rc) return rc;
@@ -362,7 +378,7 @@ int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int
   if (!workspace_layout(M, IC, n_shards, in, flags, &L)) return fail(EXL3_EUNSUPPORTED, "exl3_linear_multi_into: no plan");
   if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int rc = use_decode_path(M, flags)
+  const int rc = use_decode_path(M, flags, max_oc(n_shards, in))
                      ? run_decode("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L, st)
                      : run_gemm("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L, flags,
                                 st);

@@ -50,7 +50,7 @@ class Bank(ctypes.Structure):
 _SIGS = {
     "exl3_last_error": (ctypes.c_char_p, []),
     "exl3_version": (ctypes.c_int, []),
-    "exl3_gemv_max_rows": (ctypes.c_int64, []),
+    "exl3_gemv_max_rows": (ctypes.c_int64, [ctypes.c_int64]),
     "exl3_linear_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint]),
     "exl3_linear_into": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,

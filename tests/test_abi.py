@@ -32,7 +32,9 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_limits():
     L = exl3.lib()
     assert L.exl3_version() >= 100
-    assert L.exl3_gemv_max_rows() >= 8
+    # the measured crossover rule: 16 * clamp(40960 // OC, 1, 8)
+    for OC, rows in ((17408, 32), (14336, 32), (7168, 80), (5120, 128), (256, 128), (81920, 16)):
+        assert L.exl3_gemv_max_rows(OC) == rows, OC
 
 
 def _linear(**kw):

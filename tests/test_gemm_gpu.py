@@ -44,9 +44,9 @@ def test_mfma_path_other_k(K):
 
 
 def test_default_dispatch_uses_mfma_above_threshold():
-    """Above exl3_gemv_max_rows() the default call equals the forced MFMA call bit for bit; at or below
+    """Above exl3_gemv_max_rows(OC) the default call equals the forced MFMA call bit for bit; at or below
     it equals the forced decode-phase call."""
-    thr = exl3.lib().exl3_gemv_max_rows()
+    thr = exl3.lib().exl3_gemv_max_rows(256)
     for M, force in ((thr, exl3.FORCE_GEMV), (thr + 1, exl3.FORCE_MFMA), (200, exl3.FORCE_MFMA)):
         c = synth.linear_case(5200 + M, M, 512, 256, 3)
         d = _dev_case(c)
