@@ -140,6 +140,17 @@ __device__ __forceinline__ void decode_column(const uint32_t (&w)[Geom<K>::kNW],
   out[7] = decode_pair<K, 7>(r, c);
 }
 
+// Staging of trellis words.  The words of one 64-feature step of a 128-column block are 4 tile rows x
+// 8 tiles x 8K words, each tile row 256K contiguous bytes: lane (n, g) loads 16 bytes at n * 16 + i * 256
+// of tile row g (i < K), fully coalesced.  A per-wave LDS slot holds that step, each tile row padded by
+// 16 words so the four groups of 16 lanes read different banks; lane (n, g) then reads the words of tile
+// column n of each tile of row g at column_word_offsets.
+template <int K>
+struct Slot {
+  static constexpr int kRowBytes = 256 * K + 64;
+  static constexpr int kBytes = 4 * kRowBytes;
+};
+
 __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4 v = {a, b, c, d};
   return __builtin_bit_cast(half8, v);

@@ -52,13 +52,6 @@ struct DecArgs {
   DecShard sh[kMaxShards];
 };
 
-// Per-wave LDS slot holding one 64-feature step of trellis words: 4 tile rows (g) x 8 tiles x 8K words,
-// each tile row padded by 16 words so the four groups of 16 lanes read different banks.
-template <int K>
-struct Slot {
-  static constexpr int kRowBytes = 256 * K + 64;
-  static constexpr int kBytes = 4 * kRowBytes;
-};
 
 template <int K, int SPW, int MR>
 __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& sh, int local, char* lds) {

@@ -31,6 +31,11 @@ constexpr int kMoeRows = 32;          // rows of one chunk: two 16-row MFMA grou
 constexpr int kMoeWaves = 4;          // waves per w13 / w2 workgroup: two per half
 constexpr int kRedStride = kHad + 4;  // padded fp32 row of the reduction buffers (spreads LDS banks)
 constexpr int kRouteThreads = 1024;
+// w13 / w2 workgroups: the reduction buffer [2 halves][32 rows][kRedStride] and, before it is used, the
+// four waves' trellis staging slots share one LDS array
+constexpr int kMoeRedFloats = 2 * kMoeRows * kRedStride;
+constexpr int kMoeSlotFloats = kMoeWaves * Slot<8>::kBytes / 4;
+constexpr int kMoeLdsFloats = kMoeRedFloats > kMoeSlotFloats ? kMoeRedFloats : kMoeSlotFloats;
 
 struct MoeArgs {
   const uint16_t* x;        // bf16 [T, H]
@@ -241,37 +246,37 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_rotate_kernel(MoeArgs
 
 // ---------------------------------------------------------------------------------------------------
 // Streaming core: one wave accumulates rows x [128 columns] over its 64-feature steps [st0, st0 + nst)
-// of one expert projection.  Trellis words of PD steps are in flight; the A fragments of the next step
-// are loaded one step ahead.  Loads are unconditional with clamped steps (every address stays inside the
-// tensor); only the arithmetic is predicated.
+// of one expert projection.  Each step's trellis words arrive as K coalesced 16-byte loads per lane
+// (PD steps in flight), are staged in the wave's LDS slot, and every lane then reads its tile column's
+// words from there (one column ahead) and decodes them into MFMA operands.  The A fragments of the next
+// step are loaded one step ahead.  Loads are unconditional with clamped steps (every address stays
+// inside the tensor); only the arithmetic and the staging are predicated.  LDS operations of one wave
+// complete in order, so a step's reads see that step's writes.
 // ---------------------------------------------------------------------------------------------------
 template <int K>
 __device__ __forceinline__ void moe_accumulate(const uint16_t* code, uint32_t code_bytes, int tpr, int blk,
                                                const uint16_t* arow0, const uint16_t* arow1, int st0, int nst,
-                                               bool two, float4v (&acc0)[8], float4v (&acc1)[8]) {
+                                               bool two, char* slot, float4v (&acc0)[8], float4v (&acc1)[8]) {
   using G = Geom<K>;
-  constexpr int PD = G::kNW <= 2 ? 2 : 1;
+  constexpr int PD = K <= 3 ? 2 : 1;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   int woff[G::kNW], shift;
   column_word_offsets<K>(n, woff, shift);
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(code), (short)0, (int)code_bytes, kBufferFlags);
-  uint32_t lane_off[G::kNW];
-#pragma unroll
-  for (int w = 0; w < G::kNW; ++w) lane_off[w] = (uint32_t(g) * uint32_t(tpr) * G::kWords + uint32_t(woff[w])) * 4u;
+  const uint32_t lane_off = uint32_t(g) * uint32_t(tpr) * G::kWords * 4u + uint32_t(n) * 16u;
   const uint32_t step_stride = 4u * uint32_t(tpr) * G::kWords * 4u;
   const uint32_t base_blk = uint32_t(blk) * 8u * G::kWords * 4u;
   const int last = st0 + (nst > 0 ? nst - 1 : 0);
+  char* my_row = slot + g * Slot<K>::kRowBytes;
 
-  uint32_t buf[PD][8][G::kNW];
+  u32x4 tb[PD][K];
   half8 A[2][2][2];   // [ring][row group][k half]
-  auto load_step = [&](int st, uint32_t (&dst)[8][G::kNW]) {
+  auto load_step = [&](int st, u32x4 (&dst)[K]) {
     const uint32_t soff = uint32_t(st < last ? st : last) * step_stride + base_blk;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int w = 0; w < G::kNW; ++w)
-        dst[j][w] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off[w] + uint32_t(j * G::kWords * 4), soff, 0);
+    for (int i = 0; i < K; ++i)
+      dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off + uint32_t(i * 256), soff, 0));
   };
   auto load_a = [&](int st, half8 (&dst)[2][2]) {
     const int o = 64 * (st < last ? st : last);
@@ -280,9 +285,13 @@ __device__ __forceinline__ void moe_accumulate(const uint16_t* code, uint32_t co
     dst[1][0] = *reinterpret_cast<const half8*>(arow1 + o);
     dst[1][1] = *reinterpret_cast<const half8*>(arow1 + o + 8);
   };
+  auto read_col = [&](int j, uint32_t (&dst)[G::kNW]) {
+#pragma unroll
+    for (int w = 0; w < G::kNW; ++w) dst[w] = *reinterpret_cast<const uint32_t*>(my_row + (j * G::kWords + woff[w]) * 4);
+  };
   load_a(st0, A[0]);
 #pragma unroll
-  for (int p = 0; p < PD; ++p) load_step(st0 + p, buf[p]);
+  for (int p = 0; p < PD; ++p) load_step(st0 + p, tb[p]);
   __builtin_amdgcn_sched_barrier(0);
 
   const CodebookRegs cb = codebook_regs();
@@ -297,11 +306,19 @@ __device__ __forceinline__ void moe_accumulate(const uint16_t* code, uint32_t co
       const int st = s + p;
       load_a(st0 + st + 1, A[(p + 1) & 1]);
       const bool live = st < nst;
+      if (live) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (live) {
+        for (int i = 0; i < K; ++i) *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tb[p % PD][i];
+      }
+      load_step(st0 + st + PD, tb[p % PD]);
+      if (live) {
+        uint32_t wv[2][G::kNW];
+        read_col(0, wv[0]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j + 1 < 8) read_col(j + 1, wv[(j + 1) & 1]);
           uint32_t b[8];
-          decode_column<K>(buf[p % PD][j], shift, b, cb);
+          decode_column<K>(wv[j & 1], shift, b, cb);
           const half8 b0 = as_half8(b[0], b[1], b[2], b[3]);
           const half8 b1 = as_half8(b[4], b[5], b[6], b[7]);
           acc0[j] = mfma16(A[p][0][0], b0, acc0[j]);
@@ -311,13 +328,6 @@ __device__ __forceinline__ void moe_accumulate(const uint16_t* code, uint32_t co
             acc1[j] = mfma16(A[p][1][1], b1, acc1[j]);
           }
         }
-        // refill this slot with the same column of step st + PD
-        const uint32_t soff =
-            uint32_t(st0 + st + PD < last ? st0 + st + PD : last) * step_stride + base_blk;
-#pragma unroll
-        for (int w = 0; w < G::kNW; ++w)
-          buf[p % PD][j][w] =
-              __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off[w] + uint32_t(j * G::kWords * 4), soff, 0);
       }
     }
   }
@@ -378,7 +388,9 @@ __device__ __forceinline__ void moe_w13_block(const MoeArgs& a, const int4v ch, 
   const int r1 = a.rows[row0 + (16 + n < nrows ? 16 + n : nrows - 1)];
   float4v acc0[8], acc1[8];
   moe_accumulate<K>(a.w13 + off, uint32_t(int64_t(a.H) * a.I * K / 8), a.I / 16, cb, A + int64_t(r0) * a.H + 16 * g,
-                    A + int64_t(r1) * a.H + 16 * g, st0, st1 - st0, two, acc0, acc1);
+                    A + int64_t(r1) * a.H + 16 * g, st0, st1 - st0, two,
+                    reinterpret_cast<char*>(red) + wave * Slot<K>::kBytes, acc0, acc1);
+  __syncthreads();                               // the staging slots share LDS with the reduction buffer
   moe_reduce(red + h * kMoeRows * kRedStride, wq, two, acc0, acc1);
 
   // epilogue: lane l owns intermediate features f, f + 8 of this block (PERM16 positions 2l, 2l+1)
@@ -424,8 +436,9 @@ __device__ __forceinline__ void moe_w2_block(const MoeArgs& a, const int4v ch, i
   const int r1 = a.rows[row0 + (16 + n < nrows ? 16 + n : nrows - 1)];
   float4v acc0[8], acc1[8];
   moe_accumulate<K>(a.w2 + a.off_w2[slot], uint32_t(int64_t(a.I) * a.H * K / 8), a.H / 16, active ? cb : 0,
-                    a.ah + int64_t(r0) * a.I + 16 * g, a.ah + int64_t(r1) * a.I + 16 * g, st0, st1 - st0, two, acc0,
-                    acc1);
+                    a.ah + int64_t(r0) * a.I + 16 * g, a.ah + int64_t(r1) * a.I + 16 * g, st0, st1 - st0, two,
+                    reinterpret_cast<char*>(red) + wave * Slot<K>::kBytes, acc0, acc1);
+  __syncthreads();                               // the staging slots share LDS with the reduction buffer
   float* rh = red + h * kMoeRows * kRedStride;
   moe_reduce(rh, wq, two, acc0, acc1);
   if (!active) return;
@@ -458,7 +471,7 @@ __device__ __forceinline__ void moe_dispatch(int k, F&& f) {
 
 template <int KSET>
 __global__ __launch_bounds__(kMoeWaves * 64, 3) void moe_w13_kernel(MoeArgs a) {
-  __shared__ float red[2 * kMoeRows * kRedStride];
+  __shared__ __attribute__((aligned(16))) float red[kMoeLdsFloats];
   int c, cb;
   moe_tile(a.I / kHad, c, cb);
   int4v ch;
@@ -468,7 +481,7 @@ __global__ __launch_bounds__(kMoeWaves * 64, 3) void moe_w13_kernel(MoeArgs a) {
 
 template <int KSET>
 __global__ __launch_bounds__(kMoeWaves * 64) void moe_w2_kernel(MoeArgs a) {
-  __shared__ float red[2 * kMoeRows * kRedStride];
+  __shared__ __attribute__((aligned(16))) float red[kMoeLdsFloats];
   int c, cbp;
   moe_tile((a.H / kHad + 1) / 2, c, cbp);
   int4v ch;
