@@ -4,18 +4,20 @@
 // prefill/decode choice is made inside the op; `apply`: each shard writes its own column slice).
 //
 // At decode M the trellis words are the whole cost, so the kernel is shaped around streaming them once:
-//   * a block of 16 waves owns one 128-column output block of one shard (one Hadamard-128 block, so the
-//     output transform needs no other block) over a range of the input features (usually all of IC);
-//   * the 16 waves split that feature range; every lane streams the words of one tile column through a
-//     small register pipeline (buffer loads, kPipe units in flight), decodes them in registers
+//   * a block of 8 waves owns one 128-column output block of one shard (one Hadamard-128 block, so the
+//     output transform needs no other block) over a range of the input features; two blocks share a CU
+//     (the dispatcher deals blocks i and i + 256 to one CU, and shards are laid out heavier K first, so
+//     most CUs pair a K=3 block with a K=2 one);
+//   * the 8 waves split that feature range; each step's trellis words arrive as coalesced 16-byte loads,
+//     pass through the wave's LDS slot, and every lane decodes one tile column in registers
 //     (exl3_device.hpp) straight into MFMA B fragments and accumulates [16 rows x 128 cols] in fp32;
 //   * while the first words are in flight the block computes its own slice of the rotated activations
 //     (x * s_in * rin, Hadamard-128, fp16, permuted order) into LDS -- no separate pre-pass launch and no
 //     round trip of the activations through HBM;
-//   * the 16 partial accumulators are summed in LDS in a fixed order (deterministic), then one wave per
-//     row applies the output Hadamard, rout and s_out and writes bf16;
-//   * only when a shard has too few 128-column blocks to fill the chip is its feature range split over
-//     several blocks (S > 1): each writes its partial rows to the split-K slab with agent-coherent
+//   * the 8 partial accumulators are summed in LDS in a fixed order (deterministic), then each wave
+//     takes output rows wave, wave + 8 and applies the output Hadamard, rout and s_out and writes bf16;
+//   * when a shard has too few 128-column blocks to fill both block slots of every CU its feature range
+//     is split over several blocks (S > 1): each writes its partial rows to the split-K slab with agent-coherent
 //     stores, bumps the block counter (agent-scope atomic, no L2-wide fences), and the last one to arrive
 //     finishes the block and resets the counter for the next launch or graph replay.  The slab and the
 //     counters live in the caller's workspace ("radiance_escha.py", `_ensure_scratch`: split-K partial
@@ -27,7 +29,7 @@
 
 namespace exl3 {
 
-constexpr int kWaves = 16;       // waves per block
+constexpr int kWaves = 8;        // waves per block (two blocks share a CU)
 constexpr int kNB = 8;           // tile columns per wave = one 128-column block
 
 struct DecShard {
@@ -56,7 +58,9 @@ struct DecArgs {
 template <int K, int SPW, int MR>
 __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& sh, int local, char* lds) {
   using G = Geom<K>;
-  constexpr int kD = K <= 3 ? 3 : 2;                                // steps of trellis words in flight per wave
+  // steps of trellis words in flight per wave: one.  Every block requests its first step at once, so
+  // deeper prefetch only queues the first data of late waves behind the early waves' later steps.
+  constexpr int kD = 1;
   constexpr int kPB = SPW > 1 ? SPW / 2 : 1;                        // Hadamard blocks per wave (pre-pass)
   static_assert(SPW % 2 == 0, "steps come in Hadamard-block pairs");
 
@@ -183,7 +187,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
     }
   }
 
-  // ---- 5. sum the 16 waves' partials in LDS (fixed order), one wave per output row
+  // ---- 5. sum the waves' partials in LDS (fixed order); wave w finishes output rows w, w + kWaves
   __syncthreads();                                          // everyone is done reading xs
   float* red = reinterpret_cast<float*>(lds);               // [kWaves][M][128]
 #pragma unroll
@@ -270,7 +274,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
 }
 
 template <int KSET, int SPW, int MR>
-__global__ __launch_bounds__(1024) void decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(512, 4) void decode_kernel(DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int wg = blockIdx.x;
   int i = 0;
@@ -317,9 +321,9 @@ size_t lds_bytes_for(int M, int lds_row, int K) {
 // Splits of one shard's feature range.  A function of (M, IC, OC, K) alone -- never of the other shards
 // in the call -- so a merged call reduces every shard in the same order as a call of that shard by
 // itself and the two agree bit for bit.  Split only as far as needed: until the shard has kFillBlocks blocks
-// (C1's 14336-column shards already do, and together fill 224 of the 256 CUs), a wave's steps fit the
+// (C1's 14336-column shards reach it at S = 2: 448 blocks, two per CU), a wave's steps fit the
 // largest unrolled variant, and the activation slice fits in LDS.
-constexpr int kFillBlocks = 112;
+constexpr int kFillBlocks = 224;
 
 int shard_splits(int64_t M, int B, int nblk, int K) {
   for (int S = 1;; ++S) {
