@@ -200,10 +200,10 @@ __device__ __forceinline__ float lane_xor16(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));  // xor 16 in 32
 }
 
-// butterfly with the partner value p: lower lanes keep v + p, upper lanes p - v
-__device__ __forceinline__ float bfly(float v, float p, bool upper) {
-  return p + __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) ^ (upper ? 0x80000000u : 0u));
-}
+// Butterfly with the partner value p: lower lanes get p + v, upper lanes p - v, written as
+// fma(v, +-1, p) (exact: one rounding of the same sum) so the compiler can use v_fmac_f32 on the value the
+// lane-exchange move produced.
+__device__ __forceinline__ float bfly(float v, float p, bool upper) { return fmaf(v, upper ? -1.0f : 1.0f, p); }
 
 __device__ __forceinline__ void had128_wave(float& v0, float& v1, int lane) {
   float a = v0 + v1, b = v0 - v1;

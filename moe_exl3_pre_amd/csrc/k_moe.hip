@@ -110,7 +110,7 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
 
 constexpr int kSlotCache = 16384;   // pairs whose slots the route keeps in LDS between its two passes
 
-__device__ void moe_route(const MoeArgs& a, int* lds) {
+__device__ void moe_route_general(const MoeArgs& a, int* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kW = kRouteThreads / 64;
   const int E = a.E;
@@ -187,12 +187,97 @@ __device__ void moe_route(const MoeArgs& a, int* lds) {
   }
 }
 
+// Fast path of the route when one bit per (slot, pair) fits in LDS (E * ceil(P/32) <= kBitmapWords): the
+// pairs set bits of a [slot][P/32] bitmap, one wave per slot turns its row into exclusive popcount prefixes,
+// and a pair's position in its slot's list is the number of set bits before it -- the same stable order
+// (pair ids ascending inside a slot) without any serial pass.
+constexpr int kBitmapWords = 8192;
+constexpr int kBitmapSlotCache = 8192;   // pairs whose slots the bitmap route keeps in LDS
+
+__device__ void moe_route_bitmap(const MoeArgs& a, int* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kW = kRouteThreads / 64;
+  const int E = a.E, W = (a.P + 31) / 32;
+  uint32_t* bm = reinterpret_cast<uint32_t*>(lds);   // [E][W]
+  int* pre = lds + E * W;                             // [E][W] exclusive prefix of popcounts
+  int* cnt = pre + E * W;                             // [E]
+  int* tmp = cnt + E;                                 // [48]
+  int* slot_of = tmp + 48;                            // [P] when it fits (see moe_route_lds_bytes), else null
+  if (a.P > kBitmapSlotCache) slot_of = nullptr;
+  for (int i = tid; i < E * W; i += kRouteThreads) bm[i] = 0u;
+  __syncthreads();
+  for (int q = tid; q < a.P; q += kRouteThreads) {
+    const int s = pair_slot(a, q);
+    a.pslot[q] = s;
+    if (slot_of) slot_of[q] = s;
+    if (s >= 0) atomicOr(&bm[s * W + (q >> 5)], 1u << (q & 31));
+  }
+  __syncthreads();
+  for (int s = wave; s < E; s += kW) {
+    int carry = 0;
+    for (int j0 = 0; j0 < W; j0 += 64) {
+      const int j = j0 + lane;
+      const int v = j < W ? __popc(bm[s * W + j]) : 0;
+      int inc = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += u;
+      }
+      if (j < W) pre[s * W + j] = carry + inc - v;
+      carry += __shfl(inc, 63, 64);
+    }
+    if (lane == 0) cnt[s] = carry;
+  }
+  __syncthreads();
+  const int s = tid;
+  const int c = s < E ? cnt[s] : 0;
+  int total = 0, chunk_total = 0;
+  const int off = block_excl_scan(c, tmp, &total);
+  const int nch = (c + kMoeRows - 1) / kMoeRows;
+  const int coff = block_excl_scan(nch, tmp, &chunk_total);
+  if (s < E) {
+    a.offs[s] = off;
+    cnt[s] = off;                                     // from here on: first row of the slot
+    int gk = 0;
+    for (int g = 0; g < a.n_groups; ++g)
+      if (s < a.g_hi[g]) {
+        gk = a.g_k[g];
+        break;
+      }
+    for (int i = 0; i < nch; ++i) {
+      const int r0 = off + i * kMoeRows;
+      const int nr = c - i * kMoeRows < kMoeRows ? c - i * kMoeRows : kMoeRows;
+      a.chunks[coff + i] = (int4v){s, r0, nr, gk};
+    }
+  }
+  if (s == 0) {
+    a.offs[E] = total;
+    a.n_chunks[0] = chunk_total;
+  }
+  __syncthreads();
+  for (int q = tid; q < a.P; q += kRouteThreads) {
+    const int sl = slot_of ? slot_of[q] : a.pslot[q];   // this thread wrote both above
+    if (sl >= 0) {
+      const int w = sl * W + (q >> 5);
+      a.rows[cnt[sl] + pre[w] + __popc(bm[w] & ((1u << (q & 31)) - 1u))] = q;
+    }
+  }
+}
+
+__device__ void moe_route(const MoeArgs& a, int* lds) {
+  if (a.E * ((a.P + 31) / 32) <= kBitmapWords)
+    moe_route_bitmap(a, lds);
+  else
+    moe_route_general(a, lds);
+}
+
 // ---------------------------------------------------------------------------------------------------
 // 1b. Rotation of gathered activations for w1 and w3: one wave per (token, 128-block).  The token's x
 // block is loaded once and rotated for each of its top-k pairs and both projections; the pair slots and
 // every sign/scale load are issued before the first Hadamard.
 // ---------------------------------------------------------------------------------------------------
-constexpr int kRotBatch = 8;    // pairs whose loads are in flight together
+constexpr int kRotBatch = 4;    // pairs whose loads are in flight together
 
 __device__ void moe_rotate(const MoeArgs& a, int64_t unit) {
   const int lane = threadIdx.x & 63;
@@ -213,7 +298,7 @@ __device__ void moe_rotate(const MoeArgs& a, int64_t unit) {
       const int sc = sl[r] < 0 ? 0 : sl[r];
 #pragma unroll
       for (int proj = 0; proj < 2; ++proj) {
-        const uint16_t* su = a.w13_suh + (int64_t(sc) * 2 + proj) * a.H + f;
+        const uint16_t* su = a.w13_suh + uint32_t((sc * 2 + proj) * a.H + f);   // < 2^27: 32-bit offset
         sv[r][proj] = uint32_t(su[0]) | (uint32_t(su[8]) << 16);
       }
     }
@@ -234,7 +319,7 @@ __device__ void moe_rotate(const MoeArgs& a, int64_t unit) {
   }
 }
 
-__global__ __launch_bounds__(kRouteThreads) void moe_route_rotate_kernel(MoeArgs a) {
+__global__ __launch_bounds__(kRouteThreads, 8) void moe_route_rotate_kernel(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) int route_lds[];
   if (blockIdx.x == 0) {
     moe_route(a, route_lds);
@@ -529,6 +614,8 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
 int64_t moe_max_chunks(int64_t P, int E) { return (P + kMoeRows - 1) / kMoeRows + E; }
 
 static size_t moe_route_lds_bytes(int E, int P) {
+  const size_t words = size_t(E) * ((P + 31) / 32);
+  if (words <= size_t(kBitmapWords)) return (2 * words + E + 48 + (P <= kBitmapSlotCache ? P : 0)) * sizeof(int);
   return size_t(2 * E + (kRouteThreads / 64) * E + 48 + (P <= kSlotCache ? P : 0)) * sizeof(int);
 }
 
