@@ -32,10 +32,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the EXL3 library)")
 
 
-# Per-file code generation options.  The GEMM and the MoE kernels keep their MFMA accumulators in
-# ordinary VGPRs: with the accumulator-register form the compiler retargets every MFMA result and copies
-# the accumulators around the loop (GEMM), or splits the budget between the two files (MoE).
-EXTRA = {"k_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "k_moe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file code generation options.  The MoE kernels keep their MFMA accumulators in ordinary VGPRs
+# (with the accumulator-register form the compiler splits the budget between the two files).  The
+# prefill GEMM's 256 accumulators fill the accumulator file: the register-pressure-first scheduler keeps
+# every MFMA accumulating in place (the default schedulers rename the results and copy them back each
+# step).
+EXTRA = {"k_moe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "k_gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]}
 
 
 def _compile(src: str) -> str:

@@ -132,7 +132,7 @@ Layout layout_for(size_t slab_bytes, int64_t M = 0, int64_t IC = 0, int n_xh = 0
   L.slab_off = align_up(kCounterBytes);
   L.slab_bytes = align_up(slab_bytes);
   L.xh_off = L.slab_off + L.slab_bytes;
-  L.scale_off = align_up(size_t(M) * size_t(IC) * 2);
+  L.scale_off = align_up(size_t((M + 15) / 16 * 16) * size_t(IC) * 2);   // fragment-major: rows padded to 16
   L.xh_bytes = L.scale_off + (int8 ? align_up(size_t(M) * 4) : 0);
   L.total = L.xh_off + L.xh_bytes * size_t(n_xh);
   return L;
@@ -197,7 +197,7 @@ int run_gemm(const char* who, void* out, int64_t ldo, const void* x, int64_t M, 
     float* scale = int8 ? reinterpret_cast<float*>(region + L.scale_off) : nullptr;
     if (slot[i] > done) {
       hipError_t e = int8 ? launch_prepass_i8(x, in[i].s_in, in[i].rin, region, scale, M, IC, true, stream, true)
-                          : launch_prepass_f16(x, in[i].s_in, in[i].rin, region, M, IC, true, stream);
+                          : launch_prepass_f16(x, in[i].s_in, in[i].rin, region, M, IC, true, stream, (M + 15) / 16 * 16);
       if (int rc = launch_status(e, who)) return rc;
       done = slot[i];
     }

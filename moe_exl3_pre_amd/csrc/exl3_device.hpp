@@ -27,7 +27,9 @@ namespace exl3 {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -171,6 +173,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {   // round to nearest
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two values at once with the hardware conversion (round to nearest even, the default rounding mode; fp32
+// denormals are kept): the same bits as f32_to_bf16 for every non-NaN input.  lo in bits 0..15.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, bf16x2v));
+}
+
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 __device__ __forceinline__ uint16_t f32_to_f16(float f) {   // round to nearest even
@@ -193,6 +201,7 @@ constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kQuadXor3 = 0x1B;       // quad_perm [3,2,1,0]
 constexpr int kRowMirror = 0x140;     // lane i <- lane 15 - i within each row of 16
 constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7 - i within each half-row of 8
+constexpr int kRowRor8 = 0x128;       // lane i <- lane (i + 8) mod 16 within each row of 16 (= lane xor 8)
 
 __device__ __forceinline__ float lane_xor4(float v) { return dpp<kRowHalfMirror>(dpp<kQuadXor3>(v)); }   // ^3 ^7
 __device__ __forceinline__ float lane_xor8(float v) { return dpp<kRowMirror>(dpp<kRowHalfMirror>(v)); }  // ^7 ^15

@@ -46,16 +46,19 @@ bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl
 hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,
                          void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream);
 
-// Rows [M, M_pad) of xh are written as zeros.
+// permuted: the GEMM's fragment-major layout (k_gemm.hip), else natural row-major.  Rows
+// [M, M_pad) of xh are written as zeros.
 hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, void* xh, int64_t M, int64_t IC,
                               bool permuted, hipStream_t stream, int64_t M_pad = 0);
-// q receives int8 codes, or with f16_codes the same codes as fp16 numbers (the GEMM's operand).
+// q receives int8 codes, or with f16_codes the same codes as fp16 numbers (the GEMM's operand; with
+// permuted, fragment-major with the rows up to a multiple of 16 written as zeros).
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
                              int64_t IC, bool permuted, hipStream_t stream, bool f16_codes = false);
 hipError_t launch_decode_tiles(void* w, const int16_t* code, int64_t IC, int64_t OC, int K, hipStream_t stream);
-// Prefill-phase GEMM of one shard; xh is the pre-pass output (fp16 [M, IC], PERM16 order).  With
-// row_scale (8-bit path) every output row is multiplied by row_scale[row] before the output transform.
-hipError_t launch_gemm(const void* xh, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
+// Prefill-phase GEMM of one shard (one wave per 128 x 128 output tile); xf is the pre-pass output in the
+// fragment-major layout (rows padded to 16).  With row_scale (8-bit path) every output row is multiplied
+// by row_scale[row] before the output transform.
+hipError_t launch_gemm(const void* xf, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
                        int64_t ldo, int64_t col0, int64_t M, int64_t IC, int64_t OC, hipStream_t stream,
                        const float* row_scale = nullptr);
 

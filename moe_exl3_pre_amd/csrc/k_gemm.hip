@@ -1,253 +1,285 @@
-// Prefill-phase kernel: at large M the layer really is a dense contraction, so it runs as a tiled MFMA
-// GEMM whose B operand is produced by the trellis decode on the fly ("radiance_escha.py",
-// `escha_linear_into`: prefill GEMM chosen inside the op by M).
+// Prefill-phase GEMM, one wave per 128 x 128 output tile ("radiance_escha.py", `escha_linear_into`: at
+// large M the layer is a dense contraction against the decoded weights).
 //
-//   * the activation pre-pass (k_prepass.hip) has written xh = Had128((x * s_in) * rin) in fp16, PERM16
-//     order, to the workspace;
-//   * a block of 4 waves owns a 256 x 128 output tile (one Hadamard-128 block of columns); wave (wm, wn)
-//     owns 128 rows x 64 columns;
-//   * per 64-feature step (4 tile rows) the block stages the A tile [256 rows x 64] through LDS (double
-//     buffered, one barrier per step) and each wave streams the trellis words of its 8 tile columns
-//     one step ahead; lane (n, g) decodes
-//     column n of tile row g of each tile column in registers (exl3_device.hpp) -- the two halves of
-//     that column are the B fragments of two MFMA 16x16x32 f16 -- and the wave issues 64 MFMAs into
-//     128 fp32 accumulators; the next step's loads are in flight meanwhile;
-//   * epilogue: Hadamard-128 over the block's 128 columns -- DPP across the 16 lanes of a column group,
-//     register butterflies across a wave's 4 groups, and the last stage (columns c, c+64) between the
-//     two waves of a row half through LDS -- then * 1/sqrt(128) * rout * s_out, bf16 into the slice;
-//   * blocks are ordered so that the ~32 blocks running on one XCD (consecutive block ids go to
-//     different XCDs) share 4 row tiles and 8 column tiles, keeping A and the trellis words in its L2.
+// Why this shape on gfx950.  A 16x16x32 f16 MFMA keeps the matrix core busy for 16 cycles but holds the
+// wave's issue port for about 8, and each VALU instruction costs about 4.5 more, so the trellis decode
+// (the B operand) only hides behind the MFMAs when each decoded column feeds enough of them: here every
+// column feeds 16 (8 row groups x 2 k-halves).  The A operand needs no LDS at all: the pre-pass writes
+// the rotated activations fragment-major (below), so each A fragment is one contiguous 1 KB wave load
+// that the four waves of a block share through L1.  With 128 columns per wave every wave owns one whole
+// Hadamard-128 block of outputs, so the output transform is done in registers too: no barrier anywhere
+// in the kernel, and each wave runs independently.
+//
+//   * fragment-major activations: for row block rb (16 rows), 64-feature step s and half h, 1 KB holds
+//     lane (n, g) = row 16 rb + n, PERM16 positions 64 s + 16 g + 8 h .. +8 -- exactly the A operand
+//     of one 16x16x32 MFMA (rows past M are zero);
+//   * per step, the wave's trellis words arrive as K coalesced 16-byte loads per lane and pass through a
+//     per-wave LDS slot (instead of several scattered word loads per tile column), lane
+//     (n, g) decodes column n of tile row 4 s + g of each of the wave's 8 tile columns
+//     (exl3_device.hpp) and the wave issues 128 MFMAs into 256 fp32 accumulators (accumulator VGPRs);
+//     the next step's A fragments and trellis words are in flight meanwhile (two register buffers,
+//     the loop unrolled by two so neither is copied);
+//   * epilogue per 16-row group: Hadamard-128 over the wave's columns (column = 16 nb + n: DPP
+//     butterflies over the lane bits, stage by stage over all 32 values, register butterflies over nb),
+//     * 1/sqrt(128) * rout * s_out (* the row scale first on the 8-bit path), bf16 into the slice;
+//   * a block is 4 waves on the same 128 rows and 4 consecutive column blocks; blocks are ordered so
+//     that the blocks running on one XCD (consecutive block ids go to different XCDs) share row tiles
+//     and column groups in its L2.
 #include "exl3_device.hpp"
 #include "exl3_internal.hpp"
 
 namespace exl3 {
 
-constexpr int kBM = 256, kBN = 128;       // block tile
-constexpr int kWM = 128, kWN = 64;        // wave tile
-constexpr int kNBW = kWN / 16;            // column groups per wave
-constexpr int kGroupM = 4;                // row tiles per XCD group
+namespace {
+
+constexpr int kRows = 128;                // rows per wave (and per block)
+constexpr int kCols = 128;                // columns per wave
+constexpr int kWavesN = 4;                // waves (column blocks) per block
+constexpr int kGroupRows = 8;             // row tiles per XCD group
 
 struct GemmArgs {
-  const uint16_t* xh;       // fp16 [M, IC], PERM16 order
+  const uint16_t* xf;       // fragment-major fp16 activations, M rounded up to 16 rows
+  int64_t xf_bytes;
   const uint32_t* code;
   const uint16_t* rout;
   const uint16_t* s_out;
-  const float* row_scale;   // 8-bit path: per-row scale of the integer codes in xh (else null)
+  const float* row_scale;   // 8-bit path: per-row scale of the integer codes (else null)
   uint16_t* out;            // bf16 [M, ldo]
   int64_t ldo, col0;
   int M, IC, OC;
-  int mt, nt;               // row / column tiles
+  int mt, nt;               // row tiles (128 rows) / column groups (512 columns)
   uint32_t code_bytes;
 };
 
-// Hadamard butterflies across the 16 lanes of a 16x16 accumulator column group (lane bits 0..3 =
-// column bits 0..3).
-__device__ __forceinline__ float had16_lanes(float v, int lane) {
-  v = bfly(v, dpp<kQuadXor1>(v), lane & 1);
-  v = bfly(v, dpp<kQuadXor2>(v), lane & 2);
-  v = bfly(v, lane_xor4(v), lane & 4);
-  v = bfly(v, lane_xor8(v), lane & 8);
-  return v;
+// One butterfly stage of the Hadamard over the lane bits of a 16x16 accumulator group (lane bit b =
+// column bit b), applied to all 32 values of a row group before the next stage so that the lane
+// exchanges of different values fill each other's wait states.
+template <int S>
+__device__ __forceinline__ float lane_partner(float v) {
+  if constexpr (S == 1) return dpp<kQuadXor1>(v);
+  else if constexpr (S == 2) return dpp<kQuadXor2>(v);
+  else if constexpr (S == 4) return lane_xor4(v);
+  else return dpp<kRowRor8>(v);
+}
+
+template <int S>
+__device__ __forceinline__ void lane_stage(float (&v)[8][4], int lane) {
+  float q[8][4];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) q[nb][r] = lane_partner<S>(v[nb][r]);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[nb][r] = bfly(v[nb][r], q[nb][r], lane & S);
 }
 
 template <int K>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   using G = Geom<K>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
   const int n = lane & 15, g = lane >> 4;
 
-  // ---- block -> (row tile, column tile): XCD-grouped order
+  // ---- block -> (row tile, column group): a contiguous range of tiles per XCD, grouped by row tiles
   const int T = p.mt * p.nt;
   const int nxcd = 8;
   const int bid = blockIdx.x;
   const int xcd = bid % nxcd, j = bid / nxcd;
   const int per = T / nxcd, extra = T % nxcd;
-  const int tile = xcd * per + (xcd < extra ? xcd : extra) + j;   // contiguous range per XCD
-  const int group = tile / (kGroupM * p.nt);
-  const int gm = (p.mt - group * kGroupM) < kGroupM ? (p.mt - group * kGroupM) : kGroupM;
-  const int in_group = tile - group * kGroupM * p.nt;
-  const int mtile = group * kGroupM + in_group % gm;
-  const int ntile = in_group / gm;
+  const int tile = xcd * per + (xcd < extra ? xcd : extra) + j;
+  const int group = tile / (kGroupRows * p.nt);
+  const int gm = (p.mt - group * kGroupRows) < kGroupRows ? (p.mt - group * kGroupRows) : kGroupRows;
+  const int in_group = tile - group * kGroupRows * p.nt;
+  const int mtile = group * kGroupRows + in_group % gm;
+  const int ctile = (in_group / gm) * kWavesN + wave;      // this wave's 128-column block
+  if (ctile * kCols >= p.OC) return;                        // past the last column block (no barriers below)
 
-  const int row0 = mtile * kBM + wm * kWM;                  // first output row of this wave
-  const int col0 = ntile * kBN + wn * kWN;                  // first shard column of this wave
-  const uint32_t tpr = uint32_t(p.OC / kTile);
+  const int row0 = mtile * kRows;
+  const int col0 = ctile * kCols;
+  const int steps = p.IC / 64;                              // even: IC is a multiple of 128
 
-  // ---- A tile of the block: rows mtile*256 .. +256, one 64-feature step per LDS buffer, stored in
-  //      MFMA fragment order: fragment (wm, mb, h) is 64 slots of 16 bytes; lane (n, g) of it is row
-  //      wm*128 + 16*mb + n, PERM16 features 16g + 8h .. +8 of the step, kept in slot
-  //      (16g + n) ^ (4g + 2h).  The XOR keeps each 16-lane read group on one contiguous 256-byte span
-  //      (the conflict-free ds_read_b128 pattern) and sends the 8 chunks of a row, which 8 consecutive
-  //      threads write after a coalesced global load, to 8 different bank groups.
-  constexpr int kAFrag = 64 * 8;                            // halves per fragment
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][2 * 8 * 2 * kAFrag];
-  const int steps = p.IC / 64;
-  // staging: thread t copies row (t + 256 q) / 8, chunk (t + 256 q) % 8 of the step (coalesced rows)
-  const uint16_t* asrc[8];
-  int adst[8];
+  // ---- A: a buffer resource based at this row tile; group mb, step st, half h of the lane's fragment is
+  //      at mb * steps * 2048 + st * 2048 + h * 1024 + lane * 16 bytes.  The record count ends at the last
+  //      written row block, so fragments of row blocks past it read as zeros (those rows are not stored).
+  const int64_t tile_bytes = int64_t(row0 >> 4) * steps * 2048;
+  const int64_t left = p.xf_bytes - tile_bytes;
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.xf) + tile_bytes / 2, (short)0, (int)(left < 0x7FFFFFFF ? left : 0x7FFFFFFF), kBufferFlags);
+  const uint32_t lane_byte = uint32_t(lane) * 16u;
+  const uint32_t mb_stride = uint32_t(steps) * 2048u;
+  auto load_a = [&](int st, half8 (&dst)[8][2]) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int cidx = threadIdx.x + 256 * q, r = cidx >> 3, c = cidx & 7;
-    const int grow = mtile * kBM + r;
-    asrc[q] = p.xh + int64_t(grow < p.M ? grow : p.M - 1) * p.IC + 8 * c;
-    const int fwm = r >> 7, fmb = (r >> 4) & 7, fn = r & 15, fg = c >> 1, fh = c & 1;
-    const int frag = (fwm * 8 + fmb) * 2 + fh;
-    adst[q] = (frag * 64 + ((16 * fg + fn) ^ (4 * fg + 2 * fh))) * 8;
-  }
-  u32x4 astage[8];
-  auto load_a = [&](int st) {
-    const int s = st < steps ? st : steps - 1;
+    for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) astage[q] = *reinterpret_cast<const u32x4*>(asrc[q] + 64 * s);
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4*>(&As[buf][adst[q]]) = astage[q];
+      for (int h = 0; h < 2; ++h)
+        dst[mb][h] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
+            arsrc, lane_byte + uint32_t(h * 1024), uint32_t(mb) * mb_stride + uint32_t(st) * 2048u, 0));
   };
 
-  // ---- B: tile columns col0/16 + nb; lane (n, g) decodes column n of tile row 4*step + g
+  // ---- B: the words of one step of this wave's 8 tile columns are 4 tile rows x 256K contiguous bytes
+  //      (tiles of a tile row are adjacent).  Lane group g loads its tile row with K coalesced 16-byte
+  //      loads per lane; the wave parks them in its LDS slot (each row padded by 64 bytes so the four
+  //      groups read different banks) and lane (n, g) reads the words of column n of each tile back.
+  //      A step read past the shard re-reads the last one (the range check covers the vector offset only).
+  __shared__ __attribute__((aligned(16))) char slots[kWavesN * Slot<K>::kBytes];
+  char* my_row = slots + wave * Slot<K>::kBytes + g * Slot<K>::kRowBytes;
   int woff[G::kNW], shift;
   column_word_offsets<K>(n, woff, shift);
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(p.code), (short)0, (int)p.code_bytes, kBufferFlags);
-  uint32_t lane_off[G::kNW];
-#pragma unroll
-  for (int w = 0; w < G::kNW; ++w) lane_off[w] = (uint32_t(g) * tpr * G::kWords + uint32_t(woff[w])) * 4u;
+  const uint32_t tpr = uint32_t(p.OC / kTile);
+  const uint32_t lane_off = uint32_t(g) * tpr * G::kWords * 4u + uint32_t(n) * 16u;
   const uint32_t col_base = uint32_t(col0 / kTile) * G::kWords * 4u;
-  const uint32_t step_stride = 4u * tpr * G::kWords * 4u;   // four tile rows per 64-feature step
-  uint32_t wcur[kNBW][G::kNW], wnext[kNBW][G::kNW];
-  auto load_w = [&](int st, uint32_t (&dst)[kNBW][G::kNW]) {
-    const int s = st < steps ? st : steps - 1;                // clamped: the data is simply not used
-    const uint32_t soff = uint32_t(s) * step_stride + col_base;
+  const uint32_t step_stride = 4u * tpr * G::kWords * 4u;
+  auto load_t = [&](int st, u32x4 (&dst)[K]) {
+    const uint32_t soff = uint32_t(st) * step_stride + col_base;
 #pragma unroll
-    for (int nb = 0; nb < kNBW; ++nb)
+    for (int i = 0; i < K; ++i)
+      dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off + uint32_t(i * 256), soff, 0));
+  };
+  auto read_col = [&](int nb, uint32_t (&dst)[G::kNW]) {
 #pragma unroll
-      for (int w = 0; w < G::kNW; ++w)
-        dst[nb][w] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off[w] + uint32_t(nb * G::kWords * 4), soff, 0);
+    for (int w = 0; w < G::kNW; ++w) dst[w] = *reinterpret_cast<const uint32_t*>(my_row + (nb * G::kWords + woff[w]) * 4);
   };
 
-  float4v acc[8][kNBW];
+  float4v acc[8][8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < kNBW; ++nb) acc[mb][nb] = (float4v){0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (float4v){0.f, 0.f, 0.f, 0.f};
 
   const CodebookRegs cb = codebook_regs();
-  load_a(0);
-  load_w(0, wcur);
-  store_a(0);
-  __syncthreads();
-  const int aslot0 = wm * 16 * kAFrag + (lane ^ (4 * g)) * 8;       // fragment (wm, mb, 0)
-  const int aslot1 = wm * 16 * kAFrag + (lane ^ (4 * g + 2)) * 8;   // fragment (wm, mb, 1), less kAFrag
-  // One step per iteration (no unrolled pair: that makes the compiler move the accumulators between
-  // register files at the back edge); the double buffers rotate by value instead.
-  for (int st = 0; st < steps; ++st) {
-    const int buf = st & 1;
-    load_a(st + 1);
-    load_w(st + 1, wnext);
-    half8 a[8][2];
+  // One step: park the step's words in the slot (this wave's LDS operations complete in order, so the
+  // previous step's reads are not overtaken), then per tile column read its words one column ahead,
+  // decode and issue 16 MFMAs.
+  auto compute = [&](const half8 (&a)[8][2], const u32x4 (&tb)[K]) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      a[mb][0] = *reinterpret_cast<const half8*>(&As[buf][aslot0 + (2 * mb) * kAFrag]);
-      a[mb][1] = *reinterpret_cast<const half8*>(&As[buf][aslot1 + (2 * mb + 1) * kAFrag]);
-    }
+    for (int i = 0; i < K; ++i) *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tb[i];
+    uint32_t wv[2][G::kNW];
+    read_col(0, wv[0]);
 #pragma unroll
-    for (int nb = 0; nb < kNBW; ++nb) {
+    for (int nb = 0; nb < 8; ++nb) {
+      if (nb + 1 < 8) read_col(nb + 1, wv[(nb + 1) & 1]);
       uint32_t v[8];
-      decode_column<K>(wcur[nb], shift, v, cb);
+      decode_column<K>(wv[nb & 1], shift, v, cb);
       const half8 b0 = as_half8(v[0], v[1], v[2], v[3]), b1 = as_half8(v[4], v[5], v[6], v[7]);
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        acc[mb][nb] = mfma16(a[mb][0], b0, acc[mb][nb]);
-        acc[mb][nb] = mfma16(a[mb][1], b1, acc[mb][nb]);
-      }
+      for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = mfma16(a[mb][0], b0, acc[mb][nb]);
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = mfma16(a[mb][1], b1, acc[mb][nb]);
     }
-    store_a(buf ^ 1);                                       // the other buffer: last read one step ago
-#pragma unroll
-    for (int nb = 0; nb < kNBW; ++nb)
-#pragma unroll
-      for (int w = 0; w < G::kNW; ++w) wcur[nb][w] = wnext[nb][w];
-    __syncthreads();
+  };
+
+  half8 a0[8][2], a1[8][2];
+  u32x4 t0[K], t1[K];
+  load_a(0, a0);
+  load_t(0, t0);
+  // Each half of the loop body first issues the loads of the buffers the other half has just finished
+  // with, then computes; the scheduling barriers keep the halves apart so that every load has a whole
+  // step of MFMAs to arrive in.
+  for (int st = 0; st < steps; st += 2) {
+    load_a(st + 1, a1);
+    load_t(st + 1, t1);
+    compute(a0, t0);
+    __builtin_amdgcn_sched_barrier(0);
+    const int nx = st + 2 < steps ? st + 2 : steps - 1;     // the last prefetch is not used
+    load_a(nx, a0);
+    load_t(nx, t0);
+    compute(a1, t1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue, one 16-row group at a time: Hadamard-128 over the block's 128 columns (column =
-  //      64*wn + 16*nb + n: lane bits give column bits 0..3, nb bits 4..5, wn bit 6), then
-  //      * 1/sqrt(128) * rout * s_out, bf16 into the slice.  The last stage pairs column c of wave
-  //      (wm, 0) with column c + 64 of wave (wm, 1): each wave publishes its values in LDS.
-  float* xch = reinterpret_cast<float*>(&As[0][0]);        // [4 waves][4 regs][kNBW][64 lanes], reused
-  float sc[kNBW];
+  // ---- epilogue, one 16-row group at a time: Hadamard-128 over the wave's 128 columns, lane stages
+  //      then register stages (the same butterflies in the same order for every value), * 1/sqrt(128) *
+  //      rout * s_out (after * the row scale on the 8-bit path), rows 4g + r and 4g + r + 1 rounded to
+  //      bf16 together and stored as 2-byte halves.
+  float sc[8];
 #pragma unroll
-  for (int nb = 0; nb < kNBW; ++nb) {
+  for (int nb = 0; nb < 8; ++nb) {
     const int c = col0 + 16 * nb + n;
     sc[nb] = kInvSqrt128 * f16_to_f32(p.rout[c]) * f16_to_f32(p.s_out[c]);
   }
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) {                          // unrolled: acc must stay in registers
-    float v[kNBW][4];
+  for (int mb = 0; mb < 8; ++mb) {
+    float v[8][4];
 #pragma unroll
-    for (int nb = 0; nb < kNBW; ++nb)
+    for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[nb][r] = had16_lanes(acc[mb][nb][r], lane);
+      for (int r = 0; r < 4; ++r) v[nb][r] = acc[mb][nb][r];
+    lane_stage<1>(v, lane);
+    lane_stage<2>(v, lane);
+    lane_stage<4>(v, lane);
+    lane_stage<8>(v, lane);
 #pragma unroll
-    for (int h = 1; h < kNBW; h <<= 1)
+    for (int hb = 1; hb < 8; hb <<= 1)
 #pragma unroll
-      for (int nb = 0; nb < kNBW; ++nb)
-        if (!(nb & h))
+      for (int nb = 0; nb < 8; ++nb)
+        if (!(nb & hb))
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float lo = v[nb][r], hi = v[nb | h][r];
+            const float lo = v[nb][r], hi = v[nb | hb][r];
             v[nb][r] = lo + hi;
-            v[nb | h][r] = lo - hi;
+            v[nb | hb][r] = lo - hi;
           }
-    __syncthreads();                                        // previous group's reads (and the main loop) done
-#pragma unroll
-    for (int nb = 0; nb < kNBW; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) xch[((wave * 4 + r) * kNBW + nb) * 64 + lane] = v[nb][r];
-    __syncthreads();
-    const int partner = wave ^ 1;                           // same wm, other column half
-#pragma unroll
-    for (int nb = 0; nb < kNBW; ++nb)
+    const int rbase = row0 + 16 * mb + 4 * g;
+    if (p.row_scale) {                                        // 8-bit path: the row scale first
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float o = xch[((partner * 4 + r) * kNBW + nb) * 64 + lane];
-        v[nb][r] = wn == 0 ? v[nb][r] + o : o - v[nb][r];
+        const float rs = p.row_scale[rbase + r < p.M ? rbase + r : p.M - 1];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) v[nb][r] *= rs;
       }
+    }
+    const bool full = row0 + 16 * mb + 16 <= p.M;             // wave-uniform: no row of the group is past M
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 16 * mb + 4 * g + r;
-      if (row < p.M) {
-        // the row scale commutes with the column transform; 1.0 on the 16-bit path (exact)
-        const float rs = p.row_scale ? p.row_scale[row] : 1.0f;
-        uint16_t* dst = p.out + int64_t(row) * p.ldo + p.col0 + col0 + n;
+    for (int rp = 0; rp < 4; rp += 2) {
+      uint16_t* d0 = p.out + int64_t(rbase + rp) * p.ldo + p.col0 + col0 + n;
+      uint16_t* d1 = d0 + p.ldo;
+      uint32_t w[8];
 #pragma unroll
-        for (int nb = 0; nb < kNBW; ++nb) dst[16 * nb] = (uint16_t)f32_to_bf16(v[nb][r] * rs * sc[nb]);
+      for (int nb = 0; nb < 8; ++nb) w[nb] = f32x2_to_bf16x2(v[nb][rp] * sc[nb], v[nb][rp + 1] * sc[nb]);
+      if (full) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          d0[16 * nb] = uint16_t(w[nb] & 0xFFFFu);
+          d1[16 * nb] = uint16_t(w[nb] >> 16);
+        }
+      } else {
+        const bool ok0 = rbase + rp < p.M, ok1 = rbase + rp + 1 < p.M;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          if (ok0) d0[16 * nb] = uint16_t(w[nb] & 0xFFFFu);
+          if (ok1) d1[16 * nb] = uint16_t(w[nb] >> 16);
+        }
       }
     }
   }
 }
 
-hipError_t launch_gemm(const void* xh, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
+}  // namespace
+
+hipError_t launch_gemm(const void* xf, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
                        int64_t ldo, int64_t col0, int64_t M, int64_t IC, int64_t OC, hipStream_t stream,
                        const float* row_scale) {
   GemmArgs a;
-  a.xh = (const uint16_t*)xh;
-  a.row_scale = row_scale;
+  a.xf = (const uint16_t*)xf;
+  a.xf_bytes = (M + 15) / 16 * 16 * IC * 2;
   a.code = (const uint32_t*)code;
   a.rout = (const uint16_t*)rout;
   a.s_out = (const uint16_t*)s_out;
+  a.row_scale = row_scale;
   a.out = (uint16_t*)out;
   a.ldo = ldo;
   a.col0 = col0;
   a.M = (int)M;
   a.IC = (int)IC;
   a.OC = (int)OC;
-  a.mt = (int)((M + kBM - 1) / kBM);
-  a.nt = (int)((OC + kBN - 1) / kBN);
+  a.mt = (int)((M + kRows - 1) / kRows);
+  a.nt = (int)((OC + kCols * kWavesN - 1) / (kCols * kWavesN));
   a.code_bytes = uint32_t(IC / 16 * (OC / 16) * 32 * K);
-  dim3 grid((unsigned)(a.mt * a.nt)), block(256);
+  dim3 grid((unsigned)(a.mt * a.nt)), block(64 * kWavesN);
   switch (K) {
     case 1: hipLaunchKernelGGL(gemm_kernel<1>, grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL(gemm_kernel<2>, grid, block, 0, stream, a); break;

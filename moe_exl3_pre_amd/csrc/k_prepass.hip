@@ -4,11 +4,20 @@
 //   * fp16 (the GEMM operand; "vllm-quantpack 0.1.0", `Exl3LinearMethod._forward` casts to fp16), or
 //   * per-row 8-bit codes with a float32 scale ("radiance_escha.py", `escha_linear_into` stages a
 //     uint8 [M, IC] buffer and a float32 [M] scale): sc = max|xh| / 127, q = clamp(rne(xh / sc), +-127).
-// One 256-thread block per row; each wave transforms whole 128-blocks, two features per lane.
+// Layouts: natural row-major [M, IC] (exl3_rotate_activations), or the GEMM's fragment-major layout
+// (PERM16 order inside every 16-feature group, then 1 KB per 16-row x 32-position MFMA A operand:
+// row block rb, 64-position step s and half h hold lane (n, g) = row 16 rb + n, positions
+// 64 s + 16 g + 8 h .. +8), with the rows up to the next multiple of 16 written as zeros.
 #include "exl3_device.hpp"
 #include "exl3_internal.hpp"
 
 namespace exl3 {
+
+// Index (in halves) of PERM16 position P of row m in the fragment-major layout.
+__device__ __forceinline__ int64_t frag_index(int64_t m, int64_t P, int64_t IC) {
+  const int w = int(P & 63);
+  return ((m >> 4) * (IC >> 6) + (P >> 6)) * 1024 + ((w >> 3) & 1) * 512 + (16 * (w >> 4) + int(m & 15)) * 8 + (w & 7);
+}
 
 // Transform one 128-block.  Natural order: lane l holds features 2l, 2l+1.  PERMUTED order: lane l holds
 // features perm_pair_feature(l) and +8, which the PERM16 layout stores at positions 2l, 2l+1.
@@ -75,7 +84,8 @@ __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __rest
       had128_wave(v0, v1, lane);
       packed = uint32_t(f32_to_f16(v0 * kInvSqrt128)) | (uint32_t(f32_to_f16(v1 * kInvSqrt128)) << 16);
     }
-    *reinterpret_cast<uint32_t*>(xh + m * IC + k0 + 2 * lane) = packed;
+    const int64_t at = PERMUTED ? frag_index(m, k0 + 2 * lane, IC) : m * IC + k0 + 2 * lane;
+    *reinterpret_cast<uint32_t*>(xh + at) = packed;
   }
 }
 
@@ -94,6 +104,13 @@ __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restr
   __shared__ float red[4];
   const int64_t m = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (m >= M) {                                        // padding row of the fragment-major layout: zeros
+    if constexpr (F16OUT && PERMUTED) {
+      for (int64_t q = wave; q < IC / kHad; q += 4)
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(q_out) + frag_index(m, q * kHad + 2 * lane, IC)) = 0u;
+    }
+    return;
+  }
   const uint16_t* xr = x + m * IC;
   float amax = 0.f;
   for (int64_t q = wave; q < IC / kHad; q += 4) {
@@ -118,8 +135,8 @@ __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restr
     }
     const int64_t k = q * kHad + 2 * lane;             // natural: features k, k+1; permuted: positions k, k+1
     if constexpr (F16OUT) {
-      uint16_t* dst = static_cast<uint16_t*>(q_out) + m * IC;
-      *reinterpret_cast<uint32_t*>(dst + k) = uint32_t(f32_to_f16(float(q0))) | (uint32_t(f32_to_f16(float(q1))) << 16);
+      uint16_t* dst = static_cast<uint16_t*>(q_out) + (PERMUTED ? frag_index(m, k, IC) : m * IC + k);
+      *reinterpret_cast<uint32_t*>(dst) = uint32_t(f32_to_f16(float(q0))) | (uint32_t(f32_to_f16(float(q1))) << 16);
     } else {
       int8_t* dst = static_cast<int8_t*>(q_out) + m * IC;
       *reinterpret_cast<uint16_t*>(dst + k) = uint16_t(uint8_t(q0)) | uint16_t(uint16_t(uint8_t(q1)) << 8);
@@ -145,7 +162,9 @@ hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, 
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
                              int64_t IC, bool permuted, hipStream_t stream, bool f16_codes) {
   if (M <= 0) return hipSuccess;
-  dim3 grid((unsigned)M), block(256);
+  // the fragment-major layout (permuted fp16 codes) also gets its padding rows
+  const int64_t rows = permuted && f16_codes ? (M + 15) / 16 * 16 : M;
+  dim3 grid((unsigned)rows), block(256);
   const uint16_t *xx = (const uint16_t*)x, *si = (const uint16_t*)s_in, *ri = (const uint16_t*)rin;
   if (permuted && f16_codes)
     hipLaunchKernelGGL((prepass_i8_kernel<true, true>), grid, block, 0, stream, xx, si, ri, q, scale, M, IC);
