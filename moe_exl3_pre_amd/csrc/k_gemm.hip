@@ -17,8 +17,9 @@
 //     per-wave LDS slot (instead of several scattered word loads per tile column), lane
 //     (n, g) decodes column n of tile row 4 s + g of each of the wave's 8 tile columns
 //     (exl3_device.hpp) and the wave issues 128 MFMAs into 256 fp32 accumulators (accumulator VGPRs);
-//     the next step's A fragments and trellis words are in flight meanwhile (two register buffers,
-//     the loop unrolled by two so neither is copied);
+//     the next step's A fragments (two register buffers, the loop unrolled by two so neither is
+//     copied) and the trellis words of the step after (parked in the slot at the end of each step) are
+//     in flight meanwhile;
 //   * epilogue per 16-row group: Hadamard-128 over the wave's columns (column = 16 nb + n: DPP
 //     butterflies over the lane bits, stage by stage over all 32 values, register butterflies over nb),
 //     * 1/sqrt(128) * rout * s_out (* the row scale first on the 8-bit path), bf16 into the slice;
@@ -151,43 +152,58 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (float4v){0.f, 0.f, 0.f, 0.f};
 
   const CodebookRegs cb = codebook_regs();
-  // One step: park the step's words in the slot (this wave's LDS operations complete in order, so the
-  // previous step's reads are not overtaken), then per tile column read its words one column ahead,
-  // decode and issue 16 MFMAs.
-  auto compute = [&](const half8 (&a)[8][2], const u32x4 (&tb)[K]) {
+  // Trellis pipeline: the slot holds the current step's words, written at the end of the previous step;
+  // the one register buffer tn holds the next step's, loaded a whole step before it is parked.  So a step
+  // starts by reading its columns from LDS without waiting for any load, and every load has a step of
+  // MFMAs to arrive in.  This wave's LDS operations complete in order, so parking the next step after the
+  // current step's reads is safe.
+  u32x4 tn[K];
+  auto park = [&]() {
 #pragma unroll
-    for (int i = 0; i < K; ++i) *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tb[i];
-    uint32_t wv[2][G::kNW];
-    read_col(0, wv[0]);
+    for (int i = 0; i < K; ++i) *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tn[i];
+  };
+  // One step: read every column's words at once (the LDS latency is paid once), then per tile column
+  // decode and issue 16 MFMAs, then park the next step and load the one after.  The scheduling groups ask
+  // for the LDS reads first and then one MFMA per kValuPerMfma VALU instructions, so the decode of the
+  // next columns fills the MFMA issue gaps instead of running in bursts with the matrix core idle.
+  constexpr int kValuPerMfma = K <= 1 ? 1 : K == 2 ? 2 : K <= 4 ? 3 : 4;
+  auto step = [&](int st, const half8 (&a)[8][2]) {
+    uint32_t wv[8][G::kNW];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) read_col(nb, wv[nb]);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      if (nb + 1 < 8) read_col(nb + 1, wv[(nb + 1) & 1]);
       uint32_t v[8];
-      decode_column<K>(wv[nb & 1], shift, v, cb);
+      decode_column<K>(wv[nb], shift, v, cb);
       const half8 b0 = as_half8(v[0], v[1], v[2], v[3]), b1 = as_half8(v[4], v[5], v[6], v[7]);
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = mfma16(a[mb][0], b0, acc[mb][nb]);
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = mfma16(a[mb][1], b1, acc[mb][nb]);
     }
+    park();                                                 // step st + 1 (a clamped copy past the end)
+    load_t(st + 2 < steps ? st + 2 : steps - 1, tn);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 * G::kNW, 0);      // LDS reads
+#pragma unroll
+    for (int i = 0; i < 128; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // then VALU
+    }
   };
 
   half8 a0[8][2], a1[8][2];
-  u32x4 t0[K], t1[K];
+  load_t(0, tn);
   load_a(0, a0);
-  load_t(0, t0);
-  // Each half of the loop body first issues the loads of the buffers the other half has just finished
-  // with, then computes; the scheduling barriers keep the halves apart so that every load has a whole
-  // step of MFMAs to arrive in.
+  park();
+  load_t(steps > 1 ? 1 : 0, tn);
+  // Two steps per iteration with the A buffers swapped, so neither is copied; the scheduling barriers
+  // keep the halves apart so that the next step's A loads have a whole step of MFMAs to arrive in.
   for (int st = 0; st < steps; st += 2) {
     load_a(st + 1, a1);
-    load_t(st + 1, t1);
-    compute(a0, t0);
+    step(st, a0);
     __builtin_amdgcn_sched_barrier(0);
-    const int nx = st + 2 < steps ? st + 2 : steps - 1;     // the last prefetch is not used
-    load_a(nx, a0);
-    load_t(nx, t0);
-    compute(a1, t1);
+    load_a(st + 2 < steps ? st + 2 : steps - 1, a0);        // the last prefetch is not used
+    step(st + 1, a1);
     __builtin_amdgcn_sched_barrier(0);
   }
 
