@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="the M sweep over a 64-layer projection set on both paths (prints its own report)")
     ap.add_argument("--sweep-ms", default="1,4,8,16,24,32,48,64,128,512,8192")
+    ap.add_argument("--pmc-prefill", action="store_true",
+                    help="counter runs: 1 GiB device copies (known bytes), then two eager calls of each prefill projection")
     ap.add_argument("--pmc-ref", action="store_true",
                     help="eager decode launches (no graph) plus a plain 1 GiB copy, for hardware-counter runs")
     return ap.parse_args()
@@ -304,6 +306,15 @@ def main():
 
     if a.sweep:
         run_sweep(torch, exl3, synth, dev, [int(m) for m in a.sweep_ms.split(",") if m])
+        return
+    if a.pmc_prefill:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        del src, dst
+        time_prefill(torch, exl3, synth, dev, reps=1)
+        print(json.dumps({"pmc_prefill": True, "copy_bytes": 1 << 30}), flush=True)
         return
     IC, ldo, sets, trellis_bytes = build_gate_up(torch, dev, synth, COPIES)
     rng = np.random.default_rng(77)

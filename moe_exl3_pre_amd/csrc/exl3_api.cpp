@@ -124,6 +124,7 @@ struct Layout {
   size_t slab_off, slab_bytes;   // decode-phase split-K slab
   size_t xh_off, xh_bytes;       // prefill-phase rotated activations, one region per distinct (s_in, rin)
   size_t scale_off;              // 8-bit path: the row scales, at this offset inside each region
+  size_t part_off;               // 8-bit path: per-(row, 128-block) max |xh|, at this offset inside each region
   size_t total;
 };
 
@@ -133,7 +134,8 @@ Layout layout_for(size_t slab_bytes, int64_t M = 0, int64_t IC = 0, int n_xh = 0
   L.slab_bytes = align_up(slab_bytes);
   L.xh_off = L.slab_off + L.slab_bytes;
   L.scale_off = align_up(size_t((M + 15) / 16 * 16) * size_t(IC) * 2);   // fragment-major: rows padded to 16
-  L.xh_bytes = L.scale_off + (int8 ? align_up(size_t(M) * 4) : 0);
+  L.part_off = L.scale_off + (int8 ? align_up(size_t(M) * 4) : 0);
+  L.xh_bytes = L.part_off + (int8 ? align_up(size_t(M) * size_t(IC / 128) * 4) : 0);
   L.total = L.xh_off + L.xh_bytes * size_t(n_xh);
   return L;
 }
@@ -196,7 +198,8 @@ int run_gemm(const char* who, void* out, int64_t ldo, const void* x, int64_t M, 
     char* region = ws + L.xh_off + L.xh_bytes * size_t(slot[i]);
     float* scale = int8 ? reinterpret_cast<float*>(region + L.scale_off) : nullptr;
     if (slot[i] > done) {
-      hipError_t e = int8 ? launch_prepass_i8(x, in[i].s_in, in[i].rin, region, scale, M, IC, true, stream, true)
+      hipError_t e = int8 ? launch_prepass_i8(x, in[i].s_in, in[i].rin, region, scale, M, IC, true, stream, true,
+                                              reinterpret_cast<float*>(region + L.part_off))
                           : launch_prepass_f16(x, in[i].s_in, in[i].rin, region, M, IC, true, stream, (M + 15) / 16 * 16);
       if (int rc = launch_status(e, who)) return rc;
       done = slot[i];

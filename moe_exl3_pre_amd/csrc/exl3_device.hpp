@@ -179,6 +179,11 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, bf16x2v));
 }
 
+// Two values to fp16 at once (hardware conversion, round to nearest even): the same bits as f32_to_f16.
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, half2v));
+}
+
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 __device__ __forceinline__ uint16_t f32_to_f16(float f) {   // round to nearest even

@@ -50,10 +50,12 @@ hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC
 // [M, M_pad) of xh are written as zeros.
 hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, void* xh, int64_t M, int64_t IC,
                               bool permuted, hipStream_t stream, int64_t M_pad = 0);
-// q receives int8 codes, or with f16_codes the same codes as fp16 numbers (the GEMM's operand; with
-// permuted, fragment-major with the rows up to a multiple of 16 written as zeros).
+// Natural layout: q receives int8 codes.  permuted with f16_codes: the same codes as fp16 numbers in the
+// fragment-major layout (the GEMM's operand; rows up to a multiple of 16 written as zeros), which needs
+// part, M * (IC / 128) floats of scratch.  Other combinations are rejected.
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
-                             int64_t IC, bool permuted, hipStream_t stream, bool f16_codes = false);
+                             int64_t IC, bool permuted, hipStream_t stream, bool f16_codes = false,
+                             float* part = nullptr);
 hipError_t launch_decode_tiles(void* w, const int16_t* code, int64_t IC, int64_t OC, int K, hipStream_t stream);
 // Prefill-phase GEMM of one shard (one wave per 128 x 128 output tile); xf is the pre-pass output in the
 // fragment-major layout (rows padded to 16).  With row_scale (8-bit path) every output row is multiplied

@@ -13,42 +13,26 @@
 
 namespace exl3 {
 
-// Index (in halves) of PERM16 position P of row m in the fragment-major layout.
-__device__ __forceinline__ int64_t frag_index(int64_t m, int64_t P, int64_t IC) {
-  const int w = int(P & 63);
-  return ((m >> 4) * (IC >> 6) + (P >> 6)) * 1024 + ((w >> 3) & 1) * 512 + (16 * (w >> 4) + int(m & 15)) * 8 + (w & 7);
-}
-
-// Transform one 128-block.  Natural order: lane l holds features 2l, 2l+1.  PERMUTED order: lane l holds
-// features perm_pair_feature(l) and +8, which the PERM16 layout stores at positions 2l, 2l+1.
-template <bool PERMUTED>
+// Transform one 128-block in natural order: lane l holds features 2l, 2l+1.
 __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ x, const uint16_t* __restrict__ s_in,
                                              const uint16_t* __restrict__ rin, int64_t k0, int lane,
                                              float& v0, float& v1) {
-  if (PERMUTED) {
-    const int64_t f = k0 + perm_pair_feature(lane);
-    v0 = bf16_to_f32(x[f]) * f16_to_f32(s_in[f]) * f16_to_f32(rin[f]);
-    v1 = bf16_to_f32(x[f + 8]) * f16_to_f32(s_in[f + 8]) * f16_to_f32(rin[f + 8]);
-  } else {
-    const int64_t k = k0 + 2 * lane;
-    const uint32_t xb = *reinterpret_cast<const uint32_t*>(x + k);
-    const uint32_t sb = *reinterpret_cast<const uint32_t*>(s_in + k);
-    const uint32_t rb = *reinterpret_cast<const uint32_t*>(rin + k);
-    v0 = bf16_to_f32(xb & 0xFFFFu) * f16_to_f32(sb & 0xFFFFu) * f16_to_f32(rb & 0xFFFFu);
-    v1 = bf16_to_f32(xb >> 16) * f16_to_f32(sb >> 16) * f16_to_f32(rb >> 16);
-  }
+  const int64_t k = k0 + 2 * lane;
+  const uint32_t xb = *reinterpret_cast<const uint32_t*>(x + k);
+  const uint32_t sb = *reinterpret_cast<const uint32_t*>(s_in + k);
+  const uint32_t rb = *reinterpret_cast<const uint32_t*>(rin + k);
+  v0 = bf16_to_f32(xb & 0xFFFFu) * f16_to_f32(sb & 0xFFFFu) * f16_to_f32(rb & 0xFFFFu);
+  v1 = bf16_to_f32(xb >> 16) * f16_to_f32(sb >> 16) * f16_to_f32(rb >> 16);
   had128_wave(v0, v1, lane);
   v0 *= kInvSqrt128;
   v1 *= kInvSqrt128;
 }
 
-// One wave per 8 rows of one 128-block: the block's s_in / rin are loaded once, every input load is
-// issued before any arithmetic (the kernel is latency-bound otherwise), and each row's result is one
-// coalesced 256-byte store.  Rows M .. M_pad-1 are padding and are written as zeros (the decode-phase
-// kernel reads whole 16-row blocks).
+// Natural layout.  One wave per 8 rows of one 128-block: the block's s_in / rin are loaded once, every
+// input load is issued before any arithmetic (the kernel is latency-bound otherwise), and each row's
+// result is one coalesced 256-byte store.  Rows M .. M_pad-1, when asked for, are written as zeros.
 constexpr int kPrepassRows = 8;
 
-template <bool PERMUTED>
 __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ s_in,
                                                           const uint16_t* __restrict__ rin,
@@ -61,9 +45,7 @@ __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __rest
   if (unit >= ngroups * nblk) return;
   const int64_t m0 = (unit / nblk) * kPrepassRows, q = unit % nblk;
   const int64_t k0 = q * kHad;
-  // this lane's two features: natural (2l, 2l+1) or PERM16 pair (f, f+8) stored at (2l, 2l+1)
-  const int64_t f0 = PERMUTED ? k0 + perm_pair_feature(lane) : k0 + 2 * lane;
-  const int64_t f1 = PERMUTED ? f0 + 8 : f0 + 1;
+  const int64_t f0 = k0 + 2 * lane, f1 = f0 + 1;              // this lane's two features
   const float si0 = f16_to_f32(s_in[f0]), ri0 = f16_to_f32(rin[f0]);
   const float si1 = f16_to_f32(s_in[f1]), ri1 = f16_to_f32(rin[f1]);
   uint32_t xv[kPrepassRows];
@@ -84,38 +66,204 @@ __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __rest
       had128_wave(v0, v1, lane);
       packed = uint32_t(f32_to_f16(v0 * kInvSqrt128)) | (uint32_t(f32_to_f16(v1 * kInvSqrt128)) << 16);
     }
-    const int64_t at = PERMUTED ? frag_index(m, k0 + 2 * lane, IC) : m * IC + k0 + 2 * lane;
-    *reinterpret_cast<uint32_t*>(xh + at) = packed;
+    *reinterpret_cast<uint32_t*>(xh + m * IC + k0 + 2 * lane) = packed;
   }
 }
 
-// 8-bit variant ("radiance_escha.py", `escha_linear_into`: an 8-bit activation buffer plus one float
-// scale per row).  Two passes over the row: the first finds max |xh| over the row, the second recomputes
-// the same fp32 features (identical instruction sequence, so identical values) and quantises them:
-// sc = amax / 127, q = clamp(rne(xh / sc), -127, 127), and q = 0 for a row whose amax is 0.
-// F16OUT writes each code as the fp16 number q (exact: |q| <= 127), which the fp16 MFMA GEMM consumes;
-// otherwise the codes are written as int8.
-template <bool PERMUTED, bool F16OUT>
+// The GEMM's fragment-major layout, fp16.  One wave per (16-row block, 128-feature block): lane (n, g)
+// holds row n's features of the 16-groups g and g + 4 (32 values), loaded as four coalesced 16-byte
+// chunks.  The Hadamard-128 then runs as register butterflies over feature bits 0..3 and 6 and as
+// lane-pair exchanges (v_permlane16_swap / v_permlane32_swap) over bits 4 and 5, and the wave's output is
+// exactly 4 KB of the layout (the four 1 KB fragments of its two 64-position steps), written as four
+// 1 KB wave stores.  Rows past M are written as zeros.
+//
+// Lane-pair butterfly over lane bit 4 (resp. 5) for two values X, Y of every lane: after swapping the odd
+// rows (halves) of X with the even ones of Y, the lower lane of each pair holds both X values and the
+// upper lane both Y values, in the order (lower lane's, upper lane's); both form (a + b, a - b), and
+// the same swap puts the four results back in place.
+template <bool HALF32>
+__device__ __forceinline__ void lane_pair_bfly(float& x, float& y) {
+  uint32_t a = __float_as_uint(x), b = __float_as_uint(y);
+  auto r = HALF32 ? __builtin_amdgcn_permlane32_swap(a, b, false, false)
+                  : __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  const float p = __uint_as_float(r[0]), q = __uint_as_float(r[1]);
+  auto t = HALF32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(p + q), __float_as_uint(p - q), false, false)
+                  : __builtin_amdgcn_permlane16_swap(__float_as_uint(p + q), __float_as_uint(p - q), false, false);
+  x = __uint_as_float(t[0]);
+  y = __uint_as_float(t[1]);
+}
+
+// The rotated features of one (16-row block rb, 128-block q) unit, before the 1/sqrt(128) normalisation:
+// lane (n, g) ends with row 16 rb + n, features 16 (g + 4t) + w of the block in v[t][w] (zeros past M).
+__device__ __forceinline__ void frag_transform(const uint16_t* __restrict__ x, const uint16_t* __restrict__ s_in,
+                                               const uint16_t* __restrict__ rin, int64_t M, int64_t IC, int64_t rb,
+                                               int64_t q, int lane, float (&v)[2][16]) {
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t row = rb * 16 + n;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int64_t f = q * kHad + 16 * (g + 4 * t);
+    u32x4 sv[2], rv[2], xv[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      sv[c] = *reinterpret_cast<const u32x4*>(s_in + f + 8 * c);
+      rv[c] = *reinterpret_cast<const u32x4*>(rin + f + 8 * c);
+      xv[c] = row < M ? *reinterpret_cast<const u32x4*>(x + row * IC + f + 8 * c) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const uint32_t xw = xv[w >> 3][(w >> 1) & 3], sw = sv[w >> 3][(w >> 1) & 3], rw = rv[w >> 3][(w >> 1) & 3];
+      const int sh = (w & 1) * 16;
+      // (x * s_in) * rin, in the order the layer defines
+      v[t][w] = bf16_to_f32((xw >> sh) & 0xFFFFu) * f16_to_f32(uint16_t(sw >> sh)) * f16_to_f32(uint16_t(rw >> sh));
+    }
+  }
+  // feature bits 0..3: register butterflies inside each 16-group
+#pragma unroll
+  for (int b = 1; b < 16; b <<= 1)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int w = 0; w < 16; ++w)
+        if (!(w & b)) {
+          const float lo = v[t][w], hi = v[t][w | b];
+          v[t][w] = lo + hi;
+          v[t][w | b] = lo - hi;
+        }
+  // bits 4 and 5: lane pairs (lane bit 4, lane bit 5), two values per exchange
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int w = 0; w < 16; w += 2) lane_pair_bfly<false>(v[t][w], v[t][w + 1]);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int w = 0; w < 16; w += 2) lane_pair_bfly<true>(v[t][w], v[t][w + 1]);
+  // bit 6: the two groups of the lane
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const float lo = v[0][w], hi = v[1][w];
+    v[0][w] = lo + hi;
+    v[1][w] = lo - hi;
+  }
+}
+
+// Fragment (step 2q + t, half h), lane (n, g) holds PERM16 positions 8h .. 8h+7 of 16-group g + 4t, i.e. the
+// features (4h + j, 4h + j + 8) for j = 0..3: o(t, h)[j] packs those two of u (already converted).
+__device__ __forceinline__ uint16_t* frag_unit_base(uint16_t* xf, int64_t IC, int64_t rb, int64_t q, int lane) {
+  return xf + ((rb * (IC / 64) + 2 * q) * 2) * 512 + lane * 8;
+}
+
+__global__ __launch_bounds__(256) void prepass_frag_f16_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ s_in,
+                                                               const uint16_t* __restrict__ rin,
+                                                               uint16_t* __restrict__ xf, int64_t M, int64_t IC) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nq = IC / kHad;
+  const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (unit >= (M + 15) / 16 * nq) return;
+  const int64_t rb = unit / nq, q = unit % nq;
+  float v[2][16];
+  frag_transform(x, s_in, rin, M, IC, rb, q, lane, v);
+  uint16_t* base = frag_unit_base(xf, IC, rb, q, lane);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = f32x2_to_f16x2(v[t][4 * h + j] * kInvSqrt128, v[t][4 * h + j + 8] * kInvSqrt128);
+      *reinterpret_cast<u32x4*>(base + (2 * t + h) * 512) = o;
+    }
+}
+
+// 8-bit codes in the fragment-major layout, in three launches over the same units: the per-(row, block)
+// max |xh| (frag_amax), the row scale sc = max / 127 (row_scale), and the codes q = clamp(rne(xh / sc),
+// +-127) written as fp16 numbers (frag_codes; q = 0 for a row whose max is 0, zeros past M).  Both unit
+// kernels compute xh with the same inlined transform, so the codes are taken on the values the scale
+// came from.
+__global__ __launch_bounds__(256) void prepass_frag_amax_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ s_in,
+                                                                const uint16_t* __restrict__ rin,
+                                                                float* __restrict__ part, int64_t M, int64_t IC) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nq = IC / kHad;
+  const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (unit >= (M + 15) / 16 * nq) return;
+  const int64_t rb = unit / nq, q = unit % nq;
+  float v[2][16];
+  frag_transform(x, s_in, rin, M, IC, rb, q, lane, v);
+  float a = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int w = 0; w < 16; ++w) a = fmaxf(a, fabsf(v[t][w] * kInvSqrt128));
+  a = fmaxf(a, __shfl_xor(a, 16, 64));                     // the four lanes of row n
+  a = fmaxf(a, __shfl_xor(a, 32, 64));
+  const int64_t row = rb * 16 + (lane & 15);
+  if (lane < 16 && row < M) part[row * nq + q] = a;
+}
+
+__global__ __launch_bounds__(256) void prepass_row_scale_kernel(const float* __restrict__ part,
+                                                                float* __restrict__ scale, int64_t M, int64_t nq) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  float a = 0.f;
+  for (int64_t q = lane; q < nq; q += 64) a = fmaxf(a, part[row * nq + q]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) a = fmaxf(a, __shfl_xor(a, d, 64));
+  if (lane == 0) scale[row] = __fdiv_rn(a, 127.0f);
+}
+
+__global__ __launch_bounds__(256) void prepass_frag_codes_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ s_in,
+                                                                 const uint16_t* __restrict__ rin,
+                                                                 const float* __restrict__ scale,
+                                                                 uint16_t* __restrict__ xf, int64_t M, int64_t IC) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nq = IC / kHad;
+  const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (unit >= (M + 15) / 16 * nq) return;
+  const int64_t rb = unit / nq, q = unit % nq;
+  float v[2][16];
+  frag_transform(x, s_in, rin, M, IC, rb, q, lane, v);
+  const int64_t row = rb * 16 + (lane & 15);
+  const float sc = row < M ? scale[row] : 0.f;
+  auto code = [&](float xv) -> float {
+    return sc > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(xv * kInvSqrt128, sc)), -127.f), 127.f) : 0.f;
+  };
+  uint16_t* base = frag_unit_base(xf, IC, rb, q, lane);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = f32x2_to_f16x2(code(v[t][4 * h + j]), code(v[t][4 * h + j + 8]));
+      *reinterpret_cast<u32x4*>(base + (2 * t + h) * 512) = o;
+    }
+}
+
+// 8-bit variant, natural layout ("radiance_escha.py", `escha_linear_into`: an 8-bit activation buffer
+// plus one float scale per row).  One block per row, two passes over it: the first finds max |xh| over
+// the row, the second recomputes the same fp32 features (identical instruction sequence, so identical
+// values) and quantises them: sc = amax / 127, q = clamp(rne(xh / sc), -127, 127), and q = 0 for a row
+// whose amax is 0.
 __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ s_in,
                                                          const uint16_t* __restrict__ rin,
-                                                         void* __restrict__ q_out, float* __restrict__ scale,
+                                                         int8_t* __restrict__ q_out, float* __restrict__ scale,
                                                          int64_t M, int64_t IC) {
   __shared__ float red[4];
   const int64_t m = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (m >= M) {                                        // padding row of the fragment-major layout: zeros
-    if constexpr (F16OUT && PERMUTED) {
-      for (int64_t q = wave; q < IC / kHad; q += 4)
-        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(q_out) + frag_index(m, q * kHad + 2 * lane, IC)) = 0u;
-    }
-    return;
-  }
   const uint16_t* xr = x + m * IC;
   float amax = 0.f;
   for (int64_t q = wave; q < IC / kHad; q += 4) {
     float v0, v1;
-    rotate_block<PERMUTED>(xr, s_in, rin, q * kHad, lane, v0, v1);
+    rotate_block(xr, s_in, rin, q * kHad, lane, v0, v1);
     amax = fmaxf(amax, fmaxf(fabsf(v0), fabsf(v1)));
   }
 #pragma unroll
@@ -127,53 +275,52 @@ __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restr
   if (threadIdx.x == 0) scale[m] = sc;
   for (int64_t q = wave; q < IC / kHad; q += 4) {
     float v0, v1;
-    rotate_block<PERMUTED>(xr, s_in, rin, q * kHad, lane, v0, v1);
+    rotate_block(xr, s_in, rin, q * kHad, lane, v0, v1);
     int q0 = 0, q1 = 0;
     if (sc > 0.f) {
       q0 = (int)fminf(fmaxf(rintf(__fdiv_rn(v0, sc)), -127.f), 127.f);
       q1 = (int)fminf(fmaxf(rintf(__fdiv_rn(v1, sc)), -127.f), 127.f);
     }
-    const int64_t k = q * kHad + 2 * lane;             // natural: features k, k+1; permuted: positions k, k+1
-    if constexpr (F16OUT) {
-      uint16_t* dst = static_cast<uint16_t*>(q_out) + (PERMUTED ? frag_index(m, k, IC) : m * IC + k);
-      *reinterpret_cast<uint32_t*>(dst) = uint32_t(f32_to_f16(float(q0))) | (uint32_t(f32_to_f16(float(q1))) << 16);
-    } else {
-      int8_t* dst = static_cast<int8_t*>(q_out) + m * IC;
-      *reinterpret_cast<uint16_t*>(dst + k) = uint16_t(uint8_t(q0)) | uint16_t(uint16_t(uint8_t(q1)) << 8);
-    }
+    const int64_t k = q * kHad + 2 * lane;             // features k, k + 1
+    *reinterpret_cast<uint16_t*>(q_out + m * IC + k) = uint16_t(uint8_t(q0)) | uint16_t(uint16_t(uint8_t(q1)) << 8);
   }
 }
 
 hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, void* xh, int64_t M, int64_t IC,
                               bool permuted, hipStream_t stream, int64_t M_pad) {
   if (M <= 0) return hipSuccess;
+  if (permuted) {                                         // fragment-major: rows padded to 16 with zeros
+    const int64_t units = (M + 15) / 16 * (IC / kHad);
+    hipLaunchKernelGGL(prepass_frag_f16_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream,
+                       (const uint16_t*)x, (const uint16_t*)s_in, (const uint16_t*)rin, (uint16_t*)xh, M, IC);
+    return hipGetLastError();
+  }
   const int64_t rows = M_pad > M ? M_pad : M;
   const int64_t units = (rows + kPrepassRows - 1) / kPrepassRows * (IC / kHad);
   dim3 grid((unsigned)((units + 3) / 4)), block(256);
-  if (permuted)
-    hipLaunchKernelGGL(prepass_f16_kernel<true>, grid, block, 0, stream, (const uint16_t*)x, (const uint16_t*)s_in,
-                       (const uint16_t*)rin, (uint16_t*)xh, M, rows, IC);
-  else
-    hipLaunchKernelGGL(prepass_f16_kernel<false>, grid, block, 0, stream, (const uint16_t*)x, (const uint16_t*)s_in,
-                       (const uint16_t*)rin, (uint16_t*)xh, M, rows, IC);
+  hipLaunchKernelGGL(prepass_f16_kernel, grid, block, 0, stream, (const uint16_t*)x, (const uint16_t*)s_in,
+                     (const uint16_t*)rin, (uint16_t*)xh, M, rows, IC);
   return hipGetLastError();
 }
 
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
-                             int64_t IC, bool permuted, hipStream_t stream, bool f16_codes) {
+                             int64_t IC, bool permuted, hipStream_t stream, bool f16_codes, float* part) {
   if (M <= 0) return hipSuccess;
-  // the fragment-major layout (permuted fp16 codes) also gets its padding rows
-  const int64_t rows = permuted && f16_codes ? (M + 15) / 16 * 16 : M;
-  dim3 grid((unsigned)rows), block(256);
-  const uint16_t *xx = (const uint16_t*)x, *si = (const uint16_t*)s_in, *ri = (const uint16_t*)rin;
-  if (permuted && f16_codes)
-    hipLaunchKernelGGL((prepass_i8_kernel<true, true>), grid, block, 0, stream, xx, si, ri, q, scale, M, IC);
-  else if (permuted)
-    hipLaunchKernelGGL((prepass_i8_kernel<true, false>), grid, block, 0, stream, xx, si, ri, q, scale, M, IC);
-  else if (f16_codes)
-    hipLaunchKernelGGL((prepass_i8_kernel<false, true>), grid, block, 0, stream, xx, si, ri, q, scale, M, IC);
-  else
-    hipLaunchKernelGGL((prepass_i8_kernel<false, false>), grid, block, 0, stream, xx, si, ri, q, scale, M, IC);
+  if (permuted && f16_codes) {                            // fragment-major fp16 codes (the GEMM operand)
+    if (!part) return hipErrorInvalidValue;
+    const int64_t units = (M + 15) / 16 * (IC / kHad);
+    const dim3 ug((unsigned)((units + 3) / 4)), blk(256);
+    const uint16_t *xx = (const uint16_t*)x, *si = (const uint16_t*)s_in, *ri = (const uint16_t*)rin;
+    hipLaunchKernelGGL(prepass_frag_amax_kernel, ug, blk, 0, stream, xx, si, ri, part, M, IC);
+    hipLaunchKernelGGL(prepass_row_scale_kernel, dim3((unsigned)((M + 3) / 4)), blk, 0, stream, (const float*)part,
+                       scale, M, IC / kHad);
+    hipLaunchKernelGGL(prepass_frag_codes_kernel, ug, blk, 0, stream, xx, si, ri, (const float*)scale, (uint16_t*)q, M,
+                       IC);
+    return hipGetLastError();
+  }
+  if (permuted || f16_codes) return hipErrorInvalidValue;  // natural layout: int8 codes only
+  hipLaunchKernelGGL(prepass_i8_kernel, dim3((unsigned)M), dim3(256), 0, stream, (const uint16_t*)x,
+                     (const uint16_t*)s_in, (const uint16_t*)rin, (int8_t*)q, scale, M, IC);
   return hipGetLastError();
 }
 
