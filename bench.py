@@ -222,7 +222,8 @@ def run_sweep(torch, exl3, synth, dev, ms):
     """M sweep over one 64-layer decoder's projections (hidden 5120, intermediate 17408): every layer has
     its own seeded random trellis words and scales (generated on the GPU), so successive calls stream new
     weights.  Each (projection, M) is timed on the decode-phase path (FORCE_GEMV, 16-row launches) and on
-    the MFMA path (FORCE_MFMA): one call per layer, all 64 layers, events around the whole pass."""
+    the MFMA path (FORCE_MFMA, with its automatic feature split): one call per layer, all 64 layers, events
+    around the whole pass."""
     cfg = synth.SWEEP
     L = cfg["layers"]
     gen = torch.Generator(device=dev)
@@ -238,7 +239,8 @@ def run_sweep(torch, exl3, synth, dev, ms):
         for M in ms:
             x = (torch.randn((M, IC), device=dev, generator=gen)).to(torch.bfloat16)
             out = torch.empty((M, OC), dtype=torch.bfloat16, device=dev)
-            row = {"projection": name, "IC": IC, "OC": OC, "K": K, "M": M}
+            row = {"projection": name, "IC": IC, "OC": OC, "K": K, "M": M,
+                   "mfma_splits": exl3.lib().exl3_gemm_splits(M, IC, OC)}
             for tag, flags in (("gemv", exl3.FORCE_GEMV), ("mfma", exl3.FORCE_MFMA)):
                 ws = exl3.alloc_workspace(exl3.linear_workspace_bytes(M, IC, OC, flags), dev)
                 step = lambda i: exl3.linear_into(out, x, layers[i % L]["code"], K, layers[i % L]["s_in"],

@@ -59,7 +59,9 @@ enum {
   EXL3_ACT_INT8 = 1u << 0,   /* per-row 8-bit activations: sc = max|xh| / 127, q = clamp(rne(xh / sc), +-127),
                                  Y = sc * (q . W); runs on the MFMA GEMM at every M (not with FORCE_GEMV) */
   EXL3_FORCE_GEMV = 1u << 1, /* force the decode-phase (streaming split-K) kernel whatever M is */
-  EXL3_FORCE_MFMA = 1u << 2  /* force the prefill-phase (tiled MFMA GEMM) kernel whatever M is */
+  EXL3_FORCE_MFMA = 1u << 2, /* force the prefill-phase (tiled MFMA GEMM) kernel whatever M is */
+  EXL3_GEMM_NO_SPLIT = 1u << 3 /* never split the GEMM's input features (exl3_gemm_splits): one fixed-order
+                                 reduction per output element, so a row's result does not depend on M */
 };
 
 /* Text of the last failure on the calling thread ("" if none). */
@@ -69,9 +71,17 @@ const char* exl3_last_error(void);
 int exl3_version(void);
 
 /* Largest M served by the decode-phase path (launches of up to 16 rows) when no FORCE flag is given,
- * for a call whose widest shard has OC output columns: 16 * clamp(40960 / OC, 1, 8), the measured
- * crossover against the MFMA GEMM over a 5120/17408 decoder's projections. */
+ * for a call whose widest shard has OC output columns: 16 * clamp(14336 / OC, 1, 8), the measured
+ * crossover against the (feature-split) MFMA GEMM over a 5120/17408 decoder's projections. */
 int64_t exl3_gemv_max_rows(int64_t OC);
+
+/* Number of input-feature splits the prefill-phase GEMM uses for M rows of an IC -> OC shard when no
+ * FORCE flag is given: 1 once the shard has 1024 output tiles of 128 x 128 (one wave each fills the
+ * chip), otherwise about 1024 / tiles, each split keeping at least 512 input features.  The splits'
+ * fp32 partial tiles are summed in split order by a second launch, so the result is deterministic but
+ * differs in rounding from the unsplit GEMM (EXL3_GEMM_NO_SPLIT), and a row's result depends on M
+ * through the split count.  1 for invalid shapes. */
+int exl3_gemm_splits(int64_t M, int64_t IC, int64_t OC);
 
 /* --------------------------------------------------------------------------------------------------
  * One projection written into its column slice ("radiance_escha.py", `escha_linear_into`: one escha
@@ -88,8 +98,10 @@ int64_t exl3_gemv_max_rows(int64_t OC);
  * rout/s_out 2-byte aligned, IC*OC*K/8 < 2 GiB.
  * Precision: x * s_in * rin and the Hadamard in fp32, the rotated activations rounded once to fp16, fp16 x
  * fp16 products accumulated in fp32, output transform and scales in fp32, one round-to-nearest-even to
- * bf16.  Row results do not depend on the other rows; M <= exl3_gemv_max_rows(OC) runs the decode-phase
- * kernel, larger M the MFMA GEMM (the two agree to rounding, not bitwise).
+ * bf16.  M <= exl3_gemv_max_rows(OC) runs the decode-phase kernel, larger M the MFMA GEMM (the two agree
+ * to rounding, not bitwise), split over the input features when the shard is small (exl3_gemm_splits).
+ * For a given split count a row's result does not depend on the other rows; on the GEMM with
+ * EXL3_GEMM_NO_SPLIT it does not depend on M at all.
  * 8-bit path (EXL3_ACT_INT8): the codes q are exact in fp16 and every q * W product is exact in fp32,
  * so the contraction is the integer dot product up to fp32 summation; the row scale is applied before
  * the output transform.

@@ -38,14 +38,15 @@ int launch_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-constexpr unsigned kKnownFlags = EXL3_ACT_INT8 | EXL3_FORCE_GEMV | EXL3_FORCE_MFMA;
+constexpr unsigned kKnownFlags = EXL3_ACT_INT8 | EXL3_FORCE_GEMV | EXL3_FORCE_MFMA | EXL3_GEMM_NO_SPLIT;
 // Dispatch threshold.  The decode-phase path streams every weight once per 16-row launch, so its time
-// grows with ceil(M/16) * OC; the MFMA GEMM keeps one 256-row tile per 128 output columns, so below
-// M = 256 it runs OC/128 workgroups whose time does not depend on OC.  Measured over the projections of
-// a 5120/17408 decoder (M sweep, 64 layers) the crossover sits at ceil(M/16) ~ 40960/OC (gate and up:
-// 32 rows, qkv: 64, o and down: 128); the threshold follows that, between one and eight launches.
+// grows with ceil(M/16) * OC; the MFMA GEMM splits the input features of a shard with few output tiles
+// so that about 1024 waves run, which keeps its time nearly flat in M up to a few hundred rows.
+// Measured over the projections of a 5120/17408 decoder (M sweep, 64 layers) the decode path is faster
+// up to 16 rows for 17408 outputs, 32 for 7168 and for 5120 (the o projection ties at 48); the threshold
+// 16 * clamp(14336 / OC, 1, 8) follows that, between one and eight launches.
 int64_t gemv_max_rows(int64_t OC) {
-  int64_t chunks = OC > 0 ? 40960 / OC : 1;
+  int64_t chunks = OC > 0 ? 14336 / OC : 1;
   chunks = chunks < 1 ? 1 : (chunks > 8 ? 8 : chunks);
   return chunks * kDecodeMaxRows;
 }
@@ -121,7 +122,7 @@ bool decode_slab_bytes(int64_t M, int64_t IC, int n, const DecShardIn* in, size_
 }
 
 struct Layout {
-  size_t slab_off, slab_bytes;   // decode-phase split-K slab
+  size_t slab_off, slab_bytes;   // split-K slab: decode-phase partials, or the prefill GEMM's partial tiles
   size_t xh_off, xh_bytes;       // prefill-phase rotated activations, one region per distinct (s_in, rin)
   size_t scale_off;              // 8-bit path: the row scales, at this offset inside each region
   size_t part_off;               // 8-bit path: per-(row, 128-block) max |xh|, at this offset inside each region
@@ -204,8 +205,9 @@ int run_gemm(const char* who, void* out, int64_t ldo, const void* x, int64_t M, 
       if (int rc = launch_status(e, who)) return rc;
       done = slot[i];
     }
+    const GemmSplit sp = (flags & EXL3_GEMM_NO_SPLIT) ? GemmSplit{1, int(IC / 64)} : gemm_split(M, IC, in[i].OC);
     hipError_t e = launch_gemm(region, in[i].code, in[i].K, in[i].rout, in[i].s_out, out, ldo, in[i].col0, M, IC,
-                               in[i].OC, stream, scale);
+                               in[i].OC, stream, scale, sp, reinterpret_cast<float*>(ws + L.slab_off));
     if (int rc = launch_status(e, who)) return rc;
   }
   return EXL3_OK;
@@ -302,8 +304,14 @@ bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsign
     if (!decode_slab_bytes(M, IC, n, in, &slab)) return false;
     *L = layout_for(slab);
   } else {
+    size_t slab = 0;                                      // shards run one after another: the largest split
+    if (!(flags & EXL3_GEMM_NO_SPLIT))
+      for (int i = 0; i < n; ++i) {
+        const size_t b = gemm_slab_bytes(M, in[i].OC, gemm_split(M, IC, in[i].OC));
+        slab = b > slab ? b : slab;
+      }
     int slot[kMaxShards];
-    *L = layout_for(0, M, IC, distinct_inputs(n, in, slot), (flags & EXL3_ACT_INT8) != 0);
+    *L = layout_for(slab, M, IC, distinct_inputs(n, in, slot), (flags & EXL3_ACT_INT8) != 0);
   }
   return true;
 }
@@ -317,6 +325,11 @@ const char* exl3_last_error(void) { return g_error.c_str(); }
 int exl3_version(void) { return 100; }
 
 int64_t exl3_gemv_max_rows(int64_t OC) { return gemv_max_rows(OC); }
+
+int exl3_gemm_splits(int64_t M, int64_t IC, int64_t OC) {
+  if (M <= 0 || IC <= 0 || OC <= 0 || IC % 128 || OC % 128) return 1;
+  return gemm_split(M, IC, OC).splits;
+}
 
 size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned flags) {
   if (M <= 0 || IC <= 0 || OC <= 0 || IC % 128 || OC % 128) return align_up(kCounterBytes);

@@ -57,12 +57,37 @@ hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, v
                              int64_t IC, bool permuted, hipStream_t stream, bool f16_codes = false,
                              float* part = nullptr);
 hipError_t launch_decode_tiles(void* w, const int16_t* code, int64_t IC, int64_t OC, int K, hipStream_t stream);
+// K split of the prefill GEMM.  One wave owns a 128 x 128 output tile and the chip holds 1024 of them at a
+// time; a shard with fewer tiles has its 64-feature steps split so that about 1024 waves run, each split
+// keeping at least 8 steps (an even count), and a second launch sums the splits' partial tiles.
+struct GemmSplit {
+  int splits;   // 1: no split
+  int sps;      // steps per split (the last split may have fewer; every count is even)
+};
+
+inline GemmSplit gemm_split(int64_t M, int64_t IC, int64_t OC) {
+  const int64_t steps = IC / 64, tiles = (M + 127) / 128 * (OC / 128);
+  int64_t s = tiles > 0 ? 1024 / tiles : 1;
+  if (s > steps / 8) s = steps / 8;
+  if (s > 1) {
+    const int64_t sps = 2 * ((steps + 2 * s - 1) / (2 * s));
+    const int64_t n = (steps + sps - 1) / sps;
+    if (n > 1) return GemmSplit{int(n), int(sps)};
+  }
+  return GemmSplit{1, int(steps)};
+}
+
+// Partial-sum slab of a split GEMM: one 64 KB fp32 tile per (split, 128-row tile, 128-column tile).
+inline size_t gemm_slab_bytes(int64_t M, int64_t OC, GemmSplit sp) {
+  return sp.splits > 1 ? size_t(sp.splits) * size_t((M + 127) / 128) * size_t(OC / 128) * 65536 : 0;
+}
+
 // Prefill-phase GEMM of one shard (one wave per 128 x 128 output tile); xf is the pre-pass output in the
 // fragment-major layout (rows padded to 16).  With row_scale (8-bit path) every output row is multiplied
-// by row_scale[row] before the output transform.
+// by row_scale[row] before the output transform.  split.splits > 1 needs slab (gemm_slab_bytes).
 hipError_t launch_gemm(const void* xf, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
                        int64_t ldo, int64_t col0, int64_t M, int64_t IC, int64_t OC, hipStream_t stream,
-                       const float* row_scale = nullptr);
+                       const float* row_scale, GemmSplit split, float* slab);
 
 // ---- MoE expert bank
 constexpr int kMoeMaxGroups = 64;

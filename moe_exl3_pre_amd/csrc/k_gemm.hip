@@ -50,6 +50,8 @@ struct GemmArgs {
   int M, IC, OC;
   int mt, nt;               // row tiles (128 rows) / column groups (512 columns)
   uint32_t code_bytes;
+  int splits, sps;          // K split: splits of sps 64-feature steps each (1: no split)
+  float4v* slab;            // splits > 1: [split][row tile][column tile][mb * 8 + nb][lane] partial sums
 };
 
 // One butterfly stage of the Hadamard over the lane bits of a 16x16 accumulator group (lane bit b =
@@ -76,7 +78,72 @@ __device__ __forceinline__ void lane_stage(float (&v)[8][4], int lane) {
     for (int r = 0; r < 4; ++r) v[nb][r] = bfly(v[nb][r], q[nb][r], lane & S);
 }
 
-template <int K>
+// Output transform of one 16-row group of a 128-column tile (rows r0 .. r0+15, columns col0 .. +127 of
+// the shard): v[nb][r] holds row r0 + 4g + r, column 16 nb + n.  Hadamard-128 over the columns, lane
+// stages then register stages (the same butterflies in the same order for every value), * 1/sqrt(128) *
+// rout * s_out (after * the row scale on the 8-bit path), rows 4g + r and 4g + r + 1 rounded to bf16
+// together and stored as 2-byte halves.
+__device__ __forceinline__ void column_scales(const GemmArgs& p, int col0, int n, float (&sc)[8]) {
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const int c = col0 + 16 * nb + n;
+    sc[nb] = kInvSqrt128 * f16_to_f32(p.rout[c]) * f16_to_f32(p.s_out[c]);
+  }
+}
+
+__device__ __forceinline__ void epilogue_group(const GemmArgs& p, float (&v)[8][4], const float (&sc)[8], int r0,
+                                               int col0, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  lane_stage<1>(v, lane);
+  lane_stage<2>(v, lane);
+  lane_stage<4>(v, lane);
+  lane_stage<8>(v, lane);
+#pragma unroll
+  for (int hb = 1; hb < 8; hb <<= 1)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      if (!(nb & hb))
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float lo = v[nb][r], hi = v[nb | hb][r];
+          v[nb][r] = lo + hi;
+          v[nb | hb][r] = lo - hi;
+        }
+  const int rbase = r0 + 4 * g;
+  if (p.row_scale) {                                        // 8-bit path: the row scale first
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float rs = p.row_scale[rbase + r < p.M ? rbase + r : p.M - 1];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) v[nb][r] *= rs;
+    }
+  }
+  const bool full = r0 + 16 <= p.M;                         // wave-uniform: no row of the group is past M
+#pragma unroll
+  for (int rp = 0; rp < 4; rp += 2) {
+    uint16_t* d0 = p.out + int64_t(rbase + rp) * p.ldo + p.col0 + col0 + n;
+    uint16_t* d1 = d0 + p.ldo;
+    uint32_t w[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) w[nb] = f32x2_to_bf16x2(v[nb][rp] * sc[nb], v[nb][rp + 1] * sc[nb]);
+    if (full) {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        d0[16 * nb] = uint16_t(w[nb] & 0xFFFFu);
+        d1[16 * nb] = uint16_t(w[nb] >> 16);
+      }
+    } else {
+      const bool ok0 = rbase + rp < p.M, ok1 = rbase + rp + 1 < p.M;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        if (ok0) d0[16 * nb] = uint16_t(w[nb] & 0xFFFFu);
+        if (ok1) d1[16 * nb] = uint16_t(w[nb] >> 16);
+      }
+    }
+  }
+}
+
+template <int K, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   using G = Geom<K>;
   const int lane = threadIdx.x & 63;
@@ -85,8 +152,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 
   // ---- block -> (row tile, column group): a contiguous range of tiles per XCD, grouped by row tiles
   const int T = p.mt * p.nt;
+  const int split = SPLIT ? __builtin_amdgcn_readfirstlane(int(blockIdx.x) / T) : 0;   // K split of this block
   const int nxcd = 8;
-  const int bid = blockIdx.x;
+  const int bid = SPLIT ? int(blockIdx.x) - split * T : int(blockIdx.x);
   const int xcd = bid % nxcd, j = bid / nxcd;
   const int per = T / nxcd, extra = T % nxcd;
   const int tile = xcd * per + (xcd < extra ? xcd : extra) + j;
@@ -100,6 +168,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   const int row0 = mtile * kRows;
   const int col0 = ctile * kCols;
   const int steps = p.IC / 64;                              // even: IC is a multiple of 128
+  const int s0 = SPLIT ? split * p.sps : 0;                 // this split's steps [s0, s1), an even count
+  const int s1 = SPLIT ? (s0 + p.sps < steps ? s0 + p.sps : steps) : steps;
 
   // ---- A: a buffer resource based at this row tile; group mb, step st, half h of the lane's fragment is
   //      at mb * steps * 2048 + st * 2048 + h * 1024 + lane * 16 bytes.  The record count ends at the last
@@ -182,7 +252,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = mfma16(a[mb][1], b1, acc[mb][nb]);
     }
     park();                                                 // step st + 1 (a clamped copy past the end)
-    load_t(st + 2 < steps ? st + 2 : steps - 1, tn);
+    load_t(st + 2 < s1 ? st + 2 : s1 - 1, tn);
     __builtin_amdgcn_sched_group_barrier(0x100, 8 * G::kNW, 0);      // LDS reads
 #pragma unroll
     for (int i = 0; i < 128; ++i) {
@@ -192,93 +262,81 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   };
 
   half8 a0[8][2], a1[8][2];
-  load_t(0, tn);
-  load_a(0, a0);
+  load_t(s0, tn);
+  load_a(s0, a0);
   park();
-  load_t(steps > 1 ? 1 : 0, tn);
+  load_t(s0 + 1, tn);
   // Two steps per iteration with the A buffers swapped, so neither is copied; the scheduling barriers
   // keep the halves apart so that the next step's A loads have a whole step of MFMAs to arrive in.
-  for (int st = 0; st < steps; st += 2) {
+  for (int st = s0; st < s1; st += 2) {
     load_a(st + 1, a1);
     step(st, a0);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(st + 2 < steps ? st + 2 : steps - 1, a0);        // the last prefetch is not used
+    load_a(st + 2 < s1 ? st + 2 : s1 - 1, a0);              // the last prefetch is not used
     step(st + 1, a1);
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue, one 16-row group at a time: Hadamard-128 over the wave's 128 columns, lane stages
-  //      then register stages (the same butterflies in the same order for every value), * 1/sqrt(128) *
-  //      rout * s_out (after * the row scale on the 8-bit path), rows 4g + r and 4g + r + 1 rounded to
-  //      bf16 together and stored as 2-byte halves.
-  float sc[8];
+  // ---- a split parks its partial sums (1 KB wave stores; the reduction kernel finishes the tile)
+  if constexpr (SPLIT) {
+    const int ctiles = p.OC / kCols;
+    float4v* dst = p.slab + (((int64_t(split) * p.mt + mtile) * ctiles + ctile) * 64) * 64 + lane;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const int c = col0 + 16 * nb + n;
-    sc[nb] = kInvSqrt128 * f16_to_f32(p.rout[c]) * f16_to_f32(p.s_out[c]);
-  }
+    for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) {
-    float v[8][4];
+      for (int nb = 0; nb < 8; ++nb) dst[(mb * 8 + nb) * 64] = acc[mb][nb];
+  } else {
+    // ---- epilogue, one 16-row group at a time
+    float sc[8];
+    column_scales(p, col0, n, sc);
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[nb][r] = acc[mb][nb][r];
-    lane_stage<1>(v, lane);
-    lane_stage<2>(v, lane);
-    lane_stage<4>(v, lane);
-    lane_stage<8>(v, lane);
-#pragma unroll
-    for (int hb = 1; hb < 8; hb <<= 1)
+    for (int mb = 0; mb < 8; ++mb) {
+      float v[8][4];
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb)
-        if (!(nb & hb))
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float lo = v[nb][r], hi = v[nb | hb][r];
-            v[nb][r] = lo + hi;
-            v[nb | hb][r] = lo - hi;
-          }
-    const int rbase = row0 + 16 * mb + 4 * g;
-    if (p.row_scale) {                                        // 8-bit path: the row scale first
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float rs = p.row_scale[rbase + r < p.M ? rbase + r : p.M - 1];
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) v[nb][r] *= rs;
-      }
-    }
-    const bool full = row0 + 16 * mb + 16 <= p.M;             // wave-uniform: no row of the group is past M
-#pragma unroll
-    for (int rp = 0; rp < 4; rp += 2) {
-      uint16_t* d0 = p.out + int64_t(rbase + rp) * p.ldo + p.col0 + col0 + n;
-      uint16_t* d1 = d0 + p.ldo;
-      uint32_t w[8];
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) w[nb] = f32x2_to_bf16x2(v[nb][rp] * sc[nb], v[nb][rp + 1] * sc[nb]);
-      if (full) {
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          d0[16 * nb] = uint16_t(w[nb] & 0xFFFFu);
-          d1[16 * nb] = uint16_t(w[nb] >> 16);
-        }
-      } else {
-        const bool ok0 = rbase + rp < p.M, ok1 = rbase + rp + 1 < p.M;
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          if (ok0) d0[16 * nb] = uint16_t(w[nb] & 0xFFFFu);
-          if (ok1) d1[16 * nb] = uint16_t(w[nb] >> 16);
-        }
-      }
+        for (int r = 0; r < 4; ++r) v[nb][r] = acc[mb][nb][r];
+      epilogue_group(p, v, sc, row0 + 16 * mb, col0, lane);
     }
   }
+}
+
+// K-split reduction: one wave per (16-row group, 128-column tile) sums the splits' partials in split order
+// (fixed, so the result is deterministic) and applies the output transform.
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int ctiles = p.OC / kCols;
+  const int64_t tiles = int64_t(p.mt) * ctiles;
+  const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (unit >= tiles * 8) return;
+  const int64_t tile = unit >> 3;
+  const int mb = int(unit & 7);
+  const int mtile = int(tile / ctiles), ctile = int(tile % ctiles);
+  const int r0 = mtile * kRows + 16 * mb;
+  if (r0 >= p.M) return;                                    // the whole group is past M
+  float4v sum[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) sum[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < p.splits; ++sp) {
+    const float4v* src = p.slab + ((int64_t(sp) * tiles + tile) * 64 + mb * 8) * 64 + lane;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) sum[nb] += src[nb * 64];
+  }
+  float v[8][4], sc[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[nb][r] = sum[nb][r];
+  column_scales(p, ctile * kCols, lane & 15, sc);
+  epilogue_group(p, v, sc, r0, ctile * kCols, lane);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const void* xf, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
                        int64_t ldo, int64_t col0, int64_t M, int64_t IC, int64_t OC, hipStream_t stream,
-                       const float* row_scale) {
+                       const float* row_scale, GemmSplit split, float* slab) {
+  if (split.splits > 1 && !slab) return hipErrorInvalidValue;
   GemmArgs a;
   a.xf = (const uint16_t*)xf;
   a.xf_bytes = (M + 15) / 16 * 16 * IC * 2;
@@ -295,17 +353,30 @@ hipError_t launch_gemm(const void* xf, const int16_t* code, int K, const void* r
   a.mt = (int)((M + kRows - 1) / kRows);
   a.nt = (int)((OC + kCols * kWavesN - 1) / (kCols * kWavesN));
   a.code_bytes = uint32_t(IC / 16 * (OC / 16) * 32 * K);
-  dim3 grid((unsigned)(a.mt * a.nt)), block(64 * kWavesN);
+  a.splits = split.splits > 1 ? split.splits : 1;
+  a.sps = split.splits > 1 ? split.sps : int(IC / 64);
+  a.slab = reinterpret_cast<float4v*>(slab);
+  dim3 grid((unsigned)(a.mt * a.nt * a.splits)), block(64 * kWavesN);
+#define EXL3_GEMM_CASE(KK)                                                                   \
+  case KK:                                                                                   \
+    if (a.splits > 1) hipLaunchKernelGGL((gemm_kernel<KK, true>), grid, block, 0, stream, a);  \
+    else hipLaunchKernelGGL((gemm_kernel<KK, false>), grid, block, 0, stream, a);              \
+    break;
   switch (K) {
-    case 1: hipLaunchKernelGGL(gemm_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(gemm_kernel<2>, grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(gemm_kernel<3>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(gemm_kernel<4>, grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL(gemm_kernel<5>, grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL(gemm_kernel<6>, grid, block, 0, stream, a); break;
-    case 7: hipLaunchKernelGGL(gemm_kernel<7>, grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(gemm_kernel<8>, grid, block, 0, stream, a); break;
+    EXL3_GEMM_CASE(1)
+    EXL3_GEMM_CASE(2)
+    EXL3_GEMM_CASE(3)
+    EXL3_GEMM_CASE(4)
+    EXL3_GEMM_CASE(5)
+    EXL3_GEMM_CASE(6)
+    EXL3_GEMM_CASE(7)
+    EXL3_GEMM_CASE(8)
     default: return hipErrorInvalidValue;
+  }
+#undef EXL3_GEMM_CASE
+  if (a.splits > 1) {
+    const int64_t units = int64_t(a.mt) * (OC / kCols) * 8;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libexl3.so")
 
 OK, EINVAL, EWORKSPACE, EUNSUPPORTED, ELAUNCH = 0, -1, -2, -3, -4
-ACT_INT8, FORCE_GEMV, FORCE_MFMA = 1, 2, 4
+ACT_INT8, FORCE_GEMV, FORCE_MFMA, GEMM_NO_SPLIT = 1, 2, 4, 8
 
 _lib = None
 
@@ -51,6 +51,7 @@ _SIGS = {
     "exl3_last_error": (ctypes.c_char_p, []),
     "exl3_version": (ctypes.c_int, []),
     "exl3_gemv_max_rows": (ctypes.c_int64, [ctypes.c_int64]),
+    "exl3_gemm_splits": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
     "exl3_linear_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint]),
     "exl3_linear_into": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,

@@ -32,8 +32,8 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_limits():
     L = exl3.lib()
     assert L.exl3_version() >= 100
-    # the measured crossover rule: 16 * clamp(40960 // OC, 1, 8)
-    for OC, rows in ((17408, 32), (14336, 32), (7168, 80), (5120, 128), (256, 128), (81920, 16)):
+    # the measured crossover rule against the (feature-split) GEMM: 16 * clamp(14336 // OC, 1, 8)
+    for OC, rows in ((17408, 16), (14336, 16), (7168, 32), (5120, 32), (4096, 48), (256, 128), (81920, 16)):
         assert L.exl3_gemv_max_rows(OC) == rows, OC
 
 
@@ -120,3 +120,21 @@ def test_rotate_rejects():
     assert L.exl3_rotate_activations(FAKE, None, FAKE, 4, 100, FAKE, FAKE, 0, None) == exl3.EINVAL
     assert L.exl3_rotate_activations(FAKE, None, FAKE, 4, 128, FAKE, FAKE, exl3.ACT_INT8, None) == exl3.EINVAL
     assert L.exl3_rotate_activations(FAKE, None, FAKE, 0, 128, FAKE, FAKE, 0, None) == exl3.OK
+
+
+def test_gemm_split_plan():
+    """The K split fills about 1024 one-wave tiles, keeps >= 8 steps (512 features) per split, is 1 once
+    the shard has 1024 tiles, and the workspace holds the partial tiles."""
+    L = exl3.lib()
+    for M, IC, OC in ((200, 2048, 256), (1, 17408, 5120), (64, 5120, 17408), (8192, 5120, 17408),
+                      (1024, 4096, 14336), (129, 512, 128), (300, 1536, 384)):
+        s = L.exl3_gemm_splits(M, IC, OC)
+        tiles = -(-M // 128) * (OC // 128)
+        assert 1 <= s <= max(1, (IC // 64) // 8)
+        assert s == 1 or s * tiles <= 1024
+        if tiles >= 1024:
+            assert s == 1
+        if s > 1 and M > L.exl3_gemv_max_rows(OC):
+            assert exl3.linear_workspace_bytes(M, IC, OC) >= s * tiles * 65536 + M * IC * 2
+    assert L.exl3_gemm_splits(200, 2048, 256) == 4
+    assert L.exl3_gemm_splits(0, 2048, 256) == 1 and L.exl3_gemm_splits(4, 100, 256) == 1

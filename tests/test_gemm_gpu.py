@@ -84,13 +84,15 @@ def test_mfma_exact_symmetries_and_determinism():
 
 
 def test_mfma_batch_invariance():
-    """A row's output does not depend on the other rows (each output element is one fixed-order
-    reduction), so a prefix of the batch reproduces the same rows."""
-    c = synth.linear_case(5600, 300, 512, 256, 2)
+    """Without the feature split a row's output does not depend on the other rows (each output element is
+    one fixed-order reduction), so a prefix of the batch reproduces the same rows."""
+    c = synth.linear_case(5600, 300, 1024, 256, 2)
     d = _dev_case(c)
-    full = _run(c, d, exl3.FORCE_MFMA)
+    flags = exl3.FORCE_MFMA | exl3.GEMM_NO_SPLIT
+    full = _run(c, d, flags)
+    assert exl3.lib().exl3_gemm_splits(77, 1024, 256) > 1     # the split would change the rounding
     for M in (1, 77, 256):
-        part = _run(dict(c, M=M), dict(d, x=d["x"][:M].contiguous()), exl3.FORCE_MFMA)
+        part = _run(dict(c, M=M), dict(d, x=d["x"][:M].contiguous()), flags)
         assert torch.equal(part, full[:M]), M
 
 
@@ -133,4 +135,45 @@ def test_prefill_down_full_size_sampled():
     log("prefill down 8192 x 17408 -> 5120")
     out = _run(c, _dev_case(c), 0)
     rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(2).choice(M, 10, replace=False)]))
+    _sampled_check(c["x"], [dict(c, col0=0)], out, rows)
+
+
+# ------------------------------------------------------------------ K-split GEMM (default flags, small M)
+
+@pytest.mark.parametrize("M,IC,OC,K", [(200, 2048, 256, 2), (300, 1536, 384, 3), (131, 4096, 128, 4)])
+def test_split_k_parity(M, IC, OC, K):
+    """Above the decode-phase threshold but with few output tiles the GEMM splits the input features;
+    the split partial tiles summed in order match the oracle like the unsplit GEMM."""
+    splits = exl3.lib().exl3_gemm_splits(M, IC, OC)
+    assert splits > 1 and M > exl3.lib().exl3_gemv_max_rows(OC)
+    log(f"split-K M={M} IC={IC} OC={OC} K={K}: {splits} splits")
+    c = synth.linear_case(5700 + M + K, M, IC, OC, K)
+    d = _dev_case(c)
+    out = _run(c, d, 0)
+    args = (c["code"], K, c["s_in"], c["rin"], c["rout"], c["s_out"])
+    assert_close_linear(bf16_to_f64(out), O.linear(c["x"], *args, act="f16"), O.linear(c["x"], *args))
+    assert torch.equal(_run(c, d, 0), out)                    # fixed summation order: deterministic
+    unsplit = bf16_to_f64(_run(c, d, exl3.FORCE_MFMA | exl3.GEMM_NO_SPLIT))
+    assert rel_fro(bf16_to_f64(out), unsplit) < 1e-2
+
+
+def test_split_k_int8_small_m():
+    M, IC, OC = 20, 2048, 256
+    assert exl3.lib().exl3_gemm_splits(M, IC, OC) > 1
+    c = synth.linear_case(5800, M, IC, OC, 3)
+    d = _dev_case(c)
+    out = _run(c, d, exl3.ACT_INT8)
+    args = (c["code"], 3, c["s_in"], c["rin"], c["rout"], c["s_out"])
+    assert_close_linear(bf16_to_f64(out), O.linear(c["x"], *args, act="int8"), O.linear(c["x"], *args),
+                        tol=3e-2)
+
+
+def test_split_k_down_full_width_sampled():
+    """M=200 rows of the 17408 -> 5120 down projection (K=3): 80 tiles, the features split in many."""
+    cfg = synth.PREFILL["down"]
+    M = 200
+    assert exl3.lib().exl3_gemm_splits(M, cfg["IC"], cfg["OC"]) > 4
+    c = synth.linear_case(2002, M, cfg["IC"], cfg["OC"], cfg["K"])
+    out = _run(c, _dev_case(c), 0)
+    rows = np.array([0, 77, 128, 199])
     _sampled_check(c["x"], [dict(c, col0=0)], out, rows)
