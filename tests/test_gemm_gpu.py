@@ -177,3 +177,60 @@ def test_split_k_down_full_width_sampled():
     out = _run(c, _dev_case(c), 0)
     rows = np.array([0, 77, 128, 199])
     _sampled_check(c["x"], [dict(c, col0=0)], out, rows)
+
+
+def _merged_dev(case):
+    x = to_dev_x(case["x_bits"])
+    s_in, rin = to_dev(case["shards"][0]["s_in"]), to_dev(case["shards"][0]["rin"])
+    return x, [shard_to_dev(s, s_in, rin) for s in case["shards"]]
+
+
+def test_split_k_merged_equals_separate():
+    """Shards with different split plans in one call: each shard's split depends only on (M, IC, OC), so
+    the merged call equals one call per shard bit for bit (the slab is shared, the shards run in turn)."""
+    M, IC = 200, 1024
+    case = synth.merged_case(5900, M, IC, [(256, 2), (384, 3), (128, 4)])
+    plans = [exl3.lib().exl3_gemm_splits(M, IC, s["OC"]) for s in case["shards"]]
+    assert all(p > 1 for p in plans) and M > exl3.lib().exl3_gemv_max_rows(384)
+    x, shards = _merged_dev(case)
+    merged = torch.full((M, case["ldo"]), SENTINEL, dtype=torch.bfloat16, device=dev())
+    exl3.linear_multi_into(merged, x, shards)
+    sep = torch.full_like(merged, SENTINEL)
+    for s in shards:
+        exl3.linear_multi_into(sep, x, [s])
+    torch.cuda.synchronize()
+    assert torch.equal(merged, sep)
+    _sampled_check(case["x"], case["shards"], merged, np.arange(0, M, 17), blocks_per_shard=1)
+
+
+def test_split_k_graph_replay_matches_eager():
+    """The split path (GEMM launch + reduction launch, no memset) captured in a graph and replayed with eager
+    work between the replays."""
+    M, IC = 150, 2048
+    case = synth.merged_case(5901, M, IC, [(256, 3)])
+    assert exl3.lib().exl3_gemm_splits(M, IC, 256) > 1
+    x, shards = _merged_dev(case)
+    ws = exl3.alloc_workspace(exl3.linear_multi_workspace_bytes(M, IC, shards), dev())
+    eager = torch.zeros((M, case["ldo"]), dtype=torch.bfloat16, device=dev())
+    exl3.linear_multi_into(eager, x, shards, ws=ws)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        exl3.linear_multi_into(out, x, shards, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        exl3.linear_multi_into(out, x, shards, ws=ws)
+    for i in range(3):
+        out.fill_(float(i))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        tmp = torch.zeros_like(eager)
+        exl3.linear_multi_into(tmp, x, shards, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(tmp, eager)
