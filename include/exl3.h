@@ -160,7 +160,7 @@ int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int
  * The device tables (perm, off_w*) are trusted: the host cannot read them without synchronising.  A perm
  * entry outside [0, E) drops the expert like an out-of-range id; offsets must address the banks.
  * Limits: 1 <= E <= 1024, H and I multiples of 128 up to 65536, 1 <= n_groups <= 64, k_gu, k_d in 1..8,
- * 1 <= topk <= E, T * topk <= 2^24; w13/w2, x and out 16-byte aligned, vectors 2-byte aligned, offset
+ * 1 <= topk <= E, T * topk <= 2^24; w13/w2, w13_suh, x and out 16-byte aligned, other vectors 2-byte aligned, offset
  * tables 8-byte and perm/topk arrays 4-byte aligned.
  * Precision: each projection as in exl3_linear_into (fp16 operands, fp32 accumulation); h1, h3 and
  * silu(h1) * h3 stay in fp32 until w2's rotation rounds them to fp16; the top-k sum is taken in fp32 in

@@ -278,8 +278,9 @@ int check_bank(const exl3_bank* b) {
     return fail(EXL3_EINVAL, "bank.w13/w2: null or not 16-byte aligned");
   if (!b->w13_suh || !b->w13_svh || !b->w2_suh || !b->w2_svh)
     return fail(EXL3_EINVAL, "bank.w13_suh/w13_svh/w2_suh/w2_svh: null");
-  if (!aligned(b->w13_suh, 2) || !aligned(b->w13_svh, 2) || !aligned(b->w2_suh, 2) || !aligned(b->w2_svh, 2))
-    return fail(EXL3_EINVAL, "bank.w13_suh/w13_svh/w2_suh/w2_svh: not 2-byte aligned");
+  if (!aligned(b->w13_suh, 16)) return fail(EXL3_EINVAL, "bank.w13_suh: not 16-byte aligned");
+  if (!aligned(b->w13_svh, 2) || !aligned(b->w2_suh, 2) || !aligned(b->w2_svh, 2))
+    return fail(EXL3_EINVAL, "bank.w13_svh/w2_suh/w2_svh: not 2-byte aligned");
   if (!b->off_w1 || !b->off_w3 || !b->off_w2 || !aligned(b->off_w1, 8) || !aligned(b->off_w3, 8) ||
       !aligned(b->off_w2, 8))
     return fail(EXL3_EINVAL, "bank.off_w1/off_w3/off_w2: null or not 8-byte aligned");

@@ -219,6 +219,22 @@ __device__ __forceinline__ float lane_xor16(float v) {
 // lane-exchange move produced.
 __device__ __forceinline__ float bfly(float v, float p, bool upper) { return fmaf(v, upper ? -1.0f : 1.0f, p); }
 
+// Lane-pair butterfly over lane bit 4 (resp. 5) for two values X, Y of every lane: after swapping the odd
+// rows (halves) of X with the even ones of Y, the lower lane of each pair holds both X values and the
+// upper lane both Y values, in the order (lower lane's, upper lane's); both form (a + b, a - b), and
+// the same swap puts the four results back in place.
+template <bool HALF32>
+__device__ __forceinline__ void lane_pair_bfly(float& x, float& y) {
+  uint32_t a = __float_as_uint(x), b = __float_as_uint(y);
+  auto r = HALF32 ? __builtin_amdgcn_permlane32_swap(a, b, false, false)
+                  : __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  const float p = __uint_as_float(r[0]), q = __uint_as_float(r[1]);
+  auto t = HALF32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(p + q), __float_as_uint(p - q), false, false)
+                  : __builtin_amdgcn_permlane16_swap(__float_as_uint(p + q), __float_as_uint(p - q), false, false);
+  x = __uint_as_float(t[0]);
+  y = __uint_as_float(t[1]);
+}
+
 __device__ __forceinline__ void had128_wave(float& v0, float& v1, int lane) {
   float a = v0 + v1, b = v0 - v1;
   v0 = bfly(a, dpp<kQuadXor1>(a), lane & 1);

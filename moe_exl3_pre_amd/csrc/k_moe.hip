@@ -80,24 +80,27 @@ __device__ __forceinline__ int pair_slot(const MoeArgs& a, int q) {
 // ---------------------------------------------------------------------------------------------------
 // Exclusive scan of v over the block's 1024 threads; returns the prefix and leaves the total in *total.
 // tmp holds 48 ints of LDS.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP (no LDS round trips): shifts by 1, 2, 4 and 8
+// inside each row of 16 lanes, then the last lane of rows 0 and 2 added to rows 1 and 3 and lane 31 added
+// to rows 2 and 3.  Lanes without a source lane add the zero old value.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 __device__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(inc, d, 64);
-    if (lane >= d) inc += u;
-  }
+  const int inc = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = inc;
   __syncthreads();
   if (wave == 0) {
     int w = lane < kRouteThreads / 64 ? tmp[lane] : 0;
-    int winc = w;
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-      const int u = __shfl_up(winc, d, 64);
-      if (lane >= d) winc += u;
-    }
+    const int winc = wave_incl_scan(w);
     if (lane < kRouteThreads / 64) tmp[16 + lane] = winc - w;   // exclusive wave offsets
     if (lane == 15) tmp[32] = winc;
   }
@@ -202,14 +205,28 @@ __device__ void moe_route_bitmap(const MoeArgs& a, int* lds) {
   int* pre = lds + E * W;                             // [E][W] exclusive prefix of popcounts
   int* cnt = pre + E * W;                             // [E]
   int* tmp = cnt + E;                                 // [48]
-  int* slot_of = tmp + 48;                            // [P] when it fits (see moe_route_lds_bytes), else null
+  int* perm_l = tmp + 48;                             // [E] the slot of each logical expert
+  int* slot_of = perm_l + E;                          // [P] when it fits (see moe_route_lds_bytes), else null
   if (a.P > kBitmapSlotCache) slot_of = nullptr;
+  if (slot_of) {
+    // every expert id and the slot table are loaded at once (no load waits for another), the slots are
+    // then LDS lookups
+    for (int q = tid; q < a.P; q += kRouteThreads) slot_of[q] = a.ids[q];
+    for (int e = tid; e < E; e += kRouteThreads) perm_l[e] = a.perm[e];
+  }
   for (int i = tid; i < E * W; i += kRouteThreads) bm[i] = 0u;
   __syncthreads();
   for (int q = tid; q < a.P; q += kRouteThreads) {
-    const int s = pair_slot(a, q);
+    int s;
+    if (slot_of) {
+      const int e = slot_of[q];
+      s = (e >= 0 && e < E) ? perm_l[e] : -1;
+      s = (s >= 0 && s < E) ? s : -1;
+      slot_of[q] = s;
+    } else {
+      s = pair_slot(a, q);
+    }
     a.pslot[q] = s;
-    if (slot_of) slot_of[q] = s;
     if (s >= 0) atomicOr(&bm[s * W + (q >> 5)], 1u << (q & 31));
   }
   __syncthreads();
@@ -218,14 +235,9 @@ __device__ void moe_route_bitmap(const MoeArgs& a, int* lds) {
     for (int j0 = 0; j0 < W; j0 += 64) {
       const int j = j0 + lane;
       const int v = j < W ? __popc(bm[s * W + j]) : 0;
-      int inc = v;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int u = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += u;
-      }
+      const int inc = wave_incl_scan(v);
       if (j < W) pre[s * W + j] = carry + inc - v;
-      carry += __shfl(inc, 63, 64);
+      carry += __builtin_amdgcn_readlane(inc, 63);
     }
     if (lane == 0) cnt[s] = carry;
   }
@@ -273,49 +285,63 @@ __device__ void moe_route(const MoeArgs& a, int* lds) {
 }
 
 // ---------------------------------------------------------------------------------------------------
-// 1b. Rotation of gathered activations for w1 and w3: one wave per (token, 128-block).  The token's x
-// block is loaded once and rotated for each of its top-k pairs and both projections; the pair slots and
-// every sign/scale load are issued before the first Hadamard.
+// 1b. Rotation of gathered activations for w1 and w3.  One wave per (token, 128-block, group of 8 rows),
+// the rows being the token's (pair, projection) combinations (pair j = row / 2, projection row % 2):
+// lane (n, g) holds row n's features 16g .. 16g+15 of the block (the x chunk is the same for every row,
+// the sign vector is the pair's expert's).  Hadamard-128: register butterflies over feature bits 0..3,
+// a row-rotate DPP exchange over bit 4 (lane bit 3) and lane-pair swaps over bits 5 and 6 (lane bits 4
+// and 5), then each lane writes its 16-group as 32 contiguous bytes of the PERM16 layout.
 // ---------------------------------------------------------------------------------------------------
-constexpr int kRotBatch = 4;    // pairs whose loads are in flight together
-
 __device__ void moe_rotate(const MoeArgs& a, int64_t unit) {
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, n = lane & 7, g = lane >> 3;
   const int nblk = a.H / kHad;
-  const int t = int(unit / nblk), hb = int(unit % nblk);
+  const int nrh = (a.topk + 3) / 4;                        // groups of 8 rows: 2 * topk rows per token
+  const int64_t tb = unit / nrh;
+  const int rh = int(unit % nrh);
+  const int t = int(tb / nblk), hb = int(tb % nblk);
   if (t >= a.T) return;
-  const int f = hb * kHad + perm_pair_feature(lane);
-  const uint16_t* xr = a.x + int64_t(t) * a.H + f;
-  const uint32_t xv = uint32_t(xr[0]) | (uint32_t(xr[8]) << 16);
-  const float x0 = bf16_to_f32(xv & 0xFFFFu), x1 = bf16_to_f32(xv >> 16);
-  for (int j0 = 0; j0 < a.topk; j0 += kRotBatch) {
-    int sl[kRotBatch];
-    uint32_t sv[kRotBatch][2];
+  const int j = rh * 4 + (n >> 1), proj = n & 1;
+  const int sl = j < a.topk ? pair_slot(a, t * a.topk + j) : -1;
+  const int sc = sl < 0 ? 0 : sl;
+  const int f = hb * kHad + 16 * g;
+  const u32x4* xp = reinterpret_cast<const u32x4*>(a.x + int64_t(t) * a.H + f);
+  const u32x4* sp = reinterpret_cast<const u32x4*>(a.w13_suh + int64_t(sc * 2 + proj) * a.H + f);
+  const u32x4 xv[2] = {xp[0], xp[1]}, sv[2] = {sp[0], sp[1]};
+  float v[16];
 #pragma unroll
-    for (int r = 0; r < kRotBatch; ++r) {
-      const int j = j0 + r < a.topk ? j0 + r : a.topk - 1;
-      sl[r] = pair_slot(a, t * a.topk + j);
-      const int sc = sl[r] < 0 ? 0 : sl[r];
+  for (int w = 0; w < 16; ++w) {
+    const int sh = (w & 1) * 16;
+    v[w] = bf16_to_f32((xv[w >> 3][(w >> 1) & 3] >> sh) & 0xFFFFu) * f16_to_f32(uint16_t(sv[w >> 3][(w >> 1) & 3] >> sh));
+  }
 #pragma unroll
-      for (int proj = 0; proj < 2; ++proj) {
-        const uint16_t* su = a.w13_suh + uint32_t((sc * 2 + proj) * a.H + f);   // < 2^27: 32-bit offset
-        sv[r][proj] = uint32_t(su[0]) | (uint32_t(su[8]) << 16);
+  for (int b = 1; b < 16; b <<= 1)                         // feature bits 0..3
+#pragma unroll
+    for (int w = 0; w < 16; ++w)
+      if (!(w & b)) {
+        const float lo = v[w], hi = v[w | b];
+        v[w] = lo + hi;
+        v[w | b] = lo - hi;
       }
-    }
+  float q[16];
 #pragma unroll
-    for (int r = 0; r < kRotBatch; ++r) {
-      if (j0 + r >= a.topk || sl[r] < 0) continue;   // wave-uniform
-      const int64_t q = int64_t(t) * a.topk + j0 + r;
+  for (int w = 0; w < 16; ++w) q[w] = dpp<kRowRor8>(v[w]);  // bit 4: lane xor 8 within each row of 16
 #pragma unroll
-      for (int proj = 0; proj < 2; ++proj) {
-        float v0 = x0 * f16_to_f32(sv[r][proj] & 0xFFFFu);
-        float v1 = x1 * f16_to_f32(sv[r][proj] >> 16);
-        had128_wave(v0, v1, lane);
-        uint16_t* dst = a.xh13 + (int64_t(proj) * a.P + q) * a.H + hb * kHad + 2 * lane;
-        *reinterpret_cast<uint32_t*>(dst) =
-            uint32_t(f32_to_f16(v0 * kInvSqrt128)) | (uint32_t(f32_to_f16(v1 * kInvSqrt128)) << 16);
-      }
+  for (int w = 0; w < 16; ++w) v[w] = bfly(v[w], q[w], lane & 8);
+#pragma unroll
+  for (int w = 0; w < 16; w += 2) lane_pair_bfly<false>(v[w], v[w + 1]);   // bit 5: lane bit 4
+#pragma unroll
+  for (int w = 0; w < 16; w += 2) lane_pair_bfly<true>(v[w], v[w + 1]);    // bit 6: lane bit 5
+  if (sl >= 0) {
+    const int64_t qi = int64_t(t) * a.topk + j;
+    u32x4* dst = reinterpret_cast<u32x4*>(a.xh13 + (int64_t(proj) * a.P + qi) * a.H + f);
+    u32x4 o0, o1;                                          // PERM16: positions (2i, 2i+1) hold features (i, i+8)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o0[i] = f32x2_to_f16x2(v[i] * kInvSqrt128, v[i + 8] * kInvSqrt128);
+      o1[i] = f32x2_to_f16x2(v[i + 4] * kInvSqrt128, v[i + 12] * kInvSqrt128);
     }
+    dst[0] = o0;
+    dst[1] = o1;
   }
 }
 
@@ -615,7 +641,7 @@ int64_t moe_max_chunks(int64_t P, int E) { return (P + kMoeRows - 1) / kMoeRows 
 
 static size_t moe_route_lds_bytes(int E, int P) {
   const size_t words = size_t(E) * ((P + 31) / 32);
-  if (words <= size_t(kBitmapWords)) return (2 * words + E + 48 + (P <= kBitmapSlotCache ? P : 0)) * sizeof(int);
+  if (words <= size_t(kBitmapWords)) return (2 * words + 2 * E + 48 + (P <= kBitmapSlotCache ? P : 0)) * sizeof(int);
   return size_t(2 * E + (kRouteThreads / 64) * E + 48 + (P <= kSlotCache ? P : 0)) * sizeof(int);
 }
 
@@ -655,7 +681,7 @@ hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream) {
     a.g_hi[g] = g < m.n_groups ? m.g_hi[g] : 0;
     a.g_k[g] = g < m.n_groups ? m.g_k[g] : 0;
   }
-  const int64_t rot_units = int64_t(a.T) * (a.H / kHad);
+  const int64_t rot_units = int64_t(a.T) * (a.H / kHad) * ((a.topk + 3) / 4);
   const int64_t rot_blocks = (rot_units + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
   hipLaunchKernelGGL(moe_route_rotate_kernel, dim3(unsigned(1 + rot_blocks)), dim3(kRouteThreads),
                      moe_route_lds_bytes(a.E, a.P), stream, a);

@@ -77,22 +77,6 @@ __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __rest
 // exactly 4 KB of the layout (the four 1 KB fragments of its two 64-position steps), written as four
 // 1 KB wave stores.  Rows past M are written as zeros.
 //
-// Lane-pair butterfly over lane bit 4 (resp. 5) for two values X, Y of every lane: after swapping the odd
-// rows (halves) of X with the even ones of Y, the lower lane of each pair holds both X values and the
-// upper lane both Y values, in the order (lower lane's, upper lane's); both form (a + b, a - b), and
-// the same swap puts the four results back in place.
-template <bool HALF32>
-__device__ __forceinline__ void lane_pair_bfly(float& x, float& y) {
-  uint32_t a = __float_as_uint(x), b = __float_as_uint(y);
-  auto r = HALF32 ? __builtin_amdgcn_permlane32_swap(a, b, false, false)
-                  : __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  const float p = __uint_as_float(r[0]), q = __uint_as_float(r[1]);
-  auto t = HALF32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(p + q), __float_as_uint(p - q), false, false)
-                  : __builtin_amdgcn_permlane16_swap(__float_as_uint(p + q), __float_as_uint(p - q), false, false);
-  x = __uint_as_float(t[0]);
-  y = __uint_as_float(t[1]);
-}
-
 // The rotated features of one (16-row block rb, 128-block q) unit, before the 1/sqrt(128) normalisation:
 // lane (n, g) ends with row 16 rb + n, features 16 (g + 4t) + w of the block in v[t][w] (zeros past M).
 __device__ __forceinline__ void frag_transform(const uint16_t* __restrict__ x, const uint16_t* __restrict__ s_in,

@@ -98,6 +98,7 @@ def _fwd(bank, T=4, topk=2, flags=0, ws=FAKE, ws_bytes=1 << 30, out=FAKE, x=FAKE
     (dict(w13=None), {}, exl3.EINVAL, "bank.w13"),
     (dict(w2=FAKE + 8), {}, exl3.EINVAL, "bank.w13/w2"),
     (dict(w2_svh=None), {}, exl3.EINVAL, "w2_svh"),
+    (dict(w13_suh=FAKE + 2), {}, exl3.EINVAL, "w13_suh"),
     (dict(off_w3=FAKE + 4), {}, exl3.EINVAL, "off_w"),
     (dict(perm=None), {}, exl3.EINVAL, "bank.perm"),
     ({}, dict(topk=0), exl3.EINVAL, "topk"),
