@@ -108,11 +108,26 @@ __device__ __forceinline__ uint32_t codebook2(uint32_t states, const CodebookReg
   return (__builtin_bit_cast(uint32_t, s) & c.mask) | c.bias;
 }
 
-template <int K, int P>
+// PAIR64 selects the 64-bit-shift form below.  It saves VALU wherever registers are not scarce; a kernel
+// that already fills the register file (the prefill GEMM) keeps the 32-bit form, because the aligned
+// register pairs the 64-bit shift needs cost it more moves than the shift saves.
+template <int K, int P, bool PAIR64>
 __device__ __forceinline__ uint32_t decode_pair(const uint32_t (&r)[Geom<K>::kNR], const CodebookRegs& c) {
+  // States p and p+8 start 8K bits (K bytes) apart.  When both fit one 64-bit window of the realigned
+  // stream, a single 64-bit shift brings state p to bit 0 and one byte permute picks bytes (0, 1) and
+  // (K, K+1) of the shifted pair; otherwise each state gets its own 32-bit window.
+  constexpr int kA = P * K, kJ = kA >> 5, kSh = kA & 31;
+  constexpr bool kFits64 = PAIR64 && kJ + 1 < Geom<K>::kNR && kSh + 8 * K + 16 <= 64;
   if constexpr (K == 2) {
     // state p at bit 2p, state p+8 at bit 2p+16: one 32-bit window holds both.
     return codebook2(P == 0 ? r[0] : __builtin_amdgcn_alignbit(r[1], r[0], 2 * P), c);
+  } else if constexpr (kFits64) {
+    uint64_t q = (uint64_t(r[kJ + 1]) << 32) | r[kJ];
+    // One v_lshrrev_b64 (full rate on gfx950).  Written out because the compiler otherwise splits the
+    // shift into two 32-bit funnel shifts when only some bytes of the result are used.
+    if constexpr (kSh != 0) asm("v_lshrrev_b64 %0, %2, %1" : "=v"(q) : "v"(q), "n"(kSh));
+    constexpr uint32_t kSel = 0x0100u | (uint32_t(K) << 16) | (uint32_t(K + 1) << 24);
+    return codebook2(__builtin_amdgcn_perm(uint32_t(q >> 32), uint32_t(q), kSel), c);
   } else {
     const uint32_t lo = window16<K, P * K>(r);
     const uint32_t hi = window16<K, (P + 8) * K>(r);
@@ -121,7 +136,7 @@ __device__ __forceinline__ uint32_t decode_pair(const uint32_t (&r)[Geom<K>::kNR
 }
 
 // Decode one tile column from the words loaded at column_word_offsets: out[p] = (row p, row p+8).
-template <int K>
+template <int K, bool PAIR64 = true>
 __device__ __forceinline__ void decode_column(const uint32_t (&w)[Geom<K>::kNW], int shift, uint32_t (&out)[8],
                                               const CodebookRegs& c) {
   uint32_t r[Geom<K>::kNR];
@@ -132,14 +147,14 @@ __device__ __forceinline__ void decode_column(const uint32_t (&w)[Geom<K>::kNW],
 #pragma unroll
     for (int j = 0; j < Geom<K>::kNR; ++j) r[j] = w[j];
   }
-  out[0] = decode_pair<K, 0>(r, c);
-  out[1] = decode_pair<K, 1>(r, c);
-  out[2] = decode_pair<K, 2>(r, c);
-  out[3] = decode_pair<K, 3>(r, c);
-  out[4] = decode_pair<K, 4>(r, c);
-  out[5] = decode_pair<K, 5>(r, c);
-  out[6] = decode_pair<K, 6>(r, c);
-  out[7] = decode_pair<K, 7>(r, c);
+  out[0] = decode_pair<K, 0, PAIR64>(r, c);
+  out[1] = decode_pair<K, 1, PAIR64>(r, c);
+  out[2] = decode_pair<K, 2, PAIR64>(r, c);
+  out[3] = decode_pair<K, 3, PAIR64>(r, c);
+  out[4] = decode_pair<K, 4, PAIR64>(r, c);
+  out[5] = decode_pair<K, 5, PAIR64>(r, c);
+  out[6] = decode_pair<K, 6, PAIR64>(r, c);
+  out[7] = decode_pair<K, 7, PAIR64>(r, c);
 }
 
 // Staging of trellis words.  The words of one 64-feature step of a 128-column block are 4 tile rows x

@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
       uint32_t v[8];
-      decode_column<K>(wv[nb], shift, v, cb);
+      decode_column<K, false>(wv[nb], shift, v, cb);
       const half8 b0 = as_half8(v[0], v[1], v[2], v[3]), b1 = as_half8(v[4], v[5], v[6], v[7]);
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = mfma16(a[mb][0], b0, acc[mb][nb]);
