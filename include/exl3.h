@@ -101,7 +101,9 @@ int exl3_gemm_splits(int64_t M, int64_t IC, int64_t OC);
  * bf16.  M <= exl3_gemv_max_rows(OC) runs the decode-phase kernel, larger M the MFMA GEMM (the two agree
  * to rounding, not bitwise), split over the input features when the shard is small (exl3_gemm_splits).
  * For a given split count a row's result does not depend on the other rows; on the GEMM with
- * EXL3_GEMM_NO_SPLIT it does not depend on M at all.
+ * EXL3_GEMM_NO_SPLIT it does not depend on M at all.  Decode-phase launches of 5..16 rows rotate the
+ * activations once per call into the workspace (16 x IC fp16 per distinct (s_in, rin)) before the
+ * decode kernel; smaller ones rotate inside the kernel.  Both rotations give the same bits.
  * 8-bit path (EXL3_ACT_INT8): the codes q are exact in fp16 and every q * W product is exact in fp32,
  * so the contraction is the integer dot product up to fp32 summation; the row scale is applied before
  * the output transform.

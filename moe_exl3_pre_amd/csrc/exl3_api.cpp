@@ -160,15 +160,35 @@ int check_workspace(const Layout& L, void* ws, size_t ws_bytes) {
   return EXL3_OK;
 }
 
-// The decode-phase path: one launch per chunk of <= 16 rows covering every shard.
+// The decode-phase path: one launch per chunk of <= 16 rows covering every shard.  A chunk of at least
+// kPreRotateRows rows first rotates its activations once per distinct (s_in, rin) into the workspace
+// (fragment-major, 16 rows), and the decode launch reads them from there.
 int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n,
-               const DecShardIn* in, char* ws, const Layout& L, hipStream_t stream) {
+               const DecShardIn* in_, char* ws, const Layout& L, hipStream_t stream) {
+  DecShardIn in[kMaxShards];
+  for (int i = 0; i < n; ++i) in[i] = in_[i];
+  int slot[kMaxShards];
+  distinct_inputs(n, in, slot);
   for (int64_t r0 = 0; r0 < M; r0 += kDecodeMaxRows) {
     const int64_t rows = (M - r0) < kDecodeMaxRows ? (M - r0) : kDecodeMaxRows;
     const void* xr = static_cast<const uint16_t*>(x) + r0 * IC;
     void* orow = static_cast<uint16_t*>(out) + r0 * ldo;
     DecPlan pl;
     if (!plan_decode(rows, IC, n, in, &pl)) return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
+    if (pl.pre) {
+      int done = -1;
+      for (int i = 0; i < n; ++i) {
+        char* region = ws + L.xh_off + L.xh_bytes * size_t(slot[i]);
+        if (slot[i] > done) {
+          if (L.xh_bytes < size_t(kDecodeMaxRows) * size_t(IC) * 2)
+            return fail(EXL3_EWORKSPACE, "%s: workspace has no pre-rotation region", who);
+          hipError_t e = launch_prepass_f16(xr, in[i].s_in, in[i].rin, region, rows, IC, true, stream, kDecodeMaxRows);
+          if (int rc = launch_status(e, who)) return rc;
+          done = slot[i];
+        }
+        in[i].xf = region;
+      }
+    }
     if (pl.kset >= 0) {
       hipError_t e = launch_decode(pl, xr, rows, IC, n, in, orow, ldo, reinterpret_cast<float*>(ws + L.slab_off),
                                    reinterpret_cast<int*>(ws), stream);
@@ -303,7 +323,9 @@ bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsign
   if (use_decode_path(M, flags, max_oc(n, in))) {
     size_t slab = 0;
     if (!decode_slab_bytes(M, IC, n, in, &slab)) return false;
-    *L = layout_for(slab);
+    int slot[kMaxShards];
+    const bool pre = first_chunk(M) >= kPreRotateRows || last_chunk(M) >= kPreRotateRows;
+    *L = layout_for(slab, kDecodeMaxRows, IC, pre ? distinct_inputs(n, in, slot) : 0);
   } else {
     size_t slab = 0;                                      // shards run one after another: the largest split
     if (!(flags & EXL3_GEMM_NO_SPLIT))

@@ -250,6 +250,12 @@ __device__ __forceinline__ void lane_pair_bfly(float& x, float& y) {
   y = __uint_as_float(t[1]);
 }
 
+// The same transform for the pre-pass lane layout (perm_pair_feature): lane l holds features
+// f = 16*(l/8) + l%8 (v0) and f + 8 (v1).  Stages run in natural feature-bit order 0..6 (lane bits 0..2,
+// the in-lane pair, lane bits 3..5), the order of the fragment-major pre-pass, so that the two produce the
+// same fp32 sums bit for bit and a row's rotated activations do not depend on which pre-pass ran.
+__device__ __forceinline__ void had128_wave_pairs8(float& v0, float& v1, int lane);
+
 __device__ __forceinline__ void had128_wave(float& v0, float& v1, int lane) {
   float a = v0 + v1, b = v0 - v1;
   v0 = bfly(a, dpp<kQuadXor1>(a), lane & 1);
@@ -263,6 +269,25 @@ __device__ __forceinline__ void had128_wave(float& v0, float& v1, int lane) {
   v0 = bfly(a, lane_xor16(a), lane & 16);
   v1 = bfly(b, lane_xor16(b), lane & 16);
   a = bfly(v0, __shfl_xor(v0, 32, 64), lane & 32);
+  b = bfly(v1, __shfl_xor(v1, 32, 64), lane & 32);
+  v0 = a;
+  v1 = b;
+}
+
+__device__ __forceinline__ void had128_wave_pairs8(float& v0, float& v1, int lane) {
+  float a = bfly(v0, dpp<kQuadXor1>(v0), lane & 1);   // feature bit 0
+  float b = bfly(v1, dpp<kQuadXor1>(v1), lane & 1);
+  v0 = bfly(a, dpp<kQuadXor2>(a), lane & 2);          // bit 1
+  v1 = bfly(b, dpp<kQuadXor2>(b), lane & 2);
+  a = bfly(v0, lane_xor4(v0), lane & 4);              // bit 2
+  b = bfly(v1, lane_xor4(v1), lane & 4);
+  v0 = a + b;                                          // bit 3: the lane's own pair
+  v1 = a - b;
+  a = bfly(v0, lane_xor8(v0), lane & 8);              // bit 4
+  b = bfly(v1, lane_xor8(v1), lane & 8);
+  v0 = bfly(a, lane_xor16(a), lane & 16);             // bit 5
+  v1 = bfly(b, lane_xor16(b), lane & 16);
+  a = bfly(v0, __shfl_xor(v0, 32, 64), lane & 32);    // bit 6
   b = bfly(v1, __shfl_xor(v1, 32, 64), lane & 32);
   v0 = a;
   v1 = b;

@@ -13,6 +13,11 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxShards = 16;
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kDecodeMaxRows = 16;      // rows one decode-phase launch covers
+// Decode-phase launches of at least this many rows take activations rotated once per call by the
+// fragment-major pre-pass instead of rotating them in every block.  The separate launch costs ~4 us; the
+// in-block rotation grows with the rows (gate_up IC=4096 at M = 4 / 5: 19.0 / 20.9 us in-block against
+// 20.0 / 20.3 us pre-rotated, measured on one box).
+constexpr int kPreRotateRows = 5;
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
@@ -23,6 +28,7 @@ struct DecShardIn {
   int K;
   int64_t col0;
   const void *s_in, *rin, *rout, *s_out;
+  const void* xf = nullptr;   // decode phase, pre-rotated launches: this shard's fragment-major activations
 };
 
 struct DecPlan {
@@ -32,6 +38,7 @@ struct DecPlan {
   int tr_off;               // LDS byte offset of the trellis staging slots
   size_t lds_bytes;         // dynamic LDS per block
   int kset;                 // kernel K set: 1..8 single K, 0 mixed {2,3,4}, -1 unsupported mix
+  bool pre;                 // activations pre-rotated once per launch (M >= kPreRotateRows)
   int order[kMaxShards];    // shard processed in grid position r
   int wg_begin[kMaxShards];
   size_t slab_off[kMaxShards];

@@ -34,6 +34,7 @@ constexpr int kNB = 8;           // tile columns per wave = one 128-column block
 
 struct DecShard {
   const uint32_t* code;
+  const uint16_t* xf;            // pre-rotated activations, fragment-major (MR == 0 only)
   const uint16_t* s_in;
   const uint16_t* rin;
   const uint16_t* rout;
@@ -55,8 +56,13 @@ struct DecArgs {
 };
 
 
+// MR: activation rows the fused pre-pass loads (1, 4 or 16).  MR == 0: the activations were rotated once
+// for the whole launch by the fragment-major pre-pass (the prefill path's, k_prepass.hip), and each step's
+// two A fragments are 16-byte loads from that buffer issued with the step's trellis words.  Then no block
+// repeats the rotation, which at M = 8 costs about as much VALU as the decode itself.
 template <int K, int SPW, int MR>
 __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& sh, int local, char* lds) {
+  constexpr bool kPre = MR == 0;
   using G = Geom<K>;
   // steps of trellis words in flight per wave: one.  Every block requests its first step at once, so
   // deeper prefetch only queues the first data of late waves behind the early waves' later steps.
@@ -85,9 +91,10 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   // ---- 1. pre-pass inputs of this wave's Hadamard blocks (issued first: they are needed first).
   // Unconditional loads with clamped rows and blocks: a load under a branch would make the compiler
   // wait for the weight stream behind it before the pre-pass can start.
-  uint32_t xv[kPB][MR], sv[kPB], rv[kPB];
+  constexpr int kMR = kPre ? 1 : MR;
+  uint32_t xv[kPB][kMR], sv[kPB], rv[kPB];
 #pragma unroll
-  for (int pb = 0; pb < kPB; ++pb) {
+  for (int pb = 0; pb < (kPre ? 0 : kPB); ++pb) {
     const int hb = hb0 + pb < hb1 ? hb0 + pb : (hb1 > hb0 ? hb1 - 1 : 0);
     // lane transforms features f and f + 8 (perm_pair_feature), stored at PERM16 positions 2l, 2l+1
     const int64_t f = int64_t(ba + hb) * kHad + perm_pair_feature(lane);
@@ -110,6 +117,13 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   const uint32_t step_stride = 4u * tpr * G::kWords * 4u;
   const uint32_t base_blk = uint32_t(blk) * kNB * G::kWords * 4u;
   u32x4 tb[kD][K];
+  half8 ta[kD][2];   // pre-rotated A fragments of the staged steps (kPre)
+  auto load_a = [&](int st, half8 (&dst)[2]) {
+    const int step = 2 * ba + (cnt > 0 ? w_s0 + (st < cnt ? st : cnt - 1) : 0);
+    const uint16_t* f = sh.xf + (int64_t(step) * 2 * 512 + lane * 8);
+    dst[0] = *reinterpret_cast<const half8*>(f);
+    dst[1] = *reinterpret_cast<const half8*>(f + 512);
+  };
   auto load_step = [&](int st, u32x4 (&dst)[K]) {
     // Steps past this wave's count (their results are never used) re-read a step of this block's own
     // range, so every address stays inside the tensor: the buffer range check covers only the vector
@@ -121,11 +135,14 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
       dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off + uint32_t(i * 256), soff, 0));
   };
 #pragma unroll
-  for (int d = 0; d < kD; ++d) load_step(d, tb[d]);
+  for (int d = 0; d < kD; ++d) {
+    if constexpr (kPre) load_a(d, ta[d]);
+    load_step(d, tb[d]);
+  }
 
   // ---- 3. this wave's rotated activations into LDS (PERM16 order); its part of row M stays zero
 #pragma unroll
-  for (int pb = 0; pb < kPB; ++pb) {
+  for (int pb = 0; pb < (kPre ? 0 : kPB); ++pb) {
     if (hb0 + pb < hb1) {
       const float s0 = f16_to_f32(sv[pb] & 0xFFFFu), s1 = f16_to_f32(sv[pb] >> 16);
       const float r0 = f16_to_f32(rv[pb] & 0xFFFFu), r1 = f16_to_f32(rv[pb] >> 16);
@@ -135,7 +152,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
         if (m < M) {
           float v0 = bf16_to_f32(xv[pb][m] & 0xFFFFu) * s0 * r0;
           float v1 = bf16_to_f32(xv[pb][m] >> 16) * s1 * r1;
-          had128_wave(v0, v1, lane);
+          had128_wave_pairs8(v0, v1, lane);
           *reinterpret_cast<uint32_t*>(xs + m * lrow + kl) =
               uint32_t(f32_to_f16(v0 * kInvSqrt128)) | (uint32_t(f32_to_f16(v1 * kInvSqrt128)) << 16);
         }
@@ -165,10 +182,18 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
       for (int i = 0; i < K; ++i)
         *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tb[st % kD][i];
     }
+    half8 a0, a1;
+    if constexpr (kPre) {
+      a0 = ta[st % kD][0];
+      a1 = ta[st % kD][1];
+      load_a(st + kD, ta[st % kD]);
+    }
     load_step(st + kD, tb[st % kD]);
     if (st < cnt) {
-      const half8 a0 = *reinterpret_cast<const half8*>(xa + 64 * st);
-      const half8 a1 = *reinterpret_cast<const half8*>(xa + 64 * st + 8);
+      if constexpr (!kPre) {
+        a0 = *reinterpret_cast<const half8*>(xa + 64 * st);
+        a1 = *reinterpret_cast<const half8*>(xa + 64 * st + 8);
+      }
       uint32_t wv[2][G::kNW];
       auto read_col = [&](int j, uint32_t (&dst)[G::kNW]) {
 #pragma unroll
@@ -347,7 +372,8 @@ bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl
   pl->spw = spw_variant(2 * ((nb_max + kWaves - 1) / kWaves));
   int kmax = 1;
   for (int i = 0; i < n; ++i) kmax = in[i].K > kmax ? in[i].K : kmax;
-  pl->lds_row = kHad * nb_max + 8;
+  pl->pre = M >= kPreRotateRows;
+  pl->lds_row = pl->pre ? 0 : kHad * nb_max + 8;
   pl->tr_off = int(tr_offset(int(M), pl->lds_row));
   pl->lds_bytes = lds_bytes_for(int(M), pl->lds_row, kmax);
   if (pl->lds_bytes > kMaxLds) return false;
@@ -398,8 +424,10 @@ static void launch_kset_mr(const DecPlan& pl, const DecArgs& a, hipStream_t stre
 
 template <int KSET>
 static hipError_t launch_kset(const DecPlan& pl, const DecArgs& a, hipStream_t stream) {
-  // activation rows the pre-pass loads unconditionally: 1, 4 or 16
-  if (a.M <= 1)
+  // activation rows the fused pre-pass loads unconditionally: 1, 4 or 16; 0 = pre-rotated activations
+  if (pl.pre)
+    launch_kset_mr<KSET, 0>(pl, a, stream);
+  else if (a.M <= 1)
     launch_kset_mr<KSET, 1>(pl, a, stream);
   else if (a.M <= 4)
     launch_kset_mr<KSET, 4>(pl, a, stream);
@@ -424,6 +452,7 @@ hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC
     const DecShardIn& s = in[pl.order[r]];
     DecShard& d = a.sh[r];
     d.code = (const uint32_t*)s.code;
+    d.xf = (const uint16_t*)s.xf;
     d.s_in = (const uint16_t*)s.s_in;
     d.rin = (const uint16_t*)s.rin;
     d.rout = (const uint16_t*)s.rout;

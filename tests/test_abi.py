@@ -88,6 +88,18 @@ def test_int8_workspace_holds_codes_and_scales():
         assert exl3.linear_workspace_bytes(M, 4096, 14336, exl3.ACT_INT8) >= 16384 + M * 4096 * 2 + M * 4
 
 
+def test_decode_workspace_pre_rotation_region():
+    """Decode-phase launches of 5..16 rows rotate the activations once per call into the workspace
+    (fragment-major, 16 rows x IC fp16); below 5 rows each block rotates its own.  A 28672-column shard
+    over IC=2048 needs no split-K slab, so the workspace is the counter area plus that region."""
+    IC, OC = 2048, 28672
+    assert exl3.lib().exl3_gemv_max_rows(OC) == 16
+    for M in (1, 4):
+        assert exl3.linear_workspace_bytes(M, IC, OC) == 16384
+    for M in (5, 8, 16):
+        assert exl3.linear_workspace_bytes(M, IC, OC) == 16384 + 16 * IC * 2
+
+
 def test_workspace_sizes():
     """256-byte multiples, never below the counter area; above the decode-phase row limit the
     workspace holds the rotated activations (M x IC fp16)."""

@@ -173,11 +173,12 @@ def test_linear_workspace_poison_counters_and_determinism():
 
 
 def test_linear_batch_invariance_decode_rows():
-    """A row's output does not depend on the other rows of the batch (decode-phase kernel)."""
+    """A row's output does not depend on the other rows of the batch (decode-phase kernel), also across
+    the switch from in-block rotation (M <= 4) to activations rotated once per call (M >= 5)."""
     c = synth.linear_case(1006, 16, 512, 384, 2)
     d = _case_to_dev(c)
     full = _run_linear(c, d)
-    for M in (1, 5, 9):
+    for M in (1, 4, 5, 9):
         sub = dict(c, M=M)
         part = _run_linear(sub, dict(d, x=d["x"][:M].contiguous()))
         assert torch.equal(part, full[:M])
