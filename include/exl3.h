@@ -71,7 +71,7 @@ const char* exl3_last_error(void);
 int exl3_version(void);
 
 /* Largest M served by the decode-phase path (launches of up to 16 rows) when no FORCE flag is given,
- * for a call whose widest shard has OC output columns: 16 * clamp(14336 / OC, 1, 8), the measured
+ * for a call whose widest shard has OC output columns: 16 * clamp(16384 / OC, 2, 8), the measured
  * crossover against the (feature-split) MFMA GEMM over a 5120/17408 decoder's projections. */
 int64_t exl3_gemv_max_rows(int64_t OC);
 

@@ -43,11 +43,11 @@ constexpr unsigned kKnownFlags = EXL3_ACT_INT8 | EXL3_FORCE_GEMV | EXL3_FORCE_MF
 // grows with ceil(M/16) * OC; the MFMA GEMM splits the input features of a shard with few output tiles
 // so that about 1024 waves run, which keeps its time nearly flat in M up to a few hundred rows.
 // Measured over the projections of a 5120/17408 decoder (M sweep, 64 layers) the decode path is faster
-// up to 16 rows for 17408 outputs, 32 for 7168 and for 5120 (the o projection ties at 48); the threshold
-// 16 * clamp(14336 / OC, 1, 8) follows that, between one and eight launches.
+// up to 32 rows for 17408 and 7168 outputs and up to 48 for 5120; the threshold
+// 16 * clamp(16384 / OC, 2, 8) follows that, between two and eight launches.
 int64_t gemv_max_rows(int64_t OC) {
-  int64_t chunks = OC > 0 ? 14336 / OC : 1;
-  chunks = chunks < 1 ? 1 : (chunks > 8 ? 8 : chunks);
+  int64_t chunks = OC > 0 ? 16384 / OC : 2;
+  chunks = chunks < 2 ? 2 : (chunks > 8 ? 8 : chunks);
   return chunks * kDecodeMaxRows;
 }
 
