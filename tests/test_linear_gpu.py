@@ -242,10 +242,12 @@ def test_large_ic_sampled():
 
 # ------------------------------------------------------------------------------------------ graph capture
 
-def test_graph_capture_replay_matches_eager():
+@pytest.mark.parametrize("M", [4, 8])
+def test_graph_capture_replay_matches_eager(M):
+    """M=4 rotates in every block; M=8 adds the once-per-call rotation launch before the decode kernel."""
     cfg = synth.DECODE_GATE_UP
-    M = 4
-    case = synth.merged_case(1400, M, 1024, [(512, 2), (768, 3)])
+    log(f"graph capture M={M}")
+    case = synth.merged_case(1400 + M, M, 1024, [(512, 2), (768, 3)])
     x = to_dev_x(case["x_bits"])
     s_in, rin = to_dev(case["shards"][0]["s_in"]), to_dev(case["shards"][0]["rin"])
     shards = [shard_to_dev(s, s_in, rin) for s in case["shards"]]

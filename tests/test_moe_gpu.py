@@ -63,6 +63,24 @@ def test_moe_many_rows_per_expert_and_empty_expert():
     _check(m, _run(bank, x, dids, w))
 
 
+@pytest.mark.parametrize("T,E,topk", [(2048, 64, 4), (4608, 32, 4)])
+def test_moe_route_counting_sort_path(T, E, topk):
+    """Prefill-sized routing: E * ceil(T * topk / 32) exceeds the bitmap route's 8192 LDS words, so the
+    counting-sort route runs -- with its LDS cache of the pairs' slots (8192 pairs) and without it
+    (18432 pairs).  Sampled tokens against the oracle; a second call gives the same bits."""
+    P = T * topk
+    assert E * ((P + 31) // 32) > 8192
+    log(f"moe counting-sort route T={T} E={E} top-{topk} ({P} pairs)")
+    m = synth.moe_case(730 + E, T=T, E=E, topk=topk, H=256, I=128, Ks=(2, 3, 4))
+    bank, x, ids, w = _setup(m)
+    out = _run(bank, x, ids, w)
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(T)
+    tokens = sorted(set([0, 1, T // 2, T - 1] + list(rng.choice(T, 12, replace=False))))
+    _check(m, out, tokens=tokens)
+    assert torch.equal(_run(bank, x, ids, w), out)
+
+
 def test_moe_out_of_range_ids_are_ignored():
     m = synth.moe_case(712, T=32, E=8, topk=4, H=256, I=128)
     ids = m["topk_ids"].copy()
