@@ -83,6 +83,14 @@ int64_t exl3_gemv_max_rows(int64_t OC);
  * through the split count.  1 for invalid shapes. */
 int exl3_gemm_splits(int64_t M, int64_t IC, int64_t OC);
 
+/* Splits of the GEMM's tail round when exl3_gemm_splits is 1.  Blocks of 4 waves (128 rows x 512
+ * columns) run 256 at a time; when the last round of a shard's blocks is at most half full, its blocks
+ * (the last ones in launch order) run with their input features split this many ways after the other
+ * blocks ran unsplit, so that round takes a fraction of the time; a second launch sums their partial
+ * tiles in split order.  Those tiles differ in rounding from the unsplit GEMM.  1 when there is no such
+ * tail (or with EXL3_GEMM_NO_SPLIT, which the library honours for both kinds of split). */
+int exl3_gemm_tail_splits(int64_t M, int64_t IC, int64_t OC);
+
 /* --------------------------------------------------------------------------------------------------
  * One projection written into its column slice ("radiance_escha.py", `escha_linear_into`: one escha
  * projection written into out[:, col0:col0+OC]; merged modules run one call per source tensor,

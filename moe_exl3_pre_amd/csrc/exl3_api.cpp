@@ -354,6 +354,12 @@ int exl3_gemm_splits(int64_t M, int64_t IC, int64_t OC) {
   return gemm_split(M, IC, OC).splits;
 }
 
+int exl3_gemm_tail_splits(int64_t M, int64_t IC, int64_t OC) {
+  if (M <= 0 || IC <= 0 || OC <= 0 || IC % 128 || OC % 128) return 1;
+  const GemmSplit sp = gemm_split(M, IC, OC);
+  return sp.splits > 1 ? 1 : sp.tail_splits;
+}
+
 size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned flags) {
   if (M <= 0 || IC <= 0 || OC <= 0 || IC % 128 || OC % 128) return align_up(kCounterBytes);
   const DecShardIn in = shard_in(nullptr, OC, 2, 0, nullptr, nullptr, nullptr, nullptr);

@@ -64,12 +64,20 @@ hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, v
                              int64_t IC, bool permuted, hipStream_t stream, bool f16_codes = false,
                              float* part = nullptr);
 hipError_t launch_decode_tiles(void* w, const int16_t* code, int64_t IC, int64_t OC, int K, hipStream_t stream);
-// K split of the prefill GEMM.  One wave owns a 128 x 128 output tile and the chip holds 1024 of them at a
-// time; a shard with fewer tiles has its 64-feature steps split so that about 1024 waves run, each split
-// keeping at least 8 steps (an even count), and a second launch sums the splits' partial tiles.
+// K split of the prefill GEMM.  One wave owns a 128 x 128 output tile, a block is 4 waves (128 rows x 512
+// columns) and the chip holds 256 blocks (1024 waves) at a time.  A shard with fewer than 1024 tiles has
+// its 64-feature steps split so that about 1024 waves run, each split keeping at least 8 steps (an even
+// count), and a second launch sums the splits' partial tiles.  A larger shard whose blocks leave the last
+// round of 256 at most half full runs that round's blocks (tail_blocks, the last ones) split
+// tail_splits ways instead, so the round takes 1/tail_splits of the time; the other blocks run unsplit.
+constexpr int kChipBlocks = 256;
+
 struct GemmSplit {
-  int splits;   // 1: no split
-  int sps;      // steps per split (the last split may have fewer; every count is even)
+  int splits;            // 1: no split of the whole shard
+  int sps;               // steps per split (the last split may have fewer; every count is even)
+  int tail_blocks = 0;   // blocks of the partial last round run split (0: none)
+  int tail_splits = 1;
+  int tail_sps = 0;
 };
 
 inline GemmSplit gemm_split(int64_t M, int64_t IC, int64_t OC) {
@@ -81,12 +89,31 @@ inline GemmSplit gemm_split(int64_t M, int64_t IC, int64_t OC) {
     const int64_t n = (steps + sps - 1) / sps;
     if (n > 1) return GemmSplit{int(n), int(sps)};
   }
-  return GemmSplit{1, int(steps)};
+  GemmSplit g{1, int(steps)};
+  const int64_t blocks = (M + 127) / 128 * ((OC + 511) / 512);
+  const int64_t r = blocks % kChipBlocks;
+  if (blocks > kChipBlocks && r > 0) {
+    int64_t ts = kChipBlocks / r;
+    if (ts > steps / 8) ts = steps / 8;
+    if (ts > 1) {
+      const int64_t sps = 2 * ((steps + 2 * ts - 1) / (2 * ts));
+      const int64_t n = (steps + sps - 1) / sps;
+      if (n > 1) {
+        g.tail_blocks = int(r);
+        g.tail_splits = int(n);
+        g.tail_sps = int(sps);
+      }
+    }
+  }
+  return g;
 }
 
-// Partial-sum slab of a split GEMM: one 64 KB fp32 tile per (split, 128-row tile, 128-column tile).
+// Partial-sum slab of a split GEMM: one 64 KB fp32 tile per (split, block, wave) of the split launch.
 inline size_t gemm_slab_bytes(int64_t M, int64_t OC, GemmSplit sp) {
-  return sp.splits > 1 ? size_t(sp.splits) * size_t((M + 127) / 128) * size_t(OC / 128) * 65536 : 0;
+  const size_t blocks = size_t((M + 127) / 128) * size_t((OC + 511) / 512);
+  if (sp.splits > 1) return size_t(sp.splits) * blocks * 4 * 65536;
+  if (sp.tail_splits > 1) return size_t(sp.tail_splits) * size_t(sp.tail_blocks) * 4 * 65536;
+  return 0;
 }
 
 // Prefill-phase GEMM of one shard (one wave per 128 x 128 output tile); xf is the pre-pass output in the

@@ -51,8 +51,20 @@ struct GemmArgs {
   int mt, nt;               // row tiles (128 rows) / column groups (512 columns)
   uint32_t code_bytes;
   int splits, sps;          // K split: splits of sps 64-feature steps each (1: no split)
-  float4v* slab;            // splits > 1: [split][row tile][column tile][mb * 8 + nb][lane] partial sums
+  int tile0, ntiles;        // this launch's blocks: tiles [tile0, tile0 + ntiles) of the mt x nt grid
+  float4v* slab;            // splits > 1: [split][launch tile][wave][mb * 8 + nb][lane] partial sums
 };
+
+// Block tile -> (row tile, this wave's 128-column block).  Tiles run over groups of kGroupRows row tiles;
+// inside a group, consecutive tiles walk down the rows first, so the blocks one XCD runs at a time (a
+// contiguous range of tiles) share row tiles and column groups in its L2.
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int tile, int wave, int& mtile, int& ctile) {
+  const int group = tile / (kGroupRows * p.nt);
+  const int gm = (p.mt - group * kGroupRows) < kGroupRows ? (p.mt - group * kGroupRows) : kGroupRows;
+  const int in_group = tile - group * kGroupRows * p.nt;
+  mtile = group * kGroupRows + in_group % gm;
+  ctile = (in_group / gm) * kWavesN + wave;
+}
 
 // One butterfly stage of the Hadamard over the lane bits of a 16x16 accumulator group (lane bit b =
 // column bit b), applied to all 32 values of a row group before the next stage so that the lane
@@ -150,19 +162,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
 
-  // ---- block -> (row tile, column group): a contiguous range of tiles per XCD, grouped by row tiles
-  const int T = p.mt * p.nt;
+  // ---- block -> (row tile, column group): a contiguous range of the launch's tiles per XCD
+  const int T = p.ntiles;
   const int split = SPLIT ? __builtin_amdgcn_readfirstlane(int(blockIdx.x) / T) : 0;   // K split of this block
   const int nxcd = 8;
   const int bid = SPLIT ? int(blockIdx.x) - split * T : int(blockIdx.x);
   const int xcd = bid % nxcd, j = bid / nxcd;
   const int per = T / nxcd, extra = T % nxcd;
-  const int tile = xcd * per + (xcd < extra ? xcd : extra) + j;
-  const int group = tile / (kGroupRows * p.nt);
-  const int gm = (p.mt - group * kGroupRows) < kGroupRows ? (p.mt - group * kGroupRows) : kGroupRows;
-  const int in_group = tile - group * kGroupRows * p.nt;
-  const int mtile = group * kGroupRows + in_group % gm;
-  const int ctile = (in_group / gm) * kWavesN + wave;      // this wave's 128-column block
+  const int lt = xcd * per + (xcd < extra ? xcd : extra) + j;   // tile of this launch
+  int mtile, ctile;                                         // row tile, this wave's 128-column block
+  tile_coords(p, p.tile0 + lt, wave, mtile, ctile);
   if (ctile * kCols >= p.OC) return;                        // past the last column block (no barriers below)
 
   const int row0 = mtile * kRows;
@@ -279,8 +288,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 
   // ---- a split parks its partial sums (1 KB wave stores; the reduction kernel finishes the tile)
   if constexpr (SPLIT) {
-    const int ctiles = p.OC / kCols;
-    float4v* dst = p.slab + (((int64_t(split) * p.mt + mtile) * ctiles + ctile) * 64) * 64 + lane;
+    float4v* dst = p.slab + ((int64_t(split) * p.ntiles + lt) * kWavesN + wave) * 4096 + lane;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
@@ -301,24 +309,23 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   }
 }
 
-// K-split reduction: one wave per (16-row group, 128-column tile) sums the splits' partials in split order
-// (fixed, so the result is deterministic) and applies the output transform.
+// K-split reduction over the launch's tiles: one wave per (16-row group, 128-column tile) sums the splits'
+// partials in split order (fixed, so the result is deterministic) and applies the output transform.
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs p) {
   const int lane = threadIdx.x & 63;
-  const int ctiles = p.OC / kCols;
-  const int64_t tiles = int64_t(p.mt) * ctiles;
   const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (unit >= tiles * 8) return;
-  const int64_t tile = unit >> 3;
-  const int mb = int(unit & 7);
-  const int mtile = int(tile / ctiles), ctile = int(tile % ctiles);
+  if (unit >= int64_t(p.ntiles) * kWavesN * 8) return;
+  const int lt = int(unit / (kWavesN * 8)), wave = int(unit / 8) % kWavesN, mb = int(unit & 7);
+  int mtile, ctile;
+  tile_coords(p, p.tile0 + lt, wave, mtile, ctile);
+  if (ctile * kCols >= p.OC) return;                        // past the last column block
   const int r0 = mtile * kRows + 16 * mb;
   if (r0 >= p.M) return;                                    // the whole group is past M
   float4v sum[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) sum[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
   for (int sp = 0; sp < p.splits; ++sp) {
-    const float4v* src = p.slab + ((int64_t(sp) * tiles + tile) * 64 + mb * 8) * 64 + lane;
+    const float4v* src = p.slab + ((int64_t(sp) * p.ntiles + lt) * kWavesN + wave) * 4096 + mb * 8 * 64 + lane;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) sum[nb] += src[nb * 64];
   }
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs p) {
 hipError_t launch_gemm(const void* xf, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
                        int64_t ldo, int64_t col0, int64_t M, int64_t IC, int64_t OC, hipStream_t stream,
                        const float* row_scale, GemmSplit split, float* slab) {
-  if (split.splits > 1 && !slab) return hipErrorInvalidValue;
+  if ((split.splits > 1 || split.tail_splits > 1) && !slab) return hipErrorInvalidValue;
   GemmArgs a;
   a.xf = (const uint16_t*)xf;
   a.xf_bytes = (M + 15) / 16 * 16 * IC * 2;
@@ -353,32 +360,45 @@ hipError_t launch_gemm(const void* xf, const int16_t* code, int K, const void* r
   a.mt = (int)((M + kRows - 1) / kRows);
   a.nt = (int)((OC + kCols * kWavesN - 1) / (kCols * kWavesN));
   a.code_bytes = uint32_t(IC / 16 * (OC / 16) * 32 * K);
-  a.splits = split.splits > 1 ? split.splits : 1;
-  a.sps = split.splits > 1 ? split.sps : int(IC / 64);
   a.slab = reinterpret_cast<float4v*>(slab);
-  dim3 grid((unsigned)(a.mt * a.nt * a.splits)), block(64 * kWavesN);
+  const int T = a.mt * a.nt, steps = int(IC / 64);
+  // One launch of tiles [tile0, tile0 + ntiles) with `splits` K splits of `sps` steps; a split launch is
+  // followed by the reduction of the same tiles.
+  auto launch_range = [&](int tile0, int ntiles, int splits, int sps) -> hipError_t {
+    a.tile0 = tile0;
+    a.ntiles = ntiles;
+    a.splits = splits;
+    a.sps = sps;
+    dim3 grid((unsigned)(ntiles * splits)), block(64 * kWavesN);
 #define EXL3_GEMM_CASE(KK)                                                                   \
   case KK:                                                                                   \
-    if (a.splits > 1) hipLaunchKernelGGL((gemm_kernel<KK, true>), grid, block, 0, stream, a);  \
+    if (splits > 1) hipLaunchKernelGGL((gemm_kernel<KK, true>), grid, block, 0, stream, a);    \
     else hipLaunchKernelGGL((gemm_kernel<KK, false>), grid, block, 0, stream, a);              \
     break;
-  switch (K) {
-    EXL3_GEMM_CASE(1)
-    EXL3_GEMM_CASE(2)
-    EXL3_GEMM_CASE(3)
-    EXL3_GEMM_CASE(4)
-    EXL3_GEMM_CASE(5)
-    EXL3_GEMM_CASE(6)
-    EXL3_GEMM_CASE(7)
-    EXL3_GEMM_CASE(8)
-    default: return hipErrorInvalidValue;
-  }
+    switch (K) {
+      EXL3_GEMM_CASE(1)
+      EXL3_GEMM_CASE(2)
+      EXL3_GEMM_CASE(3)
+      EXL3_GEMM_CASE(4)
+      EXL3_GEMM_CASE(5)
+      EXL3_GEMM_CASE(6)
+      EXL3_GEMM_CASE(7)
+      EXL3_GEMM_CASE(8)
+      default: return hipErrorInvalidValue;
+    }
 #undef EXL3_GEMM_CASE
-  if (a.splits > 1) {
-    const int64_t units = int64_t(a.mt) * (OC / kCols) * 8;
-    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
+    if (splits > 1) {
+      const int64_t units = int64_t(ntiles) * kWavesN * 8;
+      hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+  };
+  if (split.splits > 1) return launch_range(0, T, split.splits, split.sps);
+  if (split.tail_blocks > 0 && split.tail_splits > 1 && split.tail_blocks < T) {
+    if (hipError_t e = launch_range(0, T - split.tail_blocks, 1, steps); e != hipSuccess) return e;
+    return launch_range(T - split.tail_blocks, split.tail_blocks, split.tail_splits, split.tail_sps);
   }
-  return hipGetLastError();
+  return launch_range(0, T, 1, steps);
 }
 
 }  // namespace exl3

@@ -52,6 +52,7 @@ _SIGS = {
     "exl3_version": (ctypes.c_int, []),
     "exl3_gemv_max_rows": (ctypes.c_int64, [ctypes.c_int64]),
     "exl3_gemm_splits": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
+    "exl3_gemm_tail_splits": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
     "exl3_linear_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint]),
     "exl3_linear_into": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,

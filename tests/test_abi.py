@@ -88,6 +88,26 @@ def test_int8_workspace_holds_codes_and_scales():
         assert exl3.linear_workspace_bytes(M, 4096, 14336, exl3.ACT_INT8) >= 16384 + M * 4096 * 2 + M * 4
 
 
+def test_gemm_tail_split_plan():
+    """Large shards whose 4-wave blocks (128 x 512) leave the last round of 256 at most half full split
+    that round's blocks over the input features; the workspace holds their partial tiles."""
+    L = exl3.lib()
+    # (M, IC, OC) -> blocks = ceil(M/128) * ceil(OC/512)
+    for M, IC, OC, want in ((8192, 5120, 17408, 2),      # 2176 blocks: 128 in the last round
+                            (8192, 17408, 5120, 2),      # 640 blocks: 128 in the last round
+                            (1152, 1024, 14848, 2),      # 261 blocks: 5, capped at 2 by 16 steps
+                            (8192, 4096, 16384, 1),      # 2048 blocks: whole rounds
+                            (8192, 4096, 18432, 1),      # 2304 blocks: 0 left over
+                            (8192, 4096, 17920, 1)):     # 2240 blocks: 192 left over, more than half
+        assert L.exl3_gemm_splits(M, IC, OC) == 1
+        assert L.exl3_gemm_tail_splits(M, IC, OC) == want, (M, IC, OC)
+    assert L.exl3_gemm_tail_splits(8192, 1024, 8192 + 512) == 2   # 17 * 64 = 1088 blocks: 64 left over
+    assert L.exl3_gemm_tail_splits(200, 2048, 256) == 1           # a fully split shard has no tail split
+    ws = exl3.linear_workspace_bytes(8192, 17408, 5120)
+    assert ws >= 16384 + 2 * 128 * 4 * 65536 + 8192 * 17408 * 2
+    assert exl3.linear_workspace_bytes(8192, 17408, 5120, exl3.GEMM_NO_SPLIT) < ws
+
+
 def test_decode_workspace_pre_rotation_region():
     """Decode-phase launches of 5..16 rows rotate the activations once per call into the workspace
     (fragment-major, 16 rows x IC fp16); below 5 rows each block rotates its own.  A 28672-column shard

@@ -138,6 +138,34 @@ def test_prefill_down_full_size_sampled():
     _sampled_check(c["x"], [dict(c, col0=0)], out, rows)
 
 
+def test_tail_round_split_parity():
+    """A shard whose 4-wave blocks leave the last round at most half full runs that round's blocks with
+    their input features split (exl3_gemm_tail_splits).  Here 9 x 29 = 261 blocks: the last 5 are row
+    tile 8 x column tiles 96..115.  All rows of 7 column blocks (4 inside that region) against the
+    oracle on the 16-bit and the 8-bit path; only tiles of that region differ from the unsplit GEMM, and
+    repeated calls give the same bits."""
+    M, IC, OC, K = 1152, 1024, 14848, 3
+    L = exl3.lib()
+    assert L.exl3_gemm_splits(M, IC, OC) == 1 and L.exl3_gemm_tail_splits(M, IC, OC) == 2
+    log(f"tail-round split M={M} IC={IC} OC={OC} K={K}")
+    c = synth.linear_case(5950, M, IC, OC, K)
+    d = _dev_case(c)
+    blocks = [0, 47, 95, 96, 103, 110, 115]
+    args = (c["x"], c["code"], K, c["s_in"], c["rin"], c["rout"], c["s_out"], blocks)
+    cols, y64 = oracle_block_columns(*args)
+    out = _run(c, d, 0)
+    assert_close_linear(bf16_to_f64(out)[:, cols], oracle_block_columns(*args, act="f16")[1], y64)
+    assert torch.equal(_run(c, d, 0), out)
+    ref = _run(c, d, exl3.GEMM_NO_SPLIT)
+    differ = (out != ref).view(M // 128, 128, OC // 128, 128).any(dim=3).any(dim=1).cpu().numpy()
+    mt, ct = np.nonzero(differ)
+    assert np.all(mt == 8) and np.all(ct >= 96), (mt, ct)
+    # 8-bit path: the bar of the int8 suite (codes may flip by one at near-ties, so no element-wise bound)
+    got8 = bf16_to_f64(_run(c, d, exl3.ACT_INT8))[:, cols]
+    assert rel_fro(got8, y64) <= 3e-2
+    assert rel_fro(got8, oracle_block_columns(*args, act="int8")[1]) < 4e-3
+
+
 # ------------------------------------------------------------------ K-split GEMM (default flags, small M)
 
 @pytest.mark.parametrize("M,IC,OC,K", [(200, 2048, 256, 2), (300, 1536, 384, 3), (131, 4096, 128, 4)])
