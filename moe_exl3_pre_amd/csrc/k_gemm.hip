@@ -263,10 +263,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
     park();                                                 // step st + 1 (a clamped copy past the end)
     load_t(st + 2 < s1 ? st + 2 : s1 - 1, tn);
     __builtin_amdgcn_sched_group_barrier(0x100, 8 * G::kNW, 0);      // LDS reads
+    // The MFMA/VALU groups also make the register allocator rotate the accumulators between the two
+    // unrolled steps (~130 accumulator copies per step).  At K <= 2 the decode is short enough that the
+    // copies cost more than the interleave gains (gate 5120 -> 17408 at M = 8192: -2% without the
+    // groups, measured); at K >= 3 the interleave wins.
+    if constexpr (K >= 3) {
 #pragma unroll
-    for (int i = 0; i < 128; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // then VALU
+      for (int i = 0; i < 128; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // then VALU
+      }
     }
   };
 
