@@ -285,69 +285,97 @@ __device__ void moe_route(const MoeArgs& a, int* lds) {
 }
 
 // ---------------------------------------------------------------------------------------------------
-// 1b. Rotation of gathered activations for w1 and w3.  One wave per (token, 128-block, group of 8 rows),
-// the rows being the token's (pair, projection) combinations (pair j = row / 2, projection row % 2):
+// 1b. Rotation of gathered activations for w1 and w3.  One wave per (token, 128-block, two groups of 8
+// rows), the rows being the token's (pair, projection) combinations (pair j = row / 2, projection row % 2):
 // lane (n, g) holds row n's features 16g .. 16g+15 of the block (the x chunk is the same for every row,
 // the sign vector is the pair's expert's).  Hadamard-128: register butterflies over feature bits 0..3,
 // a row-rotate DPP exchange over bit 4 (lane bit 3) and lane-pair swaps over bits 5 and 6 (lane bits 4
-// and 5), then each lane writes its 16-group as 32 contiguous bytes of the PERM16 layout.
+// and 5), then each lane writes its 16-group as 32 contiguous bytes of the PERM16 layout.  Two groups per
+// wave: the token's x chunk is loaded once, and the launch's workgroups (every one of which reserves the
+// route's LDS) stay within what the chip holds at once (at top-8 one group per wave would need 513).
 // ---------------------------------------------------------------------------------------------------
+constexpr int kRotGroups = 2;   // groups of 8 rows one rotation wave transforms
+
+inline int64_t moe_rotate_units(int64_t T, int H, int topk) {
+  const int nrh = (topk + 3) / 4;                          // groups of 8 rows: 2 * topk rows per token
+  return T * (H / kHad) * ((nrh + kRotGroups - 1) / kRotGroups);
+}
+
 __device__ void moe_rotate(const MoeArgs& a, int64_t unit) {
   const int lane = threadIdx.x & 63, n = lane & 7, g = lane >> 3;
   const int nblk = a.H / kHad;
   const int nrh = (a.topk + 3) / 4;                        // groups of 8 rows: 2 * topk rows per token
-  const int64_t tb = unit / nrh;
-  const int rh = int(unit % nrh);
+  const int nru = (nrh + kRotGroups - 1) / kRotGroups;     // this wave: groups kRotGroups * ru + k
+  const int64_t tb = unit / nru;
+  const int ru = int(unit % nru);
   const int t = int(tb / nblk), hb = int(tb % nblk);
   if (t >= a.T) return;
-  const int j = rh * 4 + (n >> 1), proj = n & 1;
-  const int sl = j < a.topk ? pair_slot(a, t * a.topk + j) : -1;
-  const int sc = sl < 0 ? 0 : sl;
   const int f = hb * kHad + 16 * g;
   const u32x4* xp = reinterpret_cast<const u32x4*>(a.x + int64_t(t) * a.H + f);
-  const u32x4* sp = reinterpret_cast<const u32x4*>(a.w13_suh + int64_t(sc * 2 + proj) * a.H + f);
-  const u32x4 xv[2] = {xp[0], xp[1]}, sv[2] = {sp[0], sp[1]};
-  float v[16];
+  const u32x4 xv[2] = {xp[0], xp[1]};                      // the token's chunk serves every group
+  // every group's sign-scale chunk is loaded before any arithmetic (the wave is latency-bound otherwise)
+  int jj[kRotGroups], sl[kRotGroups];
+  u32x4 sv[kRotGroups][2];
+  const int proj = n & 1;
 #pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    const int sh = (w & 1) * 16;
-    v[w] = bf16_to_f32((xv[w >> 3][(w >> 1) & 3] >> sh) & 0xFFFFu) * f16_to_f32(uint16_t(sv[w >> 3][(w >> 1) & 3] >> sh));
+  for (int k = 0; k < kRotGroups; ++k) {
+    const int rh = ru * kRotGroups + k;
+    jj[k] = rh * 4 + (n >> 1);
+    sl[k] = rh < nrh && jj[k] < a.topk ? pair_slot(a, t * a.topk + jj[k]) : -1;
+    const int sc = sl[k] < 0 ? 0 : sl[k];
+    const u32x4* sp = reinterpret_cast<const u32x4*>(a.w13_suh + int64_t(sc * 2 + proj) * a.H + f);
+    sv[k][0] = sp[0];
+    sv[k][1] = sp[1];
   }
 #pragma unroll
-  for (int b = 1; b < 16; b <<= 1)                         // feature bits 0..3
+  for (int k = 0; k < kRotGroups; ++k) {
+    if (ru * kRotGroups + k >= nrh) break;                 // wave-uniform
+    float v[16];
 #pragma unroll
-    for (int w = 0; w < 16; ++w)
-      if (!(w & b)) {
-        const float lo = v[w], hi = v[w | b];
-        v[w] = lo + hi;
-        v[w | b] = lo - hi;
-      }
-  float q[16];
-#pragma unroll
-  for (int w = 0; w < 16; ++w) q[w] = dpp<kRowRor8>(v[w]);  // bit 4: lane xor 8 within each row of 16
-#pragma unroll
-  for (int w = 0; w < 16; ++w) v[w] = bfly(v[w], q[w], lane & 8);
-#pragma unroll
-  for (int w = 0; w < 16; w += 2) lane_pair_bfly<false>(v[w], v[w + 1]);   // bit 5: lane bit 4
-#pragma unroll
-  for (int w = 0; w < 16; w += 2) lane_pair_bfly<true>(v[w], v[w + 1]);    // bit 6: lane bit 5
-  if (sl >= 0) {
-    const int64_t qi = int64_t(t) * a.topk + j;
-    u32x4* dst = reinterpret_cast<u32x4*>(a.xh13 + (int64_t(proj) * a.P + qi) * a.H + f);
-    u32x4 o0, o1;                                          // PERM16: positions (2i, 2i+1) hold features (i, i+8)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o0[i] = f32x2_to_f16x2(v[i] * kInvSqrt128, v[i + 8] * kInvSqrt128);
-      o1[i] = f32x2_to_f16x2(v[i + 4] * kInvSqrt128, v[i + 12] * kInvSqrt128);
+    for (int w = 0; w < 16; ++w) {
+      const int sh = (w & 1) * 16;
+      v[w] = bf16_to_f32((xv[w >> 3][(w >> 1) & 3] >> sh) & 0xFFFFu) *
+             f16_to_f32(uint16_t(sv[k][w >> 3][(w >> 1) & 3] >> sh));
     }
-    dst[0] = o0;
-    dst[1] = o1;
+#pragma unroll
+    for (int b = 1; b < 16; b <<= 1)                       // feature bits 0..3
+#pragma unroll
+      for (int w = 0; w < 16; ++w)
+        if (!(w & b)) {
+          const float lo = v[w], hi = v[w | b];
+          v[w] = lo + hi;
+          v[w | b] = lo - hi;
+        }
+    float q[16];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) q[w] = dpp<kRowRor8>(v[w]);  // bit 4: lane xor 8 within each row of 16
+#pragma unroll
+    for (int w = 0; w < 16; ++w) v[w] = bfly(v[w], q[w], lane & 8);
+#pragma unroll
+    for (int w = 0; w < 16; w += 2) lane_pair_bfly<false>(v[w], v[w + 1]);   // bit 5: lane bit 4
+#pragma unroll
+    for (int w = 0; w < 16; w += 2) lane_pair_bfly<true>(v[w], v[w + 1]);    // bit 6: lane bit 5
+    if (sl[k] >= 0) {
+      const int64_t qi = int64_t(t) * a.topk + jj[k];
+      u32x4* dst = reinterpret_cast<u32x4*>(a.xh13 + (int64_t(proj) * a.P + qi) * a.H + f);
+      u32x4 o0, o1;                                        // PERM16: positions (2i, 2i+1) hold features (i, i+8)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o0[i] = f32x2_to_f16x2(v[i] * kInvSqrt128, v[i + 8] * kInvSqrt128);
+        o1[i] = f32x2_to_f16x2(v[i + 4] * kInvSqrt128, v[i + 12] * kInvSqrt128);
+      }
+      dst[0] = o0;
+      dst[1] = o1;
+    }
   }
 }
 
 __global__ __launch_bounds__(kRouteThreads, 8) void moe_route_rotate_kernel(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) int route_lds[];
   if (blockIdx.x == 0) {
+    // the route is the launch's long pole: its waves take issue priority over the rotation waves
+    // sharing their CU
+    __builtin_amdgcn_s_setprio(3);
     moe_route(a, route_lds);
     return;
   }
@@ -681,7 +709,7 @@ hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream) {
     a.g_hi[g] = g < m.n_groups ? m.g_hi[g] : 0;
     a.g_k[g] = g < m.n_groups ? m.g_k[g] : 0;
   }
-  const int64_t rot_units = int64_t(a.T) * (a.H / kHad) * ((a.topk + 3) / 4);
+  const int64_t rot_units = moe_rotate_units(a.T, a.H, a.topk);
   const int64_t rot_blocks = (rot_units + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
   hipLaunchKernelGGL(moe_route_rotate_kernel, dim3(unsigned(1 + rot_blocks)), dim3(kRouteThreads),
                      moe_route_lds_bytes(a.E, a.P), stream, a);
