@@ -166,6 +166,24 @@ def test_tail_round_split_parity():
     assert rel_fro(got8, oracle_block_columns(*args, act="int8")[1]) < 4e-3
 
 
+def test_tail_round_split_merged_equals_separate():
+    """Two shards that each split their tail round (K=2 | K=3, 261 blocks apiece): the merged call equals
+    one call per shard bit for bit (each shard's plan depends only on its own M, IC, OC)."""
+    M, IC, OC = 1152, 1024, 14848
+    assert exl3.lib().exl3_gemm_tail_splits(M, IC, OC) == 2
+    case = synth.merged_case(5960, M, IC, [(OC, 2), (OC, 3)])
+    x = to_dev_x(case["x_bits"])
+    s_in, rin = to_dev(case["shards"][0]["s_in"]), to_dev(case["shards"][0]["rin"])
+    shards = [shard_to_dev(s, s_in, rin) for s in case["shards"]]
+    merged = torch.full((M, case["ldo"]), SENTINEL, dtype=torch.bfloat16, device=dev())
+    exl3.linear_multi_into(merged, x, shards)
+    sep = torch.full_like(merged, SENTINEL)
+    for s in shards:
+        exl3.linear_into(sep, x, s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"], col0=s["col0"])
+    torch.cuda.synchronize()
+    assert torch.equal(merged, sep)
+
+
 # ------------------------------------------------------------------ K-split GEMM (default flags, small M)
 
 @pytest.mark.parametrize("M,IC,OC,K", [(200, 2048, 256, 2), (300, 1536, 384, 3), (131, 4096, 128, 4)])

@@ -228,10 +228,12 @@ def test_merged_shards_with_distinct_input_vectors():
                             O.linear(case["x"], *args))
 
 
-def test_large_ic_sampled():
-    """down_proj shape IC=17408, OC=5120, K=3 at decode M (many splits), sampled blocks."""
-    c = synth.linear_case(1300, 3, 17408, 5120, 3)
-    log("large IC sampled")
+@pytest.mark.parametrize("M", [3, 8])
+def test_large_ic_sampled(M):
+    """down_proj shape IC=17408, OC=5120, K=3 at decode M (many splits), sampled blocks; M=8 takes the
+    activations rotated once per call (a 16 x 17408 fragment-major region of the workspace)."""
+    c = synth.linear_case(1300 + M, M, 17408, 5120, 3)
+    log(f"large IC sampled M={M}")
     out = _run_linear(c, _case_to_dev(c))
     got = bf16_to_f64(out)
     blocks = [0, 17, 39]
