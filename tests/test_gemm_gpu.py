@@ -166,6 +166,25 @@ def test_tail_round_split_parity():
     assert rel_fro(got8, oracle_block_columns(*args, act="int8")[1]) < 4e-3
 
 
+def test_tail_round_split_poisoned_workspace():
+    """The split tail's partial tiles are written before they are read: a workspace filled with NaN bytes
+    (the counter head zeroed, as the ABI asks once) gives the same bits as a zeroed one."""
+    M, IC, OC, K = 1152, 1024, 14848, 2
+    c = synth.linear_case(5970, M, IC, OC, K)
+    d = _dev_case(c)
+    nbytes = exl3.linear_workspace_bytes(M, IC, OC)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=dev())
+        ws[:16384] = 0
+        out = torch.full((M, OC), SENTINEL, dtype=torch.bfloat16, device=dev())
+        exl3.linear_into(out, d["x"], d["code"], K, d["s_in"], d["rin"], d["rout"], d["s_out"], ws=ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.isfinite(outs[1].float()).all()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_tail_round_split_merged_equals_separate():
     """Two shards that each split their tail round (K=2 | K=3, 261 blocks apiece): the merged call equals
     one call per shard bit for bit (each shard's plan depends only on its own M, IC, OC)."""
