@@ -268,3 +268,42 @@ def moe_forward(x, topk_ids, topk_w, experts, act: str = "f64", tokens=None) -> 
         np.add.at(out, tok, w[tok, slot][:, None] * y)
     assert out.shape[0] == T
     return out
+
+
+# ---------------------------------------------------------------------------------------------
+# int8 embedding rows gathered and dequantized
+# ---------------------------------------------------------------------------------------------
+# [quantpack] exl3/embedding.py, `Exl3EmbeddingMethod.embedding`: the table stays int8 with one scale per
+# row; the rows of the requested token ids are gathered, converted to the scale's dtype (bf16 here) and
+# multiplied by their row's scale.  An int8 code times a bf16 scale is exact in any binary format with
+# 16 or more significand bits, so the result is that exact product rounded once to bf16 (nearest, ties
+# to even).  Ids outside [0, V) give zero rows: the reading of the page's tensor-parallel cut, where
+# VocabParallelEmbedding masks the ids a rank does not hold.
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) to float64: a bf16 number is the upper half of a float32."""
+    b = np.asarray(bits, dtype=np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (8 significant bits, nearest, ties to even) and return the bit
+    patterns.  Normal range only (the products here never reach bf16 subnormals); zeros keep their sign."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                                   # v = m * 2^e, 0.5 <= |m| < 1
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)         # 8 significant bits; np.rint rounds half to even
+    r = np.where(v == 0, v, r)                           # keep the sign of zero
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def embed_gather(table_q: np.ndarray, scale_bits: np.ndarray, ids) -> np.ndarray:
+    """out[t, :] = bf16(table_q[ids[t], :] * scale[ids[t]]) as bf16 bit patterns [T, H] (uint16);
+    zero rows for ids outside [0, V)."""
+    table_q = np.asarray(table_q, dtype=np.int8)
+    V, H = table_q.shape
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    s = bf16_bits_to_f64(np.asarray(scale_bits, dtype=np.uint16).reshape(-1))
+    rows = np.zeros((ids.size, H), dtype=np.float64)
+    ok = (ids >= 0) & (ids < V)
+    rows[ok] = table_q[ids[ok]].astype(np.float64) * s[ids[ok]][:, None]
+    return f64_to_bf16_bits(rows)

@@ -399,3 +399,69 @@ def test_moe_f16_operands_close_to_exact():
     b = O.moe_forward(m["x"], m["topk_ids"], m["topk_w"], m["experts"], act="f16")
     rel = np.linalg.norm(a - b) / np.linalg.norm(a)
     assert 1e-6 < rel < 2e-3
+
+
+# ------------------------------------------------------------------------------------------ int8 embedding
+
+def _golden_embed():
+    rows = []
+    with open(os.path.join(GOLDEN, "embed_int8_values.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                q, s, e = line.split()
+                rows.append((int(q), int(s, 16), int(e, 16)))
+    return rows
+
+
+def test_embed_worked_values():
+    """Hand-derived products (a tie rounded to even, rounding down and up, exact values, -0)."""
+    for q, s, e in _golden_embed():
+        table = np.array([[q] * 16], dtype=np.int8)
+        got = O.embed_gather(table, np.array([s], dtype=np.uint16), [0])
+        assert np.all(got == e), (q, hex(s), hex(int(got[0, 0])), hex(e))
+
+
+def test_embed_power_of_two_scales_are_exact():
+    """With a scale 2^k every int8 code (at most 8 significant bits) is exact in bf16: the result is the
+    upper half of the float32 q * 2^k."""
+    rng = np.random.default_rng(11)
+    table = rng.integers(-128, 128, size=(6, 64), dtype=np.int8)
+    ks = np.array([-9, -7, -3, 0, 2, 5])
+    sbits = (((ks + 127) << 7)).astype(np.uint16)          # sign 0, exponent k, mantissa 0
+    got = O.embed_gather(table, sbits, np.arange(6))
+    want = (table.astype(np.float32) * np.ldexp(np.float32(1), ks)[:, None]).astype(np.float32)
+    assert np.array_equal(got, (want.view(np.uint32) >> 16).astype(np.uint16))
+
+
+def test_embed_equals_one_hot_product():
+    """The gather is the one-hot row selection of the dequantized table (a matmul with exactly one 1 per
+    row adds a single exact term)."""
+    rng = np.random.default_rng(12)
+    V, H, T = 50, 96, 40
+    table = rng.integers(-128, 128, size=(V, H), dtype=np.int8)
+    sbits = (rng.integers(0x3B00, 0x3D00, size=V)).astype(np.uint16)
+    ids = rng.integers(0, V, size=T)
+    onehot = np.zeros((T, V))
+    onehot[np.arange(T), ids] = 1.0
+    dense = table.astype(np.float64) * O.bf16_bits_to_f64(sbits)[:, None]
+    assert np.array_equal(O.embed_gather(table, sbits, ids), O.f64_to_bf16_bits(onehot @ dense))
+
+
+def test_embed_out_of_range_ids_give_zero_rows():
+    rng = np.random.default_rng(13)
+    table = rng.integers(-128, 128, size=(8, 32), dtype=np.int8)
+    sbits = np.full(8, 0x3F80, dtype=np.uint16)
+    got = O.embed_gather(table, sbits, [3, -1, 8, 1 << 20, 3])
+    assert np.all(got[1:4] == 0)
+    assert np.array_equal(got[0], got[4])
+    assert np.array_equal(got[0], (table[3].astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+
+
+def test_bf16_rounding_ties_to_even():
+    """Halfway cases of the bf16 rounding go to the even neighbour (both directions)."""
+    lo = 1.0 + 2.0 ** -8                                     # halfway between 1 and 1 + 2^-7 -> 1 (even)
+    hi = 1.0 + 3 * 2.0 ** -8                                 # halfway between 1 + 2^-7 and 1 + 2^-6 -> 1 + 2^-6
+    assert O.f64_to_bf16_bits(np.array([lo]))[0] == 0x3F80
+    assert O.f64_to_bf16_bits(np.array([hi]))[0] == 0x3F82
+    assert O.f64_to_bf16_bits(np.array([-hi]))[0] == 0xBF82
