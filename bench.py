@@ -8,7 +8,8 @@ method's algorithmic bytes, IC*OC*K/8 per shard).  Weights rotate over 16 seeded
 256 MiB Infinity Cache cannot serve them.  Steps are captured once in a HIP graph and replayed between
 events recorded on the stream the kernels run on.
 
-Also reported (under "extra"): decode M = 2, 4, 8; prefill M=8192 gate_up and down (TFLOP/s); the MoE
+Also reported (under "extra"): decode M = 2, 4, 8; prefill M=8192 gate_up and down (TFLOP/s); the int8
+embedding gather (T = 256 and 8192 ids over a 248,320 x 5120 table; GB/s of bytes moved); the MoE
 expert bank (T=256, E=128, top-8, H=2048, I=768; 3 rotated banks).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill] [--no-moe]
@@ -50,6 +51,7 @@ def parse():
     ap.add_argument("--extra-m", default="2,4,8", help="additional decode M values reported under 'extra'")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 prefill measurements")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE bank measurement")
+    ap.add_argument("--no-embed", action="store_true", help="skip the int8 embedding gather measurement")
     ap.add_argument("--sweep", action="store_true",
                     help="the M sweep over a 64-layer projection set on both paths (prints its own report)")
     ap.add_argument("--sweep-ms", default="1,4,8,16,24,32,48,64,128,512,8192")
@@ -202,6 +204,38 @@ def time_moe(torch, exl3, synth, dev, steps=60):
     return sec, tb
 
 
+def time_embed(torch, exl3, dev, reps=50):
+    """int8 embedding gather-dequant over the pages' vocabulary (248,320 rows of 5120, a 1.27 GB table that no
+    cache holds) for T = 256 and 8192 random token ids.  Bytes moved per call: T*H int8 in, T*H bf16 out."""
+    V, H = 248320, 5120
+    g = torch.Generator(device=dev)
+    g.manual_seed(31)
+    table = torch.randint(-128, 128, (V, H), dtype=torch.int8, device=dev, generator=g)
+    scale = torch.randint(0x3A00, 0x3D80, (V,), dtype=torch.int32, device=dev, generator=g).to(torch.int16)
+    scale = scale.view(torch.bfloat16)
+    res = {}
+    for T in (256, 8192):
+        ids = torch.randint(0, V, (T,), dtype=torch.int32, device=dev, generator=g)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        exl3.embed_int8(table, scale, ids, out=out)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            exl3.embed_int8(table, scale, ids, out=out)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        sec = t0.elapsed_time(t1) / 1e3 / reps
+        nbytes = 3 * T * H
+        res[T] = (sec, nbytes)
+        print(f"# embed_int8 V={V} H={H} T={T}: {sec * 1e6:.2f} us/call, {nbytes / sec / 1e9:.1f} GB/s",
+              file=sys.stderr, flush=True)
+    del table
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(synth, O):
     """The fp64 oracle on one M=1 step of the same workload (both shards), single-threaded."""
     from threadpoolctl import threadpool_limits
@@ -338,6 +372,7 @@ def main():
 
     prefill = {} if a.no_prefill else time_prefill(torch, exl3, synth, dev)
     moe = None if a.no_moe else time_moe(torch, exl3, synth, dev)
+    embed = {} if a.no_embed else time_embed(torch, exl3, dev)
 
     sec = results[1]
     gbs = trellis_bytes / sec / 1e9
@@ -365,6 +400,10 @@ def main():
         line["extra"]["moe_T256_E128_top8"] = {"us_per_call": round(s * 1e6, 2), "trellis_MB": round(tb / 1e6, 1),
                                                "trellis_GBps": round(tb / s / 1e9, 1),
                                                "frac_hbm": round(tb / s / 1e9 / HBM_PEAK_GBS, 4)}
+    for T, (s, nbytes) in embed.items():
+        line["extra"][f"embed_int8_V248320_H5120_T{T}"] = {"us_per_call": round(s * 1e6, 2),
+                                                           "GBps": round(nbytes / s / 1e9, 1),
+                                                           "frac_hbm": round(nbytes / s / 1e9 / HBM_PEAK_GBS, 4)}
     if not a.no_cpu:
         from oracle import exl3_oracle as O
         line["cpu_baseline"] = cpu_baseline(synth, O)

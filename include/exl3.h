@@ -207,6 +207,24 @@ int exl3_moe_bank_forward(void* out, const void* x, int64_t T,
                           const exl3_bank* bank, unsigned flags, void* ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------------------
+ * int8 embedding rows gathered by token id and dequantized ("vllm-quantpack 0.1.0", exl3/embedding.py,
+ * `Exl3EmbeddingMethod.embedding`: the table stays int8 with one scale per row; the gathered rows are
+ * converted to the scale's dtype and multiplied by their row's scale, so the table is never materialised
+ * in bf16).
+ *
+ *   out    bf16 [T, H] row-major, 16-byte aligned: out[t, :] = bf16(table[ids[t], :] * scale[ids[t]]).
+ *   table  int8 [V, H] row-major, 16-byte aligned.
+ *   scale  bf16 [V], one scale per row.
+ *   ids    int32 [T] device array of token ids; ids outside [0, V) give zero rows (the page's
+ *          tensor-parallel cut masks the ids a rank does not hold).
+ * Requirements: V >= 1, H a positive multiple of 16.  The product of an int8 code and a bf16 scale is
+ * exact in fp32, so the result is bit-exact: one round-to-nearest-even to bf16.  T == 0 is a no-op.
+ * Returns EXL3_OK, EXL3_EINVAL, EXL3_ELAUNCH.
+ * ------------------------------------------------------------------------------------------------ */
+int exl3_embed_int8(void* out, const int8_t* table, const void* scale, int64_t V, int64_t H, const int32_t* ids,
+                    int64_t T, void* stream);
+
+/* --------------------------------------------------------------------------------------------------
  * Test hook: the decoded weight, fp16 [IC, OC] row-major, produced by the same device decode routine
  * the GEMM kernels use.  IC, OC multiples of 16; K in 1..8.
  * ------------------------------------------------------------------------------------------------ */

@@ -341,6 +341,13 @@ bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsign
 
 }  // namespace
 
+namespace exl3 {
+// int8 embedding gather (k_embed.hip): out bf16 [T, H] = table[ids] * scale[ids]; zero rows for ids
+// outside [0, V).
+hipError_t launch_embed_int8(void* out, const int8_t* table, const void* scale, int64_t V, int64_t H,
+                             const int32_t* ids, int64_t T, hipStream_t stream);
+}  // namespace exl3
+
 extern "C" {
 
 const char* exl3_last_error(void) { return g_error.c_str(); }
@@ -492,6 +499,21 @@ int exl3_moe_bank_forward(void* out, const void* x, int64_t T, const int32_t* to
     m.g_k[g] = g < bank->n_groups ? (bank->groups[g].k_gu | (bank->groups[g].k_d << 8)) : 0;
   }
   if (int rc = launch_status(launch_moe(m, static_cast<hipStream_t>(stream)), "exl3_moe_bank_forward")) return rc;
+  return ok();
+}
+
+int exl3_embed_int8(void* out, const int8_t* table, const void* scale, int64_t V, int64_t H, const int32_t* ids,
+                    int64_t T, void* stream) {
+  if (T < 0) return fail(EXL3_EINVAL, "T: %lld is negative", (long long)T);
+  if (V < 1) return fail(EXL3_EINVAL, "V: %lld rows", (long long)V);
+  if (H < 16 || H % 16) return fail(EXL3_EINVAL, "H: %lld is not a positive multiple of 16", (long long)H);
+  if (T == 0) return ok();
+  if (!out || !table || !scale || !ids) return fail(EXL3_EINVAL, "out/table/scale/ids: null");
+  if (!aligned(out, 16) || !aligned(table, 16)) return fail(EXL3_EINVAL, "out/table: not 16-byte aligned");
+  if (!aligned(scale, 2) || !aligned(ids, 4)) return fail(EXL3_EINVAL, "scale/ids: not 2-/4-byte aligned");
+  if (int rc = launch_status(launch_embed_int8(out, table, scale, V, H, ids, T, static_cast<hipStream_t>(stream)),
+                             "exl3_embed_int8"))
+    return rc;
   return ok();
 }
 

@@ -67,6 +67,8 @@ _SIGS = {
     "exl3_moe_bank_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(Bank), ctypes.c_uint,
                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "exl3_embed_int8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
     "exl3_decode_tiles": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                          ctypes.c_void_p]),
     "exl3_rotate_activations": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -192,6 +194,26 @@ def linear_multi_into(out, x, shards, flags: int = 0, ws=None):
 
 
 # ------------------------------------------------------------------------------------------ test hooks
+
+def embed_int8(table, scale, ids, out=None):
+    """bf16 [T, H] rows table[ids] * scale[ids] of an int8 [V, H] table with bf16 [V] row scales; ids int32 [T]."""
+    _need(table, "table", torch.int8)
+    _need(scale, "scale", torch.bfloat16)
+    _need(ids, "ids", torch.int32)
+    V, H = table.shape
+    if scale.shape != (V,):
+        raise ValueError(f"scale: shape {tuple(scale.shape)} != ({V},)")
+    if ids.dim() != 1:
+        raise ValueError(f"ids: {ids.dim()}-d, want [T]")
+    T = ids.shape[0]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=table.device)
+    _need(out, "out", torch.bfloat16)
+    if out.shape != (T, H):
+        raise ValueError(f"out: shape {tuple(out.shape)} != ({T}, {H})")
+    _check(lib().exl3_embed_int8(_ptr(out), _ptr(table), _ptr(scale), V, H, _ptr(ids), T, _stream(table.device)))
+    return out
+
 
 def decode_tiles(code, K):
     """Decoded weight fp16 [IC, OC] through the device decode routine."""

@@ -88,6 +88,18 @@ def test_int8_workspace_holds_codes_and_scales():
         assert exl3.linear_workspace_bytes(M, 4096, 14336, exl3.ACT_INT8) >= 16384 + M * 4096 * 2 + M * 4
 
 
+def test_embed_validation():
+    """Host-side checks of the embedding gather (no launch): H a positive multiple of 16, V >= 1, T >= 0,
+    non-null pointers; T == 0 is a no-op."""
+    L = exl3.lib()
+    assert L.exl3_embed_int8(None, None, None, 10, 24, None, 4, None) == -1
+    assert L.exl3_embed_int8(None, None, None, 0, 32, None, 4, None) == -1
+    assert L.exl3_embed_int8(None, None, None, 10, 32, None, -1, None) == -1
+    assert L.exl3_embed_int8(None, None, None, 10, 32, None, 3, None) == -1
+    assert b"null" in L.exl3_last_error()
+    assert L.exl3_embed_int8(None, None, None, 10, 32, None, 0, None) == 0
+
+
 def test_gemm_tail_split_plan():
     """Large shards whose 4-wave blocks (128 x 512) leave the last round of 256 at most half full split
     that round's blocks over the input features; the workspace holds their partial tiles."""
