@@ -206,7 +206,8 @@ def time_moe(torch, exl3, synth, dev, steps=60):
 
 def time_embed(torch, exl3, dev, reps=50):
     """int8 embedding gather-dequant over the pages' vocabulary (248,320 rows of 5120, a 1.27 GB table that no
-    cache holds) for T = 256 and 8192 random token ids.  Bytes moved per call: T*H int8 in, T*H bf16 out."""
+    cache holds) for T = 256 and 8192 random token ids, timed in a captured graph like the other
+    measurements.  Bytes moved per call: T*H int8 in, T*H bf16 out."""
     V, H = 248320, 5120
     g = torch.Generator(device=dev)
     g.manual_seed(31)
@@ -215,18 +216,10 @@ def time_embed(torch, exl3, dev, reps=50):
     scale = scale.view(torch.bfloat16)
     res = {}
     for T in (256, 8192):
-        ids = torch.randint(0, V, (T,), dtype=torch.int32, device=dev, generator=g)
+        # several id sets, so repeated calls do not read the same rows out of the caches
+        ids = [torch.randint(0, V, (T,), dtype=torch.int32, device=dev, generator=g) for _ in range(8)]
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        exl3.embed_int8(table, scale, ids, out=out)
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(reps):
-            exl3.embed_int8(table, scale, ids, out=out)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        sec = t0.elapsed_time(t1) / 1e3 / reps
+        sec = graph_time(torch, lambda i: exl3.embed_int8(table, scale, ids[i % len(ids)], out=out), reps, 8)
         nbytes = 3 * T * H
         res[T] = (sec, nbytes)
         print(f"# embed_int8 V={V} H={H} T={T}: {sec * 1e6:.2f} us/call, {nbytes / sec / 1e9:.1f} GB/s",
