@@ -307,3 +307,22 @@ def embed_gather(table_q: np.ndarray, scale_bits: np.ndarray, ids) -> np.ndarray
     ok = (ids >= 0) & (ids < V)
     rows[ok] = table_q[ids[ok]].astype(np.float64) * s[ids[ok]][:, None]
     return f64_to_bf16_bits(rows)
+
+
+# ---------------------------------------------------------------------------------------------
+# int8 table used as the output head (tied embedding / lm_head)
+# ---------------------------------------------------------------------------------------------
+# [quantpack] exl3/embedding.py, `Exl3EmbeddingMethod.apply`: the head multiplies the whole int8 table
+# by its row scales in the activations' dtype (bf16), so every weight is rounded once, w[v, h] =
+# bf16(q[v, h] * s[v]); the logits are the linear map x @ w^T, rounded once to bf16.  Here the sum is
+# taken in float64 before that rounding.  No bias: a tied head has none (the page adds one only when
+# given).
+
+def lm_head_int8(x_bits: np.ndarray, table_q: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """logits[m, v] = bf16(sum_h x[m, h] * bf16(q[v, h] * s[v])) as bf16 bit patterns [M, V] (uint16).
+    x_bits: [M, H] bf16 bit patterns; table_q: [V, H] int8; scale_bits: [V] bf16 bit patterns."""
+    x = bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16))
+    q = np.asarray(table_q, dtype=np.int8).astype(np.float64)
+    s = bf16_bits_to_f64(np.asarray(scale_bits, dtype=np.uint16).reshape(-1))
+    w = bf16_bits_to_f64(f64_to_bf16_bits(q * s[:, None]))
+    return f64_to_bf16_bits(x @ w.T)

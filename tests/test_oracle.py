@@ -1,5 +1,6 @@
 """Pins for the fp64 CPU oracle: worked values, closed forms, invariants, library routines and
 brute force on tiny inputs.  None of these re-derives a value through the oracle itself."""
+from fractions import Fraction
 import os
 
 import numpy as np
@@ -465,3 +466,77 @@ def test_bf16_rounding_ties_to_even():
     assert O.f64_to_bf16_bits(np.array([lo]))[0] == 0x3F80
     assert O.f64_to_bf16_bits(np.array([hi]))[0] == 0x3F82
     assert O.f64_to_bf16_bits(np.array([-hi]))[0] == 0xBF82
+
+
+# ------------------------------------------------------------------------------------------ int8 output head
+
+def _bits(v):
+    return O.f64_to_bf16_bits(np.asarray(v, dtype=np.float64))
+
+
+def test_lm_head_hand_values():
+    """Worked by hand.  Rows q = (1, -2) and (3, 4) with scales 0.5 and 0.25 dequantize exactly to (0.5, -1)
+    and (0.75, 1); x = (1, 2) gives 0.5 - 2 = -1.5 and 0.75 + 2 = 2.75."""
+    got = O.lm_head_int8(_bits([[1.0, 2.0]]), np.array([[1, -2], [3, 4]], dtype=np.int8), _bits([0.5, 0.25]))
+    assert np.array_equal(got, _bits([[-1.5, 2.75]]))
+
+
+def test_lm_head_rounds_each_weight_before_the_sum():
+    """The head rounds every dequantized weight to bf16 first.  With s = 1 + 2^-7 the codes 127 and -126
+    give 127.9921875 -> 128 and -126.984375 -> -127 (bf16 steps 0.5 in [64, 128)), so x = (1, 1) gives
+    exactly 1.0; the unrounded product would be 1.0078125, itself a bf16 number."""
+    got = O.lm_head_int8(_bits([[1.0, 1.0]]), np.array([[127, -126]], dtype=np.int8), np.array([0x3F81], np.uint16))
+    assert got[0, 0] == 0x3F80
+
+
+def test_lm_head_identity_rows_give_the_embedding_table():
+    """With x the H x H identity each logit is one weight: logits^T equals every row of the table gathered
+    and dequantized by the embedding (a separate function of the oracle)."""
+    rng = np.random.default_rng(21)
+    V, H = 40, 32
+    table = rng.integers(-128, 128, size=(V, H), dtype=np.int8)
+    sbits = rng.integers(0x3A00, 0x3E00, size=V).astype(np.uint16)
+    got = O.lm_head_int8(_bits(np.eye(H)), table, sbits)
+    assert np.array_equal(got.T, O.embed_gather(table, sbits, np.arange(V)))
+
+
+def _round_bf16_exact(v: Fraction) -> Fraction:
+    """Nearest bf16 (8 significant bits, ties to even) of an exact rational, by integer arithmetic."""
+    if v == 0:
+        return Fraction(0)
+    e = 0
+    a = abs(v)
+    while a >= 256:
+        a /= 2
+        e += 1
+    while a < 128:
+        a *= 2
+        e -= 1
+    n = round(a)                                       # Fraction rounds half to even
+    return (1 if v > 0 else -1) * Fraction(n) * Fraction(2) ** e
+
+
+def test_lm_head_brute_force_exact_rationals():
+    """Small random case recomputed with exact rationals and an integer-only bf16 rounding."""
+    rng = np.random.default_rng(22)
+    M, V, H = 3, 5, 24
+    table = rng.integers(-128, 128, size=(V, H), dtype=np.int8)
+    sbits = rng.integers(0x3A00, 0x3E00, size=V).astype(np.uint16)
+    xbits = _bits(rng.normal(size=(M, H)))
+    xf = [[Fraction(float(v)) for v in row] for row in O.bf16_bits_to_f64(xbits)]
+    sf = [Fraction(float(v)) for v in O.bf16_bits_to_f64(sbits)]
+    got = O.bf16_bits_to_f64(O.lm_head_int8(xbits, table, sbits))
+    for m in range(M):
+        for v in range(V):
+            acc = sum(xf[m][h] * _round_bf16_exact(int(table[v, h]) * sf[v]) for h in range(H))
+            assert Fraction(float(got[m, v])) == _round_bf16_exact(acc), (m, v)
+
+
+def test_lm_head_sign_and_power_of_two_scaling_are_exact():
+    rng = np.random.default_rng(23)
+    table = rng.integers(-128, 128, size=(16, 64), dtype=np.int8)
+    sbits = rng.integers(0x3A00, 0x3E00, size=16).astype(np.uint16)
+    x = O.bf16_bits_to_f64(_bits(rng.normal(size=(4, 64))))
+    base = O.bf16_bits_to_f64(O.lm_head_int8(_bits(x), table, sbits))
+    assert np.array_equal(O.bf16_bits_to_f64(O.lm_head_int8(_bits(-x), table, sbits)), -base)
+    assert np.array_equal(O.bf16_bits_to_f64(O.lm_head_int8(_bits(4 * x), table, sbits)), 4 * base)
