@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--extra-m", default="2,4,8", help="additional decode M values reported under 'extra'")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 prefill measurements")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE bank measurement")
-    ap.add_argument("--no-embed", action="store_true", help="skip the int8 embedding gather measurement")
+    ap.add_argument("--no-embed", action="store_true", help="skip the int8 embedding gather and output-head measurements")
     ap.add_argument("--sweep", action="store_true",
                     help="the M sweep over a 64-layer projection set on both paths (prints its own report)")
     ap.add_argument("--sweep-ms", default="1,4,8,16,24,32,48,64,128,512,8192")
@@ -205,9 +205,12 @@ def time_moe(torch, exl3, synth, dev, steps=60):
 
 
 def time_embed(torch, exl3, dev, reps=50):
-    """int8 embedding gather-dequant over the pages' vocabulary (248,320 rows of 5120, a 1.27 GB table that no
-    cache holds) for T = 256 and 8192 random token ids, timed in a captured graph like the other
-    measurements.  Bytes moved per call: T*H int8 in, T*H bf16 out."""
+    """The int8 table over the pages' vocabulary (248,320 rows of 5120, a 1.27 GB table that no cache holds),
+    timed in captured graphs like the other measurements:
+      - embedding gather-dequant for T = 256 and 8192 random token ids; bytes per call: T*H int8 in,
+        T*H bf16 out;
+      - the same table as the output head for M = 1 and 16 rows of x; bytes per call: the table (V*H), its
+        scales (2V), x (2MH) and the logits (2MV)."""
     V, H = 248320, 5120
     g = torch.Generator(device=dev)
     g.manual_seed(31)
@@ -221,8 +224,16 @@ def time_embed(torch, exl3, dev, reps=50):
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         sec = graph_time(torch, lambda i: exl3.embed_int8(table, scale, ids[i % len(ids)], out=out), reps, 8)
         nbytes = 3 * T * H
-        res[T] = (sec, nbytes)
+        res[f"embed_int8_V{V}_H{H}_T{T}"] = (sec, nbytes)
         print(f"# embed_int8 V={V} H={H} T={T}: {sec * 1e6:.2f} us/call, {nbytes / sec / 1e9:.1f} GB/s",
+              file=sys.stderr, flush=True)
+    for M in (1, 16):
+        x = torch.randn((M, H), device=dev, generator=g).to(torch.bfloat16)
+        out = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+        sec = graph_time(torch, lambda i: exl3.lm_head_int8(x, table, scale, out=out), max(reps // 5, 8), 4)
+        nbytes = V * H + 2 * V + 2 * M * H + 2 * M * V
+        res[f"lm_head_int8_V{V}_H{H}_M{M}"] = (sec, nbytes)
+        print(f"# lm_head_int8 V={V} H={H} M={M}: {sec * 1e6:.2f} us/call, {nbytes / sec / 1e9:.1f} GB/s",
               file=sys.stderr, flush=True)
     del table
     torch.cuda.empty_cache()
@@ -393,8 +404,8 @@ def main():
         line["extra"]["moe_T256_E128_top8"] = {"us_per_call": round(s * 1e6, 2), "trellis_MB": round(tb / 1e6, 1),
                                                "trellis_GBps": round(tb / s / 1e9, 1),
                                                "frac_hbm": round(tb / s / 1e9 / HBM_PEAK_GBS, 4)}
-    for T, (s, nbytes) in embed.items():
-        line["extra"][f"embed_int8_V248320_H5120_T{T}"] = {"us_per_call": round(s * 1e6, 2),
+    for key, (s, nbytes) in embed.items():
+        line["extra"][key] = {"us_per_call": round(s * 1e6, 2),
                                                            "GBps": round(nbytes / s / 1e9, 1),
                                                            "frac_hbm": round(nbytes / s / 1e9 / HBM_PEAK_GBS, 4)}
     if not a.no_cpu:

@@ -225,6 +225,25 @@ int exl3_embed_int8(void* out, const int8_t* table, const void* scale, int64_t V
                     int64_t T, void* stream);
 
 /* --------------------------------------------------------------------------------------------------
+ * The same int8 table as the output head (tied embedding / lm_head; "vllm-quantpack 0.1.0",
+ * exl3/embedding.py, `Exl3EmbeddingMethod.apply`: the table is multiplied by its row scales in bf16, so
+ * every weight is rounded once, then mapped linearly onto x).
+ *
+ *   out    bf16 [M, V] with row stride ldo (elements); written 8 bytes at a time when out is 8-byte
+ *          aligned and ldo a multiple of 4, element by element otherwise:
+ *          out[m, v] = bf16(sum_h x[m, h] * bf16(table[v, h] * scale[v])), summed in fp32.
+ *   x      bf16 [M, H] row-major, 16-byte aligned.
+ *   table  int8 [V, H] row-major, 16-byte aligned;  scale  bf16 [V].
+ * Requirements: V >= 1; H a positive multiple of 64; ldo >= V.  No bias (a tied head
+ * has none).  M == 0 is a no-op.  Every 64 rows of x stream the table once (one launch per 64 rows).
+ * The weights are the page's bf16(q * s) bit for bit; the sum order differs from any library GEMM, so
+ * results agree with an exact sum to the bf16 rounding of the output.
+ * Returns EXL3_OK, EXL3_EINVAL, EXL3_ELAUNCH.
+ * ------------------------------------------------------------------------------------------------ */
+int exl3_lm_head_int8(void* out, int64_t ldo, const void* x, int64_t M, const int8_t* table, const void* scale,
+                      int64_t V, int64_t H, void* stream);
+
+/* --------------------------------------------------------------------------------------------------
  * Test hook: the decoded weight, fp16 [IC, OC] row-major, produced by the same device decode routine
  * the GEMM kernels use.  IC, OC multiples of 16; K in 1..8.
  * ------------------------------------------------------------------------------------------------ */

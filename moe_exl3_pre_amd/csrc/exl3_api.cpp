@@ -346,6 +346,10 @@ namespace exl3 {
 // outside [0, V).
 hipError_t launch_embed_int8(void* out, const int8_t* table, const void* scale, int64_t V, int64_t H,
                              const int32_t* ids, int64_t T, hipStream_t stream);
+// the int8 table as the output head (k_embed.hip): logits bf16 [M, V] (row stride ldo) =
+// x [M, H] . bf16(table * scale)^T.
+hipError_t launch_lm_head_int8(void* out, int64_t ldo, const void* x, int64_t M, const int8_t* table,
+                               const void* scale, int64_t V, int64_t H, hipStream_t stream);
 }  // namespace exl3
 
 extern "C" {
@@ -513,6 +517,22 @@ int exl3_embed_int8(void* out, const int8_t* table, const void* scale, int64_t V
   if (!aligned(scale, 2) || !aligned(ids, 4)) return fail(EXL3_EINVAL, "scale/ids: not 2-/4-byte aligned");
   if (int rc = launch_status(launch_embed_int8(out, table, scale, V, H, ids, T, static_cast<hipStream_t>(stream)),
                              "exl3_embed_int8"))
+    return rc;
+  return ok();
+}
+
+int exl3_lm_head_int8(void* out, int64_t ldo, const void* x, int64_t M, const int8_t* table, const void* scale,
+                      int64_t V, int64_t H, void* stream) {
+  if (M < 0) return fail(EXL3_EINVAL, "M: %lld is negative", (long long)M);
+  if (V < 1) return fail(EXL3_EINVAL, "V: %lld rows", (long long)V);
+  if (H < 64 || H % 64) return fail(EXL3_EINVAL, "H: %lld is not a positive multiple of 64", (long long)H);
+  if (ldo < V) return fail(EXL3_EINVAL, "ldo: %lld is below V", (long long)ldo);
+  if (M == 0) return ok();
+  if (!out || !x || !table || !scale) return fail(EXL3_EINVAL, "out/x/table/scale: null");
+  if (!aligned(x, 16) || !aligned(table, 16)) return fail(EXL3_EINVAL, "x/table: not 16-byte aligned");
+  if (!aligned(out, 2) || !aligned(scale, 2)) return fail(EXL3_EINVAL, "out/scale: not 2-byte aligned");
+  if (int rc = launch_status(launch_lm_head_int8(out, ldo, x, M, table, scale, V, H, static_cast<hipStream_t>(stream)),
+                             "exl3_lm_head_int8"))
     return rc;
   return ok();
 }

@@ -8,6 +8,10 @@
 //
 // One wave per (token, 1024 columns): each lane loads 16 codes as one 16-byte load and stores 16 bf16 as
 // two 16-byte stores.  The kernel moves T*H bytes in and 2*T*H out; at decode sizes it is latency-bound.
+//
+// The same table as the output head ("vllm-quantpack 0.1.0", exl3/embedding.py, `Exl3EmbeddingMethod.apply`):
+// logits[m, v] = bf16(sum_h x[m, h] * w[v, h]) with every weight rounded once, w[v, h] = bf16(q[v, h] * s[v]),
+// as the page dequantizes the table in bf16 before its linear map.  See lm_head_int8_kernel.
 #include "exl3_device.hpp"
 #include "exl3_internal.hpp"
 
@@ -50,7 +54,172 @@ __global__ __launch_bounds__(256) void embed_int8_kernel(uint16_t* __restrict__ 
   dst[1] = (u32x4){o[4], o[5], o[6], o[7]};
 }
 
+// ---------------------------------------------------------------------------------------------------
+// Output head over the int8 table.  One wave per 32 table rows (two 16-row MFMA groups) streams those rows
+// once over all H; the x rows (up to 16 * MR) are the MFMA's other operand and stay in the caches.
+//
+// Operands of v_mfma_f32_16x16x32_bf16: A = 16 table rows x 32 features, B = 32 features x 16 x rows.
+// Lane l holds A row (l % 16) and B column (l % 16), features 8 * (l / 16) .. +8 of the instruction's 32.
+// The 64 features of one step are split so that lane l owns features 16 * (l / 16) .. +16 of the step in
+// both operands: one 16-byte load of int8 codes and two of bf16 x; the first 8 feed the first MFMA and the
+// last 8 the second (the same permutation of the summation index on both sides).
+//
+// The weight: the code byte is biased to unsigned (q + 128, one xor per 4 codes), converted with the
+// unsigned-byte conversion and scaled by fma(q + 128, s, -128 s) = q * s, exact in fp32 (at most 16
+// significant bits), then rounded to bf16 by the hardware conversion: the page's bf16(q * s).
+// The result D: lane l holds x row (l % 16) and table rows 4 * (l / 16) .. +4, written as 8 bytes when
+// the output's base and row stride allow it (vec_store), else element by element.
+// ---------------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kHeadRowsPerWave = 32;
+
+__device__ __forceinline__ bf16x8 head_weights(uint32_t w0, uint32_t w1, float s, float c) {
+  uint32_t o[4];
+  const uint32_t u[2] = {w0 ^ 0x80808080u, w1 ^ 0x80808080u};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float f0 = fmaf(float(u[j] & 0xFFu), s, c), f1 = fmaf(float((u[j] >> 8) & 0xFFu), s, c);
+    const float f2 = fmaf(float((u[j] >> 16) & 0xFFu), s, c), f3 = fmaf(float(u[j] >> 24), s, c);
+    o[2 * j] = f32x2_to_bf16x2(f0, f1);
+    o[2 * j + 1] = f32x2_to_bf16x2(f2, f3);
+  }
+  return __builtin_bit_cast(bf16x8, (u32x4){o[0], o[1], o[2], o[3]});
+}
+
+__device__ __forceinline__ float4v mfma_bf16(bf16x8 a, bf16x8 b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// MR groups of 16 x rows (M <= 16 * MR); U steps of 64 features loaded before they are used.
+template <int MR, int U>
+__global__ __launch_bounds__(256) void lm_head_int8_kernel(uint16_t* __restrict__ out, int64_t ldo,
+                                                           const uint16_t* __restrict__ x, int M,
+                                                           const int8_t* __restrict__ table,
+                                                           const uint16_t* __restrict__ scale, int64_t V, int64_t H,
+                                                           bool vec_store) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, quarter = lane >> 4;
+  const int64_t v0 = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kHeadRowsPerWave;
+  if (v0 >= V) return;
+
+  const int8_t* trow[2];
+  bool tok[2];
+  float s[2], c[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int64_t v = v0 + 16 * g + r16;
+    tok[g] = v < V;
+    trow[g] = table + (tok[g] ? v : 0) * H + 16 * quarter;
+    s[g] = tok[g] ? bf16_to_f32(scale[v]) : 0.0f;
+    c[g] = -128.0f * s[g];
+  }
+  const uint16_t* xrow[MR];
+  bool xok[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    const int m = 16 * r + r16;
+    xok[r] = m < M;
+    xrow[r] = x + int64_t(xok[r] ? m : 0) * H + 16 * quarter;
+  }
+
+  float4v acc[MR][2];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) acc[r][0] = acc[r][1] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto step = [&](const u32x4 (&q)[2], const u32x4 (&xb)[MR][2]) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const bf16x8 w0 = head_weights(q[g][0], q[g][1], s[g], c[g]);
+      const bf16x8 w1 = head_weights(q[g][2], q[g][3], s[g], c[g]);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        acc[r][g] = mfma_bf16(w0, __builtin_bit_cast(bf16x8, xb[r][0]), acc[r][g]);
+        acc[r][g] = mfma_bf16(w1, __builtin_bit_cast(bf16x8, xb[r][1]), acc[r][g]);
+      }
+    }
+  };
+
+  int64_t h = 0;
+  for (; h + 64 * U <= H; h += 64 * U) {
+    u32x4 q[U][2], xb[U][MR][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        q[u][g] = tok[g] ? *reinterpret_cast<const u32x4*>(trow[g] + h + 64 * u) : zero;
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(xrow[r] + h + 64 * u);
+        xb[u][r][0] = xok[r] ? p[0] : zero;
+        xb[u][r][1] = xok[r] ? p[1] : zero;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) step(q[u], xb[u]);
+  }
+  for (; h < H; h += 64) {
+    u32x4 q[2], xb[MR][2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) q[g] = tok[g] ? *reinterpret_cast<const u32x4*>(trow[g] + h) : zero;
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(xrow[r] + h);
+      xb[r][0] = xok[r] ? p[0] : zero;
+      xb[r][1] = xok[r] ? p[1] : zero;
+    }
+    step(q, xb);
+  }
+
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    if (!xok[r]) continue;
+    uint16_t* orow = out + int64_t(16 * r + r16) * ldo;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int64_t v = v0 + 16 * g + 4 * quarter;
+      const uint32_t lo = f32x2_to_bf16x2(acc[r][g][0], acc[r][g][1]);
+      const uint32_t hi = f32x2_to_bf16x2(acc[r][g][2], acc[r][g][3]);
+      if (vec_store && v + 4 <= V) {
+        *reinterpret_cast<uint2*>(orow + v) = make_uint2(lo, hi);
+      } else {
+        const uint16_t e[4] = {uint16_t(lo), uint16_t(lo >> 16), uint16_t(hi), uint16_t(hi >> 16)};
+        for (int i = 0; i < 4 && v + i < V; ++i) orow[v + i] = e[i];
+      }
+    }
+  }
+}
+
+template <int MR, int U>
+void launch_head_mr(uint16_t* out, int64_t ldo, const uint16_t* x, int M, const int8_t* table, const uint16_t* scale,
+                    int64_t V, int64_t H, bool vec_store, hipStream_t stream) {
+  const int64_t waves = (V + kHeadRowsPerWave - 1) / kHeadRowsPerWave;
+  hipLaunchKernelGGL((lm_head_int8_kernel<MR, U>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, out, ldo,
+                     x, M, table, scale, V, H, vec_store);
+}
+
 }  // namespace
+
+// x rows in chunks of up to 64 (four 16-row MFMA groups); each chunk streams the whole table once.
+hipError_t launch_lm_head_int8(void* out, int64_t ldo, const void* x, int64_t M, const int8_t* table,
+                               const void* scale, int64_t V, int64_t H, hipStream_t stream) {
+  const bool vec_store = ldo % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0;
+  for (int64_t m0 = 0; m0 < M; m0 += 64) {
+    const int rows = int(M - m0 < 64 ? M - m0 : 64);
+    uint16_t* o = static_cast<uint16_t*>(out) + m0 * ldo;
+    const uint16_t* xs = static_cast<const uint16_t*>(x) + m0 * H;
+    const uint16_t* sc = static_cast<const uint16_t*>(scale);
+    switch ((rows + 15) / 16) {
+      case 1: launch_head_mr<1, 4>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream); break;
+      case 2: launch_head_mr<2, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream); break;
+      case 3: launch_head_mr<3, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream); break;
+      default: launch_head_mr<4, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream); break;
+    }
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_embed_int8(void* out, const int8_t* table, const void* scale, int64_t V, int64_t H,
                              const int32_t* ids, int64_t T, hipStream_t stream) {

@@ -67,6 +67,9 @@ _SIGS = {
     "exl3_moe_bank_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(Bank), ctypes.c_uint,
                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "exl3_lm_head_int8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_void_p]),
     "exl3_embed_int8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
     "exl3_decode_tiles": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
@@ -212,6 +215,27 @@ def embed_int8(table, scale, ids, out=None):
     if out.shape != (T, H):
         raise ValueError(f"out: shape {tuple(out.shape)} != ({T}, {H})")
     _check(lib().exl3_embed_int8(_ptr(out), _ptr(table), _ptr(scale), V, H, _ptr(ids), T, _stream(table.device)))
+    return out
+
+
+def lm_head_int8(x, table, scale, out=None):
+    """bf16 logits [M, V] = x [M, H] . bf16(table * scale)^T for an int8 [V, H] table with bf16 [V] row
+    scales; `out` may be a wider [M, ldo] buffer's leading V columns."""
+    _need(x, "x", torch.bfloat16)
+    _need(table, "table", torch.int8)
+    _need(scale, "scale", torch.bfloat16)
+    V, H = table.shape
+    if scale.shape != (V,):
+        raise ValueError(f"scale: shape {tuple(scale.shape)} != ({V},)")
+    if x.dim() != 2 or x.shape[1] != H:
+        raise ValueError(f"x: shape {tuple(x.shape)}, want [M, {H}]")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.bfloat16, device=x.device)
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or out.shape != (M, V) or out.stride(1) != 1:
+        raise ValueError(f"out: want bf16 [{M}, {V}] with unit column stride")
+    _check(lib().exl3_lm_head_int8(_ptr(out), out.stride(0), _ptr(x), M, _ptr(table), _ptr(scale), V, H,
+                                   _stream(x.device)))
     return out
 
 

@@ -182,3 +182,17 @@ def test_gemm_split_plan():
             assert exl3.linear_workspace_bytes(M, IC, OC) >= s * tiles * 65536 + M * IC * 2
     assert L.exl3_gemm_splits(200, 2048, 256) == 4
     assert L.exl3_gemm_splits(0, 2048, 256) == 1 and L.exl3_gemm_splits(4, 100, 256) == 1
+
+
+def test_lm_head_validation():
+    """Host-side checks of the output head (no launch): H a positive multiple of 64, ldo >= V, M >= 0, non-null and aligned pointers; M == 0 is a no-op."""
+    L = exl3.lib()
+    f = L.exl3_lm_head_int8
+    assert f(FAKE, 100, FAKE, 2, FAKE, FAKE, 100, 96, None) == exl3.EINVAL and "H" in exl3.last_error()
+    assert f(FAKE, 99, FAKE, 2, FAKE, FAKE, 100, 128, None) == exl3.EINVAL and "ldo" in exl3.last_error()
+    assert f(FAKE, 100, FAKE, -1, FAKE, FAKE, 100, 128, None) == exl3.EINVAL and "M" in exl3.last_error()
+    assert f(FAKE, 100, FAKE, 2, FAKE, FAKE, 0, 128, None) == exl3.EINVAL and "V" in exl3.last_error()
+    assert f(FAKE, 100, None, 2, FAKE, FAKE, 100, 128, None) == exl3.EINVAL and "null" in exl3.last_error()
+    assert f(FAKE, 100, FAKE + 8, 2, FAKE, FAKE, 100, 128, None) == exl3.EINVAL and "aligned" in exl3.last_error()
+    assert f(FAKE + 1, 100, FAKE, 2, FAKE, FAKE, 100, 128, None) == exl3.EINVAL and "aligned" in exl3.last_error()
+    assert f(None, 100, None, 0, None, None, 100, 128, None) == exl3.OK
