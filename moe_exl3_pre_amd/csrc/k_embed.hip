@@ -55,8 +55,11 @@ __global__ __launch_bounds__(256) void embed_int8_kernel(uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------------------
-// Output head over the int8 table.  One wave per 32 table rows (two 16-row MFMA groups) streams those rows
-// once over all H; the x rows (up to 16 * MR) are the MFMA's other operand and stay in the caches.
+// Output head over the int8 table.  A workgroup of 4 waves owns 16 * G table rows; its waves split the
+// H/64 feature steps into 4 contiguous parts, each wave streams its part of those rows once, and wave 0
+// adds the four partial tiles from LDS in part order.  The x rows (up to 16 * MR) are the MFMA's other
+// operand and come from the caches.  Small work items (V / 16G workgroups) keep the last round of
+// workgroups short; more rows per wave (G) amortize the x loads when many x rows are live.
 //
 // Operands of v_mfma_f32_16x16x32_bf16: A = 16 table rows x 32 features, B = 32 features x 16 x rows.
 // Lane l holds A row (l % 16) and B column (l % 16), features 8 * (l / 16) .. +8 of the instruction's 32.
@@ -69,10 +72,13 @@ __global__ __launch_bounds__(256) void embed_int8_kernel(uint16_t* __restrict__ 
 // significant bits), then rounded to bf16 by the hardware conversion: the page's bf16(q * s).
 // The result D: lane l holds x row (l % 16) and table rows 4 * (l / 16) .. +4, written as 8 bytes when
 // the output's base and row stride allow it (vec_store), else element by element.
+//
+// The summation order of a logit depends only on H (steps in order within a part, parts in order), not on
+// M, G or MR, so a row's logits are the same bits whatever else is in the batch.
 // ---------------------------------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kHeadRowsPerWave = 32;
+constexpr int kHeadParts = 4;   // waves per workgroup, each a contiguous quarter of the feature steps
 
 __device__ __forceinline__ bf16x8 head_weights(uint32_t w0, uint32_t w1, float s, float c) {
   uint32_t o[4];
@@ -91,23 +97,26 @@ __device__ __forceinline__ float4v mfma_bf16(bf16x8 a, bf16x8 b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// MR groups of 16 x rows (M <= 16 * MR); U steps of 64 features loaded before they are used.
-template <int MR, int U>
+// MR groups of 16 x rows (M <= 16 * MR), G groups of 16 table rows per workgroup, U steps of 64 features
+// loaded before they are used.
+template <int MR, int G, int U>
 __global__ __launch_bounds__(256) void lm_head_int8_kernel(uint16_t* __restrict__ out, int64_t ldo,
                                                            const uint16_t* __restrict__ x, int M,
                                                            const int8_t* __restrict__ table,
                                                            const uint16_t* __restrict__ scale, int64_t V, int64_t H,
                                                            bool vec_store) {
-  const int lane = threadIdx.x & 63;
+  __shared__ float4v red[kHeadParts][MR * G][64];
+  const int lane = threadIdx.x & 63, part = threadIdx.x >> 6;
   const int r16 = lane & 15, quarter = lane >> 4;
-  const int64_t v0 = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kHeadRowsPerWave;
-  if (v0 >= V) return;
+  const int64_t v0 = int64_t(blockIdx.x) * 16 * G;
+  const int64_t steps = H / 64;
+  const int64_t h_lo = steps * part / kHeadParts * 64, h_hi = steps * (part + 1) / kHeadParts * 64;
 
-  const int8_t* trow[2];
-  bool tok[2];
-  float s[2], c[2];
+  const int8_t* trow[G];
+  bool tok[G];
+  float s[G], c[G];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
+  for (int g = 0; g < G; ++g) {
     const int64_t v = v0 + 16 * g + r16;
     tok[g] = v < V;
     trow[g] = table + (tok[g] ? v : 0) * H + 16 * quarter;
@@ -123,14 +132,16 @@ __global__ __launch_bounds__(256) void lm_head_int8_kernel(uint16_t* __restrict_
     xrow[r] = x + int64_t(xok[r] ? m : 0) * H + 16 * quarter;
   }
 
-  float4v acc[MR][2];
+  float4v acc[MR][G];
 #pragma unroll
-  for (int r = 0; r < MR; ++r) acc[r][0] = acc[r][1] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[r][g] = (float4v){0.f, 0.f, 0.f, 0.f};
 
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  auto step = [&](const u32x4 (&q)[2], const u32x4 (&xb)[MR][2]) {
+  auto step = [&](const u32x4 (&q)[G], const u32x4 (&xb)[MR][2]) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < G; ++g) {
       const bf16x8 w0 = head_weights(q[g][0], q[g][1], s[g], c[g]);
       const bf16x8 w1 = head_weights(q[g][2], q[g][3], s[g], c[g]);
 #pragma unroll
@@ -141,13 +152,13 @@ __global__ __launch_bounds__(256) void lm_head_int8_kernel(uint16_t* __restrict_
     }
   };
 
-  int64_t h = 0;
-  for (; h + 64 * U <= H; h += 64 * U) {
-    u32x4 q[U][2], xb[U][MR][2];
+  int64_t h = h_lo;
+  for (; h + 64 * U <= h_hi; h += 64 * U) {
+    u32x4 q[U][G], xb[U][MR][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int g = 0; g < G; ++g)
         q[u][g] = tok[g] ? *reinterpret_cast<const u32x4*>(trow[g] + h + 64 * u) : zero;
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
@@ -159,10 +170,10 @@ __global__ __launch_bounds__(256) void lm_head_int8_kernel(uint16_t* __restrict_
 #pragma unroll
     for (int u = 0; u < U; ++u) step(q[u], xb[u]);
   }
-  for (; h < H; h += 64) {
-    u32x4 q[2], xb[MR][2];
+  for (; h < h_hi; h += 64) {
+    u32x4 q[G], xb[MR][2];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) q[g] = tok[g] ? *reinterpret_cast<const u32x4*>(trow[g] + h) : zero;
+    for (int g = 0; g < G; ++g) q[g] = tok[g] ? *reinterpret_cast<const u32x4*>(trow[g] + h) : zero;
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
       const u32x4* p = reinterpret_cast<const u32x4*>(xrow[r] + h);
@@ -172,15 +183,25 @@ __global__ __launch_bounds__(256) void lm_head_int8_kernel(uint16_t* __restrict_
     step(q, xb);
   }
 
+  // partial tiles to LDS; wave 0 adds them in part order and writes the logits
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int g = 0; g < G; ++g) red[part][r * G + g][lane] = acc[r][g];
+  __syncthreads();
+  if (part != 0) return;
 #pragma unroll
   for (int r = 0; r < MR; ++r) {
     if (!xok[r]) continue;
     uint16_t* orow = out + int64_t(16 * r + r16) * ldo;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < G; ++g) {
+      float4v t = red[0][r * G + g][lane];
+#pragma unroll
+      for (int k = 1; k < kHeadParts; ++k) t += red[k][r * G + g][lane];
       const int64_t v = v0 + 16 * g + 4 * quarter;
-      const uint32_t lo = f32x2_to_bf16x2(acc[r][g][0], acc[r][g][1]);
-      const uint32_t hi = f32x2_to_bf16x2(acc[r][g][2], acc[r][g][3]);
+      const uint32_t lo = f32x2_to_bf16x2(t[0], t[1]);
+      const uint32_t hi = f32x2_to_bf16x2(t[2], t[3]);
       if (vec_store && v + 4 <= V) {
         *reinterpret_cast<uint2*>(orow + v) = make_uint2(lo, hi);
       } else {
@@ -191,31 +212,33 @@ __global__ __launch_bounds__(256) void lm_head_int8_kernel(uint16_t* __restrict_
   }
 }
 
-template <int MR, int U>
-void launch_head_mr(uint16_t* out, int64_t ldo, const uint16_t* x, int M, const int8_t* table, const uint16_t* scale,
-                    int64_t V, int64_t H, bool vec_store, hipStream_t stream) {
-  const int64_t waves = (V + kHeadRowsPerWave - 1) / kHeadRowsPerWave;
-  hipLaunchKernelGGL((lm_head_int8_kernel<MR, U>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, out, ldo,
-                     x, M, table, scale, V, H, vec_store);
+template <int MR, int G, int U>
+void launch_head(uint16_t* out, int64_t ldo, const uint16_t* x, int M, const int8_t* table, const uint16_t* scale,
+                 int64_t V, int64_t H, bool vec_store, hipStream_t stream) {
+  const int64_t blocks = (V + 16 * G - 1) / (16 * G);
+  hipLaunchKernelGGL((lm_head_int8_kernel<MR, G, U>), dim3((unsigned)blocks), dim3(64 * kHeadParts), 0, stream, out,
+                     ldo, x, M, table, scale, V, H, vec_store);
 }
 
 }  // namespace
 
-// x rows in chunks of up to 64 (four 16-row MFMA groups); each chunk streams the whole table once.
+// x rows in chunks of up to 64 (four 16-row MFMA groups); each chunk streams the whole table once.  Rows per
+// workgroup by the number of live x rows, from a sweep at V = 248,320, H = 5120: 16 while few x lanes load
+// (M <= 4), 32 up to 8 rows, 64 above (the x loads then cost as much as the table's).
 hipError_t launch_lm_head_int8(void* out, int64_t ldo, const void* x, int64_t M, const int8_t* table,
                                const void* scale, int64_t V, int64_t H, hipStream_t stream) {
   const bool vec_store = ldo % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0;
+  const uint16_t* sc = static_cast<const uint16_t*>(scale);
   for (int64_t m0 = 0; m0 < M; m0 += 64) {
     const int rows = int(M - m0 < 64 ? M - m0 : 64);
     uint16_t* o = static_cast<uint16_t*>(out) + m0 * ldo;
     const uint16_t* xs = static_cast<const uint16_t*>(x) + m0 * H;
-    const uint16_t* sc = static_cast<const uint16_t*>(scale);
-    switch ((rows + 15) / 16) {
-      case 1: launch_head_mr<1, 4>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream); break;
-      case 2: launch_head_mr<2, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream); break;
-      case 3: launch_head_mr<3, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream); break;
-      default: launch_head_mr<4, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream); break;
-    }
+    if (rows <= 4) launch_head<1, 1, 4>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream);
+    else if (rows <= 8) launch_head<1, 2, 4>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream);
+    else if (rows <= 16) launch_head<1, 4, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream);
+    else if (rows <= 32) launch_head<2, 2, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream);
+    else if (rows <= 48) launch_head<3, 1, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream);
+    else launch_head<4, 1, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream);
     if (hipError_t e = hipGetLastError()) return e;
   }
   return hipSuccess;

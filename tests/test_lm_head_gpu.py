@@ -55,6 +55,32 @@ def test_lm_head_rows(M):
     _check(_bits(out), x, table, scale)
 
 
+@pytest.mark.parametrize("M", [3, 7, 12, 30])
+def test_lm_head_batched_steps(M):
+    """H = 2112 is 33 feature steps: parts of 8, 8, 8 and 9 steps, so the batched loads and the single-step
+    tail both run in every row-group configuration."""
+    V, H = 997, 2112
+    rng, table, scale = _table(60 + M, V, H)
+    x = _bf16_bits(rng.normal(size=(M, H)))
+    log(f"lm_head V={V} H={H} M={M}")
+    out = exl3.lm_head_int8(_to_dev(x), _to_dev(table, torch.int8), _to_dev(scale))
+    torch.cuda.synchronize()
+    _check(_bits(out), x, table, scale)
+
+
+def test_lm_head_batch_invariant():
+    """A row's logits do not depend on the other rows in the call: the summation order depends only on H,
+    whatever row-group configuration the call's M selects."""
+    V, H = 997, 2112
+    rng, table, scale = _table(70, V, H)
+    x = _to_dev(_bf16_bits(rng.normal(size=(70, H))))
+    t, s = _to_dev(table, torch.int8), _to_dev(scale)
+    full = _bits(exl3.lm_head_int8(x, t, s))
+    for M in (1, 4, 6, 9, 17, 33, 49):
+        part = _bits(exl3.lm_head_int8(x[:M].contiguous(), t, s))
+        assert np.array_equal(part, full[:M]), M
+
+
 def test_lm_head_strided_output_keeps_other_columns():
     V, H, M, ldo = 96, 128, 3, 132
     rng, table, scale = _table(50, V, H)
