@@ -326,3 +326,35 @@ def lm_head_int8(x_bits: np.ndarray, table_q: np.ndarray, scale_bits: np.ndarray
     s = bf16_bits_to_f64(np.asarray(scale_bits, dtype=np.uint16).reshape(-1))
     w = bf16_bits_to_f64(f64_to_bf16_bits(q * s[:, None]))
     return f64_to_bf16_bits(x @ w.T)
+
+
+# ---------------------------------------------------------------------------------------------
+# Dense MLP block: merged gate/up, SiLU * mul, down
+# ---------------------------------------------------------------------------------------------
+# [quantpack] exl3/linear.py module docstring: gate and up are two shards of one fused gate_up layer (their
+# own EXL3 tensors, possibly of different K) whose outputs are concatenated; the model's activation then
+# takes silu(gate) * up and feeds down_proj.  Reading: the serving stack's dense block, where the fused
+# layer's output is bf16, the activation is evaluated on those bf16 values and rounded once to bf16, and
+# down_proj consumes that bf16 tensor.  (The MoE bank above keeps its intermediates in fp32 instead.)
+
+def silu_mul_bf16(g_bits: np.ndarray, u_bits: np.ndarray) -> np.ndarray:
+    """h = bf16(silu(g) * u) for bf16 bit patterns g, u of the same shape; returns bf16 bit patterns."""
+    g = bf16_bits_to_f64(np.asarray(g_bits, dtype=np.uint16))
+    u = bf16_bits_to_f64(np.asarray(u_bits, dtype=np.uint16))
+    return f64_to_bf16_bits(silu(g) * u)
+
+
+def mlp_forward(x, gate: dict, up: dict, down: dict, act: str = "f64", round_mid: bool = True) -> np.ndarray:
+    """down( silu(gate(x)) * up(x) ), float64 before the output's bf16 rounding.
+
+    gate, up and down are dicts with keys code, K, s_in, rin, rout, s_out (the arguments of `linear`).  With
+    round_mid the gate and up outputs are rounded to bf16 and the activation is rounded to bf16 (the reading
+    above); without it every intermediate stays float64.  `act` is passed to each projection."""
+    def proj(v, p):
+        return linear(v, p["code"], p["K"], p["s_in"], p["rin"], p["rout"], p["s_out"], act=act)
+    g, u = proj(x, gate), proj(x, up)
+    if round_mid:
+        h = bf16_bits_to_f64(silu_mul_bf16(f64_to_bf16_bits(g), f64_to_bf16_bits(u)))
+    else:
+        h = silu(g) * u
+    return proj(h, down)

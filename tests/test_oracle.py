@@ -544,3 +544,57 @@ def test_lm_head_sign_and_power_of_two_scaling_are_exact():
     base = O.bf16_bits_to_f64(O.lm_head_int8(_bits(x), table, sbits))
     assert np.array_equal(O.bf16_bits_to_f64(O.lm_head_int8(_bits(-x), table, sbits)), -base)
     assert np.array_equal(O.bf16_bits_to_f64(O.lm_head_int8(_bits(4 * x), table, sbits)), 4 * base)
+
+
+# ------------------------------------------------------------------------------------------ dense MLP block
+
+def test_silu_identities():
+    """silu(g) - silu(-g) = g exactly in real arithmetic, and silu(g) + silu(-g) = g tanh(g/2)."""
+    g = np.linspace(-12, 12, 97)
+    assert np.allclose(O.silu(g) - O.silu(-g), g, rtol=0, atol=1e-13)
+    assert np.allclose(O.silu(g) + O.silu(-g), g * np.tanh(g / 2), rtol=0, atol=1e-13)
+
+
+def test_silu_mul_hand_values():
+    """silu(1) = 1 / (1 + e^-1) = 0.7310585...; 8 significant bits: 1.4621 x 2^-1 -> 187/128 x 2^-1 =
+    0.73046875 = 0x3F3B.  silu(64) * 3 rounds to 192 = 0x4340 (silu(64) = 64 (1 - 1.6e-28)).  A zero gate or
+    a zero up gives 0."""
+    one, three, s64 = 0x3F80, 0x4040, 0x4280
+    assert O.silu_mul_bf16(np.array([one]), np.array([one]))[0] == 0x3F3B
+    assert O.silu_mul_bf16(np.array([s64]), np.array([three]))[0] == 0x4340
+    assert O.bf16_bits_to_f64(O.silu_mul_bf16(np.array([0, one]), np.array([one, 0]))).tolist() == [0.0, 0.0]
+
+
+def _mlp_case(seed, IC, I, Kg, Ku, Kd):
+    rng = np.random.default_rng(seed)
+
+    def proj(ic, oc, K, shared=None):
+        p = dict(code=rng.integers(-32768, 32768, size=(ic // 16, oc // 16, 16 * K), dtype=np.int16), K=K,
+                 rout=rng.uniform(0.5, 1.5, size=oc), s_out=rng.choice([-1.0, 1.0], size=oc))
+        p.update(shared or dict(s_in=rng.choice([-1.0, 1.0], size=ic), rin=rng.uniform(0.5, 1.5, size=ic)))
+        return p
+    shared = dict(s_in=rng.choice([-1.0, 1.0], size=IC), rin=rng.uniform(0.5, 1.5, size=IC))
+    x = O.bf16_bits_to_f64(O.f64_to_bf16_bits(rng.normal(size=(3, IC))))
+    return x, proj(IC, I, Kg, shared), proj(IC, I, Ku, shared), proj(I, IC, Kd)
+
+
+def test_mlp_without_rounding_is_the_expert_forward():
+    """With every intermediate kept in float64 and unit rin/rout, the block is the MoE bank's expert MLP
+    (a separately pinned function): w1 = gate, w3 = up, w2 = down, suh = s_in, svh = s_out."""
+    x, gate, up, down = _mlp_case(31, 256, 384, 2, 2, 3)
+    for p in (gate, up, down):
+        p["rin"] = np.ones_like(p["rin"])
+        p["rout"] = np.ones_like(p["rout"])
+    e = dict(w1=gate["code"], w3=up["code"], w2=down["code"], k_gu=2, k_d=3, w1_suh=gate["s_in"],
+             w3_suh=up["s_in"], w1_svh=gate["s_out"], w3_svh=up["s_out"], w2_suh=down["s_in"], w2_svh=down["s_out"])
+    a = O.mlp_forward(x, gate, up, down, round_mid=False)
+    assert np.allclose(a, O.expert_forward(x, e), rtol=1e-12, atol=1e-12)
+
+
+def test_mlp_rounding_is_small_and_zero_input_gives_zero():
+    x, gate, up, down = _mlp_case(32, 256, 384, 2, 3, 3)
+    a = O.mlp_forward(x, gate, up, down)
+    b = O.mlp_forward(x, gate, up, down, round_mid=False)
+    rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert 1e-5 < rel < 1e-2
+    assert np.all(O.mlp_forward(np.zeros_like(x), gate, up, down) == 0)
