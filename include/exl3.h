@@ -207,6 +207,38 @@ int exl3_moe_bank_forward(void* out, const void* x, int64_t T,
                           const exl3_bank* bank, unsigned flags, void* ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------------------
+ * Dense MLP block ("vllm-quantpack 0.1.0", exl3/linear.py module docstring: gate and up are two shards of
+ * one fused gate_up layer, each its own EXL3 tensor of any K, whose outputs are concatenated; the model's
+ * activation takes silu(gate) * up and feeds down_proj):
+ *
+ *   gu  = [gate(x) | up(x)]          one exl3_linear_multi_into call, bf16 [M, 2I] in the workspace
+ *   h   = bf16(silu(g) * u)          exl3_silu_mul on gu (fp32 arithmetic), bf16 [M, I] in the workspace
+ *   out = down(h)                    one exl3_linear_into call, bf16 [M, H]
+ *
+ *   out   bf16 [M, H] row-major, 16-byte aligned;  x  bf16 [M, H] row-major, 16-byte aligned.
+ *   gate, up   shard descriptors over IC = H with OC = I (their col0 is ignored: gate fills columns
+ *              [0, I) of gu and up [I, 2I));  down   a shard descriptor over IC = I with OC = H (col0 ignored).
+ *   flags      as for exl3_linear_into, applied to every projection.
+ *   ws         exl3_mlp_workspace_bytes(M, H, I, gate, up, flags) bytes, 256-byte aligned, zeroed once
+ *              before first use (the projections' counter area sits at its start); the calls it makes are
+ *              stream-ordered, so they share it.
+ * H and I positive multiples of 128.  The result is bitwise identical to the three calls made one by one.
+ * M == 0 is a no-op.  Returns EXL3_OK / EXL3_EINVAL / EXL3_EWORKSPACE / EXL3_EUNSUPPORTED / EXL3_ELAUNCH
+ * (from the first step that fails; the message names the argument).
+ * ------------------------------------------------------------------------------------------------ */
+size_t exl3_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, const exl3_shard* gate, const exl3_shard* up,
+                                unsigned flags);
+int exl3_mlp_forward(void* out, const void* x, int64_t M, int64_t H, int64_t I, const exl3_shard* gate,
+                     const exl3_shard* up, const exl3_shard* down, unsigned flags, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* The block's activation on its own: h bf16 [M, I] (16-byte aligned, row-major) = bf16(silu(g) * u) with
+ * g = gu[m, j] and u = gu[m, I + j] of a bf16 [M, 2I] input (16-byte aligned); silu(g) = g / (1 + exp(-g))
+ * in fp32, one round-to-nearest-even to bf16.  I a positive multiple of 8; M == 0 is a no-op.
+ * Returns EXL3_OK / EXL3_EINVAL / EXL3_ELAUNCH. */
+int exl3_silu_mul(void* h, const void* gu, int64_t M, int64_t I, void* stream);
+
+/* --------------------------------------------------------------------------------------------------
  * int8 embedding rows gathered by token id and dequantized ("vllm-quantpack 0.1.0", exl3/embedding.py,
  * `Exl3EmbeddingMethod.embedding`: the table stays int8 with one scale per row; the gathered rows are
  * converted to the scale's dtype and multiplied by their row's scale, so the table is never materialised

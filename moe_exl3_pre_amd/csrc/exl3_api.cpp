@@ -350,6 +350,8 @@ hipError_t launch_embed_int8(void* out, const int8_t* table, const void* scale, 
 // x [M, H] . bf16(table * scale)^T.
 hipError_t launch_lm_head_int8(void* out, int64_t ldo, const void* x, int64_t M, const int8_t* table,
                                const void* scale, int64_t V, int64_t H, hipStream_t stream);
+// dense MLP activation (k_mlp.hip): h bf16 [M, I] = bf16(silu(gu[:, :I]) * gu[:, I:]) of a bf16 [M, 2I] input.
+hipError_t launch_silu_mul(void* h, const void* gu, int64_t M, int64_t I, hipStream_t stream);
 }  // namespace exl3
 
 extern "C" {
@@ -533,6 +535,82 @@ int exl3_lm_head_int8(void* out, int64_t ldo, const void* x, int64_t M, const in
   if (!aligned(out, 2) || !aligned(scale, 2)) return fail(EXL3_EINVAL, "out/scale: not 2-byte aligned");
   if (int rc = launch_status(launch_lm_head_int8(out, ldo, x, M, table, scale, V, H, static_cast<hipStream_t>(stream)),
                              "exl3_lm_head_int8"))
+    return rc;
+  return ok();
+}
+
+// Dense MLP block: the workspace holds, in order, the projections' own workspace (its counter area first, so
+// zeroing the whole buffer once zeroes it), the gate_up output bf16 [M, 2I] and the activation bf16 [M, I].
+namespace {
+struct MlpLayout {
+  size_t inner, gu_off, h_off, total;
+};
+
+bool mlp_layout(int64_t M, int64_t H, int64_t I, const exl3_shard* gate, const exl3_shard* up, unsigned flags,
+                MlpLayout* L) {
+  exl3_shard gu[2] = {*gate, *up};
+  gu[0].col0 = 0;
+  gu[1].col0 = I;
+  const size_t a = exl3_linear_multi_workspace_bytes(M, H, 2, gu, flags);
+  const size_t b = exl3_linear_workspace_bytes(M, I, H, flags);
+  L->inner = align_up(a > b ? a : b);
+  L->gu_off = L->inner;
+  L->h_off = L->gu_off + align_up(size_t(M) * 2 * I * 2);
+  L->total = L->h_off + align_up(size_t(M) * I * 2);
+  return true;
+}
+
+int check_mlp(int64_t M, int64_t H, int64_t I, const exl3_shard* gate, const exl3_shard* up, const exl3_shard* down) {
+  if (M < 0) return fail(EXL3_EINVAL, "M: %lld is negative", (long long)M);
+  if (H < 128 || H % 128) return fail(EXL3_EINVAL, "H: %lld is not a positive multiple of 128", (long long)H);
+  if (I < 128 || I % 128) return fail(EXL3_EINVAL, "I: %lld is not a positive multiple of 128", (long long)I);
+  if (!gate || !up || !down) return fail(EXL3_EINVAL, "gate/up/down: null");
+  if (gate->OC != I || up->OC != I) return fail(EXL3_EINVAL, "gate/up: OC must equal I");
+  if (down->OC != H) return fail(EXL3_EINVAL, "down: OC must equal H");
+  return 0;
+}
+}  // namespace
+
+size_t exl3_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, const exl3_shard* gate, const exl3_shard* up,
+                                unsigned flags) {
+  if (M <= 0 || !gate || !up || H < 128 || H % 128 || I < 128 || I % 128) return align_up(kCounterBytes);
+  MlpLayout L;
+  mlp_layout(M, H, I, gate, up, flags, &L);
+  return L.total;
+}
+
+int exl3_mlp_forward(void* out, const void* x, int64_t M, int64_t H, int64_t I, const exl3_shard* gate,
+                     const exl3_shard* up, const exl3_shard* down, unsigned flags, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (int rc = check_flags(flags)) return rc;
+  if (int rc = check_mlp(M, H, I, gate, up, down)) return rc;
+  if (M == 0) return ok();
+  if (!ws) return fail(EXL3_EWORKSPACE, "ws: null");
+  if (!aligned(ws, kAlign)) return fail(EXL3_EINVAL, "ws: not %zu-byte aligned", kAlign);
+  MlpLayout L;
+  mlp_layout(M, H, I, gate, up, flags, &L);
+  if (ws_bytes < L.total)
+    return fail(EXL3_EWORKSPACE, "ws_bytes: %zu < %zu (exl3_mlp_workspace_bytes)", ws_bytes, L.total);
+  char* w = static_cast<char*>(ws);
+  exl3_shard gu[2] = {*gate, *up};
+  gu[0].col0 = 0;
+  gu[1].col0 = I;
+  if (int rc = exl3_linear_multi_into(w + L.gu_off, 2 * I, x, M, H, 2, gu, flags, w, L.inner, stream)) return rc;
+  if (int rc = launch_status(launch_silu_mul(w + L.h_off, w + L.gu_off, M, I, static_cast<hipStream_t>(stream)),
+                             "exl3_mlp_forward"))
+    return rc;
+  if (int rc = exl3_linear_into(out, H, 0, w + L.h_off, M, I, down->code, H, down->K, down->s_in, down->rin,
+                                down->rout, down->s_out, flags, w, L.inner, stream))
+    return rc;
+  return ok();
+}
+
+int exl3_silu_mul(void* h, const void* gu, int64_t M, int64_t I, void* stream) {
+  if (M < 0) return fail(EXL3_EINVAL, "M: %lld is negative", (long long)M);
+  if (I < 8 || I % 8) return fail(EXL3_EINVAL, "I: %lld is not a positive multiple of 8", (long long)I);
+  if (M == 0) return ok();
+  if (!h || !gu || !aligned(h, 16) || !aligned(gu, 16)) return fail(EXL3_EINVAL, "h/gu: null or not 16-byte aligned");
+  if (int rc = launch_status(launch_silu_mul(h, gu, M, I, static_cast<hipStream_t>(stream)), "exl3_silu_mul"))
     return rc;
   return ok();
 }

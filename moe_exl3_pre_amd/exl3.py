@@ -70,6 +70,14 @@ _SIGS = {
     "exl3_lm_head_int8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_void_p]),
+    "exl3_mlp_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                  ctypes.POINTER(Shard), ctypes.POINTER(Shard), ctypes.c_uint]),
+    "exl3_mlp_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.POINTER(Shard), ctypes.POINTER(Shard),
+                                        ctypes.POINTER(Shard), ctypes.c_uint, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]),
+    "exl3_silu_mul": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_void_p]),
     "exl3_embed_int8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
     "exl3_decode_tiles": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
@@ -193,6 +201,55 @@ def linear_multi_into(out, x, shards, flags: int = 0, ws=None):
         ws = alloc_workspace(lib().exl3_linear_multi_workspace_bytes(M, IC, len(shards), arr, flags), dev)
     _check(lib().exl3_linear_multi_into(_ptr(out), out.shape[1], _ptr(x), M, IC, len(shards), arr, flags, _ptr(ws),
                                         ws.numel(), _stream(dev)))
+    return out
+
+
+# ------------------------------------------------------------------------------------------ dense MLP block
+
+def _one_shard(s, IC, dev, name):
+    _need(s["code"], f"{name}.code", torch.int16, device=dev)
+    if s["code"].dim() != 3 or s["code"].shape[0] * 16 != IC or s["code"].shape[2] != 16 * s["K"]:
+        raise ValueError(f"{name}.code: shape {tuple(s['code'].shape)} does not match IC={IC}, K={s['K']}")
+    OC = s["code"].shape[1] * 16
+    for key, n in (("s_in", IC), ("rin", IC), ("rout", OC), ("s_out", OC)):
+        _need(s[key], f"{name}.{key}", torch.float16, (n,), dev)
+    return Shard(_ptr(s["code"]), OC, s["K"], 0, 0, _ptr(s["s_in"]), _ptr(s["rin"]), _ptr(s["rout"]), _ptr(s["s_out"]))
+
+
+def mlp_workspace_bytes(M: int, H: int, I: int, gate, up, flags: int = 0) -> int:
+    g, u = _one_shard(gate, H, gate["code"].device, "gate"), _one_shard(up, H, up["code"].device, "up")
+    return int(lib().exl3_mlp_workspace_bytes(M, H, I, ctypes.byref(g), ctypes.byref(u), flags))
+
+
+def mlp_forward(x, gate, up, down, out=None, flags: int = 0, ws=None):
+    """Dense MLP block: down(bf16(silu(gate(x)) * up(x))) for x bf16 [M, H]; gate, up and down are dicts with
+    code, K, s_in, rin, rout, s_out (gate and up over H -> I, down over I -> H).  See exl3_mlp_forward."""
+    dev = x.device
+    _need(x, "x", torch.bfloat16, device=dev)
+    M, H = x.shape
+    g, u = _one_shard(gate, H, dev, "gate"), _one_shard(up, H, dev, "up")
+    I = g.OC
+    d = _one_shard(down, I, dev, "down")
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (M, H), dev)
+    if ws is None:
+        ws = alloc_workspace(lib().exl3_mlp_workspace_bytes(M, H, I, ctypes.byref(g), ctypes.byref(u), flags), dev)
+    _check(lib().exl3_mlp_forward(_ptr(out), _ptr(x), M, H, I, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                  flags, _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def silu_mul(gu, out=None):
+    """bf16 [M, I] = bf16(silu(gu[:, :I]) * gu[:, I:]) of a bf16 [M, 2I] tensor; see exl3_silu_mul."""
+    _need(gu, "gu", torch.bfloat16)
+    M, I2 = gu.shape
+    if I2 % 2:
+        raise ValueError(f"gu: {I2} columns, want 2I")
+    if out is None:
+        out = torch.empty((M, I2 // 2), dtype=torch.bfloat16, device=gu.device)
+    _need(out, "out", torch.bfloat16, (M, I2 // 2), gu.device)
+    _check(lib().exl3_silu_mul(_ptr(out), _ptr(gu), M, I2 // 2, _stream(gu.device)))
     return out
 
 

@@ -128,3 +128,16 @@ def moe_case(seed: int, T: int = 256, E: int = 128, topk: int = 8, H: int = 2048
             w1_svh=sign_scale(rng, I), w3_svh=sign_scale(rng, I),
             w2_suh=sign_scale(rng, I), w2_svh=sign_scale(rng, H)))
     return dict(T=T, E=E, topk=topk, H=H, I=I, x=x, x_bits=xb, topk_ids=ids, topk_w=w, experts=experts)
+
+
+def mlp_case(seed: int, M: int, H: int, I: int, K_gate: int, K_up: int, K_down: int) -> dict:
+    """A dense MLP block: gate and up over H -> I sharing s_in / rin, down over I -> H with its own."""
+    rng = np.random.default_rng(seed)
+    x, xb = random_activations(rng, M, H)
+    s_in, rin = random_signs(rng, H), random_scales(rng, H)
+    gate, up = shard(rng, H, I, K_gate), shard(rng, H, I, K_up)
+    for d in (gate, up):
+        d.update(s_in=s_in, rin=rin)
+    down = shard(rng, I, H, K_down)
+    down.update(s_in=random_signs(rng, I), rin=random_scales(rng, I))
+    return dict(M=M, H=H, I=I, x=x, x_bits=xb, gate=gate, up=up, down=down)

@@ -196,3 +196,23 @@ def test_lm_head_validation():
     assert f(FAKE, 100, FAKE + 8, 2, FAKE, FAKE, 100, 128, None) == exl3.EINVAL and "aligned" in exl3.last_error()
     assert f(FAKE + 1, 100, FAKE, 2, FAKE, FAKE, 100, 128, None) == exl3.EINVAL and "aligned" in exl3.last_error()
     assert f(None, 100, None, 0, None, None, 100, 128, None) == exl3.OK
+
+
+def test_mlp_validation():
+    """Host-side checks of the dense MLP block (no launch)."""
+    L = exl3.lib()
+    g = exl3.Shard(FAKE, 256, 2, 0, 0, FAKE, FAKE, FAKE, FAKE)
+    d = exl3.Shard(FAKE, 128, 3, 0, 0, FAKE, FAKE, FAKE, FAKE)
+    call = lambda M, H, I, gate, up, down, ws=FAKE, nb=1 << 30: L.exl3_mlp_forward(
+        FAKE, FAKE, M, H, I, ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down), 0, ws, nb, None)
+    assert call(2, 100, 256, g, g, d) == exl3.EINVAL and "H" in exl3.last_error()
+    assert call(2, 128, 200, g, g, d) == exl3.EINVAL and "I" in exl3.last_error()
+    assert call(2, 128, 256, g, d, d) == exl3.EINVAL and "OC" in exl3.last_error()
+    assert call(2, 128, 256, g, g, g) == exl3.EINVAL and "down" in exl3.last_error()
+    assert call(2, 128, 256, g, g, d, ws=None) == exl3.EWORKSPACE
+    need = L.exl3_mlp_workspace_bytes(2, 128, 256, ctypes.byref(g), ctypes.byref(g), 0)
+    assert need >= 16384 + 2 * 512 * 2 + 2 * 256 * 2 and need % 256 == 0
+    assert call(2, 128, 256, g, g, d, nb=need - 1) == exl3.EWORKSPACE and "ws_bytes" in exl3.last_error()
+    assert call(0, 128, 256, g, g, d) == exl3.OK
+    assert L.exl3_silu_mul(FAKE, FAKE, 2, 12, None) == exl3.EINVAL
+    assert L.exl3_silu_mul(None, None, 0, 16, None) == exl3.OK

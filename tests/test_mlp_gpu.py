@@ -1,0 +1,112 @@
+"""GPU parity of the dense MLP block (merged gate/up, SiLU * mul, down) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import exl3_oracle as O
+from moe_exl3_pre_amd import exl3, synth
+from tests.helpers import bf16_to_f64, dev, log, rel_fro, shard_to_dev, to_dev, to_dev_x
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _oracle_args(p):
+    return dict(code=p["code"], K=p["K"], s_in=p["s_in"], rin=p["rin"], rout=p["rout"], s_out=p["s_out"])
+
+
+def _to_dev_case(c):
+    s_in, rin = to_dev(c["gate"]["s_in"]), to_dev(c["gate"]["rin"])
+    return (to_dev_x(c["x_bits"]), shard_to_dev(c["gate"], s_in, rin), shard_to_dev(c["up"], s_in, rin),
+            shard_to_dev(c["down"]))
+
+
+def _assert_close_mlp(got, ref16, ref64):
+    """The block's bar.  Its bf16 intermediates (the gate and up outputs, then h) are rounding decisions that
+    the GPU takes on fp32 sums and the oracle on fp64 sums, so an intermediate can land one unit apart (2^-8
+    of its value; about 0.4% of them at M = 200 here).  A row's few such h_j move each of its outputs by
+    their units times down's gain: up to 0.41% of the output rms measured (an output of 298 against 333,
+    where down applied to the same h gives 297.4).  Bars: relative Frobenius error <= 1e-2 against the exact
+    oracle and <= 4e-3 against the fp16-operand oracle; every element within 2^-8 |ref| + 2^-7 rms(ref); at
+    least 99% within the single-projection bar 2^-8 |ref| + 2^-10 rms(ref)."""
+    e64, e16 = rel_fro(got, ref64), rel_fro(got, ref16)
+    assert e64 <= 1e-2 and e16 <= 4e-3, (e64, e16)
+    rms = float(np.sqrt(np.mean(ref16 ** 2)))
+    d = np.abs(got - ref16)
+    assert np.all(d <= 2.0 ** -8 * np.abs(ref16) + 2.0 ** -7 * rms), float(np.max(d / rms))
+    assert np.mean(d <= 2.0 ** -8 * np.abs(ref16) + 2.0 ** -10 * rms) >= 0.99
+    log(f"  rel err {e64:.3e} (exact), {e16:.3e} (fp16 operands); worst |d|/rms {float(np.max(d)) / rms:.2e}")
+
+
+def test_silu_mul_against_oracle():
+    """fp32 silu on bf16 inputs, one bf16 rounding: equal to the fp64 oracle except where the exact value
+    lies within fp32 error of a bf16 rounding boundary (then one unit in the last place)."""
+    rng = np.random.default_rng(80)
+    M, I = 7, 1024
+    gu = rng.normal(scale=3.0, size=(M, 2 * I))
+    gu[0, :8] = [0.0, -0.0, 60.0, -60.0, 1e-3, -1e-3, 8.0, -8.0]
+    gu_bits = O.f64_to_bf16_bits(gu)
+    got = _bits(exl3.silu_mul(to_dev_x(gu_bits)))
+    torch.cuda.synchronize()
+    want = O.silu_mul_bf16(gu_bits[:, :I], gu_bits[:, I:])
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    sign_zero = ((got & 0x7FFF) == 0) & ((want & 0x7FFF) == 0)
+    assert np.all((diff <= 1) | sign_zero)
+    assert np.mean(got == want) >= 0.999
+
+
+@pytest.mark.parametrize("M", [1, 4, 8, 40, 200])
+def test_mlp_against_oracle(M):
+    """H = 512, I = 1024, gate K=2, up K=3, down K=3: the decode-phase kernel up to 128 rows, the GEMM above."""
+    c = synth.mlp_case(81 + M, M, 512, 1024, 2, 3, 3)
+    x, g, u, d = _to_dev_case(c)
+    log(f"mlp H=512 I=1024 M={M}")
+    out = exl3.mlp_forward(x, g, u, d)
+    torch.cuda.synchronize()
+    args = [_oracle_args(c[k]) for k in ("gate", "up", "down")]
+    ref16 = O.mlp_forward(c["x"], *args, act="f16")
+    ref64 = O.mlp_forward(c["x"], *args)
+    _assert_close_mlp(bf16_to_f64(out), ref16, ref64)
+
+
+@pytest.mark.parametrize("M", [3, 200])
+def test_mlp_equals_the_three_calls(M):
+    """The block is bitwise the merged gate_up call, the activation hook and the down call made one by one."""
+    c = synth.mlp_case(90 + M, M, 512, 1024, 3, 2, 4)
+    x, g, u, d = _to_dev_case(c)
+    out = exl3.mlp_forward(x, g, u, d)
+    gu = torch.empty((M, 2048), dtype=torch.bfloat16, device=dev())
+    exl3.linear_multi_into(gu, x, [dict(g, col0=0), dict(u, col0=1024)])
+    h = exl3.silu_mul(gu)
+    ref = torch.empty_like(out)
+    exl3.linear_into(ref, h, d["code"], d["K"], d["s_in"], d["rin"], d["rout"], d["s_out"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_mlp_rejects_mismatched_shapes():
+    c = synth.mlp_case(95, 2, 512, 1024, 2, 3, 3)
+    x, g, u, d = _to_dev_case(c)
+    with pytest.raises(ValueError):                       # the binding checks down's shape (I -> H)
+        exl3.mlp_forward(x, g, u, g)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_mlp_decoder_shapes_equal_the_three_calls(M):
+    """One decoder layer's block at full size (hidden 5120, intermediate 17408; gate K=2, up K=3, down K=3):
+    bitwise equal to the three calls, finite, and not all zero."""
+    c = synth.mlp_case(96 + M, M, 5120, 17408, 2, 3, 3)
+    x, g, u, d = _to_dev_case(c)
+    log(f"mlp H=5120 I=17408 M={M}")
+    out = exl3.mlp_forward(x, g, u, d)
+    gu = torch.empty((M, 2 * 17408), dtype=torch.bfloat16, device=dev())
+    exl3.linear_multi_into(gu, x, [dict(g, col0=0), dict(u, col0=17408)])
+    h = exl3.silu_mul(gu)
+    ref = torch.empty_like(out)
+    exl3.linear_into(ref, h, d["code"], d["K"], d["s_in"], d["rin"], d["rout"], d["s_out"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.isfinite(out.float()).all() and out.float().abs().max() > 0
