@@ -8,11 +8,13 @@ method's algorithmic bytes, IC*OC*K/8 per shard).  Weights rotate over 16 seeded
 256 MiB Infinity Cache cannot serve them.  Steps are captured once in a HIP graph and replayed between
 events recorded on the stream the kernels run on.
 
-Also reported (under "extra"): decode M = 2, 4, 8; prefill M=8192 gate_up and down (TFLOP/s); the int8
-embedding gather (T = 256 and 8192 ids over a 248,320 x 5120 table; GB/s of bytes moved); the MoE
-expert bank (T=256, E=128, top-8, H=2048, I=768; 3 rotated banks).
+Also reported (under "extra"): decode M = 2, 4, 8; prefill M=8192 gate_up and down (TFLOP/s); the MoE
+expert bank (T=256, E=128, top-8, H=2048, I=768; 3 rotated banks); the dense MLP block of one decoder
+layer (5120 -> 2 x 17408 -> 5120) at M = 1 and 8; the int8 embedding gather (T = 256 and 8192 ids over a
+248,320 x 5120 table) and the same table as the output head (M = 1 and 16; GB/s of bytes moved).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill] [--no-moe]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill] [--no-moe] [--no-mlp]
+                    [--no-embed]
     python bench.py --pmc-ref ...     # eager launches plus a 1 GiB copy, for counter runs
 """
 from __future__ import annotations
@@ -51,6 +53,7 @@ def parse():
     ap.add_argument("--extra-m", default="2,4,8", help="additional decode M values reported under 'extra'")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 prefill measurements")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE bank measurement")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the dense MLP block measurement")
     ap.add_argument("--no-embed", action="store_true", help="skip the int8 embedding gather and output-head measurements")
     ap.add_argument("--sweep", action="store_true",
                     help="the M sweep over a 64-layer projection set on both paths (prints its own report)")
@@ -136,6 +139,41 @@ def time_decode(torch, exl3, dev, x, out, sets, steps, warmup):
     M, IC = x.shape
     ws = exl3.alloc_workspace(max(exl3.linear_multi_workspace_bytes(M, IC, s) for s in sets), dev)
     return graph_time(torch, lambda i: exl3.linear_multi_into(out, x, sets[i % len(sets)], ws=ws), steps, warmup)
+
+
+def time_mlp(torch, exl3, synth, dev, copies=8, steps=64):
+    """Dense MLP block of one decoder layer (hidden 5120, intermediate 17408; gate K=2, up K=3, down K=3) at
+    decode sizes M = 1 and 8: merged gate_up, SiLU * mul, down, over `copies` weight sets in turn (89 MB of
+    trellis words each, beyond the last-level cache).  Returns ({M: seconds per call}, trellis bytes per
+    call = 5120 * 17408 * (2 + 3 + 3) / 8)."""
+    H, I = 5120, 17408
+    sets = []
+    for r in range(copies):
+        c = synth.mlp_case(6000 + r, 1, H, I, 2, 3, 3)
+        s_in = torch.from_numpy(c["gate"]["s_in"]).to(dev)
+        rin = torch.from_numpy(c["gate"]["rin"]).to(dev)
+        one = []
+        for key in ("gate", "up", "down"):
+            p = c[key]
+            t = {k: torch.from_numpy(p[k]).to(dev) for k in ("code", "rout", "s_out", "s_in", "rin")}
+            if key != "down":
+                t.update(s_in=s_in, rin=rin)
+            t["K"] = p["K"]
+            one.append(t)
+        sets.append(one)
+    tbytes = H * I * (2 + 3 + 3) // 8
+    res = {}
+    for M in (1, 8):
+        x = torch.randn((M, H), device=dev).to(torch.bfloat16)
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        ws = exl3.alloc_workspace(exl3.mlp_workspace_bytes(M, H, I, sets[0][0], sets[0][1]), dev)
+        sec = graph_time(torch, lambda i: exl3.mlp_forward(x, *sets[i % copies], out=out, ws=ws), steps, copies)
+        res[M] = sec
+        print(f"# mlp H={H} I={I} M={M}: {sec * 1e6:.2f} us/call, {tbytes / sec / 1e9:.1f} GB/s trellis",
+              file=sys.stderr, flush=True)
+    del sets
+    torch.cuda.empty_cache()
+    return res, tbytes
 
 
 def time_prefill(torch, exl3, synth, dev, reps=5):
@@ -376,6 +414,7 @@ def main():
 
     prefill = {} if a.no_prefill else time_prefill(torch, exl3, synth, dev)
     moe = None if a.no_moe else time_moe(torch, exl3, synth, dev)
+    mlp = None if a.no_mlp else time_mlp(torch, exl3, synth, dev)
     embed = {} if a.no_embed else time_embed(torch, exl3, dev)
 
     sec = results[1]
@@ -404,6 +443,12 @@ def main():
         line["extra"]["moe_T256_E128_top8"] = {"us_per_call": round(s * 1e6, 2), "trellis_MB": round(tb / 1e6, 1),
                                                "trellis_GBps": round(tb / s / 1e9, 1),
                                                "frac_hbm": round(tb / s / 1e9 / HBM_PEAK_GBS, 4)}
+    if mlp is not None:
+        times, tb = mlp
+        for M, s in times.items():
+            line["extra"][f"mlp_H5120_I17408_M{M}"] = {"us_per_call": round(s * 1e6, 2),
+                                                        "trellis_GBps": round(tb / s / 1e9, 1),
+                                                        "frac_hbm": round(tb / s / 1e9 / HBM_PEAK_GBS, 4)}
     for key, (s, nbytes) in embed.items():
         line["extra"][key] = {"us_per_call": round(s * 1e6, 2),
                                                            "GBps": round(nbytes / s / 1e9, 1),
