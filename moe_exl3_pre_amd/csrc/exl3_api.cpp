@@ -12,6 +12,13 @@
 
 using namespace exl3;
 
+namespace exl3 {
+// the dense MLP block's down input from its gate_up output (k_prepass.hip): h = bf16(silu(g) * u) rotated into the
+// fragment-major fp16 operand of launch_prepass_f16.
+hipError_t launch_prepass_silu_f16(const void* gu, const void* s_in, const void* rin, void* xh, int64_t M, int64_t IC,
+                                   hipStream_t stream);
+}  // namespace exl3
+
 namespace {
 
 thread_local std::string g_error;
@@ -163,8 +170,10 @@ int check_workspace(const Layout& L, void* ws, size_t ws_bytes) {
 // The decode-phase path: one launch per chunk of <= 16 rows covering every shard.  A chunk of at least
 // kPreRotateRows rows first rotates its activations once per distinct (s_in, rin) into the workspace
 // (fragment-major, 16 rows), and the decode launch reads them from there.
+// gu (optional): the dense MLP block's gate_up output [M, 2 IC]; the pre-rotation then forms the input
+// h = bf16(silu(g) * u) itself (chunks below kPreRotateRows rows still read x = h).
 int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n,
-               const DecShardIn* in_, char* ws, const Layout& L, hipStream_t stream) {
+               const DecShardIn* in_, char* ws, const Layout& L, hipStream_t stream, const void* gu = nullptr) {
   DecShardIn in[kMaxShards];
   for (int i = 0; i < n; ++i) in[i] = in_[i];
   int slot[kMaxShards];
@@ -182,7 +191,10 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
         if (slot[i] > done) {
           if (L.xh_bytes < size_t(kDecodeMaxRows) * size_t(IC) * 2)
             return fail(EXL3_EWORKSPACE, "%s: workspace has no pre-rotation region", who);
-          hipError_t e = launch_prepass_f16(xr, in[i].s_in, in[i].rin, region, rows, IC, true, stream, kDecodeMaxRows);
+          hipError_t e =
+              gu ? launch_prepass_silu_f16(static_cast<const uint16_t*>(gu) + r0 * 2 * IC, in[i].s_in, in[i].rin,
+                                           region, rows, IC, stream)
+                 : launch_prepass_f16(xr, in[i].s_in, in[i].rin, region, rows, IC, true, stream, kDecodeMaxRows);
           if (int rc = launch_status(e, who)) return rc;
           done = slot[i];
         }
@@ -209,8 +221,9 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
 // The prefill-phase path: one pre-pass per distinct (s_in, rin), then one GEMM per shard.  On the 8-bit
 // path the pre-pass writes the integer codes (as fp16 numbers, exact) and the row scales, and the GEMM
 // applies the row scale in its epilogue.
+// gu (optional, 16-bit path only): as for run_decode.
 int run_gemm(const char* who, void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,
-             char* ws, const Layout& L, unsigned flags, hipStream_t stream) {
+             char* ws, const Layout& L, unsigned flags, hipStream_t stream, const void* gu = nullptr) {
   const bool int8 = (flags & EXL3_ACT_INT8) != 0;
   int slot[kMaxShards];
   distinct_inputs(n, in, slot);
@@ -221,6 +234,7 @@ int run_gemm(const char* who, void* out, int64_t ldo, const void* x, int64_t M, 
     if (slot[i] > done) {
       hipError_t e = int8 ? launch_prepass_i8(x, in[i].s_in, in[i].rin, region, scale, M, IC, true, stream, true,
                                               reinterpret_cast<float*>(region + L.part_off))
+                     : gu ? launch_prepass_silu_f16(gu, in[i].s_in, in[i].rin, region, M, IC, stream)
                           : launch_prepass_f16(x, in[i].s_in, in[i].rin, region, M, IC, true, stream, (M + 15) / 16 * 16);
       if (int rc = launch_status(e, who)) return rc;
       done = slot[i];
@@ -381,9 +395,12 @@ size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned f
   return L.total;
 }
 
-int exl3_linear_into(void* out, int64_t ldo, int64_t col0, const void* x, int64_t M, int64_t IC,
-                     const int16_t* code, int64_t OC, int K, const void* s_in, const void* rin, const void* rout,
-                     const void* s_out, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+int linear_into_impl(void* out, int64_t ldo, int64_t col0, const void* x, int64_t M, int64_t IC, const int16_t* code,
+                     int64_t OC, int K, const void* s_in, const void* rin, const void* rout, const void* s_out,
+                     unsigned flags, void* ws, size_t ws_bytes, void* stream, const void* gu) {
   if (int rc = check_flags(flags)) return rc;
   if (int rc = check_dims(M, IC)) return rc;
   if (int rc = check_shard("", IC, code, OC, K, col0, ldo, s_in, rin, rout, s_out)) return rc;
@@ -396,10 +413,20 @@ int exl3_linear_into(void* out, int64_t ldo, int64_t col0, const void* x, int64_
   if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rc = use_decode_path(M, flags, OC)
-                     ? run_decode("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, st)
-                     : run_gemm("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, flags, st);
+                     ? run_decode("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, st, gu)
+                     : run_gemm("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, flags, st, gu);
   if (rc) return rc;
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+int exl3_linear_into(void* out, int64_t ldo, int64_t col0, const void* x, int64_t M, int64_t IC,
+                     const int16_t* code, int64_t OC, int K, const void* s_in, const void* rin, const void* rout,
+                     const void* s_out, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+  return linear_into_impl(out, ldo, col0, x, M, IC, code, OC, K, s_in, rin, rout, s_out, flags, ws, ws_bytes, stream,
+                          nullptr);
 }
 
 size_t exl3_linear_multi_workspace_bytes(int64_t M, int64_t IC, int n_shards, const exl3_shard* shards,
@@ -596,11 +623,19 @@ int exl3_mlp_forward(void* out, const void* x, int64_t M, int64_t H, int64_t I, 
   gu[0].col0 = 0;
   gu[1].col0 = I;
   if (int rc = exl3_linear_multi_into(w + L.gu_off, 2 * I, x, M, H, 2, gu, flags, w, L.inner, stream)) return rc;
-  if (int rc = launch_status(launch_silu_mul(w + L.h_off, w + L.gu_off, M, I, static_cast<hipStream_t>(stream)),
-                             "exl3_mlp_forward"))
-    return rc;
-  if (int rc = exl3_linear_into(out, H, 0, w + L.h_off, M, I, down->code, H, down->K, down->s_in, down->rin,
-                                down->rout, down->s_out, flags, w, L.inner, stream))
+  // down's activation pre-pass forms h itself on the 16-bit path; h is written out only for what still reads
+  // it: the 8-bit pre-pass and decode chunks of fewer than kPreRotateRows rows (rotated inside the kernel)
+  const bool int8 = (flags & EXL3_ACT_INT8) != 0;
+  const bool gemm = !use_decode_path(M, flags, H);
+  const bool fold = !int8;
+  const bool need_h = int8 || (!gemm && M % kDecodeMaxRows != 0 && M % kDecodeMaxRows < kPreRotateRows);
+  if (need_h) {
+    if (int rc = launch_status(launch_silu_mul(w + L.h_off, w + L.gu_off, M, I, static_cast<hipStream_t>(stream)),
+                               "exl3_mlp_forward"))
+      return rc;
+  }
+  if (int rc = linear_into_impl(out, H, 0, w + L.h_off, M, I, down->code, H, down->K, down->s_in, down->rin,
+                                down->rout, down->s_out, flags, w, L.inner, stream, fold ? w + L.gu_off : nullptr))
     return rc;
   return ok();
 }

@@ -8,12 +8,11 @@
 // launch-latency-bound.
 #include "exl3_device.hpp"
 #include "exl3_internal.hpp"
+#include "k_silu.hpp"
 
 namespace exl3 {
 
 namespace {
-
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 __global__ __launch_bounds__(256) void silu_mul_kernel(uint16_t* __restrict__ h, const uint16_t* __restrict__ gu,
                                                        int64_t M, int64_t I) {
@@ -23,14 +22,8 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(uint16_t* __restrict__ h,
   const int64_t m = t / per_row, j = (t % per_row) * 8;
   const u32x4 g = *reinterpret_cast<const u32x4*>(gu + m * 2 * I + j);
   const u32x4 u = *reinterpret_cast<const u32x4*>(gu + m * 2 * I + I + j);
-  uint32_t o[4];
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float g0 = bf16_to_f32(g[w] & 0xFFFFu), g1 = bf16_to_f32(g[w] >> 16);
-    const float u0 = bf16_to_f32(u[w] & 0xFFFFu), u1 = bf16_to_f32(u[w] >> 16);
-    o[w] = f32x2_to_bf16x2(silu_f32(g0) * u0, silu_f32(g1) * u1);
-  }
-  *reinterpret_cast<u32x4*>(h + m * I + j) = (u32x4){o[0], o[1], o[2], o[3]};
+  *reinterpret_cast<u32x4*>(h + m * I + j) = (u32x4){silu_mul_bf16x2(g[0], u[0]), silu_mul_bf16x2(g[1], u[1]),
+                                                      silu_mul_bf16x2(g[2], u[2]), silu_mul_bf16x2(g[3], u[3])};
 }
 
 }  // namespace

@@ -10,6 +10,7 @@
 // 64 s + 16 g + 8 h .. +8), with the rows up to the next multiple of 16 written as zeros.
 #include "exl3_device.hpp"
 #include "exl3_internal.hpp"
+#include "k_silu.hpp"
 
 namespace exl3 {
 
@@ -79,6 +80,9 @@ __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __rest
 //
 // The rotated features of one (16-row block rb, 128-block q) unit, before the 1/sqrt(128) normalisation:
 // lane (n, g) ends with row 16 rb + n, features 16 (g + 4t) + w of the block in v[t][w] (zeros past M).
+// SILU: x is the dense MLP block's gate_up output [M, 2 IC] and the transform's input is h = bf16(silu(g) * u)
+// with g = x[row, k] and u = x[row, IC + k], formed exactly as the block's activation kernel forms it.
+template <bool SILU = false>
 __device__ __forceinline__ void frag_transform(const uint16_t* __restrict__ x, const uint16_t* __restrict__ s_in,
                                                const uint16_t* __restrict__ rin, int64_t M, int64_t IC, int64_t rb,
                                                int64_t q, int lane, float (&v)[2][16]) {
@@ -92,7 +96,18 @@ __device__ __forceinline__ void frag_transform(const uint16_t* __restrict__ x, c
     for (int c = 0; c < 2; ++c) {
       sv[c] = *reinterpret_cast<const u32x4*>(s_in + f + 8 * c);
       rv[c] = *reinterpret_cast<const u32x4*>(rin + f + 8 * c);
-      xv[c] = row < M ? *reinterpret_cast<const u32x4*>(x + row * IC + f + 8 * c) : (u32x4){0u, 0u, 0u, 0u};
+      if constexpr (SILU) {
+        if (row < M) {
+          const u32x4 g = *reinterpret_cast<const u32x4*>(x + row * 2 * IC + f + 8 * c);
+          const u32x4 u = *reinterpret_cast<const u32x4*>(x + row * 2 * IC + IC + f + 8 * c);
+          xv[c] = (u32x4){silu_mul_bf16x2(g[0], u[0]), silu_mul_bf16x2(g[1], u[1]), silu_mul_bf16x2(g[2], u[2]),
+                          silu_mul_bf16x2(g[3], u[3])};
+        } else {
+          xv[c] = (u32x4){0u, 0u, 0u, 0u};
+        }
+      } else {
+        xv[c] = row < M ? *reinterpret_cast<const u32x4*>(x + row * IC + f + 8 * c) : (u32x4){0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int w = 0; w < 16; ++w) {
@@ -138,6 +153,7 @@ __device__ __forceinline__ uint16_t* frag_unit_base(uint16_t* xf, int64_t IC, in
   return xf + ((rb * (IC / 64) + 2 * q) * 2) * 512 + lane * 8;
 }
 
+template <bool SILU>
 __global__ __launch_bounds__(256) void prepass_frag_f16_kernel(const uint16_t* __restrict__ x,
                                                                const uint16_t* __restrict__ s_in,
                                                                const uint16_t* __restrict__ rin,
@@ -148,7 +164,7 @@ __global__ __launch_bounds__(256) void prepass_frag_f16_kernel(const uint16_t* _
   if (unit >= (M + 15) / 16 * nq) return;
   const int64_t rb = unit / nq, q = unit % nq;
   float v[2][16];
-  frag_transform(x, s_in, rin, M, IC, rb, q, lane, v);
+  frag_transform<SILU>(x, s_in, rin, M, IC, rb, q, lane, v);
   uint16_t* base = frag_unit_base(xf, IC, rb, q, lane);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -275,7 +291,7 @@ hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, 
   if (M <= 0) return hipSuccess;
   if (permuted) {                                         // fragment-major: rows padded to 16 with zeros
     const int64_t units = (M + 15) / 16 * (IC / kHad);
-    hipLaunchKernelGGL(prepass_frag_f16_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(prepass_frag_f16_kernel<false>, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream,
                        (const uint16_t*)x, (const uint16_t*)s_in, (const uint16_t*)rin, (uint16_t*)xh, M, IC);
     return hipGetLastError();
   }
@@ -284,6 +300,17 @@ hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, 
   dim3 grid((unsigned)((units + 3) / 4)), block(256);
   hipLaunchKernelGGL(prepass_f16_kernel, grid, block, 0, stream, (const uint16_t*)x, (const uint16_t*)s_in,
                      (const uint16_t*)rin, (uint16_t*)xh, M, rows, IC);
+  return hipGetLastError();
+}
+
+// The dense MLP block's down input straight from its gate_up output gu [M, 2 IC]: h = bf16(silu(g) * u)
+// formed in registers, then the fragment-major fp16 rotation of launch_prepass_f16 (rows padded to 16).
+hipError_t launch_prepass_silu_f16(const void* gu, const void* s_in, const void* rin, void* xh, int64_t M, int64_t IC,
+                                   hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  const int64_t units = (M + 15) / 16 * (IC / kHad);
+  hipLaunchKernelGGL(prepass_frag_f16_kernel<true>, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream,
+                     (const uint16_t*)gu, (const uint16_t*)s_in, (const uint16_t*)rin, (uint16_t*)xh, M, IC);
   return hipGetLastError();
 }
 
