@@ -9,7 +9,7 @@ method's algorithmic bytes, IC*OC*K/8 per shard).  Weights rotate over 16 seeded
 events recorded on the stream the kernels run on.
 
 Also reported (under "extra"): decode M = 2, 4, 8; prefill M=8192 gate_up and down (TFLOP/s); the MoE
-expert bank (T=256, E=128, top-8, H=2048, I=768; 3 rotated banks); the dense MLP block of one decoder
+expert bank (T=256, E=128, top-8, H=2048, I=768; 3 rotated banks; also T=4096 in TFLOP/s); the dense MLP block of one decoder
 layer (5120 -> 2 x 17408 -> 5120) at M = 1 and 8; the int8 embedding gather (T = 256 and 8192 ids over a
 248,320 x 5120 table) and the same table as the output head (M = 1 and 16; GB/s of bytes moved).
 
@@ -239,7 +239,23 @@ def time_moe(torch, exl3, synth, dev, steps=60):
                      MOE_COPIES * 2)
     print(f"# moe T={cfg['T']} E={cfg['E']} top{cfg['topk']}: {sec * 1e6:.1f} us/call, "
           f"{tb / sec / 1e9:.1f} GB/s trellis ({tb / 1e6:.1f} MB touched)", file=sys.stderr, flush=True)
-    return sec, tb
+    # a prefill-sized batch on the same banks: T = 4096 tokens (32,768 routed pairs; the route's counting
+    # sort); MFMA-bound, so reported as TFLOP/s of the experts' products, 2 * pairs * (2 H I + I H)
+    T = 4096
+    rng = np.random.default_rng(1009)
+    xp = torch.from_numpy(synth.random_activations(rng, T, cfg["H"])[1].view(np.int16).copy()).to(dev)
+    xp = xp.view(torch.bfloat16)
+    pid, pw = synth.routing(rng, T, cfg["E"], cfg["topk"])
+    pid = torch.from_numpy(pid.astype(np.int32)).to(dev)
+    pw = torch.from_numpy(pw.astype(np.float32)).to(dev)
+    outp = torch.empty_like(xp)
+    wsp = exl3.alloc_workspace(exl3.moe_workspace_bytes(banks[0], T, cfg["topk"]), dev)
+    secp = graph_time(torch, lambda i: exl3.moe_bank_forward(outp, xp, pid, pw, banks[i % MOE_COPIES], ws=wsp), 12,
+                      MOE_COPIES)
+    flop = 2.0 * T * cfg["topk"] * (2 * cfg["H"] * cfg["I"] + cfg["I"] * cfg["H"])
+    print(f"# moe T={T} E={cfg['E']} top{cfg['topk']}: {secp * 1e6:.1f} us/call, {flop / secp / 1e12:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    return sec, tb, (T, secp, flop)
 
 
 def time_embed(torch, exl3, dev, reps=50):
@@ -439,7 +455,10 @@ def main():
         line["extra"][f"prefill_{name}_M8192"] = {"ms_per_call": round(s * 1e3, 4), "TFLOPs": round(flop / s / 1e12, 1),
                                                   "frac_of_f16_peak": round(flop / s / 1e12 / F16_PEAK_TFLOPS, 4)}
     if moe is not None:
-        s, tb = moe
+        s, tb, (Tp, sp, flp) = moe
+        line["extra"][f"moe_T{Tp}_E128_top8"] = {"us_per_call": round(sp * 1e6, 1),
+                                                 "TFLOPs": round(flp / sp / 1e12, 1),
+                                                 "frac_of_f16_peak": round(flp / sp / 1e12 / F16_PEAK_TFLOPS, 4)}
         line["extra"]["moe_T256_E128_top8"] = {"us_per_call": round(s * 1e6, 2), "trellis_MB": round(tb / 1e6, 1),
                                                "trellis_GBps": round(tb / s / 1e9, 1),
                                                "frac_hbm": round(tb / s / 1e9 / HBM_PEAK_GBS, 4)}

@@ -63,11 +63,12 @@ def test_moe_many_rows_per_expert_and_empty_expert():
     _check(m, _run(bank, x, dids, w))
 
 
-@pytest.mark.parametrize("T,E,topk", [(2048, 64, 4), (4608, 32, 4)])
+@pytest.mark.parametrize("T,E,topk", [(2048, 64, 4), (4608, 32, 4), (4096, 128, 8)])
 def test_moe_route_counting_sort_path(T, E, topk):
     """Prefill-sized routing: E * ceil(T * topk / 32) exceeds the bitmap route's 8192 LDS words, so the
     counting-sort route runs -- with its LDS cache of the pairs' slots (8192 pairs) and without it
-    (18432 pairs).  Sampled tokens against the oracle; a second call gives the same bits."""
+    (18432 pairs; 32,768 pairs over 128 experts, the prefill-sized bank's routing).  Sampled tokens against
+    the oracle; a second call gives the same bits."""
     P = T * topk
     assert E * ((P + 31) // 32) > 8192
     log(f"moe counting-sort route T={T} E={E} top-{topk} ({P} pairs)")
