@@ -5,8 +5,9 @@
 //   out[t] = bf16( sum_j topk_w[t, j] * E_{topk_ids[t, j]}(x[t]) ),   E(v) = L_w2( silu(L_w1 v) * L_w3 v )
 //
 // Four launches, all sized from host-known quantities so the call is graph-capturable:
-//   1. route + rotate.  Workgroup 0 sorts the (token, slot) pairs by slot with a stable counting sort
-//      (pair ids ascending inside a slot) and cuts every slot's list into chunks of at most 32 rows.
+//   1. route + rotate.  Workgroup 0 sorts the (token, slot) pairs by slot with a counting sort (pair ids
+//      ascending inside a slot on the bitmap path; any order on the general path, which no result
+//      depends on) and cuts every slot's list into chunks of at most 32 rows.
 //      Every other workgroup rotates gathered activations for w1 and w3 of each pair
 //      (x[t] * suh, Hadamard-128, fp16, PERM16 order) -- that needs only the pair's slot, not the sort.
 //   2. w13.  One workgroup per (chunk, 128-column block of I): two waves stream w1's trellis words and
@@ -76,7 +77,7 @@ __device__ __forceinline__ int pair_slot(const MoeArgs& a, int q) {
 }
 
 // ---------------------------------------------------------------------------------------------------
-// 1a. Route: stable counting sort of the pairs by slot, done by one workgroup of 1024 threads.
+// 1a. Route: counting sort of the pairs by slot, done by one workgroup of 1024 threads.
 // ---------------------------------------------------------------------------------------------------
 // Exclusive scan of v over the block's 1024 threads; returns the prefix and leaves the total in *total.
 // tmp holds 48 ints of LDS.
@@ -157,36 +158,13 @@ __device__ void moe_route_general(const MoeArgs& a, int* lds) {
     a.offs[E] = total;
     a.n_chunks[0] = chunk_total;
   }
-  // stable placement, 1024 pairs at a time: rank inside the wave by ballots, then per-slot prefix over
-  // the waves in wave order
-  for (int q0 = 0; q0 < a.P; q0 += kRouteThreads) {
-    for (int i = tid; i < kW * E; i += kRouteThreads) wcnt[i] = 0;
-    __syncthreads();
-    const int q = q0 + tid;
-    const int sl = q < a.P ? (cache ? cache[q] : pair_slot(a, q)) : -1;
-    uint64_t remaining = __ballot(sl >= 0);
-    int rank = 0;
-    while (remaining) {
-      const int leader = __builtin_ctzll(remaining);
-      const int ls = __builtin_amdgcn_readlane(sl, leader);
-      const uint64_t m = __ballot(sl == ls);
-      if (sl == ls) rank = __popcll(m & ((1ull << lane) - 1ull));
-      if (lane == leader) wcnt[wave * E + ls] = __popcll(m);
-      remaining &= ~m;
-    }
-    __syncthreads();
-    for (int t = tid; t < E; t += kRouteThreads) {
-      int b = next[t];
-      for (int w = 0; w < kW; ++w) {
-        const int v = wcnt[w * E + t];
-        wcnt[w * E + t] = b;
-        b += v;
-      }
-      next[t] = b;
-    }
-    __syncthreads();
-    if (sl >= 0) a.rows[wcnt[wave * E + sl] + rank] = q;
-    __syncthreads();
+  // placement: one LDS atomic per pair on its slot's cursor.  The order inside a slot is whatever the
+  // atomics give; nothing depends on it (every row of the w13 / w2 lists is computed on its own and every
+  // result is indexed by pair id), so the outputs are the same bits as with a stable order.
+  __syncthreads();
+  for (int q = tid; q < a.P; q += kRouteThreads) {
+    const int sl = cache ? cache[q] : pair_slot(a, q);
+    if (sl >= 0) a.rows[atomicAdd(&next[sl], 1)] = q;
   }
 }
 
