@@ -212,6 +212,83 @@ __global__ __launch_bounds__(256) void lm_head_int8_kernel(uint16_t* __restrict_
   }
 }
 
+// 5..16 x rows, H a multiple of 256: x is the larger stream (as many bytes per 64-feature step as 64 table
+// rows), so a workgroup of 4 waves owning 64 table rows stages each 256-feature slice of x in LDS once and
+// every wave reads its B operands from there.  Each wave streams its own 16 rows over all of H, keeping
+// one accumulator per quarter of the feature steps (the same quarters as lm_head_int8_kernel) and adding
+// them in the same order, so the logits are the same bits as that kernel's.
+constexpr int kHeadXStride = 256 + 8;   // halves per staged x row: 528 bytes, rows 4 banks apart
+
+__global__ __launch_bounds__(256) void lm_head_int8_xlds_kernel(uint16_t* __restrict__ out, int64_t ldo,
+                                                                const uint16_t* __restrict__ x, int M,
+                                                                const int8_t* __restrict__ table,
+                                                                const uint16_t* __restrict__ scale, int64_t V,
+                                                                int64_t H, bool vec_store) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[16 * kHeadXStride];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, quarter = lane >> 4;
+  const int64_t v = int64_t(blockIdx.x) * 64 + wave * 16 + r16;
+  const bool tok = v < V;
+  const int8_t* trow = table + (tok ? v : 0) * H + 16 * quarter;
+  const float s = tok ? bf16_to_f32(scale[v]) : 0.0f, c = -128.0f * s;
+  const int64_t steps = H / 64;
+  int64_t bound[kHeadParts];
+#pragma unroll
+  for (int p = 0; p < kHeadParts; ++p) bound[p] = steps * (p + 1) / kHeadParts * 64;
+  // staging: thread tid copies 16 features (32 bytes) of x row tid / 16
+  const int sr = tid >> 4, sc = (tid & 15) * 16;
+  const bool sok = sr < M;
+  const uint16_t* xsrc = x + int64_t(sok ? sr : 0) * H + sc;
+
+  float4v acc[kHeadParts];
+#pragma unroll
+  for (int p = 0; p < kHeadParts; ++p) acc[p] = (float4v){0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int64_t h = 0; h < H; h += 256) {
+    u32x4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = tok ? *reinterpret_cast<const u32x4*>(trow + h + 64 * u) : zero;
+    const u32x4 x0 = sok ? *reinterpret_cast<const u32x4*>(xsrc + h) : zero;
+    const u32x4 x1 = sok ? *reinterpret_cast<const u32x4*>(xsrc + h + 8) : zero;
+    __syncthreads();                                       // the previous slice is no longer read
+    *reinterpret_cast<u32x4*>(xs + sr * kHeadXStride + sc) = x0;
+    *reinterpret_cast<u32x4*>(xs + sr * kHeadXStride + sc + 8) = x1;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t hs = h + 64 * u;
+      const int part = hs < bound[0] ? 0 : hs < bound[1] ? 1 : hs < bound[2] ? 2 : 3;
+      const uint16_t* xp = xs + r16 * kHeadXStride + 64 * u + 16 * quarter;
+      const u32x4 b0 = *reinterpret_cast<const u32x4*>(xp), b1 = *reinterpret_cast<const u32x4*>(xp + 8);
+      const bf16x8 w0 = head_weights(q[u][0], q[u][1], s, c), w1 = head_weights(q[u][2], q[u][3], s, c);
+      float4v t = acc[0];
+      if (part == 1) t = acc[1];
+      if (part == 2) t = acc[2];
+      if (part == 3) t = acc[3];
+      t = mfma_bf16(w0, __builtin_bit_cast(bf16x8, b0), t);
+      t = mfma_bf16(w1, __builtin_bit_cast(bf16x8, b1), t);
+      if (part == 0) acc[0] = t;
+      if (part == 1) acc[1] = t;
+      if (part == 2) acc[2] = t;
+      if (part == 3) acc[3] = t;
+    }
+  }
+  if (r16 >= M) return;
+  float4v t = acc[0];
+#pragma unroll
+  for (int p = 1; p < kHeadParts; ++p) t += acc[p];
+  uint16_t* orow = out + int64_t(r16) * ldo;
+  const int64_t v4 = int64_t(blockIdx.x) * 64 + wave * 16 + 4 * quarter;
+  const uint32_t lo = f32x2_to_bf16x2(t[0], t[1]);
+  const uint32_t hi = f32x2_to_bf16x2(t[2], t[3]);
+  if (vec_store && v4 + 4 <= V) {
+    *reinterpret_cast<uint2*>(orow + v4) = make_uint2(lo, hi);
+  } else {
+    const uint16_t e[4] = {uint16_t(lo), uint16_t(lo >> 16), uint16_t(hi), uint16_t(hi >> 16)};
+    for (int i = 0; i < 4 && v4 + i < V; ++i) orow[v4 + i] = e[i];
+  }
+}
+
 template <int MR, int G, int U>
 void launch_head(uint16_t* out, int64_t ldo, const uint16_t* x, int M, const int8_t* table, const uint16_t* scale,
                  int64_t V, int64_t H, bool vec_store, hipStream_t stream) {
@@ -234,6 +311,9 @@ hipError_t launch_lm_head_int8(void* out, int64_t ldo, const void* x, int64_t M,
     uint16_t* o = static_cast<uint16_t*>(out) + m0 * ldo;
     const uint16_t* xs = static_cast<const uint16_t*>(x) + m0 * H;
     if (rows <= 4) launch_head<1, 1, 4>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream);
+    else if (rows <= 16 && H % 256 == 0)
+      hipLaunchKernelGGL(lm_head_int8_xlds_kernel, dim3((unsigned)((V + 63) / 64)), dim3(256), 0, stream, o, ldo, xs,
+                         rows, table, sc, V, H, vec_store);
     else if (rows <= 8) launch_head<1, 2, 4>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream);
     else if (rows <= 16) launch_head<1, 4, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream);
     else if (rows <= 32) launch_head<2, 2, 2>(o, ldo, xs, rows, table, sc, V, H, vec_store, stream);

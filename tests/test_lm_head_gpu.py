@@ -81,6 +81,34 @@ def test_lm_head_batch_invariant():
         assert np.array_equal(part, full[:M]), M
 
 
+@pytest.mark.parametrize("M", [5, 11, 16])
+def test_lm_head_x_staged_in_lds(M):
+    """5..16 rows with H a multiple of 256 take the kernel that stages x in LDS; H = 1280 puts quarter
+    boundaries (every 5 steps) inside its 256-feature slices."""
+    V, H = 997, 1280
+    rng, table, scale = _table(90 + M, V, H)
+    x = _bf16_bits(rng.normal(size=(M, H)))
+    log(f"lm_head staged x V={V} H={H} M={M}")
+    out = exl3.lm_head_int8(_to_dev(x), _to_dev(table, torch.int8), _to_dev(scale))
+    torch.cuda.synchronize()
+    _check(_bits(out), x, table, scale)
+
+
+def test_lm_head_batch_invariant_across_kernels():
+    """H = 1280: rows 0..63 of a 70-row call run on the 64-row kernel and rows 64..69 on the staged-x
+    kernel; calls of 1..40 rows take every kernel; a row's logits are the same bits in all of them."""
+    V, H = 997, 1280
+    rng, table, scale = _table(99, V, H)
+    x = _to_dev(_bf16_bits(rng.normal(size=(70, H))))
+    t, s = _to_dev(table, torch.int8), _to_dev(scale)
+    full = _bits(exl3.lm_head_int8(x, t, s))
+    for M in (1, 4, 5, 9, 16, 17, 40):
+        part = _bits(exl3.lm_head_int8(x[:M].contiguous(), t, s))
+        assert np.array_equal(part, full[:M]), M
+    tail = _bits(exl3.lm_head_int8(x[64:].contiguous(), t, s))
+    assert np.array_equal(tail, full[64:])
+
+
 def test_lm_head_strided_output_keeps_other_columns():
     V, H, M, ldo = 96, 128, 3, 132
     rng, table, scale = _table(50, V, H)
