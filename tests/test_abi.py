@@ -216,3 +216,18 @@ def test_mlp_validation():
     assert call(0, 128, 256, g, g, d) == exl3.OK
     assert L.exl3_silu_mul(FAKE, FAKE, 2, 12, None) == exl3.EINVAL
     assert L.exl3_silu_mul(None, None, 0, 16, None) == exl3.OK
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback: without the built library every entry point raises before doing anything."""
+    import torch
+    monkeypatch.setattr(exl3, "_lib", None)
+    monkeypatch.setattr(exl3, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libexl3.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        exl3.lib()
+    table = torch.zeros((4, 16), dtype=torch.int8)
+    scale = torch.zeros((4,), dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="not built"):
+        exl3.embed_int8(table, scale, torch.zeros((2,), dtype=torch.int32))
+    with pytest.raises(RuntimeError, match="not built"):
+        exl3.linear_workspace_bytes(4, 512, 512)
