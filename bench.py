@@ -41,7 +41,7 @@ DECODE_KERNEL = "exl3::decode_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_gate_up_m1.md")
 # sources whose change invalidates the stored counter readings of the decode kernel
 TRAFFIC_SOURCES = ["moe_exl3_pre_amd/csrc/k_decode.hip", "moe_exl3_pre_amd/csrc/exl3_device.hpp",
-                   "moe_exl3_pre_amd/csrc/exl3_internal.hpp"]
+                   "moe_exl3_pre_amd/csrc/exl3_internal.hpp", "moe_exl3_pre_amd/csrc/k_silu.hpp"]
 
 
 def parse():

@@ -212,8 +212,10 @@ int exl3_moe_bank_forward(void* out, const void* x, int64_t T,
  * activation takes silu(gate) * up and feeds down_proj):
  *
  *   gu  = [gate(x) | up(x)]          one exl3_linear_multi_into call, bf16 [M, 2I] in the workspace
- *   h   = bf16(silu(g) * u)          exl3_silu_mul on gu (fp32 arithmetic), bf16 [M, I] in the workspace
- *   out = down(h)                    one exl3_linear_into call, bf16 [M, H]
+ *   h   = bf16(silu(g) * u)          as exl3_silu_mul computes it (fp32 arithmetic)
+ *   out = down(h)                    as one exl3_linear_into call on h, bf16 [M, H]
+ * down's activation pre-pass reads g and u and forms h itself, so h is not written to memory (except on
+ * the 8-bit path, whose pre-pass reads it).
  *
  *   out   bf16 [M, H] row-major, 16-byte aligned;  x  bf16 [M, H] row-major, 16-byte aligned.
  *   gate, up   shard descriptors over IC = H with OC = I (their col0 is ignored: gate fills columns

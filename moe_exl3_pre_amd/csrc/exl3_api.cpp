@@ -170,8 +170,8 @@ int check_workspace(const Layout& L, void* ws, size_t ws_bytes) {
 // The decode-phase path: one launch per chunk of <= 16 rows covering every shard.  A chunk of at least
 // kPreRotateRows rows first rotates its activations once per distinct (s_in, rin) into the workspace
 // (fragment-major, 16 rows), and the decode launch reads them from there.
-// gu (optional): the dense MLP block's gate_up output [M, 2 IC]; the pre-rotation then forms the input
-// h = bf16(silu(g) * u) itself (chunks below kPreRotateRows rows still read x = h).
+// gu (optional): the dense MLP block's gate_up output [M, 2 IC]; the pre-rotation (5..16 rows) or the decode
+// kernel's in-block pre-pass (1..4 rows) then forms the input h = bf16(silu(g) * u) itself.
 int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n,
                const DecShardIn* in_, char* ws, const Layout& L, hipStream_t stream, const void* gu = nullptr) {
   DecShardIn in[kMaxShards];
@@ -201,7 +201,12 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
         in[i].xf = region;
       }
     }
-    if (pl.kset >= 0) {
+    if (gu && !pl.pre) {   // the folded activation in the in-block pre-pass (down is one shard)
+      if (n != 1 || pl.kset < 0) return fail(EXL3_EUNSUPPORTED, "%s: folded activation needs one shard", who);
+      hipError_t e = launch_decode(pl, static_cast<const uint16_t*>(gu) + r0 * 2 * IC, rows, IC, n, in, orow, ldo,
+                                   reinterpret_cast<float*>(ws + L.slab_off), reinterpret_cast<int*>(ws), stream, true);
+      if (int rc = launch_status(e, who)) return rc;
+    } else if (pl.kset >= 0) {
       hipError_t e = launch_decode(pl, xr, rows, IC, n, in, orow, ldo, reinterpret_cast<float*>(ws + L.slab_off),
                                    reinterpret_cast<int*>(ws), stream);
       if (int rc = launch_status(e, who)) return rc;
@@ -623,12 +628,11 @@ int exl3_mlp_forward(void* out, const void* x, int64_t M, int64_t H, int64_t I, 
   gu[0].col0 = 0;
   gu[1].col0 = I;
   if (int rc = exl3_linear_multi_into(w + L.gu_off, 2 * I, x, M, H, 2, gu, flags, w, L.inner, stream)) return rc;
-  // down's activation pre-pass forms h itself on the 16-bit path; h is written out only for what still reads
-  // it: the 8-bit pre-pass and decode chunks of fewer than kPreRotateRows rows (rotated inside the kernel)
+  // on the 16-bit path down's activation pre-pass (the rotation launch, or the decode kernel's in-block
+  // pre-pass for 1..4 rows) forms h itself; only the 8-bit pre-pass reads h from memory
   const bool int8 = (flags & EXL3_ACT_INT8) != 0;
-  const bool gemm = !use_decode_path(M, flags, H);
   const bool fold = !int8;
-  const bool need_h = int8 || (!gemm && M % kDecodeMaxRows != 0 && M % kDecodeMaxRows < kPreRotateRows);
+  const bool need_h = int8;
   if (need_h) {
     if (int rc = launch_status(launch_silu_mul(w + L.h_off, w + L.gu_off, M, I, static_cast<hipStream_t>(stream)),
                                "exl3_mlp_forward"))

@@ -50,8 +50,10 @@ struct DecPlan {
 
 // Plans one decode-phase launch of M <= 16 rows over n shards; false if it cannot be served.
 bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl);
+// silu: x is a dense MLP block's gate_up output [M, 2 IC] and the activation bf16(silu(g) * u) is formed in the
+// in-block pre-pass (one shard, 1..4 rows, no pre-rotation; otherwise hipErrorInvalidValue).
 hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,
-                         void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream);
+                         void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream, bool silu = false);
 
 // permuted: the GEMM's fragment-major layout (k_gemm.hip), else natural row-major.  Rows
 // [M, M_pad) of xh are written as zeros.

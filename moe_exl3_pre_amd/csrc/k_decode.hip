@@ -26,6 +26,7 @@
 
 #include "exl3_device.hpp"
 #include "exl3_internal.hpp"
+#include "k_silu.hpp"
 
 namespace exl3 {
 
@@ -60,9 +61,12 @@ struct DecArgs {
 // for the whole launch by the fragment-major pre-pass (the prefill path's, k_prepass.hip), and each step's
 // two A fragments are 16-byte loads from that buffer issued with the step's trellis words.  Then no block
 // repeats the rotation, which at M = 8 costs about as much VALU as the decode itself.
-template <int K, int SPW, int MR>
+// SILU (MR 1 or 4 only): a.x is a dense MLP block's gate_up output [M, 2 IC]; the pre-pass input is
+// h = bf16(silu(g) * u), g = a.x[m, k], u = a.x[m, IC + k], formed as the block's activation kernel forms it.
+template <int K, int SPW, int MR, bool SILU = false>
 __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& sh, int local, char* lds) {
   constexpr bool kPre = MR == 0;
+  static_assert(!SILU || MR == 1 || MR == 4, "the folded activation is for the in-block pre-pass");
   using G = Geom<K>;
   // steps of trellis words in flight per wave: one.  Every block requests its first step at once, so
   // deeper prefetch only queues the first data of late waves behind the early waves' later steps.
@@ -93,6 +97,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   // wait for the weight stream behind it before the pre-pass can start.
   constexpr int kMR = kPre ? 1 : MR;
   uint32_t xv[kPB][kMR], sv[kPB], rv[kPB];
+  uint32_t xu[kPB][SILU ? kMR : 1];   // SILU: the up half (xv holds the gate half)
 #pragma unroll
   for (int pb = 0; pb < (kPre ? 0 : kPB); ++pb) {
     const int hb = hb0 + pb < hb1 ? hb0 + pb : (hb1 > hb0 ? hb1 - 1 : 0);
@@ -102,8 +107,14 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
     rv[pb] = uint32_t(sh.rin[f]) | (uint32_t(sh.rin[f + 8]) << 16);
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      const uint16_t* xr = a.x + int64_t(m < M ? m : M - 1) * a.IC + f;
-      xv[pb][m] = uint32_t(xr[0]) | (uint32_t(xr[8]) << 16);
+      if constexpr (SILU) {
+        const uint16_t* gr = a.x + int64_t(m < M ? m : M - 1) * 2 * a.IC + f;
+        xv[pb][m] = uint32_t(gr[0]) | (uint32_t(gr[8]) << 16);
+        xu[pb][m] = uint32_t(gr[a.IC]) | (uint32_t(gr[a.IC + 8]) << 16);
+      } else {
+        const uint16_t* xr = a.x + int64_t(m < M ? m : M - 1) * a.IC + f;
+        xv[pb][m] = uint32_t(xr[0]) | (uint32_t(xr[8]) << 16);
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the weight stream
@@ -150,8 +161,10 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         if (m < M) {
-          float v0 = bf16_to_f32(xv[pb][m] & 0xFFFFu) * s0 * r0;
-          float v1 = bf16_to_f32(xv[pb][m] >> 16) * s1 * r1;
+          uint32_t xw = xv[pb][m];
+          if constexpr (SILU) xw = silu_mul_bf16x2(xv[pb][m], xu[pb][m]);
+          float v0 = bf16_to_f32(xw & 0xFFFFu) * s0 * r0;
+          float v1 = bf16_to_f32(xw >> 16) * s1 * r1;
           had128_wave_pairs8(v0, v1, lane);
           *reinterpret_cast<uint32_t*>(xs + m * lrow + kl) =
               uint32_t(f32_to_f16(v0 * kInvSqrt128)) | (uint32_t(f32_to_f16(v1 * kInvSqrt128)) << 16);
@@ -298,7 +311,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   }
 }
 
-template <int KSET, int SPW, int MR>
+template <int KSET, int SPW, int MR, bool SILU = false>
 __global__ __launch_bounds__(512, 4) void decode_kernel(DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int wg = blockIdx.x;
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(512, 4) void decode_kernel(DecArgs a) {
   const DecShard& sh = a.sh[i];
   const int local = wg - sh.wg_begin;
   if constexpr (KSET >= 1 && KSET <= 8) {
-    decode_block<KSET, SPW, MR>(a, sh, local, lds);
+    decode_block<KSET, SPW, MR, SILU>(a, sh, local, lds);
   } else {   // KSET 0: the mixed set {2, 3, 4}
     switch (sh.K) {
       case 2: decode_block<2, SPW, MR>(a, sh, local, lds); break;
@@ -412,18 +425,31 @@ bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl
   return counters <= kCounterSlots;
 }
 
-template <int KSET, int MR>
+template <int KSET, int MR, bool SILU = false>
 static void launch_kset_mr(const DecPlan& pl, const DecArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)pl.wg_total), block(kWaves * 64);
   const size_t lds = pl.lds_bytes;
   if (pl.spw <= 2)
-    hipLaunchKernelGGL((decode_kernel<KSET, 2, MR>), grid, block, lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<KSET, 2, MR, SILU>), grid, block, lds, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<KSET, 4, MR>), grid, block, lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<KSET, 4, MR, SILU>), grid, block, lds, stream, a);
 }
 
 template <int KSET>
-static hipError_t launch_kset(const DecPlan& pl, const DecArgs& a, hipStream_t stream) {
+static hipError_t launch_kset(const DecPlan& pl, const DecArgs& a, hipStream_t stream, bool silu) {
+  // the folded MLP activation: single-shard launches of 1..4 rows with in-block rotation only
+  if (silu) {
+    if constexpr (KSET >= 1 && KSET <= 8) {
+      if (pl.pre || a.M > 4) return hipErrorInvalidValue;
+      if (a.M <= 1)
+        launch_kset_mr<KSET, 1, true>(pl, a, stream);
+      else
+        launch_kset_mr<KSET, 4, true>(pl, a, stream);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   // activation rows the fused pre-pass loads unconditionally: 1, 4 or 16; 0 = pre-rotated activations
   if (pl.pre)
     launch_kset_mr<KSET, 0>(pl, a, stream);
@@ -437,7 +463,7 @@ static hipError_t launch_kset(const DecPlan& pl, const DecArgs& a, hipStream_t s
 }
 
 hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,
-                         void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream) {
+                         void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream, bool silu) {
   if (pl.kset < 0) return hipErrorInvalidValue;
   DecArgs a;
   a.x = (const uint16_t*)x;
@@ -467,15 +493,15 @@ hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC
     d.wg_begin = pl.wg_begin[r];
   }
   switch (pl.kset) {
-    case 0: return launch_kset<0>(pl, a, stream);
-    case 1: return launch_kset<1>(pl, a, stream);
-    case 2: return launch_kset<2>(pl, a, stream);
-    case 3: return launch_kset<3>(pl, a, stream);
-    case 4: return launch_kset<4>(pl, a, stream);
-    case 5: return launch_kset<5>(pl, a, stream);
-    case 6: return launch_kset<6>(pl, a, stream);
-    case 7: return launch_kset<7>(pl, a, stream);
-    case 8: return launch_kset<8>(pl, a, stream);
+    case 0: return launch_kset<0>(pl, a, stream, silu);
+    case 1: return launch_kset<1>(pl, a, stream, silu);
+    case 2: return launch_kset<2>(pl, a, stream, silu);
+    case 3: return launch_kset<3>(pl, a, stream, silu);
+    case 4: return launch_kset<4>(pl, a, stream, silu);
+    case 5: return launch_kset<5>(pl, a, stream, silu);
+    case 6: return launch_kset<6>(pl, a, stream, silu);
+    case 7: return launch_kset<7>(pl, a, stream, silu);
+    case 8: return launch_kset<8>(pl, a, stream, silu);
   }
   return hipErrorInvalidValue;
 }
