@@ -110,3 +110,26 @@ def test_mlp_decoder_shapes_equal_the_three_calls(M):
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
     assert torch.isfinite(out.float()).all() and out.float().abs().max() > 0
+
+
+@pytest.mark.parametrize("M", [2, 40])
+def test_mlp_int8_path(M):
+    """EXL3_ACT_INT8: every projection takes per-row 8-bit activations (on the GEMM) and the activation is
+    written out for down's 8-bit pre-pass.  Bitwise equal to the three 8-bit calls; against the oracle's
+    8-bit emulation within 1e-2 (relative Frobenius; codes may differ by one at near-ties)."""
+    c = synth.mlp_case(120 + M, M, 512, 1024, 2, 3, 3)
+    x, g, u, d = _to_dev_case(c)
+    log(f"mlp int8 M={M}")
+    f = exl3.ACT_INT8
+    out = exl3.mlp_forward(x, g, u, d, flags=f)
+    gu = torch.empty((M, 2048), dtype=torch.bfloat16, device=dev())
+    exl3.linear_multi_into(gu, x, [dict(g, col0=0), dict(u, col0=1024)], flags=f)
+    h = exl3.silu_mul(gu)
+    ref = torch.empty_like(out)
+    exl3.linear_into(ref, h, d["code"], d["K"], d["s_in"], d["rin"], d["rout"], d["s_out"], flags=f)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    args = [_oracle_args(c[k]) for k in ("gate", "up", "down")]
+    e = rel_fro(bf16_to_f64(out), O.mlp_forward(c["x"], *args, act="int8"))
+    log(f"  rel err vs 8-bit oracle {e:.3e}")
+    assert e < 1e-2
