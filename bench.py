@@ -390,8 +390,8 @@ def pmc_reference(torch, exl3, dev, x, out, sets):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {a.gpus} requested); "
-              "the multi-GPU sharding is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (--gpus {a.gpus} requested); the library has no collectives "
+              "or multi-GPU sharding", file=sys.stderr)
         sys.exit(2)
     import torch
     from moe_exl3_pre_amd import exl3, synth

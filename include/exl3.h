@@ -50,7 +50,7 @@ typedef enum {
   EXL3_OK = 0,
   EXL3_EINVAL = -1,      /* bad shape, K, alignment, null pointer or flag */
   EXL3_EWORKSPACE = -2,  /* workspace missing or smaller than required */
-  EXL3_EUNSUPPORTED = -3,/* valid request outside what this build implements */
+  EXL3_EUNSUPPORTED = -3,/* valid request outside what the library implements */
   EXL3_ELAUNCH = -4      /* a kernel launch failed (message carries the HIP error) */
 } exl3_status;
 
