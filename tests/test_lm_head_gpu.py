@@ -109,6 +109,22 @@ def test_lm_head_batch_invariant_across_kernels():
     assert np.array_equal(tail, full[64:])
 
 
+@pytest.mark.parametrize("M", [3, 9])
+def test_lm_head_vector_stores_with_ragged_tail(M):
+    """ldo = 1000 (a multiple of 4) with V = 997: 8-byte stores everywhere but the last 4-column group, which
+    is written element by element; columns past V stay untouched.  M = 3 runs the 16-row kernel, M = 9 the
+    staged-x kernel (H = 1280)."""
+    V, H, ldo = 997, 1280, 1000
+    rng, table, scale = _table(110 + M, V, H)
+    x = _bf16_bits(rng.normal(size=(M, H)))
+    buf = torch.full((M, ldo), -7.0, dtype=torch.bfloat16, device=dev())
+    exl3.lm_head_int8(_to_dev(x), _to_dev(table, torch.int8), _to_dev(scale), out=buf[:, :V])
+    torch.cuda.synchronize()
+    b = buf.cpu()
+    assert torch.all(b[:, V:] == -7.0)
+    _check(_bits(b[:, :V].contiguous()), x, table, scale)
+
+
 def test_lm_head_strided_output_keeps_other_columns():
     V, H, M, ldo = 96, 128, 3, 132
     rng, table, scale = _table(50, V, H)
