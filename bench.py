@@ -16,6 +16,7 @@ layer (5120 -> 2 x 17408 -> 5120) at M = 1 and 8; the int8 embedding gather (T =
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill] [--no-moe] [--no-mlp]
                     [--no-embed]
     python bench.py --pmc-ref ...     # eager launches plus a 1 GiB copy, for counter runs
+    python bench.py --pmc-int8        # the same for the int8 embedding gather and output head
 """
 from __future__ import annotations
 
@@ -62,6 +63,9 @@ def parse():
                     help="counter runs: 1 GiB device copies (known bytes), then two eager calls of each prefill projection")
     ap.add_argument("--pmc-ref", action="store_true",
                     help="eager decode launches (no graph) plus a plain 1 GiB copy, for hardware-counter runs")
+    ap.add_argument("--pmc-int8", action="store_true",
+                    help="counter runs: 1 GiB device copies (known bytes), then eager int8 embedding gathers "
+                         "(T=8192) and output-head calls (M=1) over the 248,320 x 5120 table")
     return ap.parse_args()
 
 
@@ -387,6 +391,33 @@ def pmc_reference(torch, exl3, dev, x, out, sets):
                       "sources_sha256_16": sources_sha()}), flush=True)
 
 
+def pmc_int8(torch, exl3, dev):
+    """Eager launches for counter runs over the int8 table: 1 GiB copies, 4 gathers of 8192 random ids (each
+    its own id set), 4 output-head calls on one row of x."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    del src, dst
+    V, H = 248320, 5120
+    g = torch.Generator(device=dev)
+    g.manual_seed(33)
+    table = torch.randint(-128, 128, (V, H), dtype=torch.int8, device=dev, generator=g)
+    scale = torch.randint(0x3A00, 0x3D80, (V,), dtype=torch.int32, device=dev, generator=g).to(torch.int16)
+    scale = scale.view(torch.bfloat16)
+    out = torch.empty((8192, H), dtype=torch.bfloat16, device=dev)
+    for _ in range(4):
+        ids = torch.randint(0, V, (8192,), dtype=torch.int32, device=dev, generator=g)
+        exl3.embed_int8(table, scale, ids, out=out)
+    x = torch.randn((1, H), device=dev, generator=g).to(torch.bfloat16)
+    logits = torch.empty((1, V), dtype=torch.bfloat16, device=dev)
+    for _ in range(4):
+        exl3.lm_head_int8(x, table, scale, out=logits)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_int8": True, "copy_bytes": 1 << 30, "embed_bytes": 3 * 8192 * H,
+                      "head_bytes": V * H + 2 * V + 2 * H + 2 * V}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -400,6 +431,9 @@ def main():
 
     if a.sweep:
         run_sweep(torch, exl3, synth, dev, [int(m) for m in a.sweep_ms.split(",") if m])
+        return
+    if a.pmc_int8:
+        pmc_int8(torch, exl3, dev)
         return
     if a.pmc_prefill:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
