@@ -242,9 +242,8 @@ int exl3_silu_mul(void* h, const void* gu, int64_t M, int64_t I, void* stream);
 
 /* --------------------------------------------------------------------------------------------------
  * int8 embedding rows gathered by token id and dequantized ("vllm-quantpack 0.1.0", exl3/embedding.py,
- * `Exl3EmbeddingMethod.embedding`: the table stays int8 with one scale per row; the gathered rows are
- * converted to the scale's dtype and multiplied by their row's scale, so the table is never materialised
- * in bf16).
+ * `Exl3EmbeddingMethod.embedding`: the table is kept as int8 codes plus one scale per row; only the
+ * requested rows are converted to the scale's dtype and scaled, and no bf16 copy of the table exists).
  *
  *   out    bf16 [T, H] row-major, 16-byte aligned: out[t, :] = bf16(table[ids[t], :] * scale[ids[t]]).
  *   table  int8 [V, H] row-major, 16-byte aligned.

@@ -1,6 +1,6 @@
 // int8 embedding rows gathered by token id and dequantized ("vllm-quantpack 0.1.0", exl3/embedding.py,
-// `Exl3EmbeddingMethod.embedding`): the table stays int8 with one scale per row, the rows of the requested
-// ids are gathered and multiplied by their row's scale, so the table is never materialised in bf16.
+// `Exl3EmbeddingMethod.embedding`): the table is kept as int8 codes plus one scale per row, and only the
+// rows a call asks for are dequantized; no bf16 copy of the whole table exists.
 //
 // out[t, :] = bf16(table[ids[t], :] * scale[ids[t]]).  An int8 code times a bf16 scale is exact in fp32,
 // so the one rounding is the conversion to bf16 (nearest, ties to even).  Ids outside [0, V) give zero
