@@ -194,11 +194,30 @@ def linear(x, code, K, s_in, rin, rout, s_out, act: str = "f64", W: np.ndarray |
         Y = round_fp16(xh) @ W
     elif act == "int8":
         q, sc = quantize_rows_int8(xh)
-        Y = sc[:, None] * (q.astype(np.float64) @ W)
+        return linear_from_int8(q, sc, code, K, rout, s_out, W=W)
     else:
         raise ValueError(f"unknown act mode {act!r}")
+    return output_transform(Y, rout, s_out)
+
+
+def output_transform(Y, rout, s_out) -> np.ndarray:
+    """Z = Had128(Y) along the output features, then * rout * s_out ([escha] module docstring: the
+    product is followed by its own Hadamard-128 and the post-scales; no bias)."""
     Z = had128(Y, axis=-1)
     return Z * np.asarray(rout, dtype=np.float64) * np.asarray(s_out, dtype=np.float64)
+
+
+def linear_from_int8(q, sc, code, K, rout, s_out, W: np.ndarray | None = None) -> np.ndarray:
+    """The 8-bit path after its quantisation step: Y = sc[m] * (q @ W), then the output transform.
+
+    q is [M, IC] (integers in [-127, 127]) and sc the [M] row scales, as `quantize_rows_int8` returns them
+    ([escha] `escha_linear_into`: the 8-bit activation buffer and its float32 row scale feed the GEMM).
+    Taking q and sc as arguments lets a test run this step on codes another implementation chose."""
+    if W is None:
+        W = decode_weight(code, K)
+    q = np.asarray(q).astype(np.float64)
+    sc = np.asarray(sc, dtype=np.float64)
+    return output_transform(sc[:, None] * (q @ W), rout, s_out)
 
 
 def linear_into(out: np.ndarray, col0: int, x, code, K, s_in, rin, rout, s_out, act: str = "f64") -> np.ndarray:

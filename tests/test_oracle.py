@@ -598,3 +598,84 @@ def test_mlp_rounding_is_small_and_zero_input_gives_zero():
     rel = np.linalg.norm(a - b) / np.linalg.norm(b)
     assert 1e-5 < rel < 1e-2
     assert np.all(O.mlp_forward(np.zeros_like(x), gate, up, down) == 0)
+
+
+# ------------------------------------------------------------------------------------------ rounding points
+# Hand-derived values (tests/golden/rounding_points.txt) that fix where the oracle rounds: the fp16
+# rounding of the rotated activations comes after the input Hadamard, the 8-bit codes round half to even,
+# and the dense MLP block rounds the gate and up outputs to bf16 before its activation.
+
+def _rounding_rows(tag):
+    return [r[1:] for r in _rows("rounding_points.txt") if r[0] == tag]
+
+
+def _zero_code(IC, OC, K=2):
+    return np.zeros((IC // 16, OC // 16, 16 * K), dtype=np.int16)
+
+
+def test_fp16_rounding_point_is_after_the_hadamard():
+    rows = _rounding_rows("f16")
+    ones = np.ones(128)
+    x = np.zeros((len(rows), 128))
+    x[:, 0] = [float(c) for c, _, _ in rows]
+    got = O.linear(x, _zero_code(128, 128), 2, ones, ones, ones, ones, act="f16")
+    for r, (c, num, wrong) in enumerate(rows):
+        want = int(num) * np.sqrt(2.0) / 16
+        assert abs(got[r, 0] - want) <= 1e-12 * want, (c, got[r, 0], want)
+        assert abs(got[r, 0] - float(wrong)) > 1e-3
+        assert np.max(np.abs(got[r, 1:])) <= 1e-12 * want
+    # the unrounded path gives the "wrong" column: the difference is the fp16 rounding and nothing else
+    exact = O.linear(x, _zero_code(128, 128), 2, ones, ones, ones, ones)
+    assert np.allclose(exact[:, 0], [float(w) for _, _, w in rows], rtol=1e-12)
+
+
+def test_int8_codes_round_half_to_even():
+    for row in _rounding_rows("i8"):
+        sc = float(row[0])
+        parts = " ".join(row[1:]).split("|")
+        v, even, up, away = ([float(t) for t in p.split()] for p in parts)
+        q, s = O.quantize_rows_int8(np.array([v]) * sc)
+        assert s[0] == sc
+        assert q[0].tolist() == even
+        assert q[0].tolist() != up and q[0].tolist() != away
+
+
+def test_int8_path_takes_the_given_codes():
+    """linear(act="int8") is quantize_rows_int8 followed by linear_from_int8; with hand-made codes the
+    latter is sc * (q @ W) through the output transform: all-zero words give out[0] = 16 sc q[0]."""
+    ones = np.ones(128)
+    q = np.zeros((2, 128), dtype=np.int8)
+    q[0, 0], q[1, :] = 5, -1
+    sc = np.array([0.5, 0.25])
+    got = O.linear_from_int8(q, sc, _zero_code(128, 128), 2, ones, ones)
+    # out[0] = sqrt(128) * 0.125 * sc * sum_k q[k];  row 1: sum_k q = -128
+    want = np.sqrt(128) * 0.125 * sc * np.array([5.0, -128.0])
+    assert np.allclose(got[:, 0], want, rtol=1e-13) and np.max(np.abs(got[:, 1:])) < 1e-12
+    c = synth.linear_case(52, 5, 256, 128, 3)
+    args = (c["code"], 3, c["s_in"], c["rin"], c["rout"], c["s_out"])
+    qq, ss = O.quantize_rows_int8(O.rotate_input(c["x"], c["s_in"], c["rin"]))
+    assert np.array_equal(O.linear(c["x"], *args, act="int8"),
+                          O.linear_from_int8(qq, ss, c["code"], 3, c["rout"], c["s_out"]))
+
+
+def test_mlp_rounds_gate_and_up_before_the_activation():
+    (x0, gbits, ubits, out0, wrong) = _rounding_rows("mlp")[0]
+    H = I = 128
+
+    def fp16(bits):
+        return float(np.array([int(bits, 16)], dtype=np.uint16).view(np.float16)[0])
+
+    def proj(ic, oc, r0=None):
+        rout = np.ones(oc)
+        if r0 is not None:
+            rout[0] = fp16(r0)
+        return dict(code=_zero_code(ic, oc), K=2, s_in=np.ones(ic), rin=np.ones(ic), rout=rout, s_out=np.ones(oc))
+    x = np.zeros((1, H))
+    x[0, 0] = float(x0)
+    gate, up, down = proj(H, I, gbits), proj(H, I, ubits), proj(I, H)
+    got = O.mlp_forward(x, gate, up, down)
+    assert abs(got[0, 0] - float(out0)) <= 1e-9, got[0, 0]
+    assert np.max(np.abs(got[0, 1:])) <= 1e-9
+    # with every intermediate in float64 the block gives 16 silu(g) u, not the golden value
+    raw = O.mlp_forward(x, gate, up, down, round_mid=False)
+    assert abs(raw[0, 0] - float(out0)) > 10 and abs(raw[0, 0] - float(wrong)) < 10
