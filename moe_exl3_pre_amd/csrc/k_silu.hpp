@@ -5,7 +5,13 @@
 
 namespace exl3 {
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g), written with t = e^-|g| in (0, 1] so that nothing overflows: for g < 0 it is
+// g t / (1 + t).  (The direct form overflows e^-g below g = -88.7 and returns -0 where the value is still
+// a normal number, e.g. silu(-89) = -2e-37.)
+__device__ __forceinline__ float silu_f32(float g) {
+  const float t = expf(-fabsf(g));
+  return (g >= 0.f ? g : g * t) / (1.0f + t);
+}
 
 // bf16(silu(g) * u) for two (g, u) pairs packed as bf16x2 words; returns the packed bf16x2 result.
 __device__ __forceinline__ uint32_t silu_mul_bf16x2(uint32_t g, uint32_t u) {

@@ -306,12 +306,15 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
-    """Round float64 values to bf16 (8 significant bits, nearest, ties to even) and return the bit
-    patterns.  Normal range only (the products here never reach bf16 subnormals); zeros keep their sign."""
+    """Round float64 values to bf16 (nearest, ties to even) and return the bit patterns.  bf16 keeps 8
+    significant bits down to 2^-126; below that its numbers (subnormals) lie on the fixed grid 2^-133, so
+    the rounding unit is 2^(e-8) for v = m 2^e, 1/2 <= |m| < 1, but never below 2^-133.  Values past the
+    largest bf16 are not handled (none arises here); zeros keep their sign."""
     v = np.asarray(v, dtype=np.float64)
-    m, e = np.frexp(v)                                   # v = m * 2^e, 0.5 <= |m| < 1
-    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)         # 8 significant bits; np.rint rounds half to even
-    r = np.where(v == 0, v, r)                           # keep the sign of zero
+    _, e = np.frexp(v)
+    unit = np.maximum(e - 8, -133)                       # exponent of the rounding unit
+    r = np.ldexp(np.rint(np.ldexp(v, -unit)), unit)      # np.rint rounds half to even
+    r = np.where(r == 0, np.copysign(0.0, v), r)         # keep the sign of zero (also of an underflow)
     return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 

@@ -468,6 +468,27 @@ def test_bf16_rounding_ties_to_even():
     assert O.f64_to_bf16_bits(np.array([-hi]))[0] == 0xBF82
 
 
+def test_bf16_rounding_subnormals():
+    """Below 2^-126 bf16 numbers lie on the grid 2^-133 (bit patterns 0x0001..0x007F).  Hand values: 1.5,
+    2.5 and 3.5 units round to the even neighbour 2, 2, 4; half a unit rounds to zero; a value just below
+    2^-126 rounds up to it (0x0080); signs are kept, also for an underflow to zero."""
+    u = 2.0 ** -133
+    v = np.array([1.5 * u, 2.5 * u, 3.5 * u, 0.5 * u, 0.75 * u, 2.0 ** -126 * (1 - 2.0 ** -10), -1.5 * u, -0.25 * u])
+    assert O.f64_to_bf16_bits(v).tolist() == [0x0002, 0x0002, 0x0004, 0x0000, 0x0001, 0x0080, 0x8002, 0x8000]
+
+
+def test_bf16_rounding_matches_float32_bit_rounding():
+    """For float32 inputs (exact in float64) bf16 rounding is the carry trick on the float32 bit pattern,
+    (bits + 0x7FFF + bit16) >> 16, which is monotone across the subnormal/normal boundary: every pattern in
+    the subnormal range, around 2^-126, and a normal stretch, both signs."""
+    pats = np.concatenate([np.arange(0, 1 << 22, 7), np.arange((1 << 23) - 70000, (1 << 23) + 70000),
+                           np.arange(0x3F7F0000, 0x3F810000)]).astype(np.uint32)
+    pats = np.concatenate([pats, pats | np.uint32(0x80000000)])
+    f = pats.view(np.float32)
+    want = ((pats.astype(np.uint64) + 0x7FFF + ((pats >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(O.f64_to_bf16_bits(f.astype(np.float64)), want)
+
+
 # ------------------------------------------------------------------------------------------ int8 output head
 
 def _bits(v):
