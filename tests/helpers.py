@@ -65,3 +65,65 @@ def oracle_block_columns(x, code, K, s_in, rin, rout, s_out, blocks, act="f64"):
     sub = np.ascontiguousarray(code[:, tiles])
     y = O.linear(x, sub, K, s_in, rin, np.asarray(rout)[cols], np.asarray(s_out)[cols], act=act)
     return cols, y
+
+
+def gpu_int8_codes(x_dev, s_in_dev, rin_dev, x64, s_in, rin):
+    """The 8-bit codes and row scales the kernels use, read back through the rotate hook, after checking
+    them against the oracle's quantize_rows_int8: scales within 2e-6 relative (fp32 against fp64 rotation),
+    codes equal except by one where xh/sc lies within 1e-4 of a rounding boundary (a decision the kernel
+    takes in fp32).  The hook and the GEMM's pre-pass compute xh with the same butterfly sequence, so these
+    are the GEMM's own codes.  Returns (q int64 [M, IC], sc float64 [M])."""
+    from moe_exl3_pre_amd import exl3
+    q, sc = exl3.rotate_activations(x_dev, s_in_dev, rin_dev, int8=True)
+    torch.cuda.synchronize()
+    q = q.cpu().numpy().astype(np.int64)
+    sc = sc.cpu().numpy().astype(np.float64)
+    xh = O.rotate_input(x64, s_in, rin)
+    q_ref, sc_ref = O.quantize_rows_int8(xh)
+    assert np.allclose(sc, sc_ref, rtol=2e-6, atol=0), "row scales"
+    assert np.abs(q).max(initial=0) <= 127
+    diff = q != q_ref
+    if diff.any():
+        frac = (xh / np.where(sc_ref > 0, sc_ref, 1.0)[:, None]) % 1.0
+        near_tie = np.abs(frac - 0.5) < 1e-4
+        assert np.all(np.abs(q - q_ref)[diff] == 1) and np.all(near_tie[diff]), int(diff.sum())
+    return q, sc
+
+
+def oracle_int8_block_columns(q, sc, code, K, rout, s_out, blocks):
+    """The oracle's 8-bit contraction and output transform on given codes, restricted to whole 128-column
+    blocks `blocks`."""
+    cols = np.concatenate([np.arange(128 * b, 128 * b + 128) for b in blocks])
+    tiles = np.concatenate([np.arange(8 * b, 8 * b + 8) for b in blocks])
+    sub = np.ascontiguousarray(code[:, tiles])
+    return cols, O.linear_from_int8(q, sc, sub, K, np.asarray(rout)[cols], np.asarray(s_out)[cols])
+
+
+def assert_bf16_activation(got_bits, want_bits, exact, loose=None):
+    """A bf16 activation the kernel forms in fp32 against the oracle's fp64 one (want_bits = bf16 of the
+    fp64 value `exact`): equal, except one unit in the last place where `exact` lies within fp32 error
+    (2^-18 relative) of the midpoint between the two bf16 neighbours, i.e. where rounding fp32 and fp64
+    values may legitimately differ; signed zeros compare equal.  Where `loose` is set the kernel's fp32
+    intermediates are subnormal (fewer significant bits), and one unit is allowed anywhere."""
+    got = np.asarray(got_bits).astype(np.int32)
+    want = np.asarray(want_bits).astype(np.int32)
+    sign_zero = ((got & 0x7FFF) == 0) & ((want & 0x7FFF) == 0)
+    diff = (got != want) & ~sign_zero
+    if diff.any():
+        assert np.all(np.abs(got - want)[diff] == 1), "activation off by more than one unit"
+        mid = (O.bf16_bits_to_f64(got[diff].astype(np.uint16)) + O.bf16_bits_to_f64(want[diff].astype(np.uint16))) / 2
+        ex = np.asarray(exact)[diff]
+        ok = np.abs(ex - mid) <= 2.0 ** -18 * np.abs(ex)
+        if loose is not None:
+            ok |= np.asarray(loose)[diff]
+        assert np.all(ok), "activation differs away from a rounding tie"
+    return int(diff.sum())
+
+
+def silu_mul_refs(gu_bits, I):
+    """(oracle bf16 bits, exact fp64 value, loose mask) of the activation of a bf16 gate_up [M, 2I]; the
+    mask marks |silu(g)| < 2^-119, where the kernel's e^g (and so its product) is an fp32 subnormal."""
+    g = O.bf16_bits_to_f64(gu_bits[:, :I])
+    u = O.bf16_bits_to_f64(gu_bits[:, I:])
+    sg = O.silu(g)
+    return O.silu_mul_bf16(gu_bits[:, :I], gu_bits[:, I:]), sg * u, np.abs(sg) < 2.0 ** -119

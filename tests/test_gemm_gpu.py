@@ -5,8 +5,8 @@ import torch
 
 from oracle import exl3_oracle as O
 from moe_exl3_pre_amd import exl3, synth
-from tests.helpers import (assert_close_linear, bf16_to_f64, dev, log, oracle_block_columns, rel_fro, shard_to_dev,
-                           to_dev, to_dev_x)
+from tests.helpers import (assert_close_linear, bf16_to_f64, dev, gpu_int8_codes, log, oracle_block_columns,
+                           oracle_int8_block_columns, rel_fro, shard_to_dev, to_dev, to_dev_x)
 
 pytestmark = pytest.mark.gpu
 
@@ -160,10 +160,12 @@ def test_tail_round_split_parity():
     differ = (out != ref).view(M // 128, 128, OC // 128, 128).any(dim=3).any(dim=1).cpu().numpy()
     mt, ct = np.nonzero(differ)
     assert np.all(mt == 8) and np.all(ct >= 96), (mt, ct)
-    # 8-bit path: the bar of the int8 suite (codes may flip by one at near-ties, so no element-wise bound)
+    # 8-bit path: the oracle's contraction on the kernel's own codes (checked against the oracle's
+    # quantisation first), every element at the same bar
     got8 = bf16_to_f64(_run(c, d, exl3.ACT_INT8))[:, cols]
-    assert rel_fro(got8, y64) <= 3e-2
-    assert rel_fro(got8, oracle_block_columns(*args, act="int8")[1]) < 4e-3
+    q, sc = gpu_int8_codes(d["x"], d["s_in"], d["rin"], c["x"], c["s_in"], c["rin"])
+    _, y8 = oracle_int8_block_columns(q, sc, c["code"], K, c["rout"], c["s_out"], blocks)
+    assert_close_linear(got8, y8, y64, tol=3e-2)
 
 
 def test_tail_round_split_poisoned_workspace():
@@ -229,8 +231,9 @@ def test_split_k_int8_small_m():
     d = _dev_case(c)
     out = _run(c, d, exl3.ACT_INT8)
     args = (c["code"], 3, c["s_in"], c["rin"], c["rout"], c["s_out"])
-    assert_close_linear(bf16_to_f64(out), O.linear(c["x"], *args, act="int8"), O.linear(c["x"], *args),
-                        tol=3e-2)
+    q, sc = gpu_int8_codes(d["x"], d["s_in"], d["rin"], c["x"], c["s_in"], c["rin"])
+    assert_close_linear(bf16_to_f64(out), O.linear_from_int8(q, sc, c["code"], 3, c["rout"], c["s_out"]),
+                        O.linear(c["x"], *args), tol=3e-2)
 
 
 def test_split_k_down_full_width_sampled():
@@ -299,3 +302,20 @@ def test_split_k_graph_replay_matches_eager():
         exl3.linear_multi_into(tmp, x, shards, ws=ws)
         torch.cuda.synchronize()
         assert torch.equal(tmp, eager)
+
+
+# ------------------------------------------------------------------ the 64-layer sweep's projections
+
+@pytest.mark.parametrize("M", [64, 512])
+@pytest.mark.parametrize("name,IC,OC,K", [("qkv", 5120, 7168, 3), ("o", 5120, 5120, 3)])
+def test_sweep_projections_both_paths_sampled(name, IC, OC, K, M):
+    """The decoder sweep's attention projections (hidden 5120: qkv 5120 -> 7168, o 5120 -> 5120, K=3) at the
+    sweep's mid sizes, on the decode-phase path (16-row launches) and on the MFMA GEMM: every row of five
+    128-column blocks (the first, the last and three at random) against the oracle."""
+    c = synth.linear_case(7000 + OC // 128 + M, M, IC, OC, K)
+    d = _dev_case(c)
+    rows = np.arange(M)
+    for tag, flags in (("decode", exl3.FORCE_GEMV), ("mfma", exl3.FORCE_MFMA)):
+        log(f"{name} {IC}->{OC} K={K} M={M} on the {tag} path")
+        out = _run(c, d, flags)
+        _sampled_check(c["x"], [dict(c, col0=0)], out, rows, seed=M)

@@ -153,16 +153,41 @@ def test_moe_graph_replay_matches_eager():
         _run(bank, x, ids, w, ws=ws)          # eager work between replays
 
 
+def _full_size_tokens(m, n=32, seed=0):
+    """At least n tokens that together route to every K group, to the most-loaded expert and to the
+    least-loaded expert that has any token; the rest drawn at random."""
+    ids = m["topk_ids"]
+    load = np.bincount(ids.ravel(), minlength=m["E"])
+    used = np.nonzero(load)[0]
+    e_max, e_min = int(used[np.argmax(load[used])]), int(used[np.argmin(load[used])])
+    pick = set()
+    for e in (e_max, e_min):
+        pick.update(np.nonzero((ids == e).any(axis=1))[0][:2].tolist())
+    ks = np.array([m["experts"][e]["k_gu"] for e in range(m["E"])])
+    for K in np.unique(ks):
+        pick.update(np.nonzero((ks[ids] == K).any(axis=1))[0][:1].tolist())
+    rng = np.random.default_rng(seed)
+    rest = [t for t in rng.permutation(m["T"]) if t not in pick]
+    pick.update(rest[:max(0, n - len(pick))])
+    tokens = sorted(pick)
+    assert e_max in ids[tokens] and e_min in ids[tokens]
+    assert set(ks[ids[tokens]].ravel()) == set(np.unique(ks))
+    return tokens, e_max, e_min
+
+
 def test_moe_full_size_sampled():
-    """T=256 tokens, 128 experts, top-8, H=2048, I=768, K in {2,3,4}: full run, three tokens checked."""
+    """T=256 tokens, 128 experts, top-8, H=2048, I=768, K in {2,3,4}: full run; 32 tokens (256 of the 2048
+    (token, expert) pairs) checked element-wise, covering every K group and the most- and least-loaded
+    experts; every other output finite."""
     cfg = synth.MOE
     m = synth.moe_case(1003, T=cfg["T"], E=cfg["E"], topk=cfg["topk"], H=cfg["H"], I=cfg["I"], Ks=cfg["Ks"])
     log("moe full size 256 x 2048, 128 experts top-8")
     bank, x, ids, w = _setup(m)
     out = _run(bank, x, ids, w)
     assert torch.isfinite(out.float()).all()
-    tokens = [0, 137, cfg["T"] - 1]
+    tokens, e_max, e_min = _full_size_tokens(m)
     used = np.unique(m["topk_ids"][tokens])
+    log(f"  {len(tokens)} tokens over {len(used)} experts (most loaded {e_max}, least loaded {e_min})")
     experts = list(m["experts"])
     for e in used:      # decode the touched experts once for both oracle variants
         d = experts[e]
