@@ -155,6 +155,24 @@ int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int
                            unsigned flags, void* ws, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------------------
+ * The same call without a workspace argument, for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation).  The workspace is a static
+ * device array of exl3_static_scratch_bytes() (16 MiB) that the library holds on every GPU it runs on
+ * until the process ends; nothing is allocated or freed per call.  A call whose workspace need
+ * (exl3_linear_multi_workspace_bytes) exceeds that size launches nothing and returns EXL3_EWORKSPACE;
+ * decode-phase calls of the usual shapes fit (the 4096 -> 2 x 14336 gate_up at 16 rows needs 3.8 MB),
+ * most prefill-phase calls do not.
+ * The first call on a device (with that device current) looks up the array's address and clears its
+ * counter head with a kernel on `stream`; make that first call outside stream capture.  Every call on a
+ * device shares the one array: calls that may overlap on one device (other streams or threads without
+ * ordering between them) race.  Results are bitwise those of exl3_linear_multi_into.
+ * ------------------------------------------------------------------------------------------------ */
+size_t exl3_static_scratch_bytes(void);
+
+int exl3_linear_multi_into_static(void* out, int64_t ldo, const void* x, int64_t M, int64_t IC,
+                                  int n_shards, const exl3_shard* shards, unsigned flags, void* stream);
+
+/* --------------------------------------------------------------------------------------------------
  * MoE expert bank ("dspark/worker/exl3/bank.py", `Exl3Bank` docstring and `allocate`): experts sit in
  * K-sorted physical slots; the trellis words of all experts share two flat int16 banks (w13 = [w1 | w3]
  * per slot, and w2); sign/scale vectors are fp16 [E, ...].

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/exl3.h"
@@ -685,6 +686,72 @@ int exl3_rotate_activations(void* q_out, float* scale_out, const void* x, int64_
   }
   if (int rc = launch_status(e, "exl3_rotate_activations")) return rc;
   return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------------
+// Allocation-free variant of exl3_linear_multi_into.  Its workspace is `scratch`, a file-scope device
+// array of kStaticScratchBytes: every GPU the library runs on holds its own copy until the process
+// ends.  Host code never uses the array's name as an address (on the host it is only a stand-in): the
+// first call on a device looks up that device's copy with hipGetSymbolAddress, with the device current,
+// and keeps the address.  The split-K counters at the head of the workspace must start at zero; that
+// first call clears them with a fill kernel on the caller's stream, and every kernel leaves them at zero
+// again when it ends.  Every call on a device shares its copy, so calls that may overlap on one device
+// (different streams, different threads without ordering) race.
+// ---------------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int n) {
+  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
+// This device's copy of `scratch`, set up on the first call made with the device current.
+int static_scratch(void** ptr, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(EXL3_ELAUNCH, "static scratch: no usable current device (%d)", dev);
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(EXL3_ELAUNCH, "static scratch: hipGetSymbolAddress failed on device %d: %s", dev, hipGetErrorString(e));
+    hipLaunchKernelGGL(zero_words_kernel, dim3((kCounterSlots + 255) / 256), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(p), kCounterSlots);
+    if (int rc = launch_status(hipGetLastError(), "static scratch: clearing the counters")) return rc;
+    g_static_ptr[dev] = p;
+  }
+  *ptr = g_static_ptr[dev];
+  return EXL3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t exl3_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int exl3_linear_multi_into_static(void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n_shards,
+                                  const exl3_shard* shards, unsigned flags, void* stream) {
+  const size_t need = exl3_linear_multi_workspace_bytes(M, IC, n_shards, shards, flags);
+  if (need > kStaticScratchBytes)
+    return fail(EXL3_EWORKSPACE,
+                "exl3_linear_multi_into_static: this call needs %zu bytes of scratch, the static scratch holds %zu; "
+                "use exl3_linear_multi_into with a workspace", need, kStaticScratchBytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (int rc = static_scratch(&ws, st)) return rc;
+  return exl3_linear_multi_into(out, ldo, x, M, IC, n_shards, shards, flags, ws, kStaticScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -63,6 +63,10 @@ _SIGS = {
     "exl3_linear_multi_into": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                               ctypes.c_int64, ctypes.c_int, ctypes.POINTER(Shard), ctypes.c_uint,
                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "exl3_static_scratch_bytes": (ctypes.c_size_t, []),
+    "exl3_linear_multi_into_static": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                                     ctypes.c_int64, ctypes.c_int, ctypes.POINTER(Shard), ctypes.c_uint,
+                                                     ctypes.c_void_p]),
     "exl3_moe_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Bank), ctypes.c_int64, ctypes.c_int, ctypes.c_uint]),
     "exl3_moe_bank_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(Bank), ctypes.c_uint,
@@ -201,6 +205,26 @@ def linear_multi_into(out, x, shards, flags: int = 0, ws=None):
         ws = alloc_workspace(lib().exl3_linear_multi_workspace_bytes(M, IC, len(shards), arr, flags), dev)
     _check(lib().exl3_linear_multi_into(_ptr(out), out.shape[1], _ptr(x), M, IC, len(shards), arr, flags, _ptr(ws),
                                         ws.numel(), _stream(dev)))
+    return out
+
+
+def linear_multi_into_static(out, x, shards, flags: int = 0):
+    """exl3_linear_multi_into with the library's static device scratch as its workspace (no allocation);
+    see exl3_linear_multi_into_static for the size limit and the sharing rule."""
+    dev = x.device
+    M, IC = x.shape
+    _need(x, "x", torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, device=dev)
+    for i, s in enumerate(shards):
+        _need(s["code"], f"shards[{i}].code", torch.int16, device=dev)
+        if s["code"].shape[0] * 16 != IC or s["code"].shape[2] != 16 * s["K"]:
+            raise ValueError(f"shards[{i}].code: shape {tuple(s['code'].shape)} does not match IC={IC}, K={s['K']}")
+        OC = s["code"].shape[1] * 16
+        for name, n in (("s_in", IC), ("rin", IC), ("rout", OC), ("s_out", OC)):
+            _need(s[name], f"shards[{i}].{name}", torch.float16, (n,), dev)
+    arr = _shard_array(shards)
+    _check(lib().exl3_linear_multi_into_static(_ptr(out), out.shape[1], _ptr(x), M, IC, len(shards), arr, flags,
+                                               _stream(dev)))
     return out
 
 
