@@ -13,6 +13,12 @@ expert bank (T=256, E=128, top-8, H=2048, I=768; 3 rotated banks; also T=4096 in
 layer (5120 -> 2 x 17408 -> 5120) at M = 1 and 8; the int8 embedding gather (T = 256 and 8192 ids over a
 248,320 x 5120 table) and the same table as the output head (M = 1 and 16; GB/s of bytes moved).
 
+Every timing is the median, p10 and p90 over at least 20 timed replays (graphs of captured calls, or eager
+calls for the prefill projections) between events on the launching stream; the headline value is the mean
+over exactly --steps calls.  Measured peaks (a 4 GiB streaming read; back-to-back f16 and i8 MFMAs) are
+reported beside the published ones as secondary denominators.  The CPU baseline is the fp64 oracle on the
+same step, on one thread and on all usable cores (with the host's CPU count and model).
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill] [--no-moe] [--no-mlp]
                     [--no-embed]
     python bench.py --pmc-ref ...     # eager launches plus a 1 GiB copy, for counter runs
@@ -36,6 +42,7 @@ sys.path.insert(0, ROOT)
 METRIC = "EXL3 linear GB/s (trellis bytes) at M=1 & TFLOP/s at M=8192; % roofline"
 HBM_PEAK_GBS = 8000.0
 F16_PEAK_TFLOPS = 2500.0
+I8_PEAK_TOPS = 5000.0
 COPIES = 16
 MOE_COPIES = 3
 DECODE_KERNEL = "exl3::decode_kernel"
@@ -56,6 +63,7 @@ def parse():
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE bank measurement")
     ap.add_argument("--no-mlp", action="store_true", help="skip the dense MLP block measurement")
     ap.add_argument("--no-embed", action="store_true", help="skip the int8 embedding gather and output-head measurements")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured streaming-read and MFMA peaks")
     ap.add_argument("--sweep", action="store_true",
                     help="the M sweep over a 64-layer projection set on both paths (prints its own report)")
     ap.add_argument("--sweep-ms", default="1,4,8,16,24,32,48,64,128,512,8192")
@@ -110,9 +118,14 @@ def build_gate_up(torch, dev, synth, copies):
     return IC, col, sets, trellis_bytes
 
 
-def graph_time(torch, step, steps, warmup):
-    """Capture `warmup` and `steps` calls of step(i) in two graphs; return seconds per step measured with
-    events on the current stream (the stream the kernels are launched on)."""
+def graph_time(torch, step, steps, warmup, reps=20, chunk=16):
+    """Time calls of step(i) replayed from captured graphs, with events recorded on the current stream (the
+    stream the kernels are launched on).
+      * headline: `warmup` untimed calls, then exactly `steps` calls in one graph, one replay between two
+        events, synchronized before and after: "mean" = seconds per call;
+      * spread: a graph of `chunk` calls replayed `reps` times (at least 20), each replay between its own
+        events (enqueued back to back, so the GPU does not wait on the host): "median", "p10", "p90" of the
+        per-replay seconds per call."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -120,23 +133,43 @@ def graph_time(torch, step, steps, warmup):
             step(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = []
-    for n in (warmup, steps):
+    graphs = {}
+    for n in sorted({warmup, steps, chunk}):
+        if n <= 0:
+            continue
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(n):
                 step(i)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    graphs[0].replay()
+        graphs[n] = g
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    if warmup > 0:
+        graphs[warmup].replay()
+    torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    graphs[1].replay()
+    graphs[steps].replay()
     t1.record(stream)
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / 1e3 / steps
+    mean = t0.elapsed_time(t1) / 1e3 / steps
+    graphs[chunk].replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for r in range(reps):
+        graphs[chunk].replay()
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[r].elapsed_time(ev[r + 1]) / 1e3 / chunk for r in range(reps)])
+    return {"mean": mean, "median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
+            "p90": float(np.percentile(per, 90)), "replays": reps, "calls_per_replay": chunk}
+
+
+def stats_us(t):
+    return {"median_us": round(t["median"] * 1e6, 3), "p10_us": round(t["p10"] * 1e6, 3),
+            "p90_us": round(t["p90"] * 1e6, 3), "replays": t["replays"],
+            "calls_per_replay": t.get("calls_per_replay", 1)}
 
 
 def time_decode(torch, exl3, dev, x, out, sets, steps, warmup):
@@ -148,7 +181,7 @@ def time_decode(torch, exl3, dev, x, out, sets, steps, warmup):
 def time_mlp(torch, exl3, synth, dev, copies=8, steps=64):
     """Dense MLP block of one decoder layer (hidden 5120, intermediate 17408; gate K=2, up K=3, down K=3) at
     decode sizes M = 1 and 8: merged gate_up, SiLU * mul, down, over `copies` weight sets in turn (89 MB of
-    trellis words each, beyond the last-level cache).  Returns ({M: seconds per call}, trellis bytes per
+    trellis words each, beyond the last-level cache).  Returns ({M: timing dict}, trellis bytes per
     call = 5120 * 17408 * (2 + 3 + 3) / 8)."""
     H, I = 5120, 17408
     sets = []
@@ -171,19 +204,21 @@ def time_mlp(torch, exl3, synth, dev, copies=8, steps=64):
         x = torch.randn((M, H), device=dev).to(torch.bfloat16)
         out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
         ws = exl3.alloc_workspace(exl3.mlp_workspace_bytes(M, H, I, sets[0][0], sets[0][1]), dev)
-        sec = graph_time(torch, lambda i: exl3.mlp_forward(x, *sets[i % copies], out=out, ws=ws), steps, copies)
-        res[M] = sec
-        print(f"# mlp H={H} I={I} M={M}: {sec * 1e6:.2f} us/call, {tbytes / sec / 1e9:.1f} GB/s trellis",
+        t = graph_time(torch, lambda i: exl3.mlp_forward(x, *sets[i % copies], out=out, ws=ws), steps, copies)
+        sec = t["median"]
+        res[M] = t
+        print(f"# mlp H={H} I={I} M={M}: {sec * 1e6:.2f} us/call (median), {tbytes / sec / 1e9:.1f} GB/s trellis",
               file=sys.stderr, flush=True)
     del sets
     torch.cuda.empty_cache()
     return res, tbytes
 
 
-def time_prefill(torch, exl3, synth, dev, reps=5):
+def time_prefill(torch, exl3, synth, dev, reps=20):
     """M=8192 prefill projections: gate_up (IC=5120 -> 2 x 17408, K=2 | K=3) and down (17408 -> 5120, K=3),
-    each on the 16-bit and on the 8-bit activation path.  Returns {name: (seconds per call, FLOP per call)};
-    FLOP = 2*M*IC*OC (decode and transforms not counted)."""
+    each on the 16-bit and on the 8-bit activation path, `reps` eager calls each between events.  Returns
+    {name: (timing dict as graph_time's, FLOP per call)}; FLOP = 2*M*IC*OC (decode and transforms not
+    counted)."""
     p = synth.PREFILL
     M = p["M"]
     res = {}
@@ -204,19 +239,22 @@ def time_prefill(torch, exl3, synth, dev, reps=5):
         out = torch.empty((M, col), dtype=torch.bfloat16, device=dev)
         for tag, flags in (("", 0), ("_int8", exl3.ACT_INT8)):
             ws = exl3.alloc_workspace(exl3.linear_multi_workspace_bytes(M, IC, sh, flags), dev)
-            exl3.linear_multi_into(out, x, sh, flags=flags, ws=ws)
+            for _ in range(2):
+                exl3.linear_multi_into(out, x, sh, flags=flags, ws=ws)
             torch.cuda.synchronize()
             stream = torch.cuda.current_stream()
-            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t0.record(stream)
-            for _ in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            ev[0].record(stream)
+            for r in range(reps):
                 exl3.linear_multi_into(out, x, sh, flags=flags, ws=ws)
-            t1.record(stream)
+                ev[r + 1].record(stream)
             torch.cuda.synchronize()
-            sec = t0.elapsed_time(t1) / 1e3 / reps
-            res[name + tag] = (sec, 2.0 * M * IC * col)
-            print(f"# prefill {name}{tag} M={M}: {sec * 1e3:.3f} ms/call, {res[name + tag][1] / sec / 1e12:.1f} TFLOP/s",
-                  file=sys.stderr, flush=True)
+            per = np.array([ev[r].elapsed_time(ev[r + 1]) / 1e3 for r in range(reps)])
+            t = {"mean": ev[0].elapsed_time(ev[-1]) / 1e3 / reps, "median": float(np.median(per)),
+                 "p10": float(np.percentile(per, 10)), "p90": float(np.percentile(per, 90)), "replays": reps}
+            res[name + tag] = (t, 2.0 * M * IC * col)
+            print(f"# prefill {name}{tag} M={M}: {t['median'] * 1e3:.3f} ms/call (median of {reps}), "
+                  f"{res[name + tag][1] / t['median'] / 1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
             del ws
         del x, out, sh
     return res
@@ -239,8 +277,9 @@ def time_moe(torch, exl3, synth, dev, steps=60):
     tb = sum(b.packed.trellis_bytes([int(b.packed.perm[e]) for e in used]) for b in banks) / MOE_COPIES
     out = torch.empty_like(x)
     ws = exl3.alloc_workspace(exl3.moe_workspace_bytes(banks[0], cfg["T"], cfg["topk"]), dev)
-    sec = graph_time(torch, lambda i: exl3.moe_bank_forward(out, x, ids, w, banks[i % MOE_COPIES], ws=ws), steps,
-                     MOE_COPIES * 2)
+    tm = graph_time(torch, lambda i: exl3.moe_bank_forward(out, x, ids, w, banks[i % MOE_COPIES], ws=ws), steps,
+                    MOE_COPIES * 2)
+    sec = tm["median"]
     print(f"# moe T={cfg['T']} E={cfg['E']} top{cfg['topk']}: {sec * 1e6:.1f} us/call, "
           f"{tb / sec / 1e9:.1f} GB/s trellis ({tb / 1e6:.1f} MB touched)", file=sys.stderr, flush=True)
     # a prefill-sized batch on the same banks: T = 4096 tokens (32,768 routed pairs; the route's counting
@@ -254,12 +293,13 @@ def time_moe(torch, exl3, synth, dev, steps=60):
     pw = torch.from_numpy(pw.astype(np.float32)).to(dev)
     outp = torch.empty_like(xp)
     wsp = exl3.alloc_workspace(exl3.moe_workspace_bytes(banks[0], T, cfg["topk"]), dev)
-    secp = graph_time(torch, lambda i: exl3.moe_bank_forward(outp, xp, pid, pw, banks[i % MOE_COPIES], ws=wsp), 12,
-                      MOE_COPIES)
+    tp = graph_time(torch, lambda i: exl3.moe_bank_forward(outp, xp, pid, pw, banks[i % MOE_COPIES], ws=wsp), 20,
+                    MOE_COPIES)
+    secp = tp["median"]
     flop = 2.0 * T * cfg["topk"] * (2 * cfg["H"] * cfg["I"] + cfg["I"] * cfg["H"])
     print(f"# moe T={T} E={cfg['E']} top{cfg['topk']}: {secp * 1e6:.1f} us/call, {flop / secp / 1e12:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
-    return sec, tb, (T, secp, flop)
+    return tm, tb, (T, tp, flop)
 
 
 def time_embed(torch, exl3, dev, reps=50):
@@ -280,17 +320,19 @@ def time_embed(torch, exl3, dev, reps=50):
         # several id sets, so repeated calls do not read the same rows out of the caches
         ids = [torch.randint(0, V, (T,), dtype=torch.int32, device=dev, generator=g) for _ in range(8)]
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        sec = graph_time(torch, lambda i: exl3.embed_int8(table, scale, ids[i % len(ids)], out=out), reps, 8)
+        t = graph_time(torch, lambda i: exl3.embed_int8(table, scale, ids[i % len(ids)], out=out), reps, 8)
+        sec = t["median"]
         nbytes = 3 * T * H
-        res[f"embed_int8_V{V}_H{H}_T{T}"] = (sec, nbytes)
+        res[f"embed_int8_V{V}_H{H}_T{T}"] = (t, nbytes)
         print(f"# embed_int8 V={V} H={H} T={T}: {sec * 1e6:.2f} us/call, {nbytes / sec / 1e9:.1f} GB/s",
               file=sys.stderr, flush=True)
     for M in (1, 16):
         x = torch.randn((M, H), device=dev, generator=g).to(torch.bfloat16)
         out = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
-        sec = graph_time(torch, lambda i: exl3.lm_head_int8(x, table, scale, out=out), max(reps // 5, 8), 4)
+        t = graph_time(torch, lambda i: exl3.lm_head_int8(x, table, scale, out=out), 20, 4)
+        sec = t["median"]
         nbytes = V * H + 2 * V + 2 * M * H + 2 * M * V
-        res[f"lm_head_int8_V{V}_H{H}_M{M}"] = (sec, nbytes)
+        res[f"lm_head_int8_V{V}_H{H}_M{M}"] = (t, nbytes)
         print(f"# lm_head_int8 V={V} H={H} M={M}: {sec * 1e6:.2f} us/call, {nbytes / sec / 1e9:.1f} GB/s",
               file=sys.stderr, flush=True)
     del table
@@ -298,20 +340,145 @@ def time_embed(torch, exl3, dev, reps=50):
     return res
 
 
-def cpu_baseline(synth, O):
-    """The fp64 oracle on one M=1 step of the same workload (both shards), single-threaded."""
+# ---- CPU oracle beside it: the fp64 oracle on the same M=1 step, one thread and all cores --------------
+# The step's output columns are independent, so the all-cores leg runs the unchanged oracle on one share of
+# each shard's 128-column blocks per worker process (spawned interpreters that import numpy and the oracle
+# only) and the single-thread leg runs it on all blocks in this process.
+
+_CPU_CASE = None
+
+
+def _cpu_case():
+    global _CPU_CASE
+    if _CPU_CASE is None:
+        from moe_exl3_pre_amd import synth
+        cfg = synth.DECODE_GATE_UP
+        _CPU_CASE = synth.merged_case(1001, 1, cfg["IC"], [(cfg["OC_gate"], cfg["K_gate"]), (cfg["OC_up"], cfg["K_up"])])
+    return _CPU_CASE
+
+
+def _cpu_part(job):
+    """Part `i` of `n` of one oracle step: for each shard, its blocks [i*B/n, (i+1)*B/n) of 128 columns."""
+    i, n = job
     from threadpoolctl import threadpool_limits
-    cfg = synth.DECODE_GATE_UP
-    case = synth.merged_case(1001, 1, cfg["IC"], [(cfg["OC_gate"], cfg["K_gate"]), (cfg["OC_up"], cfg["K_up"])])
+    from oracle import exl3_oracle as O
+    case = _cpu_case()
     with threadpool_limits(limits=1):
-        t = time.perf_counter()
         for s in case["shards"]:
-            O.linear(case["x"], s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"])
-        dt = time.perf_counter() - t
-    nbytes = sum(cfg["IC"] * s["OC"] * s["K"] // 8 for s in case["shards"])
-    return dict(value=round(nbytes / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample="one full M=1 step of the decode gate_up workload (both shards, fp64 numpy, 1 thread), "
-                       f"{dt:.1f} s")
+            nb = s["OC"] // 128
+            b0, b1 = i * nb // n, (i + 1) * nb // n
+            if b1 <= b0:
+                continue
+            code = s["code"][:, 8 * b0:8 * b1]
+            cols = slice(128 * b0, 128 * b1)
+            O.linear(case["x"], code, s["K"], s["s_in"], s["rin"], s["rout"][cols], s["s_out"][cols])
+    return i
+
+
+def _host_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "model_name": model}
+
+
+def cpu_baseline(min_seconds=10.0):
+    """The oracle on whole M=1 steps of the decode gate_up workload (both shards, 36.7 MB of trellis words
+    each): single-threaded in this process, then on all usable cores (capped at 16, the host share of one
+    GPU) as one share of the output blocks per worker.  Each leg repeats whole steps until `min_seconds`
+    have passed; rates are trellis GB/s."""
+    import multiprocessing as mp
+    from moe_exl3_pre_amd import synth
+    cfg = synth.DECODE_GATE_UP
+    nbytes = cfg["IC"] * (cfg["OC_gate"] * cfg["K_gate"] + cfg["OC_up"] * cfg["K_up"]) // 8
+    _cpu_case()
+    _cpu_part((0, 1))                                     # first touch of the arrays, untimed
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        _cpu_part((0, 1))
+        steps += 1
+        dt1 = time.perf_counter() - t0
+        if dt1 >= min_seconds or steps >= 50:
+            break
+    one = nbytes * steps / dt1 / 1e9
+    host = _host_info()
+    workers = max(1, min(16, host["usable_cpus"]))
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers) as pool:
+        pool.map(_cpu_part, [(i, workers) for i in range(workers)])      # untimed: imports and the case
+        psteps, t0 = 0, time.perf_counter()
+        while True:
+            pool.map(_cpu_part, [(i, workers) for i in range(workers)])
+            psteps += 1
+            dtn = time.perf_counter() - t0
+            if dtn >= min_seconds / 2 or psteps >= 200:
+                break
+    alln = nbytes * psteps / dtn / 1e9
+    return dict(value=round(alln, 4), unit="GB/s", cores=workers, kind="oracle",
+                single_thread={"value": round(one, 4), "cores": 1, "steps": steps, "seconds": round(dt1, 2)},
+                all_cores={"value": round(alln, 4), "cores": workers, "steps": psteps, "seconds": round(dtn, 2)},
+                host=host,
+                sample=f"whole M=1 steps of the decode gate_up workload (IC=4096, 2 x 14336, K=2 | K=3; fp64 numpy "
+                       f"oracle): {steps} steps on 1 thread in {dt1:.1f} s; {psteps} steps on {workers} worker "
+                       f"processes (one share of the 128-column blocks each) in {dtn:.1f} s")
+
+
+# ---- measured peaks: what this chip delivers, as secondary denominators -----------------------------------
+
+def measured_peaks(torch, exl3, dev):
+    """What this chip delivers: a streaming read of 4 GiB (variants of loads in flight and grid size) and
+    back-to-back MFMAs (f16 16x16x32 and 32x32x16, i8 16x16x64 and 32x32x32; 4 and 8 waves per SIMD); each
+    variant the median of 10 timed calls after 2 untimed, each figure the best variant."""
+    res, detail = {}, {}
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n=10):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(stream)
+        for r in range(n):
+            fn()
+            ev[r + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([ev[r].elapsed_time(ev[r + 1]) / 1e3 for r in range(n)]))
+
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(8192, dtype=torch.int32, device=dev)
+    best = 0.0
+    for variant in (0, 1, 2):
+        for blocks in (2048, 4096, 8192):
+            sec = timed(lambda: exl3.probe_read(buf, sink, blocks, variant))
+            gbs = buf.numel() / sec / 1e9
+            detail[f"read_v{variant}_b{blocks}"] = round(gbs, 1)
+            best = max(best, gbs)
+    res["hbm_read_GBps"] = round(best, 1)
+    del buf
+    msink = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    for key, kinds in (("mfma_f16_TFLOPs", (0, 1)), ("mfma_i8_TOPs", (2, 3))):
+        best = 0.0
+        for kind in kinds:
+            for blocks in (1024, 2048):
+                flop = exl3.probe_mfma(msink, kind, 1024, blocks)
+                sec = timed(lambda: exl3.probe_mfma(msink, kind, 1024, blocks))
+                detail[f"mfma_k{kind}_b{blocks}"] = round(flop / sec / 1e12, 1)
+                best = max(best, flop / sec / 1e12)
+        res[key] = round(best, 1)
+    torch.cuda.empty_cache()
+    print(f"# measured peaks: {res}; variants {detail}", file=sys.stderr, flush=True)
+    res["variants"] = detail
+    return res
 
 
 def run_sweep(torch, exl3, synth, dev, ms):
@@ -343,7 +510,7 @@ def run_sweep(torch, exl3, synth, dev, ms):
                                                   layers[i % L]["rin"], layers[i % L]["rout"], layers[i % L]["s_out"],
                                                   flags=flags, ws=ws)
                 if M <= 128:      # launch-bound sizes: replay a captured graph of the 64 calls
-                    sec = graph_time(torch, step, L, L)
+                    sec = graph_time(torch, step, L, L)["mean"]
                 else:
                     for i in range(L):
                         step(i)
@@ -441,7 +608,7 @@ def main():
         for _ in range(4):
             dst.copy_(src)
         del src, dst
-        time_prefill(torch, exl3, synth, dev, reps=1)
+        time_prefill(torch, exl3, synth, dev, reps=2)
         print(json.dumps({"pmc_prefill": True, "copy_bytes": 1 << 30}), flush=True)
         return
     IC, ldo, sets, trellis_bytes = build_gate_up(torch, dev, synth, COPIES)
@@ -456,18 +623,24 @@ def main():
         _, xb = synth.random_activations(rng, M, IC)
         x = torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16)
         out = torch.empty((M, ldo), dtype=torch.bfloat16, device=dev)
-        sec = time_decode(torch, exl3, dev, x, out, sets, a.steps if M == 1 else max(a.steps // 4, COPIES),
-                          a.warmup if M == 1 else COPIES)
-        results[M] = sec
-        print(f"# decode gate_up M={M}: {sec * 1e6:.2f} us/step, {trellis_bytes / sec / 1e9:.1f} GB/s trellis",
+        t = time_decode(torch, exl3, dev, x, out, sets, a.steps if M == 1 else max(a.steps // 4, 2 * COPIES),
+                        a.warmup if M == 1 else COPIES)
+        results[M] = t
+        print(f"# decode gate_up M={M}: {t['mean'] * 1e6:.2f} us/step (median {t['median'] * 1e6:.2f}, p10 "
+              f"{t['p10'] * 1e6:.2f}, p90 {t['p90'] * 1e6:.2f}), {trellis_bytes / t['mean'] / 1e9:.1f} GB/s trellis",
               file=sys.stderr, flush=True)
 
+    peaks = None if a.no_peaks else measured_peaks(torch, exl3, dev)
     prefill = {} if a.no_prefill else time_prefill(torch, exl3, synth, dev)
     moe = None if a.no_moe else time_moe(torch, exl3, synth, dev)
     mlp = None if a.no_mlp else time_mlp(torch, exl3, synth, dev)
     embed = {} if a.no_embed else time_embed(torch, exl3, dev)
 
-    sec = results[1]
+    def vs_measured(val, key):
+        return round(val / peaks[key], 4) if peaks else None
+
+    t1 = results[1]
+    sec = t1["mean"]
     gbs = trellis_bytes / sec / 1e9
     traffic = stored_traffic()
     line = {
@@ -477,38 +650,51 @@ def main():
         "config": {"workload": "decode gate_up: IC=4096, gate OC=14336 K=2 | up OC=14336 K=3, M=1, "
                                f"{COPIES} rotated weight copies", "M": 1, "IC": IC, "OC": [14336, 14336], "K": [2, 3],
                    "trellis_bytes_per_step": trellis_bytes},
+        "timing": dict(stats_us(t1), mean_us=round(sec * 1e6, 3)),
         # one step is one launch of the decode kernel, so the per-step event time is its launch duration
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": DECODE_KERNEL,
-                     "kernel_us": round(sec * 1e6, 3), "bytes_per_launch": trellis_bytes},
-        "extra": {f"decode_M{M}": {"us_per_step": round(s * 1e6, 3), "trellis_GBps": round(trellis_bytes / s / 1e9, 1),
-                                   "frac_hbm": round(trellis_bytes / s / 1e9 / HBM_PEAK_GBS, 4)}
-                  for M, s in results.items()},
+                     "kernel_us": round(sec * 1e6, 3), "bytes_per_launch": trellis_bytes,
+                     "frac_of_measured_read": vs_measured(gbs, "hbm_read_GBps")},
+        "extra": {},
     }
-    for name, (s, flop) in prefill.items():
-        line["extra"][f"prefill_{name}_M8192"] = {"ms_per_call": round(s * 1e3, 4), "TFLOPs": round(flop / s / 1e12, 1),
-                                                  "frac_of_f16_peak": round(flop / s / 1e12 / F16_PEAK_TFLOPS, 4)}
+    if peaks:
+        line["measured_peaks"] = peaks
+    for M, t in results.items():
+        g = trellis_bytes / t["mean"] / 1e9
+        line["extra"][f"decode_M{M}"] = dict(stats_us(t), us_per_step=round(t["mean"] * 1e6, 3), trellis_GBps=round(g, 1),
+                                             frac_hbm=round(g / HBM_PEAK_GBS, 4),
+                                             frac_of_measured_read=vs_measured(g, "hbm_read_GBps"))
+    for name, (t, flop) in prefill.items():
+        tf = flop / t["median"] / 1e12
+        e = dict(stats_us(t), ms_per_call=round(t["median"] * 1e3, 4), TFLOPs=round(tf, 1),
+                 frac_of_f16_peak=round(tf / F16_PEAK_TFLOPS, 4),
+                 frac_of_measured_f16=vs_measured(tf, "mfma_f16_TFLOPs"))
+        if name.endswith("_int8"):
+            # the 8-bit path's integer codes run on the f16 MFMA (exact products); also against the int8 peak
+            e.update(frac_of_i8_peak=round(tf / I8_PEAK_TOPS, 4), frac_of_measured_i8=vs_measured(tf, "mfma_i8_TOPs"))
+        line["extra"][f"prefill_{name}_M8192"] = e
     if moe is not None:
-        s, tb, (Tp, sp, flp) = moe
-        line["extra"][f"moe_T{Tp}_E128_top8"] = {"us_per_call": round(sp * 1e6, 1),
-                                                 "TFLOPs": round(flp / sp / 1e12, 1),
-                                                 "frac_of_f16_peak": round(flp / sp / 1e12 / F16_PEAK_TFLOPS, 4)}
-        line["extra"]["moe_T256_E128_top8"] = {"us_per_call": round(s * 1e6, 2), "trellis_MB": round(tb / 1e6, 1),
-                                               "trellis_GBps": round(tb / s / 1e9, 1),
-                                               "frac_hbm": round(tb / s / 1e9 / HBM_PEAK_GBS, 4)}
+        tm, tb, (Tp, tp, flp) = moe
+        tf = flp / tp["median"] / 1e12
+        line["extra"][f"moe_T{Tp}_E128_top8"] = dict(stats_us(tp), TFLOPs=round(tf, 1),
+                                                     frac_of_f16_peak=round(tf / F16_PEAK_TFLOPS, 4))
+        g = tb / tm["median"] / 1e9
+        line["extra"]["moe_T256_E128_top8"] = dict(stats_us(tm), trellis_MB=round(tb / 1e6, 1), trellis_GBps=round(g, 1),
+                                                   frac_hbm=round(g / HBM_PEAK_GBS, 4),
+                                                   frac_of_measured_read=vs_measured(g, "hbm_read_GBps"))
     if mlp is not None:
         times, tb = mlp
-        for M, s in times.items():
-            line["extra"][f"mlp_H5120_I17408_M{M}"] = {"us_per_call": round(s * 1e6, 2),
-                                                        "trellis_GBps": round(tb / s / 1e9, 1),
-                                                        "frac_hbm": round(tb / s / 1e9 / HBM_PEAK_GBS, 4)}
-    for key, (s, nbytes) in embed.items():
-        line["extra"][key] = {"us_per_call": round(s * 1e6, 2),
-                                                           "GBps": round(nbytes / s / 1e9, 1),
-                                                           "frac_hbm": round(nbytes / s / 1e9 / HBM_PEAK_GBS, 4)}
+        for M, t in times.items():
+            g = tb / t["median"] / 1e9
+            line["extra"][f"mlp_H5120_I17408_M{M}"] = dict(stats_us(t), trellis_GBps=round(g, 1),
+                                                            frac_hbm=round(g / HBM_PEAK_GBS, 4))
+    for key, (t, nbytes) in embed.items():
+        g = nbytes / t["median"] / 1e9
+        line["extra"][key] = dict(stats_us(t), GBps=round(g, 1), frac_hbm=round(g / HBM_PEAK_GBS, 4),
+                                  frac_of_measured_read=vs_measured(g, "hbm_read_GBps"))
     if not a.no_cpu:
-        from oracle import exl3_oracle as O
-        line["cpu_baseline"] = cpu_baseline(synth, O)
+        line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
 
 

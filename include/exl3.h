@@ -306,6 +306,22 @@ int exl3_decode_tiles(void* w_out, const int16_t* code, int64_t IC, int64_t OC, 
 int exl3_rotate_activations(void* q_out, float* scale_out, const void* x, int64_t M, int64_t IC,
                             const void* s_in, const void* rin, unsigned flags, void* stream);
 
+/* --------------------------------------------------------------------------------------------------
+ * Measurement hooks, not part of the layer: what the chip delivers, as secondary roofline denominators
+ * beside the published peaks (8 TB/s HBM; 2.5 PFLOP/s dense f16; 5 POP/s dense int8).
+ *   exl3_probe_read   reads `bytes` (a multiple of 16) at `src` (16-byte aligned) once with 16-byte loads
+ *                     over `blocks` workgroups of 256 threads, 4 (variant 0) or 8 (variant 1; variant 2:
+ *                     non-temporal) loads in flight per thread; sink: uint32 [blocks] (an XOR per block).
+ *   exl3_probe_mfma   `blocks` workgroups of 4 waves, each wave issuing back-to-back independent MFMAs for
+ *                     `iters` iterations: kind 0 f16 16x16x32 (8 per iteration, 16384 FLOP each), kind 1
+ *                     f16 32x32x16 (4, 32768 FLOP each), kind 2 i8 16x16x64 (8, 32768 OP each), kind 3 i8
+ *                     32x32x32 (4, 65536 OP each); sink: float [blocks * 256].
+ * Operations per call: blocks * 4 * iters * 131072 for kinds 0 and 1, * 262144 for kinds 2 and 3.
+ * Return EXL3_OK / EXL3_EINVAL / EXL3_ELAUNCH.
+ * ------------------------------------------------------------------------------------------------ */
+int exl3_probe_read(const void* src, size_t bytes, uint32_t* sink, int blocks, int variant, void* stream);
+int exl3_probe_mfma(float* sink, int kind, int iters, int blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -739,6 +739,28 @@ int static_scratch(void** ptr, hipStream_t stream) {
 
 extern "C" {
 
+int exl3_probe_read(const void* src, size_t bytes, uint32_t* sink, int blocks, int variant, void* stream) {
+  if (!src || !sink) return fail(EXL3_EINVAL, "src/sink: null");
+  if (!aligned(src, 16) || bytes % 16) return fail(EXL3_EINVAL, "src/bytes: not 16-byte aligned");
+  if (blocks < 1 || blocks > (1 << 20)) return fail(EXL3_EINVAL, "blocks: %d is outside 1..2^20", blocks);
+  if (variant < 0 || variant > 2) return fail(EXL3_EINVAL, "variant: %d is outside 0..2", variant);
+  if (int rc = launch_status(launch_probe_read(src, bytes, sink, blocks, variant, static_cast<hipStream_t>(stream)),
+                             "exl3_probe_read"))
+    return rc;
+  return ok();
+}
+
+int exl3_probe_mfma(float* sink, int kind, int iters, int blocks, void* stream) {
+  if (!sink) return fail(EXL3_EINVAL, "sink: null");
+  if (kind < 0 || kind > 3) return fail(EXL3_EINVAL, "kind: %d is outside 0..3", kind);
+  if (iters < 1) return fail(EXL3_EINVAL, "iters: %d < 1", iters);
+  if (blocks < 1 || blocks > (1 << 20)) return fail(EXL3_EINVAL, "blocks: %d is outside 1..2^20", blocks);
+  if (int rc = launch_status(launch_probe_mfma(sink, kind, iters, blocks, static_cast<hipStream_t>(stream)),
+                             "exl3_probe_mfma"))
+    return rc;
+  return ok();
+}
+
 size_t exl3_static_scratch_bytes(void) { return kStaticScratchBytes; }
 
 int exl3_linear_multi_into_static(void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n_shards,

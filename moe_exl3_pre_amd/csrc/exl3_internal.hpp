@@ -155,4 +155,9 @@ struct MoeLaunch {
 int64_t moe_max_chunks(int64_t P, int E);
 hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream);
 
+// ---- measurement hooks (k_probe.hip): a streaming read and back-to-back MFMAs, for measured peaks
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, int blocks, int variant,
+                             hipStream_t stream);
+hipError_t launch_probe_mfma(float* sink, int kind, int iters, int blocks, hipStream_t stream);
+
 }  // namespace exl3

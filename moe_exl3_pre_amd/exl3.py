@@ -63,6 +63,9 @@ _SIGS = {
     "exl3_linear_multi_into": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                               ctypes.c_int64, ctypes.c_int, ctypes.POINTER(Shard), ctypes.c_uint,
                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "exl3_probe_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]),
+    "exl3_probe_mfma": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "exl3_static_scratch_bytes": (ctypes.c_size_t, []),
     "exl3_linear_multi_into_static": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                                      ctypes.c_int64, ctypes.c_int, ctypes.POINTER(Shard), ctypes.c_uint,
@@ -226,6 +229,21 @@ def linear_multi_into_static(out, x, shards, flags: int = 0):
     _check(lib().exl3_linear_multi_into_static(_ptr(out), out.shape[1], _ptr(x), M, IC, len(shards), arr, flags,
                                                _stream(dev)))
     return out
+
+
+def probe_read(src, sink, blocks: int, variant: int = 0):
+    """Measurement hook: one streaming read of the bytes of `src` (device tensor, contiguous, 16-byte multiple);
+    sink uint32-sized tensor of `blocks` elements.  See exl3_probe_read."""
+    _check(lib().exl3_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), blocks, variant,
+                                 _stream(src.device)))
+
+
+def probe_mfma(sink, kind: int, iters: int, blocks: int):
+    """Measurement hook: back-to-back MFMAs (kind 0 f16 16x16x32, 1 f16 32x32x16, 2 i8 16x16x64, 3 i8 32x32x32);
+    sink float32 [blocks * 256].  Returns the FLOP (or OP) count of the call.  See exl3_probe_mfma."""
+    _check(lib().exl3_probe_mfma(_ptr(sink), kind, iters, blocks, _stream(sink.device)))
+    per = {0: 131072, 1: 131072, 2: 262144, 3: 262144}[kind]
+    return float(blocks) * 4 * iters * per
 
 
 # ------------------------------------------------------------------------------------------ dense MLP block
