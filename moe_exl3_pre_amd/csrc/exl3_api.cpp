@@ -17,7 +17,7 @@ namespace exl3 {
 // the dense MLP block's down input from its gate_up output (k_prepass.hip): h = bf16(silu(g) * u) rotated into the
 // fragment-major fp16 operand of launch_prepass_f16.
 hipError_t launch_prepass_silu_f16(const void* gu, const void* s_in, const void* rin, void* xh, int64_t M, int64_t IC,
-                                   hipStream_t stream);
+                                   hipStream_t stream, bool rows32 = false);
 }  // namespace exl3
 
 namespace {
@@ -142,7 +142,7 @@ Layout layout_for(size_t slab_bytes, int64_t M = 0, int64_t IC = 0, int n_xh = 0
   L.slab_off = align_up(kCounterBytes);
   L.slab_bytes = align_up(slab_bytes);
   L.xh_off = L.slab_off + L.slab_bytes;
-  L.scale_off = align_up(size_t((M + 15) / 16 * 16) * size_t(IC) * 2);   // fragment-major: rows padded to 16
+  L.scale_off = align_up(size_t((M + 31) / 32 * 32) * size_t(IC) * 2);   // fragment-major: rows padded to 32
   L.part_off = L.scale_off + (int8 ? align_up(size_t(M) * 4) : 0);
   L.xh_bytes = L.part_off + (int8 ? align_up(size_t(M) * size_t(IC / 128) * 4) : 0);
   L.total = L.xh_off + L.xh_bytes * size_t(n_xh);
@@ -239,9 +239,9 @@ int run_gemm(const char* who, void* out, int64_t ldo, const void* x, int64_t M, 
     float* scale = int8 ? reinterpret_cast<float*>(region + L.scale_off) : nullptr;
     if (slot[i] > done) {
       hipError_t e = int8 ? launch_prepass_i8(x, in[i].s_in, in[i].rin, region, scale, M, IC, true, stream, true,
-                                              reinterpret_cast<float*>(region + L.part_off))
-                     : gu ? launch_prepass_silu_f16(gu, in[i].s_in, in[i].rin, region, M, IC, stream)
-                          : launch_prepass_f16(x, in[i].s_in, in[i].rin, region, M, IC, true, stream, (M + 15) / 16 * 16);
+                                              reinterpret_cast<float*>(region + L.part_off), true)
+                     : gu ? launch_prepass_silu_f16(gu, in[i].s_in, in[i].rin, region, M, IC, stream, true)
+                          : launch_prepass_f16(x, in[i].s_in, in[i].rin, region, M, IC, true, stream, 0, true);
       if (int rc = launch_status(e, who)) return rc;
       done = slot[i];
     }

@@ -55,16 +55,17 @@ bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl
 hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,
                          void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream, bool silu = false);
 
-// permuted: the GEMM's fragment-major layout (k_gemm.hip), else natural row-major.  Rows
-// [M, M_pad) of xh are written as zeros.
+// permuted: fragment-major, with 16-row fragments (the decode-phase kernel's operand) or with rows32 the
+// 32-row fragments of the prefill GEMM (k_gemm.hip), rows past M written as zeros up to the next multiple
+// of 16 (32); else natural row-major, rows [M, M_pad) written as zeros.
 hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, void* xh, int64_t M, int64_t IC,
-                              bool permuted, hipStream_t stream, int64_t M_pad = 0);
+                              bool permuted, hipStream_t stream, int64_t M_pad = 0, bool rows32 = false);
 // Natural layout: q receives int8 codes.  permuted with f16_codes: the same codes as fp16 numbers in the
-// fragment-major layout (the GEMM's operand; rows up to a multiple of 16 written as zeros), which needs
-// part, M * (IC / 128) floats of scratch.  Other combinations are rejected.
+// fragment-major layout (16- or, with rows32, 32-row fragments), which needs part, M * (IC / 128) floats of
+// scratch.  Other combinations are rejected.
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
                              int64_t IC, bool permuted, hipStream_t stream, bool f16_codes = false,
-                             float* part = nullptr);
+                             float* part = nullptr, bool rows32 = false);
 hipError_t launch_decode_tiles(void* w, const int16_t* code, int64_t IC, int64_t OC, int K, hipStream_t stream);
 // K split of the prefill GEMM.  One wave owns a 128 x 128 output tile, a block is 4 waves (128 rows x 512
 // columns) and the chip holds 256 blocks (1024 waves) at a time.  A shard with fewer than 1024 tiles has
@@ -119,7 +120,7 @@ inline size_t gemm_slab_bytes(int64_t M, int64_t OC, GemmSplit sp) {
 }
 
 // Prefill-phase GEMM of one shard (one wave per 128 x 128 output tile); xf is the pre-pass output in the
-// fragment-major layout (rows padded to 16).  With row_scale (8-bit path) every output row is multiplied
+// 32-row fragment-major layout (rows padded to 32).  With row_scale (8-bit path) every output row is multiplied
 // by row_scale[row] before the output transform.  split.splits > 1 needs slab (gemm_slab_bytes).
 hipError_t launch_gemm(const void* xf, const int16_t* code, int K, const void* rout, const void* s_out, void* out,
                        int64_t ldo, int64_t col0, int64_t M, int64_t IC, int64_t OC, hipStream_t stream,

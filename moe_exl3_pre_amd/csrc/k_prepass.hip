@@ -147,13 +147,32 @@ __device__ __forceinline__ void frag_transform(const uint16_t* __restrict__ x, c
   }
 }
 
-// Fragment (step 2q + t, half h), lane (n, g) holds PERM16 positions 8h .. 8h+7 of 16-group g + 4t, i.e. the
-// features (4h + j, 4h + j + 8) for j = 0..3: o(t, h)[j] packs those two of u (already converted).
-__device__ __forceinline__ uint16_t* frag_unit_base(uint16_t* xf, int64_t IC, int64_t rb, int64_t q, int lane) {
-  return xf + ((rb * (IC / 64) + 2 * q) * 2) * 512 + lane * 8;
+// Where a 16-row unit's values go.  Fragment (step 2q + t, half h), lane (n, g) holds PERM16 positions
+// 8h .. 8h+7 of 16-group g + 4t, i.e. the features (4h + j, 4h + j + 8) for j = 0..3.
+//   16-row layout (the 16x16x32 MFMA's A operand): per 16-row block rb, step s, half h, 1 KB with lane
+//     (n, g) = row 16 rb + n, PERM16 positions 64 s + 16 g + 8 h .. +8;
+//   32-row layout (the 32x32x16 MFMA's A operand): per 32-row block, step s, pair j, half h, 1 KB with
+//     lane (m, k) = row 32 rb + m (m < 32), PERM16 positions 64 s + 16 (2 j + k) + 8 h .. +8, k < 2: the
+//     two halves of the wave take the same positions of two different 16-groups.
+template <bool R32>
+__device__ __forceinline__ uint16_t* frag_addr(uint16_t* xf, int64_t IC, int64_t rb, int64_t q, int lane, int t,
+                                               int h) {
+  const int64_t step = 2 * q + t;
+  if constexpr (!R32) {
+    return xf + ((rb * (IC / 64) + step) * 2 + h) * 512 + lane * 8;
+  } else {
+    const int n = lane & 15, g = lane >> 4;
+    const int lp = 16 * int(rb & 1) + n + 32 * (g & 1);
+    return xf + ((((rb >> 1) * (IC / 64) + step) * 2 + (g >> 1)) * 2 + h) * 512 + lp * 8;
+  }
 }
 
-template <bool SILU>
+// 16-row units a fragment-major launch covers: rows padded to 16, or to 32 for the 32-row layout.
+__host__ __device__ inline int64_t frag_row_units(int64_t M, bool r32) {
+  return r32 ? (M + 31) / 32 * 2 : (M + 15) / 16;
+}
+
+template <bool SILU, bool R32>
 __global__ __launch_bounds__(256) void prepass_frag_f16_kernel(const uint16_t* __restrict__ x,
                                                                const uint16_t* __restrict__ s_in,
                                                                const uint16_t* __restrict__ rin,
@@ -161,11 +180,10 @@ __global__ __launch_bounds__(256) void prepass_frag_f16_kernel(const uint16_t* _
   const int lane = threadIdx.x & 63;
   const int64_t nq = IC / kHad;
   const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (unit >= (M + 15) / 16 * nq) return;
+  if (unit >= frag_row_units(M, R32) * nq) return;
   const int64_t rb = unit / nq, q = unit % nq;
   float v[2][16];
   frag_transform<SILU>(x, s_in, rin, M, IC, rb, q, lane, v);
-  uint16_t* base = frag_unit_base(xf, IC, rb, q, lane);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -174,7 +192,7 @@ __global__ __launch_bounds__(256) void prepass_frag_f16_kernel(const uint16_t* _
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         o[j] = f32x2_to_f16x2(v[t][4 * h + j] * kInvSqrt128, v[t][4 * h + j + 8] * kInvSqrt128);
-      *reinterpret_cast<u32x4*>(base + (2 * t + h) * 512) = o;
+      *reinterpret_cast<u32x4*>(frag_addr<R32>(xf, IC, rb, q, lane, t, h)) = o;
     }
 }
 
@@ -217,6 +235,7 @@ __global__ __launch_bounds__(256) void prepass_row_scale_kernel(const float* __r
   if (lane == 0) scale[row] = __fdiv_rn(a, 127.0f);
 }
 
+template <bool R32>
 __global__ __launch_bounds__(256) void prepass_frag_codes_kernel(const uint16_t* __restrict__ x,
                                                                  const uint16_t* __restrict__ s_in,
                                                                  const uint16_t* __restrict__ rin,
@@ -225,7 +244,7 @@ __global__ __launch_bounds__(256) void prepass_frag_codes_kernel(const uint16_t*
   const int lane = threadIdx.x & 63;
   const int64_t nq = IC / kHad;
   const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (unit >= (M + 15) / 16 * nq) return;
+  if (unit >= frag_row_units(M, R32) * nq) return;
   const int64_t rb = unit / nq, q = unit % nq;
   float v[2][16];
   frag_transform(x, s_in, rin, M, IC, rb, q, lane, v);
@@ -234,7 +253,6 @@ __global__ __launch_bounds__(256) void prepass_frag_codes_kernel(const uint16_t*
   auto code = [&](float xv) -> float {
     return sc > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(xv * kInvSqrt128, sc)), -127.f), 127.f) : 0.f;
   };
-  uint16_t* base = frag_unit_base(xf, IC, rb, q, lane);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -242,7 +260,7 @@ __global__ __launch_bounds__(256) void prepass_frag_codes_kernel(const uint16_t*
       u32x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = f32x2_to_f16x2(code(v[t][4 * h + j]), code(v[t][4 * h + j + 8]));
-      *reinterpret_cast<u32x4*>(base + (2 * t + h) * 512) = o;
+      *reinterpret_cast<u32x4*>(frag_addr<R32>(xf, IC, rb, q, lane, t, h)) = o;
     }
 }
 
@@ -287,12 +305,17 @@ __global__ __launch_bounds__(256) void prepass_i8_kernel(const uint16_t* __restr
 }
 
 hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, void* xh, int64_t M, int64_t IC,
-                              bool permuted, hipStream_t stream, int64_t M_pad) {
+                              bool permuted, hipStream_t stream, int64_t M_pad, bool rows32) {
   if (M <= 0) return hipSuccess;
-  if (permuted) {                                         // fragment-major: rows padded to 16 with zeros
-    const int64_t units = (M + 15) / 16 * (IC / kHad);
-    hipLaunchKernelGGL(prepass_frag_f16_kernel<false>, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream,
-                       (const uint16_t*)x, (const uint16_t*)s_in, (const uint16_t*)rin, (uint16_t*)xh, M, IC);
+  if (permuted) {                                         // fragment-major: rows padded to 16 (32) with zeros
+    const int64_t units = frag_row_units(M, rows32) * (IC / kHad);
+    const dim3 g((unsigned)((units + 3) / 4)), b(256);
+    if (rows32)
+      hipLaunchKernelGGL((prepass_frag_f16_kernel<false, true>), g, b, 0, stream, (const uint16_t*)x,
+                         (const uint16_t*)s_in, (const uint16_t*)rin, (uint16_t*)xh, M, IC);
+    else
+      hipLaunchKernelGGL((prepass_frag_f16_kernel<false, false>), g, b, 0, stream, (const uint16_t*)x,
+                         (const uint16_t*)s_in, (const uint16_t*)rin, (uint16_t*)xh, M, IC);
     return hipGetLastError();
   }
   const int64_t rows = M_pad > M ? M_pad : M;
@@ -304,18 +327,23 @@ hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, 
 }
 
 // The dense MLP block's down input straight from its gate_up output gu [M, 2 IC]: h = bf16(silu(g) * u)
-// formed in registers, then the fragment-major fp16 rotation of launch_prepass_f16 (rows padded to 16).
+// formed in registers, then the fragment-major fp16 rotation of launch_prepass_f16 (16- or 32-row fragments).
 hipError_t launch_prepass_silu_f16(const void* gu, const void* s_in, const void* rin, void* xh, int64_t M, int64_t IC,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, bool rows32) {
   if (M <= 0) return hipSuccess;
-  const int64_t units = (M + 15) / 16 * (IC / kHad);
-  hipLaunchKernelGGL(prepass_frag_f16_kernel<true>, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream,
-                     (const uint16_t*)gu, (const uint16_t*)s_in, (const uint16_t*)rin, (uint16_t*)xh, M, IC);
+  const int64_t units = frag_row_units(M, rows32) * (IC / kHad);
+  const dim3 g((unsigned)((units + 3) / 4)), b(256);
+  if (rows32)
+    hipLaunchKernelGGL((prepass_frag_f16_kernel<true, true>), g, b, 0, stream, (const uint16_t*)gu,
+                       (const uint16_t*)s_in, (const uint16_t*)rin, (uint16_t*)xh, M, IC);
+  else
+    hipLaunchKernelGGL((prepass_frag_f16_kernel<true, false>), g, b, 0, stream, (const uint16_t*)gu,
+                       (const uint16_t*)s_in, (const uint16_t*)rin, (uint16_t*)xh, M, IC);
   return hipGetLastError();
 }
 
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
-                             int64_t IC, bool permuted, hipStream_t stream, bool f16_codes, float* part) {
+                             int64_t IC, bool permuted, hipStream_t stream, bool f16_codes, float* part, bool rows32) {
   if (M <= 0) return hipSuccess;
   if (permuted && f16_codes) {                            // fragment-major fp16 codes (the GEMM operand)
     if (!part) return hipErrorInvalidValue;
@@ -325,8 +353,14 @@ hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, v
     hipLaunchKernelGGL(prepass_frag_amax_kernel, ug, blk, 0, stream, xx, si, ri, part, M, IC);
     hipLaunchKernelGGL(prepass_row_scale_kernel, dim3((unsigned)((M + 3) / 4)), blk, 0, stream, (const float*)part,
                        scale, M, IC / kHad);
-    hipLaunchKernelGGL(prepass_frag_codes_kernel, ug, blk, 0, stream, xx, si, ri, (const float*)scale, (uint16_t*)q, M,
-                       IC);
+    const int64_t cunits = frag_row_units(M, rows32) * (IC / kHad);
+    const dim3 cg((unsigned)((cunits + 3) / 4));
+    if (rows32)
+      hipLaunchKernelGGL(prepass_frag_codes_kernel<true>, cg, blk, 0, stream, xx, si, ri, (const float*)scale,
+                         (uint16_t*)q, M, IC);
+    else
+      hipLaunchKernelGGL(prepass_frag_codes_kernel<false>, cg, blk, 0, stream, xx, si, ri, (const float*)scale,
+                         (uint16_t*)q, M, IC);
     return hipGetLastError();
   }
   if (permuted || f16_codes) return hipErrorInvalidValue;  // natural layout: int8 codes only
