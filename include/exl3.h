@@ -173,9 +173,10 @@ int exl3_linear_multi_into_static(void* out, int64_t ldo, const void* x, int64_t
                                   int n_shards, const exl3_shard* shards, unsigned flags, void* stream);
 
 /* --------------------------------------------------------------------------------------------------
- * MoE expert bank ("dspark/worker/exl3/bank.py", `Exl3Bank` docstring and `allocate`): experts sit in
- * K-sorted physical slots; the trellis words of all experts share two flat int16 banks (w13 = [w1 | w3]
- * per slot, and w2); sign/scale vectors are fp16 [E, ...].
+ * MoE expert bank (layout of "dspark/worker/exl3/bank.py", `Exl3Bank` and `allocate`): the slot order
+ * sorts the experts by bit width, so equal-K experts occupy one run of slots; one int16 array holds each
+ * slot's w1 words followed by its w3 words, a second one each slot's w2 words, and the fp16 sign/scale
+ * vectors are indexed by slot.
  *
  *   out[t] = bf16( sum_j topk_w[t, j] * E_{topk_ids[t, j]}(x[t]) )          (j in top-k order)
  *   E_e(v) = L_w2( silu(L_w1(v)) * L_w3(v) ),   silu(h) = h / (1 + exp(-h)),
@@ -218,8 +219,14 @@ size_t exl3_moe_workspace_bytes(const exl3_bank* bank, int64_t T, int topk, unsi
 
 /*   out      bf16 [T, H];  x  bf16 [T, H]
  *   topk_ids int32 [T, topk] logical expert ids in [0, E) (device);  topk_w float32 [T, topk] (device).
- * An id outside [0, E) is ignored (contributes nothing).  flags must be 0 (EXL3_ACT_INT8 answers
- * EXL3_EUNSUPPORTED).  Returns EXL3_OK / EXL3_EINVAL / EXL3_EWORKSPACE / EXL3_EUNSUPPORTED / EXL3_ELAUNCH. */
+ * An id outside [0, E) is ignored (contributes nothing).
+ * Plans: below 256 routed pairs per expert on average (T * topk < 256 E) the call streams every expert's
+ * weights once per chunk of up to 32 of its rows (the decode-sized plan); from there on it runs grouped
+ * tiles of 128 rows x 128 columns on MFMA (the prefill plan), as long as T * topk * (max(H, I) + 64) * 2 <
+ * 2^31.  flags: 0, EXL3_FORCE_GEMV (the decode-sized plan at any T) or EXL3_FORCE_MFMA (the prefill plan at
+ * any T; EXL3_EUNSUPPORTED past the size limit); the two are exclusive.  Both plans give the same results
+ * up to fp32 summation order inside each projection.  EXL3_ACT_INT8 answers EXL3_EUNSUPPORTED.
+ * Returns EXL3_OK / EXL3_EINVAL / EXL3_EWORKSPACE / EXL3_EUNSUPPORTED / EXL3_ELAUNCH. */
 int exl3_moe_bank_forward(void* out, const void* x, int64_t T,
                           const int32_t* topk_ids, const float* topk_w, int topk,
                           const exl3_bank* bank, unsigned flags, void* ws, size_t ws_bytes, void* stream);

@@ -1,9 +1,9 @@
 """Host-side packing of one layer's MoE expert bank into the layout exl3_moe_bank_forward reads.
 
-Layout ("dspark/worker/exl3/bank.py", `Exl3Bank`, `allocate` and `views`): experts are placed in
-physical slots sorted by their bit widths, so every group of slots with the same (k_gu, k_d) is a
-contiguous range; the trellis words of all slots share two flat int16 banks, w13 holding w1 then w3 of
-each slot and w2 holding the down projections; the sign/scale vectors are stacked per slot.
+Layout ("dspark/worker/exl3/bank.py", `Exl3Bank` and `allocate`): the slot order sorts the experts by
+their bit widths, so the slots of one (k_gu, k_d) pair form one contiguous run.  One int16 array holds,
+slot after slot, the w1 words and then the w3 words; a second int16 array holds the w2 words the same
+way.  The fp16 sign/scale vectors are indexed by slot.
 
 Slot order: a stable sort of the logical expert ids by (k_gu, k_d), ascending; the groups are the
 maximal runs of equal (k_gu, k_d).  perm[e] is the slot of logical expert e.
@@ -34,17 +34,22 @@ class PackedBank:
         return sum(2 * self.H * self.I * int(self.k_gu[p]) // 8 + self.H * self.I * int(self.k_d[p]) // 8
                    for p in slots)
 
-    def views(self, p: int):
-        """((trellis, suh, svh, K) for w1, w3, w2) of physical slot p, as views into the flat banks."""
+    def projection(self, p: int, name: str):
+        """Projection `name` ("w1", "w3" or "w2") of physical slot p: (trellis words reshaped to the tile grid
+        [IC/16, OC/16, 16 K] as a view of the flat bank, input sign/scale vector, output sign/scale vector,
+        K).  w1 and w3 read H features and give I, w2 the other way round."""
         H, I = self.H, self.I
-        kg, kd = int(self.k_gu[p]), int(self.k_d[p])
-        n13, n2 = H * I * kg // 16, I * H * kd // 16
-        w1 = self.w13[self.off_w1[p]:self.off_w1[p] + n13].reshape(H // 16, I // 16, 16 * kg)
-        w3 = self.w13[self.off_w3[p]:self.off_w3[p] + n13].reshape(H // 16, I // 16, 16 * kg)
-        w2 = self.w2[self.off_w2[p]:self.off_w2[p] + n2].reshape(I // 16, H // 16, 16 * kd)
-        return ((w1, self.w13_suh[p, 0], self.w13_svh[p, 0], kg),
-                (w3, self.w13_suh[p, 1], self.w13_svh[p, 1], kg),
-                (w2, self.w2_suh[p], self.w2_svh[p], kd))
+        if name == "w2":
+            K = int(self.k_d[p])
+            grid, flat, start, s_in, s_out = (I // 16, H // 16, 16 * K), self.w2, self.off_w2[p], \
+                self.w2_suh[p], self.w2_svh[p]
+        else:
+            K = int(self.k_gu[p])
+            h = {"w1": 0, "w3": 1}[name]
+            start = (self.off_w1 if h == 0 else self.off_w3)[p]
+            grid, flat, s_in, s_out = (H // 16, I // 16, 16 * K), self.w13, self.w13_suh[p, h], self.w13_svh[p, h]
+        n = grid[0] * grid[1] * grid[2]
+        return flat[start:start + n].reshape(grid), s_in, s_out, K
 
 
 def pack_bank(experts, H: int, I: int) -> PackedBank:

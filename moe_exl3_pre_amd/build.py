@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libexl3.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["exl3_api.cpp", "k_prepass.hip", "k_decode.hip", "k_gemm.hip", "k_moe.hip", "k_embed.hip", "k_mlp.hip", "k_probe.hip"]
+SOURCES = ["exl3_api.cpp", "k_prepass.hip", "k_decode.hip", "k_gemm.hip", "k_moe.hip", "k_moe_tile.hip", "k_embed.hip", "k_mlp.hip", "k_probe.hip"]
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
@@ -38,7 +38,8 @@ def hipcc() -> str:
 # every MFMA accumulating in place (the default schedulers rename the results and copy them back each
 # step).
 EXTRA = {"k_moe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "k_gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]}
+         "k_gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"],
+         "k_moe_tile.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]}
 
 
 def _compile(src: str) -> str:

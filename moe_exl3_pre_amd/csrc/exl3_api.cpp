@@ -137,12 +137,15 @@ struct Layout {
   size_t total;
 };
 
-Layout layout_for(size_t slab_bytes, int64_t M = 0, int64_t IC = 0, int n_xh = 0, bool int8 = false) {
+// rows_pad: the rotated activations' rows are padded to a multiple of this (16-row fragments for the
+// decode-phase kernel, 32-row ones for the prefill GEMM).
+Layout layout_for(size_t slab_bytes, int64_t M = 0, int64_t IC = 0, int n_xh = 0, bool int8 = false,
+                  int64_t rows_pad = 32) {
   Layout L;
   L.slab_off = align_up(kCounterBytes);
   L.slab_bytes = align_up(slab_bytes);
   L.xh_off = L.slab_off + L.slab_bytes;
-  L.scale_off = align_up(size_t((M + 31) / 32 * 32) * size_t(IC) * 2);   // fragment-major: rows padded to 32
+  L.scale_off = align_up(size_t((M + rows_pad - 1) / rows_pad * rows_pad) * size_t(IC) * 2);
   L.part_off = L.scale_off + (int8 ? align_up(size_t(M) * 4) : 0);
   L.xh_bytes = L.part_off + (int8 ? align_up(size_t(M) * size_t(IC / 128) * 4) : 0);
   L.total = L.xh_off + L.xh_bytes * size_t(n_xh);
@@ -288,8 +291,8 @@ void moe_layout(int E, int H, int I, int64_t T, int topk, MoeLayout* L) {
   L->rows = take(P * 4);
   L->chunks = take(size_t(moe_max_chunks(int64_t(P), E)) * 16);
   L->n_chunks = take(16);
-  L->xh13 = take(2 * P * size_t(H) * 2);
-  L->ah = take(P * size_t(I) * 2);
+  L->xh13 = take(2 * P * size_t(moe_row_pitch(H)) * 2);
+  L->ah = take(P * size_t(moe_row_pitch(I)) * 2);
   L->o = take(P * size_t(H) * 4);
   L->total = at;
 }
@@ -345,7 +348,7 @@ bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsign
     if (!decode_slab_bytes(M, IC, n, in, &slab)) return false;
     int slot[kMaxShards];
     const bool pre = first_chunk(M) >= kPreRotateRows || last_chunk(M) >= kPreRotateRows;
-    *L = layout_for(slab, kDecodeMaxRows, IC, pre ? distinct_inputs(n, in, slot) : 0);
+    *L = layout_for(slab, kDecodeMaxRows, IC, pre ? distinct_inputs(n, in, slot) : 0, false, kDecodeMaxRows);
   } else {
     size_t slab = 0;                                      // shards run one after another: the largest split
     if (!(flags & EXL3_GEMM_NO_SPLIT))
@@ -488,7 +491,10 @@ size_t exl3_moe_workspace_bytes(const exl3_bank* bank, int64_t T, int topk, unsi
 int exl3_moe_bank_forward(void* out, const void* x, int64_t T, const int32_t* topk_ids, const float* topk_w, int topk,
                           const exl3_bank* bank, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
   if (flags & EXL3_ACT_INT8) return fail(EXL3_EUNSUPPORTED, "flags: EXL3_ACT_INT8 is not available for the MoE bank");
-  if (flags) return fail(EXL3_EINVAL, "flags: 0x%x has no meaning for the MoE bank", flags);
+  if (flags & ~unsigned(EXL3_FORCE_GEMV | EXL3_FORCE_MFMA))
+    return fail(EXL3_EINVAL, "flags: 0x%x has no meaning for the MoE bank", flags);
+  if ((flags & EXL3_FORCE_GEMV) && (flags & EXL3_FORCE_MFMA))
+    return fail(EXL3_EINVAL, "flags: EXL3_FORCE_GEMV and EXL3_FORCE_MFMA are exclusive");
   if (int rc = check_bank(bank)) return rc;
   if (topk < 1 || topk > bank->E) return fail(EXL3_EINVAL, "topk: %d is outside 1..E (%d)", topk, bank->E);
   if (T < 0) return fail(EXL3_EINVAL, "T: %lld is negative", (long long)T);
@@ -537,6 +543,9 @@ int exl3_moe_bank_forward(void* out, const void* x, int64_t T, const int32_t* to
     m.g_hi[g] = g < bank->n_groups ? bank->groups[g].hi : 0;
     m.g_k[g] = g < bank->n_groups ? (bank->groups[g].k_gu | (bank->groups[g].k_d << 8)) : 0;
   }
+  m.plan = (flags & EXL3_FORCE_GEMV) ? 1 : (flags & EXL3_FORCE_MFMA) ? 2 : 0;
+  if (m.plan == 2 && !moe_prefill_plan(T * topk, bank->E, bank->H, bank->I, 2))
+    return fail(EXL3_EUNSUPPORTED, "flags: EXL3_FORCE_MFMA: T * topk x max(H, I) fp16 exceeds 2 GiB for the prefill plan");
   if (int rc = launch_status(launch_moe(m, static_cast<hipStream_t>(stream)), "exl3_moe_bank_forward")) return rc;
   return ok();
 }

@@ -108,9 +108,9 @@ __device__ __forceinline__ uint32_t codebook2(uint32_t states, const CodebookReg
   return (__builtin_bit_cast(uint32_t, s) & c.mask) | c.bias;
 }
 
-// PAIR64 selects the 64-bit-shift form below.  It saves VALU wherever registers are not scarce; a kernel
-// that already fills the register file (the prefill GEMM) keeps the 32-bit form, because the aligned
-// register pairs the 64-bit shift needs cost it more moves than the shift saves.
+// PAIR64 selects the 64-bit-shift form below.  It saves VALU wherever registers are not scarce; where a
+// kernel already fills the register file (the prefill GEMM at K >= 4) the 32-bit form is kept, because the
+// aligned register pairs the 64-bit shift needs would spill.
 template <int K, int P, bool PAIR64>
 __device__ __forceinline__ uint32_t decode_pair(const uint32_t (&r)[Geom<K>::kNR], const CodebookRegs& c) {
   // States p and p+8 start 8K bits (K bytes) apart.  When both fit one 64-bit window of the realigned
@@ -291,6 +291,58 @@ __device__ __forceinline__ void had128_wave_pairs8(float& v0, float& v1, int lan
   b = bfly(v1, __shfl_xor(v1, 32, 64), lane & 32);
   v0 = a;
   v1 = b;
+}
+
+// Hadamard-128 over the columns of a 128-column tile held in the accumulators of 32x32 MFMAs:
+// v[nb][r] is column 32 nb + (lane & 31) of one of the lane's rows (the rows do not matter).  Radix-2
+// butterflies in natural order of the column bits -- lane bits 0..3 by DPP, lane bit 4 by lane-pair swaps,
+// nb's two bits in registers -- each stage applied to all 64 values before the next so that the lane
+// exchanges of different values fill each other's wait states.  The 1/sqrt(128) is left to the caller.
+template <int S>
+__device__ __forceinline__ float col_partner(float v) {
+  if constexpr (S == 1) return dpp<kQuadXor1>(v);
+  else if constexpr (S == 2) return dpp<kQuadXor2>(v);
+  else if constexpr (S == 4) return lane_xor4(v);
+  else return dpp<kRowRor8>(v);
+}
+
+template <int S>
+__device__ __forceinline__ void col_stage(float (&v)[4][16], int lane) {
+  float q[4][16];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) q[nb][r] = col_partner<S>(v[nb][r]);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[nb][r] = bfly(v[nb][r], q[nb][r], lane & S);
+}
+
+__device__ __forceinline__ void had128_cols32(float (&v)[4][16], int lane) {
+  col_stage<1>(v, lane);
+  col_stage<2>(v, lane);
+  col_stage<4>(v, lane);
+  col_stage<8>(v, lane);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) lane_pair_bfly<false>(v[nb][r], v[nb][r + 1]);
+#pragma unroll
+  for (int hb = 1; hb < 4; hb <<= 1)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      if (!(nb & hb))
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float lo = v[nb][r], hi = v[nb | hb][r];
+          v[nb][r] = lo + hi;
+          v[nb | hb][r] = lo - hi;
+        }
+}
+
+__device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 }  // namespace exl3

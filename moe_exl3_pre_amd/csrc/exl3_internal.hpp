@@ -151,8 +151,18 @@ struct MoeLaunch {
   int topk, E, H, I, n_groups;
   int g_hi[kMoeMaxGroups];  // exclusive end slot of each group
   int g_k[kMoeMaxGroups];   // k_gu | k_d << 8
+  int plan = 0;             // 0: by size, 1: the decode-sized plan (32-row chunks), 2: the prefill plan
 };
 
+// The prefill plan (grouped 128 x 128 tiles) serves calls with at least this many routed pairs per expert
+// on average, when the gathered operands stay under 2 GiB.
+constexpr int kMoePrefillPairsPerExpert = 256;
+bool moe_prefill_plan(int64_t P, int E, int H, int I, int plan);
+// Row pitch (halves) of the per-pair fp16 operands (w1 / w3 rotated activations: n = H; w2's operand:
+// n = I).  The expert kernels gather these rows by pair id, one row per lane; at a pitch of a power of two
+// every row of a load falls in the same L1 set and the loads serialise on tag conflicts, so each row is
+// padded by one 128-byte line.
+inline int moe_row_pitch(int n) { return n + 64; }
 int64_t moe_max_chunks(int64_t P, int E);
 hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream);
 

@@ -71,34 +71,6 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int tile, int wav
   ctile = (in_group / gm) * kWavesN + wave;
 }
 
-__device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// One butterfly stage of the Hadamard over lane bit S (1, 2, 4, 8) of a 32x32 accumulator group (lane bit b
-// = column bit b), applied to all 64 values of a row group before the next stage so that the lane exchanges
-// of different values fill each other's wait states.
-template <int S>
-__device__ __forceinline__ float lane_partner(float v) {
-  if constexpr (S == 1) return dpp<kQuadXor1>(v);
-  else if constexpr (S == 2) return dpp<kQuadXor2>(v);
-  else if constexpr (S == 4) return lane_xor4(v);
-  else return dpp<kRowRor8>(v);
-}
-
-template <int S>
-__device__ __forceinline__ void lane_stage(float (&v)[4][16], int lane) {
-  float q[4][16];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) q[nb][r] = lane_partner<S>(v[nb][r]);
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) v[nb][r] = bfly(v[nb][r], q[nb][r], lane & S);
-}
-
 // Column scales of the wave's 4 column groups: 1/sqrt(128) * rout * s_out at column col0 + 32 nb + c.
 __device__ __forceinline__ void column_scales(const GemmArgs& p, int col0, int c, float (&sc)[4]) {
 #pragma unroll
@@ -116,25 +88,7 @@ __device__ __forceinline__ void column_scales(const GemmArgs& p, int col0, int c
 __device__ __forceinline__ void epilogue_group(const GemmArgs& p, float (&v)[4][16], const float (&sc)[4], int r0,
                                                int col0, int lane) {
   const int c = lane & 31, k = lane >> 5;
-  lane_stage<1>(v, lane);
-  lane_stage<2>(v, lane);
-  lane_stage<4>(v, lane);
-  lane_stage<8>(v, lane);
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) lane_pair_bfly<false>(v[nb][r], v[nb][r + 1]);
-#pragma unroll
-  for (int hb = 1; hb < 4; hb <<= 1)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      if (!(nb & hb))
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float lo = v[nb][r], hi = v[nb | hb][r];
-          v[nb][r] = lo + hi;
-          v[nb | hb][r] = lo - hi;
-        }
+  had128_cols32(v, lane);
   if (p.row_scale) {                                        // 8-bit path: the row scale first
 #pragma unroll
     for (int r = 0; r < 16; ++r) {

@@ -25,6 +25,7 @@
 
 #include "exl3_device.hpp"
 #include "exl3_internal.hpp"
+#include "k_moe.hpp"
 
 namespace exl3 {
 
@@ -38,35 +39,6 @@ constexpr int kMoeRedFloats = 2 * kMoeRows * kRedStride;
 constexpr int kMoeSlotFloats = kMoeWaves * Slot<8>::kBytes / 4;
 constexpr int kMoeLdsFloats = kMoeRedFloats > kMoeSlotFloats ? kMoeRedFloats : kMoeSlotFloats;
 
-struct MoeArgs {
-  const uint16_t* x;        // bf16 [T, H]
-  const int32_t* ids;       // [T * topk] logical expert ids
-  const float* wts;         // [T * topk]
-  const int32_t* perm;      // [E] logical -> slot
-  const uint16_t* w13;      // flat int16 banks
-  const uint16_t* w2;
-  const uint16_t* w13_suh;  // fp16 [E, 2, H]
-  const uint16_t* w13_svh;  // fp16 [E, 2, I]
-  const uint16_t* w2_suh;   // fp16 [E, I]
-  const uint16_t* w2_svh;   // fp16 [E, H]
-  const int64_t* off_w1;    // int16-element offsets per slot
-  const int64_t* off_w3;
-  const int64_t* off_w2;
-  uint16_t* out;            // bf16 [T, H]
-  // workspace
-  int32_t* offs;            // [E + 1] first row of each slot's list
-  int32_t* pslot;           // [P] slot of each pair, -1 if dropped (written by the route)
-  int32_t* rows;            // [P] pair ids sorted by slot
-  int4v* chunks;            // [max_chunks] {slot, first row, rows, k_gu | k_d << 8}
-  int32_t* n_chunks;        // [1]
-  uint16_t* xh13;           // fp16 [2, P, H] rotated activations of w1 (0) and w3 (1), PERM16 order
-  uint16_t* ah;             // fp16 [P, I] w2's rotated operand, PERM16 order
-  float* o;                 // fp32 [P, H] expert outputs
-  int T, topk, P, E, H, I, max_chunks;
-  int n_groups;
-  int g_hi[kMoeMaxGroups];  // group g covers slots [g_hi[g-1], g_hi[g])
-  int g_k[kMoeMaxGroups];   // k_gu | k_d << 8
-};
 
 // Slot of pair q, or -1 when its id is outside [0, E) or the permutation entry is.
 __device__ __forceinline__ int pair_slot(const MoeArgs& a, int q) {
@@ -137,7 +109,7 @@ __device__ void moe_route_general(const MoeArgs& a, int* lds) {
   const int c = s < E ? cnt[s] : 0;
   int total = 0, chunk_total = 0;
   const int off = block_excl_scan(c, tmp, &total);
-  const int nch = (c + kMoeRows - 1) / kMoeRows;
+  const int nch = (c + a.chunk_rows - 1) / a.chunk_rows;
   const int coff = block_excl_scan(nch, tmp, &chunk_total);
   if (s < E) {
     a.offs[s] = off;
@@ -149,8 +121,8 @@ __device__ void moe_route_general(const MoeArgs& a, int* lds) {
         break;
       }
     for (int i = 0; i < nch; ++i) {
-      const int r0 = off + i * kMoeRows;
-      const int nr = c - i * kMoeRows < kMoeRows ? c - i * kMoeRows : kMoeRows;
+      const int r0 = off + i * a.chunk_rows;
+      const int nr = c - i * a.chunk_rows < a.chunk_rows ? c - i * a.chunk_rows : a.chunk_rows;
       a.chunks[coff + i] = (int4v){s, r0, nr, gk};
     }
   }
@@ -224,7 +196,7 @@ __device__ void moe_route_bitmap(const MoeArgs& a, int* lds) {
   const int c = s < E ? cnt[s] : 0;
   int total = 0, chunk_total = 0;
   const int off = block_excl_scan(c, tmp, &total);
-  const int nch = (c + kMoeRows - 1) / kMoeRows;
+  const int nch = (c + a.chunk_rows - 1) / a.chunk_rows;
   const int coff = block_excl_scan(nch, tmp, &chunk_total);
   if (s < E) {
     a.offs[s] = off;
@@ -236,8 +208,8 @@ __device__ void moe_route_bitmap(const MoeArgs& a, int* lds) {
         break;
       }
     for (int i = 0; i < nch; ++i) {
-      const int r0 = off + i * kMoeRows;
-      const int nr = c - i * kMoeRows < kMoeRows ? c - i * kMoeRows : kMoeRows;
+      const int r0 = off + i * a.chunk_rows;
+      const int nr = c - i * a.chunk_rows < a.chunk_rows ? c - i * a.chunk_rows : a.chunk_rows;
       a.chunks[coff + i] = (int4v){s, r0, nr, gk};
     }
   }
@@ -335,7 +307,7 @@ __device__ void moe_rotate(const MoeArgs& a, int64_t unit) {
     for (int w = 0; w < 16; w += 2) lane_pair_bfly<true>(v[w], v[w + 1]);    // bit 6: lane bit 5
     if (sl[k] >= 0) {
       const int64_t qi = int64_t(t) * a.topk + jj[k];
-      u32x4* dst = reinterpret_cast<u32x4*>(a.xh13 + (int64_t(proj) * a.P + qi) * a.H + f);
+      u32x4* dst = reinterpret_cast<u32x4*>(a.xh13 + (int64_t(proj) * a.P + qi) * a.ldx + f);
       u32x4 o0, o1;                                        // PERM16: positions (2i, 2i+1) hold features (i, i+8)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -475,22 +447,6 @@ __device__ __forceinline__ void moe_reduce(float* red, int wq, bool two, const f
   }
 }
 
-// Chunk c of the launch (heavier K groups sit at the end of the slot order, so they go first).
-__device__ __forceinline__ bool moe_chunk(const MoeArgs& a, int c, int4v& ch) {
-  const int n = a.n_chunks[0];
-  if (c >= n) return false;
-  ch = a.chunks[n - 1 - c];
-  return true;
-}
-
-// Workgroup -> (chunk, column group).  The column groups of one chunk land on one XCD (workgroups are
-// dealt to the 8 XCDs round-robin), so the chunk's gathered activations are fetched into one L2.
-__device__ __forceinline__ void moe_tile(int ncg, int& c, int& cg) {
-  const int id = blockIdx.x, x = id & 7, y = id >> 3;
-  cg = y % ncg;
-  c = (y / ncg) * 8 + x;
-}
-
 template <int K>
 __device__ __forceinline__ void moe_w13_block(const MoeArgs& a, const int4v ch, int cb, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -500,12 +456,12 @@ __device__ __forceinline__ void moe_w13_block(const MoeArgs& a, const int4v ch, 
   const int NS = a.H / 64;
   const int st0 = NS * wq / 2, st1 = NS * (wq + 1) / 2;
   const int64_t off = h == 0 ? a.off_w1[slot] : a.off_w3[slot];
-  const uint16_t* A = a.xh13 + int64_t(h) * a.P * a.H;
+  const uint16_t* A = a.xh13 + int64_t(h) * a.P * a.ldx;
   const int r0 = a.rows[row0 + (n < nrows ? n : nrows - 1)];
   const int r1 = a.rows[row0 + (16 + n < nrows ? 16 + n : nrows - 1)];
   float4v acc0[8], acc1[8];
-  moe_accumulate<K>(a.w13 + off, uint32_t(int64_t(a.H) * a.I * K / 8), a.I / 16, cb, A + int64_t(r0) * a.H + 16 * g,
-                    A + int64_t(r1) * a.H + 16 * g, st0, st1 - st0, two,
+  moe_accumulate<K>(a.w13 + off, uint32_t(int64_t(a.H) * a.I * K / 8), a.I / 16, cb, A + int64_t(r0) * a.ldx + 16 * g,
+                    A + int64_t(r1) * a.ldx + 16 * g, st0, st1 - st0, two,
                     reinterpret_cast<char*>(red) + wave * Slot<K>::kBytes, acc0, acc1);
   __syncthreads();                               // the staging slots share LDS with the reduction buffer
   moe_reduce(red + h * kMoeRows * kRedStride, wq, two, acc0, acc1);
@@ -532,7 +488,7 @@ __device__ __forceinline__ void moe_w13_block(const MoeArgs& a, const int4v ch, 
     float va = h1a / (1.0f + __expf(-h1a)) * h3a * u2a;
     float vb = h1b / (1.0f + __expf(-h1b)) * h3b * u2b;
     had128_wave(va, vb, lane);
-    uint16_t* dst = a.ah + int64_t(a.rows[row0 + r]) * a.I + int64_t(cb) * kHad + 2 * lane;
+    uint16_t* dst = a.ah + int64_t(a.rows[row0 + r]) * a.ldh + int64_t(cb) * kHad + 2 * lane;
     *reinterpret_cast<uint32_t*>(dst) =
         uint32_t(f32_to_f16(va * kInvSqrt128)) | (uint32_t(f32_to_f16(vb * kInvSqrt128)) << 16);
   }
@@ -553,7 +509,7 @@ __device__ __forceinline__ void moe_w2_block(const MoeArgs& a, const int4v ch, i
   const int r1 = a.rows[row0 + (16 + n < nrows ? 16 + n : nrows - 1)];
   float4v acc0[8], acc1[8];
   moe_accumulate<K>(a.w2 + a.off_w2[slot], uint32_t(int64_t(a.I) * a.H * K / 8), a.H / 16, active ? cb : 0,
-                    a.ah + int64_t(r0) * a.I + 16 * g, a.ah + int64_t(r1) * a.I + 16 * g, st0, st1 - st0, two,
+                    a.ah + int64_t(r0) * a.ldh + 16 * g, a.ah + int64_t(r1) * a.ldh + 16 * g, st0, st1 - st0, two,
                     reinterpret_cast<char*>(red) + wave * Slot<K>::kBytes, acc0, acc1);
   __syncthreads();                               // the staging slots share LDS with the reduction buffer
   float* rh = red + h * kMoeRows * kRedStride;
@@ -567,22 +523,6 @@ __device__ __forceinline__ void moe_w2_block(const MoeArgs& a, const int4v ch, i
     had128_wave(v0, v1, lane);
     float* dst = a.o + int64_t(a.rows[row0 + r]) * a.H + c0;
     *reinterpret_cast<float2*>(dst) = make_float2(v0 * kInvSqrt128 * sa, v1 * kInvSqrt128 * sb);
-  }
-}
-
-// KSET 0 covers the mixed set {2, 3, 4} in one launch (one switch per workgroup); KSET k in 1..8 serves
-// the chunks of one K and skips the others, so any other mix runs as one launch per distinct K.
-template <int KSET, typename F>
-__device__ __forceinline__ void moe_dispatch(int k, F&& f) {
-  if constexpr (KSET == 0) {
-    switch (k) {
-      case 2: f(std::integral_constant<int, 2>{}); break;
-      case 3: f(std::integral_constant<int, 3>{}); break;
-      case 4: f(std::integral_constant<int, 4>{}); break;
-      default: break;
-    }
-  } else {
-    if (k == KSET) f(std::integral_constant<int, KSET>{});
   }
 }
 
@@ -648,6 +588,19 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
 // ---------------------------------------------------------------------------------------------------
 int64_t moe_max_chunks(int64_t P, int E) { return (P + kMoeRows - 1) / kMoeRows + E; }
 
+bool moe_prefill_plan(int64_t P, int E, int H, int I, int plan) {
+  const bool fits = P * int64_t(moe_row_pitch(H > I ? H : I)) * 2 < (int64_t(1) << 31);
+  if (plan == 1 || !fits) return false;
+  return plan == 2 || P >= int64_t(kMoePrefillPairsPerExpert) * E;
+}
+
+static size_t moe_slot_bytes(unsigned ks) {   // staging slot of the largest K in the bit set
+  int kmax = 1;
+  for (int k = 1; k <= 8; ++k)
+    if (ks & (1u << k)) kmax = k;
+  return size_t(4) * (256 * kmax + 64);
+}
+
 static size_t moe_route_lds_bytes(int E, int P) {
   const size_t words = size_t(E) * ((P + 31) / 32);
   if (words <= size_t(kBitmapWords)) return (2 * words + 2 * E + 48 + (P <= kBitmapSlotCache ? P : 0)) * sizeof(int);
@@ -685,16 +638,22 @@ hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream) {
   a.H = m.H;
   a.I = m.I;
   a.max_chunks = int(moe_max_chunks(a.P, m.E));
+  a.ldx = moe_row_pitch(a.H);
+  a.ldh = moe_row_pitch(a.I);
   a.n_groups = m.n_groups;
   for (int g = 0; g < kMoeMaxGroups; ++g) {
     a.g_hi[g] = g < m.n_groups ? m.g_hi[g] : 0;
     a.g_k[g] = g < m.n_groups ? m.g_k[g] : 0;
   }
+  const bool prefill = moe_prefill_plan(a.P, a.E, a.H, a.I, m.plan);
+  a.chunk_rows = prefill ? kTileRows : kMoeRows;
   const int64_t rot_units = moe_rotate_units(a.T, a.H, a.topk);
   const int64_t rot_blocks = (rot_units + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
   hipLaunchKernelGGL(moe_route_rotate_kernel, dim3(unsigned(1 + rot_blocks)), dim3(kRouteThreads),
                      moe_route_lds_bytes(a.E, a.P), stream, a);
-  const int64_t cgroups = (a.max_chunks + 7) / 8 * 8;
+  // chunk groups of 8 (moe_tile); the prefill plan's 128-row chunks number at most P / 128 + E
+  const int64_t nch = prefill ? (int64_t(a.P) + kTileRows - 1) / kTileRows + a.E : a.max_chunks;
+  const int64_t cgroups = (nch + 7) / 8 * 8;
   const dim3 g13(unsigned(cgroups * (a.I / kHad))), g2(unsigned(cgroups * ((a.H / kHad + 1) / 2)));
   for (int pass = 0; pass < 2; ++pass) {
     // the K values of this projection, as a bit set
@@ -702,10 +661,15 @@ hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream) {
     for (int g = 0; g < m.n_groups; ++g) ks |= 1u << (pass == 0 ? (m.g_k[g] & 0xFF) : (m.g_k[g] >> 8));
     auto go = [&](auto kset) {
       constexpr int KS = decltype(kset)::value;
-      if (pass == 0)
+      if (prefill) {
+        // (chunk, column group) tiles; chunk groups of 8 as in moe_tile, and the chunks past the
+        // route's count exit at once
+        launch_moe_tile_pass(a, pass, KS, KS == 0 ? moe_slot_bytes(0x1Cu) : moe_slot_bytes(1u << KS), cgroups, stream);
+      } else if (pass == 0) {
         hipLaunchKernelGGL(moe_w13_kernel<KS>, g13, dim3(kMoeWaves * 64), 0, stream, a);
-      else
+      } else {
         hipLaunchKernelGGL(moe_w2_kernel<KS>, g2, dim3(kMoeWaves * 64), 0, stream, a);
+      }
     };
     if ((ks & ~0x1Cu) == 0) {
       go(std::integral_constant<int, 0>{});

@@ -16,11 +16,12 @@ def _case(**kw):
     return synth.moe_case(a.pop("seed"), **a)
 
 
-def test_views_round_trip_every_slot():
+def test_projection_views_round_trip_every_slot():
     m = _case(k_d_independent=True)
     b = pack_bank(m["experts"], m["H"], m["I"])
     for e, ex in enumerate(m["experts"]):
-        (w1, s1, v1, k1), (w3, s3, v3, k3), (w2, s2, v2, k2) = b.views(int(b.perm[e]))
+        (w1, s1, v1, k1), (w3, s3, v3, k3), (w2, s2, v2, k2) = (b.projection(int(b.perm[e]), n)
+                                                                 for n in ("w1", "w3", "w2"))
         assert k1 == k3 == ex["k_gu"] and k2 == ex["k_d"]
         assert np.array_equal(w1, ex["w1"]) and np.array_equal(w3, ex["w3"]) and np.array_equal(w2, ex["w2"])
         assert np.array_equal(s1, ex["w1_suh"]) and np.array_equal(s3, ex["w3_suh"]) and np.array_equal(s2, ex["w2_suh"])
@@ -105,7 +106,8 @@ def _fwd(bank, T=4, topk=2, flags=0, ws=FAKE, ws_bytes=1 << 30, out=FAKE, x=FAKE
     ({}, dict(topk=9), exl3.EINVAL, "topk"),
     ({}, dict(T=-1), exl3.EINVAL, "T"),
     ({}, dict(flags=exl3.ACT_INT8), exl3.EUNSUPPORTED, "flags"),
-    ({}, dict(flags=exl3.FORCE_GEMV), exl3.EINVAL, "flags"),
+    ({}, dict(flags=exl3.GEMM_NO_SPLIT), exl3.EINVAL, "flags"),
+    ({}, dict(flags=exl3.FORCE_GEMV | exl3.FORCE_MFMA), exl3.EINVAL, "exclusive"),
     ({}, dict(out=None), exl3.EINVAL, "out"),
     ({}, dict(x=FAKE + 2), exl3.EINVAL, "x"),
     ({}, dict(ids=None), exl3.EINVAL, "topk_ids"),

@@ -20,9 +20,14 @@ def _setup(m):
     return bank, x, ids, w
 
 
-def _run(bank, x, ids, w, ws=None):
+# the two plans: the decode-sized one (32-row chunks, streaming core) and the prefill one (128-row
+# chunks, grouped 128 x 128 tiles); by default the call picks one by the pairs per expert
+PLANS = {"decode_plan": exl3.FORCE_GEMV, "prefill_plan": exl3.FORCE_MFMA}
+
+
+def _run(bank, x, ids, w, ws=None, flags=0):
     out = torch.full(x.shape, -1000.0, dtype=torch.bfloat16, device=dev())
-    exl3.moe_bank_forward(out, x, ids, w, bank, ws=ws)
+    exl3.moe_bank_forward(out, x, ids, w, bank, ws=ws, flags=flags)
     torch.cuda.synchronize()
     return out
 
@@ -44,23 +49,26 @@ def _check(m, out, tokens=None, experts=None):
     dict(T=40, E=8, topk=2, H=384, I=128, Ks=(1, 5)),                            # one launch per K; odd H blocks
     dict(T=1, E=8, topk=8, H=256, I=128, Ks=(2, 3, 4)),                          # one token, every expert
 ])
-def test_moe_small_full_parity(cfg):
+@pytest.mark.parametrize("plan", list(PLANS))
+def test_moe_small_full_parity(cfg, plan):
     cfg = dict(cfg)
-    log(f"moe parity {cfg}")
+    log(f"moe parity {cfg} {plan}")
     m = synth.moe_case(700 + cfg["T"], **cfg)
     bank, x, ids, w = _setup(m)
-    _check(m, _run(bank, x, ids, w))
+    _check(m, _run(bank, x, ids, w, flags=PLANS[plan]))
 
 
-def test_moe_many_rows_per_expert_and_empty_expert():
-    """~100 rows per expert (several 32-row chunks, one partial) and one expert with no token."""
+@pytest.mark.parametrize("plan", list(PLANS))
+def test_moe_many_rows_per_expert_and_empty_expert(plan):
+    """~100 rows per expert (several 32-row chunks, one partial; one partial 128-row chunk on the prefill
+    plan) and one expert with no token."""
     m = synth.moe_case(711, T=200, E=5, topk=2, H=256, I=256, Ks=(2, 3, 4))
     rng = np.random.default_rng(9)
     ids = np.stack([rng.choice(4, 2, replace=False) for _ in range(m["T"])]).astype(np.int32)   # expert 4 unused
     m = dict(m, topk_ids=ids)
-    log(f"moe many rows: counts {np.bincount(ids.ravel(), minlength=5)}")
+    log(f"moe many rows: counts {np.bincount(ids.ravel(), minlength=5)} {plan}")
     bank, x, dids, w = _setup(m)
-    _check(m, _run(bank, x, dids, w))
+    _check(m, _run(bank, x, dids, w, flags=PLANS[plan]))
 
 
 @pytest.mark.parametrize("T,E,topk", [(2048, 64, 4), (4608, 32, 4), (4096, 128, 8)])
@@ -82,7 +90,9 @@ def test_moe_route_counting_sort_path(T, E, topk):
     assert torch.equal(_run(bank, x, ids, w), out)
 
 
-def test_moe_out_of_range_ids_are_ignored():
+@pytest.mark.parametrize("plan", list(PLANS))
+def test_moe_out_of_range_ids_are_ignored(plan):
+    f = PLANS[plan]
     m = synth.moe_case(712, T=32, E=8, topk=4, H=256, I=128)
     ids = m["topk_ids"].copy()
     ids[3, 2] = -1
@@ -90,22 +100,24 @@ def test_moe_out_of_range_ids_are_ignored():
     ids[17, 3] = 1 << 30
     m_bad = dict(m, topk_ids=ids)
     bank, x, dids, w = _setup(m_bad)
-    out_bad = _run(bank, x, dids, w)
+    out_bad = _run(bank, x, dids, w, flags=f)
     _check(m_bad, out_bad)
     # same as routing those terms to a real expert with weight zero (rows are independent, so bitwise)
     ids0 = m["topk_ids"].copy()
     w0 = m["topk_w"].copy()
     for t, j in ((3, 2), (9, 0), (17, 3)):
         w0[t, j] = 0.0
-    out0 = _run(bank, x, to_dev(ids0.astype(np.int32)), to_dev(w0.astype(np.float32)))
+    out0 = _run(bank, x, to_dev(ids0.astype(np.int32)), to_dev(w0.astype(np.float32)), flags=f)
     assert torch.equal(out_bad, out0)
 
 
-def test_moe_deterministic_and_relabel_invariant():
+@pytest.mark.parametrize("plan", list(PLANS))
+def test_moe_deterministic_and_relabel_invariant(plan):
+    f = PLANS[plan]
     m = synth.moe_case(713, T=64, E=16, topk=4, H=256, I=256)
     bank, x, ids, w = _setup(m)
-    a = _run(bank, x, ids, w)
-    assert torch.equal(_run(bank, x, ids, w), a)
+    a = _run(bank, x, ids, w, flags=f)
+    assert torch.equal(_run(bank, x, ids, w, flags=f), a)
     # relabel the logical experts: the packed slots and every pair's computation are unchanged
     perm = np.random.default_rng(5).permutation(m["E"])
     experts2 = [None] * m["E"]
@@ -113,7 +125,7 @@ def test_moe_deterministic_and_relabel_invariant():
         experts2[perm[e]] = m["experts"][e]
     m2 = dict(m, experts=experts2, topk_ids=perm[m["topk_ids"]].astype(np.int32))
     bank2, x2, ids2, w2 = _setup(m2)
-    b = _run(bank2, x2, ids2, w2)
+    b = _run(bank2, x2, ids2, w2, flags=f)
     # slots are a stable sort by K, so relabeling can reorder slots inside a group; rows are independent
     # and every reduction is fixed-order, so the result is still bit-identical
     assert torch.equal(a, b)
@@ -190,6 +202,38 @@ def test_moe_full_size_sampled():
     log(f"  {len(tokens)} tokens over {len(used)} experts (most loaded {e_max}, least loaded {e_min})")
     experts = list(m["experts"])
     for e in used:      # decode the touched experts once for both oracle variants
+        d = experts[e]
+        experts[e] = dict(d, W1=O.decode_weight(d["w1"], d["k_gu"]), W3=O.decode_weight(d["w3"], d["k_gu"]),
+                          W2=O.decode_weight(d["w2"], d["k_d"]))
+    _check(m, out, tokens=tokens, experts=experts)
+
+
+def test_moe_plan_choice_by_pairs_per_expert():
+    """Without a FORCE flag the call runs the decode-sized plan below 256 routed pairs per expert and the
+    prefill plan from there on (bitwise the forced calls)."""
+    for T, plan in ((510, "decode_plan"), (512, "prefill_plan")):      # 8 experts, top-4: 255 and 256 per expert
+        m = synth.moe_case(740 + T, T=T, E=8, topk=4, H=256, I=128)
+        bank, x, ids, w = _setup(m)
+        assert torch.equal(_run(bank, x, ids, w), _run(bank, x, ids, w, flags=PLANS[plan])), T
+
+
+def test_moe_prefill_bank_full_size_sampled():
+    """The prefill-sized call on the full bank shape: T=4096 tokens, 128 experts, top-8 (32,768 pairs, ~256
+    rows per expert: two 128-row chunks each), H=2048, I=768, K in {2,3,4}; 16 tokens against the oracle,
+    covering every K group and the most- and least-loaded experts."""
+    cfg = synth.MOE
+    T = 4096
+    m = synth.moe_case(1103, T=T, E=cfg["E"], topk=cfg["topk"], H=cfg["H"], I=cfg["I"], Ks=cfg["Ks"])
+    log("moe prefill plan 4096 x 2048, 128 experts top-8")
+    bank, x, ids, w = _setup(m)
+    out = _run(bank, x, ids, w)
+    assert torch.isfinite(out.float()).all()
+    assert torch.equal(out, _run(bank, x, ids, w, flags=exl3.FORCE_MFMA))
+    tokens, e_max, e_min = _full_size_tokens(m, n=16, seed=3)
+    used = np.unique(m["topk_ids"][tokens])
+    log(f"  {len(tokens)} tokens over {len(used)} experts")
+    experts = list(m["experts"])
+    for e in used:
         d = experts[e]
         experts[e] = dict(d, W1=O.decode_weight(d["w1"], d["k_gu"]), W3=O.decode_weight(d["w3"], d["k_gu"]),
                           W2=O.decode_weight(d["w2"], d["k_d"]))
