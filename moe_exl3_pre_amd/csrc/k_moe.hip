@@ -85,23 +85,42 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
 }
 
 constexpr int kSlotCache = 16384;   // pairs whose slots the route keeps in LDS between its two passes
+constexpr int kRouteBatch = 16;     // pairs per thread whose loads the general route issues together
 
 __device__ void moe_route_general(const MoeArgs& a, int* lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int kW = kRouteThreads / 64;
+  const int tid = threadIdx.x;
   const int E = a.E;
   int* cnt = lds;                 // [E]
   int* next = cnt + E;            // [E] next free row of each slot
-  int* wcnt = next + E;           // [kW][E]
-  int* tmp = wcnt + kW * E;       // [48]
+  int* perm_l = next + E;         // [E] the slot of each logical expert
+  int* tmp = perm_l + E;          // [48]
   int* cache = a.P <= kSlotCache ? tmp + 48 : nullptr;   // [P] slot per pair
-  for (int s = tid; s < E; s += kRouteThreads) cnt[s] = 0;
+  for (int s = tid; s < E; s += kRouteThreads) {
+    cnt[s] = 0;
+    perm_l[s] = a.perm[s];
+  }
   __syncthreads();
-  for (int q = tid; q < a.P; q += kRouteThreads) {
-    const int s = pair_slot(a, q);
-    a.pslot[q] = s;
-    if (cache) cache[q] = s;
-    if (s >= 0) atomicAdd(&cnt[s], 1);
+  // slots and counts, kRouteBatch pairs per thread at a time: every id of a batch is requested before
+  // the first is used, so a batch costs one memory latency, not one per pair
+  constexpr int kStride = kRouteThreads * kRouteBatch;
+  for (int q0 = 0; q0 < a.P; q0 += kStride) {
+    int e[kRouteBatch];
+#pragma unroll
+    for (int k = 0; k < kRouteBatch; ++k) {
+      const int q = q0 + k * kRouteThreads + tid;
+      e[k] = q < a.P ? a.ids[q] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kRouteBatch; ++k) {
+      const int q = q0 + k * kRouteThreads + tid;
+      int s = (e[k] >= 0 && e[k] < E) ? perm_l[e[k]] : -1;
+      s = (s >= 0 && s < E) ? s : -1;
+      if (q < a.P) {
+        a.pslot[q] = s;
+        if (cache) cache[q] = s;
+        if (s >= 0) atomicAdd(&cnt[s], 1);
+      }
+    }
   }
   __syncthreads();
   // slot offsets and chunk offsets (E <= 1024: one slot per thread)
@@ -132,11 +151,20 @@ __device__ void moe_route_general(const MoeArgs& a, int* lds) {
   }
   // placement: one LDS atomic per pair on its slot's cursor.  The order inside a slot is whatever the
   // atomics give; nothing depends on it (every row of the w13 / w2 lists is computed on its own and every
-  // result is indexed by pair id), so the outputs are the same bits as with a stable order.
+  // result is indexed by pair id), so the outputs are the same bits as with a stable order.  The slots
+  // come back from the LDS cache or from pslot, which this thread wrote above (the barrier's fence has
+  // made those stores visible; no earlier load put their lines in the L1).
   __syncthreads();
-  for (int q = tid; q < a.P; q += kRouteThreads) {
-    const int sl = cache ? cache[q] : pair_slot(a, q);
-    if (sl >= 0) a.rows[atomicAdd(&next[sl], 1)] = q;
+  for (int q0 = 0; q0 < a.P; q0 += kStride) {
+    int sl[kRouteBatch];
+#pragma unroll
+    for (int k = 0; k < kRouteBatch; ++k) {
+      const int q = q0 + k * kRouteThreads + tid;
+      sl[k] = q < a.P ? (cache ? cache[q] : a.pslot[q]) : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kRouteBatch; ++k)
+      if (sl[k] >= 0) a.rows[atomicAdd(&next[sl[k]], 1)] = q0 + k * kRouteThreads + tid;
   }
 }
 
@@ -604,7 +632,7 @@ static size_t moe_slot_bytes(unsigned ks) {   // staging slot of the largest K i
 static size_t moe_route_lds_bytes(int E, int P) {
   const size_t words = size_t(E) * ((P + 31) / 32);
   if (words <= size_t(kBitmapWords)) return (2 * words + 2 * E + 48 + (P <= kBitmapSlotCache ? P : 0)) * sizeof(int);
-  return size_t(2 * E + (kRouteThreads / 64) * E + 48 + (P <= kSlotCache ? P : 0)) * sizeof(int);
+  return size_t(3 * E + 48 + (P <= kSlotCache ? P : 0)) * sizeof(int);
 }
 
 hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream) {
