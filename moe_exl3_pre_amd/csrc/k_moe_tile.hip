@@ -14,10 +14,10 @@ namespace exl3 {
 // projection runs as tiles of 128 gathered rows x 128 columns on the prefill GEMM's core (32x32x16 MFMAs,
 // every decoded tile column feeding 8 of them; k_gemm.hip), so every weight is decoded once per 128 rows.
 //   * w13: a workgroup of two waves per (chunk, 128 intermediate features): wave 0 the w1 tile, wave 1 the
-//     w3 tile of the same rows.  Both apply their output Hadamard-128 and svh in registers; wave 1 passes
-//     its tile through LDS; wave 0 forms silu(h1) * h3 * w2's suh, applies w2's input Hadamard (the same
-//     128 features) and writes w2's fp16 operand.  As in the decode-sized plan h1, h3 and the product
-//     stay in fp32 until that operand.
+//     w3 tile of the same rows.  Both apply their output Hadamard-128 and svh in registers and swap half
+//     of their rows through LDS, so that each wave holds h1 and h3 of 64 rows; each forms silu(h1) * h3 *
+//     w2's suh for its rows, applies w2's input Hadamard (the same 128 features) and writes w2's fp16
+//     operand.  As in the decode-sized plan h1, h3 and the product stay in fp32 until that operand.
 //   * w2: a workgroup of four waves per (chunk, 512 output features), one 128-column tile each; output
 //     Hadamard and svh; fp32 result per pair.
 // Rows are gathered by pair id: each lane loads 16 bytes of its own row per A fragment (the rows are the
@@ -157,13 +157,16 @@ __device__ __forceinline__ void moe_w13_tile_block(const MoeArgs& a, const int4v
   moe_tile_gemm<K>(a.w13 + off, uint32_t(int64_t(a.H) * a.I * K / 8), uint32_t(a.I / 16), ib,
                    a.xh13 + int64_t(wave) * a.P * a.ldx, a_bytes, aoff, a.H / 64, slots + wave * Slot<K>::kBytes, acc);
   const int col0 = ib * kHad;
-  float sv[4];
+  float sv[4], u2[4];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < 4; ++nb) {
     sv[nb] = kInvSqrt128 * f16_to_f32(a.w13_svh[(int64_t(slot) * 2 + wave) * a.I + col0 + 32 * nb + c]);
-  // the per-32-row-group steps below take the group as a compile-time constant, so every accumulator
-  // index is static and the 256 accumulators stay in registers
-  auto h3_group = [&](auto mbc) {                           // h3 = svh * Had128(acc) into the exchange tile
+    u2[nb] = f16_to_f32(a.w2_suh[int64_t(slot) * a.I + col0 + 32 * nb + c]);
+  }
+  // The per-32-row-group steps below take the group as a compile-time constant, so every accumulator
+  // index is static and the 256 accumulators stay in registers.
+  // 1. each wave turns its own tile into h = svh * Had128(acc) / sqrt(128) (wave 0: h1, wave 1: h3), in place
+  auto out_group = [&](auto mbc) {
     constexpr int mb = decltype(mbc)::value;
     float v[4][16];
 #pragma unroll
@@ -174,34 +177,44 @@ __device__ __forceinline__ void moe_w13_tile_block(const MoeArgs& a, const int4v
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xch[((mb * 4 + nb) * 16 + r) * 64 + lane] = v[nb][r] * sv[nb];
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = v[nb][r] * sv[nb];
   };
-  if (wave == 1) {
-    h3_group(std::integral_constant<int, 0>{});
-    h3_group(std::integral_constant<int, 1>{});
-    h3_group(std::integral_constant<int, 2>{});
-    h3_group(std::integral_constant<int, 3>{});
+  out_group(std::integral_constant<int, 0>{});
+  out_group(std::integral_constant<int, 1>{});
+  out_group(std::integral_constant<int, 2>{});
+  out_group(std::integral_constant<int, 3>{});
+  // 2. the waves split the row groups: wave 0 finishes groups 0 and 1, wave 1 groups 2 and 3; each hands
+  //    the other the half of its h it does not finish, through the exchange tile [wave][2 groups][nb][r][lane]
+  constexpr int kHalf = 2 * 4 * 16 * 64;
+  auto put_group = [&](auto mbc) {
+    constexpr int mb = decltype(mbc)::value;
+    float* dst = xch + wave * kHalf + (mb & 1) * 4 * 16 * 64;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[(nb * 16 + r) * 64 + lane] = acc[mb][nb][r];
+  };
+  if (wave == 0) {
+    put_group(std::integral_constant<int, 2>{});
+    put_group(std::integral_constant<int, 3>{});
+  } else {
+    put_group(std::integral_constant<int, 0>{});
+    put_group(std::integral_constant<int, 1>{});
   }
   __syncthreads();
-  if (wave != 0) return;
-  float u2[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) u2[nb] = f16_to_f32(a.w2_suh[int64_t(slot) * a.I + col0 + 32 * nb + c]);
+  // 3. a = silu(h1) * h3 * w2's suh, w2's input rotation of these 128 features, fp16 in PERM16 order
   auto a_group = [&](auto mbc) {
     constexpr int mb = decltype(mbc)::value;
+    const float* other = xch + (1 - wave) * kHalf + (mb & 1) * 4 * 16 * 64;
     float v[4][16];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v[nb][r] = acc[mb][nb][r];
-    had128_cols32(v, lane);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float h1 = v[nb][r] * sv[nb];
-        const float h3 = xch[((mb * 4 + nb) * 16 + r) * 64 + lane];
-        v[nb][r] = h1 / (1.0f + __expf(-h1)) * h3 * u2[nb];
+        const float mine = acc[mb][nb][r], theirs = other[(nb * 16 + r) * 64 + lane];
+        const float h1 = wave == 0 ? mine : theirs, h3 = wave == 0 ? theirs : mine;
+        // silu with the hardware reciprocal (one rounding more than a division, far below the fp16 step)
+        v[nb][r] = h1 * __builtin_amdgcn_rcpf(1.0f + __expf(-h1)) * h3 * u2[nb];
       }
     had128_cols32(v, lane);                                 // w2's input rotation of these 128 features
 #pragma unroll
@@ -216,10 +229,13 @@ __device__ __forceinline__ void moe_w13_tile_block(const MoeArgs& a, const int4v
       }
     }
   };
-  a_group(std::integral_constant<int, 0>{});
-  a_group(std::integral_constant<int, 1>{});
-  a_group(std::integral_constant<int, 2>{});
-  a_group(std::integral_constant<int, 3>{});
+  if (wave == 0) {
+    a_group(std::integral_constant<int, 0>{});
+    a_group(std::integral_constant<int, 1>{});
+  } else {
+    a_group(std::integral_constant<int, 2>{});
+    a_group(std::integral_constant<int, 3>{});
+  }
 }
 
 template <int K>
