@@ -220,9 +220,9 @@ size_t exl3_moe_workspace_bytes(const exl3_bank* bank, int64_t T, int topk, unsi
 /*   out      bf16 [T, H];  x  bf16 [T, H]
  *   topk_ids int32 [T, topk] logical expert ids in [0, E) (device);  topk_w float32 [T, topk] (device).
  * An id outside [0, E) is ignored (contributes nothing).
- * Plans: below 256 routed pairs per expert on average (T * topk < 256 E) the call streams every expert's
+ * Plans: below 128 routed pairs per expert on average (T * topk < 128 E) the call streams every expert's
  * weights once per chunk of up to 32 of its rows (the decode-sized plan); from there on it runs grouped
- * tiles of 128 rows x 128 columns on MFMA (the prefill plan), as long as T * topk * (max(H, I) + 64) * 2 <
+ * tiles of 64 rows x 128 columns on MFMA (the prefill plan), as long as T * topk * (max(H, I) + 64) * 2 <
  * 2^31.  flags: 0, EXL3_FORCE_GEMV (the decode-sized plan at any T) or EXL3_FORCE_MFMA (the prefill plan at
  * any T; EXL3_EUNSUPPORTED past the size limit); the two are exclusive.  Both plans give the same results
  * up to fp32 summation order inside each projection.  EXL3_ACT_INT8 answers EXL3_EUNSUPPORTED.

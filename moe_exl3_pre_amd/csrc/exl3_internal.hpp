@@ -154,9 +154,9 @@ struct MoeLaunch {
   int plan = 0;             // 0: by size, 1: the decode-sized plan (32-row chunks), 2: the prefill plan
 };
 
-// The prefill plan (grouped 128 x 128 tiles) serves calls with at least this many routed pairs per expert
-// on average, when the gathered operands stay under 2 GiB.
-constexpr int kMoePrefillPairsPerExpert = 256;
+// The prefill plan (grouped 64-row x 128-column tiles) serves calls with at least this many routed pairs
+// per expert on average, when the gathered operands stay under 2 GiB.
+constexpr int kMoePrefillPairsPerExpert = 128;
 bool moe_prefill_plan(int64_t P, int E, int H, int I, int plan);
 // Row pitch (halves) of the per-pair fp16 operands (w1 / w3 rotated activations: n = H; w2's operand:
 // n = I).  The expert kernels gather these rows by pair id, one row per lane; at a pitch of a power of two

@@ -679,7 +679,7 @@ hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream) {
   const int64_t rot_blocks = (rot_units + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
   hipLaunchKernelGGL(moe_route_rotate_kernel, dim3(unsigned(1 + rot_blocks)), dim3(kRouteThreads),
                      moe_route_lds_bytes(a.E, a.P), stream, a);
-  // chunk groups of 8 (moe_tile); the prefill plan's 128-row chunks number at most P / 128 + E
+  // chunk groups of 8 (moe_tile); the prefill plan's chunks of kTileRows number at most P / kTileRows + E
   const int64_t nch = prefill ? (int64_t(a.P) + kTileRows - 1) / kTileRows + a.E : a.max_chunks;
   const int64_t cgroups = (nch + 7) / 8 * 8;
   const dim3 g13(unsigned(cgroups * (a.I / kHad))), g2(unsigned(cgroups * ((a.H / kHad + 1) / 2)));

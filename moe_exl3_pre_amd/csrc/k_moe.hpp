@@ -10,7 +10,7 @@
 
 namespace exl3 {
 
-constexpr int kTileRows = 128;   // rows per chunk of the prefill plan (one 128-row tile)
+constexpr int kTileRows = 64;    // rows per chunk of the prefill plan (one tile of rows)
 
 struct MoeArgs {
   const uint16_t* x;        // bf16 [T, H]

@@ -1,6 +1,6 @@
-// MoE expert bank, the prefill-sized plan: grouped 128 x 128 tiles on the prefill GEMM's core.  Built
-// apart from k_moe.hip because these kernels keep their 256 fp32 accumulators in the accumulator
-// registers (as the prefill GEMM does), while the decode-sized plan's kernels use the VGPR form.
+// MoE expert bank, the prefill-sized plan: grouped tiles of 64 gathered rows x 128 columns on the
+// prefill GEMM's MFMA core.  Built apart from k_moe.hip with the iterative register scheduler the tile
+// loops need.
 #include <type_traits>
 
 #include "k_moe.hpp"
@@ -9,13 +9,15 @@ namespace exl3 {
 
 // ---------------------------------------------------------------------------------------------------
 // Prefill-sized plan ("vLLM PR #190", commit message: a second MoE plan for prefill with 64-row blocks
-// beside the decode plan).  With hundreds of rows per expert the streaming core above decodes each
-// expert's weights once per 32-row chunk; here a slot's list is cut into chunks of 128 rows and each
-// projection runs as tiles of 128 gathered rows x 128 columns on the prefill GEMM's core (32x32x16 MFMAs,
-// every decoded tile column feeding 8 of them; k_gemm.hip), so every weight is decoded once per 128 rows.
+// beside the decode plan).  With hundreds of rows per expert the streaming core of the decode-sized plan
+// decodes each expert's weights once per 32-row chunk; here a slot's list is cut into chunks of
+// kTileRows = 64 rows and each projection runs as tiles of 64 gathered rows x 128 columns with 32x32x16
+// MFMAs (the prefill GEMM's operand layouts, k_gemm.hip; every decoded tile column feeds 4 of them), so
+// every weight is decoded once per 64 rows.  A tile keeps 128 fp32 accumulators, so two waves share a
+// SIMD and one wave's epilogue or memory wait overlaps the other's MFMAs.
 //   * w13: a workgroup of two waves per (chunk, 128 intermediate features): wave 0 the w1 tile, wave 1 the
 //     w3 tile of the same rows.  Both apply their output Hadamard-128 and svh in registers and swap half
-//     of their rows through LDS, so that each wave holds h1 and h3 of 64 rows; each forms silu(h1) * h3 *
+//     of their rows through LDS, so that each wave holds h1 and h3 of 32 rows; each forms silu(h1) * h3 *
 //     w2's suh for its rows, applies w2's input Hadamard (the same 128 features) and writes w2's fp16
 //     operand.  As in the decode-sized plan h1, h3 and the product stay in fp32 until that operand.
 //   * w2: a workgroup of four waves per (chunk, 512 output features), one 128-column tile each; output
@@ -23,31 +25,24 @@ namespace exl3 {
 // Rows are gathered by pair id: each lane loads 16 bytes of its own row per A fragment (the rows are the
 // rotated activations the route-and-rotate launch wrote, in PERM16 order), rows past the chunk read zeros.
 // ---------------------------------------------------------------------------------------------------
-constexpr int kXchBytes = 4 * 4 * 16 * 64 * 4;   // one 128 x 128 fp32 tile in the accumulator layout
+constexpr int kMB = kTileRows / 32;               // 32-row groups per tile
+constexpr int kGroupFloats = 4 * 16 * 64;          // one 32-row group of a 128-column tile, accumulator layout
+// Waves per SIMD the tile kernels are built for: 128 accumulators leave room for two
+constexpr int kTileWavesPerSimd = kMB <= 2 ? 2 : 1;
 
-// One 128 x 128 tile of one expert projection over `steps` 64-feature steps.  A holds fp16 rows of `lda`
-// features; lane (c, k) gathers its row 32 mb + c from byte offset aoff[mb] (a_bytes or more reads zeros).
-// Trellis words as in the prefill GEMM: staged per wave in `slot`, three steps in flight.
-template <int K>
+// One (32 MB) x 128 tile of one expert projection over `steps` 64-feature steps.  A holds fp16 rows of
+// `lda` features; lane (c, k) gathers its row 32 mb + c from byte offset aoff[mb] (a_bytes or more reads
+// zeros).  Trellis words as in the prefill GEMM: coalesced loads staged per wave in `slot`.
+template <int K, int MB>
 __device__ __forceinline__ void moe_tile_gemm(const uint16_t* code, uint32_t code_bytes, uint32_t tpr, int cb,
-                                              const uint16_t* A, uint32_t a_bytes, const uint32_t (&aoff)[4],
-                                              int steps, char* slot, float16v (&acc)[4][4]) {
+                                              const uint16_t* A, uint32_t a_bytes, const uint32_t (&aoff)[MB],
+                                              int steps, char* slot, float16v (&acc)[MB][4]) {
   using G = Geom<K>;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;                   // staging: lane (n, g) loads and parks tile row g
   const int c = lane & 31, k = lane >> 5;                   // MFMA: lane (c, k)
   const __amdgpu_buffer_rsrc_t arsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), (short)0, (int)a_bytes, kBufferFlags);
-  auto load_a = [&](int st, half8 (&dst)[4][2][2]) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          dst[mb][j][h] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
-              arsrc, aoff[mb] + uint32_t((64 * st + 16 * (2 * j + k) + 8 * h) * 2), 0, 0));
-  };
   char* my_row = slot + g * Slot<K>::kRowBytes;
   int woff[G::kNW], shift;
   column_word_offsets<K>(c & 15, woff, shift);
@@ -70,7 +65,7 @@ __device__ __forceinline__ void moe_tile_gemm(const uint16_t* code, uint32_t cod
       dst[w] = *reinterpret_cast<const uint32_t*>(row + ((2 * nb + tsel) * G::kWords + woff[w]) * 4);
   };
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -81,63 +76,88 @@ __device__ __forceinline__ void moe_tile_gemm(const uint16_t* code, uint32_t cod
 #pragma unroll
     for (int i = 0; i < K; ++i) *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tn[i];
   };
-  uint32_t wv[4][2][G::kNW];
-  constexpr int kValuPerMfma = K <= 1 ? 2 : K == 2 ? 3 : K <= 4 ? 5 : 8;
-  auto step = [&](int st, const half8 (&a)[4][2][2]) {
+  // The slot holds the words of the step being decoded; each lane reads one tile column ahead (two waves
+  // share a SIMD, so one column of decode covers the LDS latency).  At the end of step st the words of
+  // step st + 1 (loaded one step earlier) are parked and those of st + 2 requested.  The A fragments live
+  // in one buffer: the tile columns run pair-half 0 first, so that half of the next step's fragments is
+  // requested halfway through the step, the other half at its end.
+  uint32_t wv[2][G::kNW];
+  // VALU slots per MFMA in the schedule: the decode of one column feeds 2 MB MFMAs
+  constexpr int kValuPerMfma = (K <= 1 ? 2 : K == 2 ? 3 : K <= 4 ? 5 : 8) * 4 / MB;
+  half8 a[MB][2][2];
+  auto load_a_half = [&](int st, int j) {
+    st = st < steps ? st : steps - 1;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint32_t v[8];
-        decode_column<K, (K <= 3)>(wv[nb][j], shift, v, cbk);
-        read_col(nb, j, wv[nb][j]);                          // the same column of step st + 1
-        const half8 b0 = as_half8(v[0], v[1], v[2], v[3]), b1 = as_half8(v[4], v[5], v[6], v[7]);
+      for (int h = 0; h < 2; ++h)
+        a[mb][j][h] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
+            arsrc, aoff[mb] + uint32_t((64 * st + 16 * (2 * j + k) + 8 * h) * 2), 0, 0));
+  };
+  auto step = [&](int st) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mfma32(a[mb][j][0], b0, acc[mb][nb]);
+    for (int i = 0; i < 8; ++i) {
+      const int j = i >> 2, nb = i & 3;
+      if (i + 1 < 8) read_col((i + 1) & 3, (i + 1) >> 2, wv[(i + 1) & 1]);
+      uint32_t v[8];
+      decode_column<K, (K <= 3)>(wv[i & 1], shift, v, cbk);
+      const half8 b0 = as_half8(v[0], v[1], v[2], v[3]), b1 = as_half8(v[4], v[5], v[6], v[7]);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mfma32(a[mb][j][1], b1, acc[mb][nb]);
-      }
+      for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma32(a[mb][j][0], b0, acc[mb][nb]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma32(a[mb][j][1], b1, acc[mb][nb]);
+      if (i == 3) load_a_half(st + 1, 0);
+    }
+    load_a_half(st + 1, 1);
     park();
-    load_t(st + 3, tn);
+    load_t(st + 2, tn);
+    read_col(0, 0, wv[0]);
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
+    for (int i = 0; i < 16 * MB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
     }
   };
-  half8 a0[4][2][2], a1[4][2][2];
   load_t(0, tn);
-  load_a(0, a0);
+  load_a_half(0, 0);
+  load_a_half(0, 1);
   park();
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) read_col(nb, j, wv[nb][j]);
   load_t(1, tn);
-  park();
-  load_t(2, tn);
-  for (int st = 0; st < steps; st += 2) {                   // steps is even: H and I are multiples of 128
-    load_a(st + 1, a1);
-    step(st, a0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(st + 2 < steps ? st + 2 : steps - 1, a0);
-    step(st + 1, a1);
+  read_col(0, 0, wv[0]);
+  for (int st = 0; st < steps; ++st) {
+    step(st);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // The chunk's pair ids (-1 past its rows) in LDS, and this lane's gathered-row offsets.
 __device__ __forceinline__ void moe_tile_rows(const MoeArgs& a, const int4v ch, int* pid, int lda, uint32_t a_bytes,
-                                              uint32_t (&aoff)[4]) {
+                                              uint32_t (&aoff)[kMB]) {
   const int row0 = ch[1], nrows = ch[2];
   for (int r = threadIdx.x; r < kTileRows; r += blockDim.x) pid[r] = r < nrows ? a.rows[row0 + r] : -1;
   __syncthreads();
   const int c = threadIdx.x & 31;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < kMB; ++mb) {
     const int q = pid[32 * mb + c];
     aoff[mb] = q >= 0 ? uint32_t(q) * uint32_t(lda) * 2u : a_bytes;
   }
+}
+
+// Row groups [mb0, mb0 + n) as compile-time constants: f(integral_constant<int, mb>) for each.
+template <int MB0, int N, typename F>
+__device__ __forceinline__ void for_groups(F&& f) {
+  if constexpr (N > 0) {
+    f(std::integral_constant<int, MB0>{});
+    for_groups<MB0 + 1, N - 1>(f);
+  }
+}
+
+// LDS of a w13 workgroup: the pair ids, then one region that holds the two waves' trellis slots during
+// the main loop and the exchange tile (kMB groups of fp32) after it.
+inline size_t moe_w13_tile_lds(size_t kslot) {
+  const size_t xch = size_t(kMB) * kGroupFloats * 4;
+  return 512 + (xch > 2 * kslot ? xch : 2 * kslot);
 }
 
 template <int K>
@@ -147,15 +167,16 @@ __device__ __forceinline__ void moe_w13_tile_block(const MoeArgs& a, const int4v
   const int c = lane & 31, k = lane >> 5;
   const int slot = ch[0];
   int* pid = reinterpret_cast<int*>(lds);
-  float* xch = reinterpret_cast<float*>(lds + 512);
-  char* slots = lds + 512 + kXchBytes;
+  char* region = lds + 512;
+  float* xch = reinterpret_cast<float*>(region);
   const uint32_t a_bytes = uint32_t(a.P) * uint32_t(a.ldx) * 2u;
-  uint32_t aoff[4];
+  uint32_t aoff[kMB];
   moe_tile_rows(a, ch, pid, a.ldx, a_bytes, aoff);
   const int64_t off = wave == 0 ? a.off_w1[slot] : a.off_w3[slot];
-  float16v acc[4][4];
-  moe_tile_gemm<K>(a.w13 + off, uint32_t(int64_t(a.H) * a.I * K / 8), uint32_t(a.I / 16), ib,
-                   a.xh13 + int64_t(wave) * a.P * a.ldx, a_bytes, aoff, a.H / 64, slots + wave * Slot<K>::kBytes, acc);
+  float16v acc[kMB][4];
+  moe_tile_gemm<K, kMB>(a.w13 + off, uint32_t(int64_t(a.H) * a.I * K / 8), uint32_t(a.I / 16), ib,
+                        a.xh13 + int64_t(wave) * a.P * a.ldx, a_bytes, aoff, a.H / 64, region + wave * Slot<K>::kBytes,
+                        acc);
   const int col0 = ib * kHad;
   float sv[4], u2[4];
 #pragma unroll
@@ -164,7 +185,7 @@ __device__ __forceinline__ void moe_w13_tile_block(const MoeArgs& a, const int4v
     u2[nb] = f16_to_f32(a.w2_suh[int64_t(slot) * a.I + col0 + 32 * nb + c]);
   }
   // The per-32-row-group steps below take the group as a compile-time constant, so every accumulator
-  // index is static and the 256 accumulators stay in registers.
+  // index is static and the accumulators stay in registers.
   // 1. each wave turns its own tile into h = svh * Had128(acc) / sqrt(128) (wave 0: h1, wave 1: h3), in place
   auto out_group = [&](auto mbc) {
     constexpr int mb = decltype(mbc)::value;
@@ -179,33 +200,29 @@ __device__ __forceinline__ void moe_w13_tile_block(const MoeArgs& a, const int4v
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = v[nb][r] * sv[nb];
   };
-  out_group(std::integral_constant<int, 0>{});
-  out_group(std::integral_constant<int, 1>{});
-  out_group(std::integral_constant<int, 2>{});
-  out_group(std::integral_constant<int, 3>{});
-  // 2. the waves split the row groups: wave 0 finishes groups 0 and 1, wave 1 groups 2 and 3; each hands
-  //    the other the half of its h it does not finish, through the exchange tile [wave][2 groups][nb][r][lane]
-  constexpr int kHalf = 2 * 4 * 16 * 64;
+  for_groups<0, kMB>(out_group);
+  // 2. the waves split the row groups: wave 0 finishes groups [0, kMB / 2), wave 1 the others; each hands
+  //    the other the groups it does not finish, through the exchange tile [wave][kMB / 2 groups][nb][r][lane],
+  //    which overlays the trellis slots (hence the first barrier)
+  constexpr int kHalfG = kMB / 2;
+  __syncthreads();
   auto put_group = [&](auto mbc) {
     constexpr int mb = decltype(mbc)::value;
-    float* dst = xch + wave * kHalf + (mb & 1) * 4 * 16 * 64;
+    float* dst = xch + (wave * kHalfG + mb % kHalfG) * kGroupFloats;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dst[(nb * 16 + r) * 64 + lane] = acc[mb][nb][r];
   };
-  if (wave == 0) {
-    put_group(std::integral_constant<int, 2>{});
-    put_group(std::integral_constant<int, 3>{});
-  } else {
-    put_group(std::integral_constant<int, 0>{});
-    put_group(std::integral_constant<int, 1>{});
-  }
+  if (wave == 0)
+    for_groups<kHalfG, kHalfG>(put_group);
+  else
+    for_groups<0, kHalfG>(put_group);
   __syncthreads();
   // 3. a = silu(h1) * h3 * w2's suh, w2's input rotation of these 128 features, fp16 in PERM16 order
   auto a_group = [&](auto mbc) {
     constexpr int mb = decltype(mbc)::value;
-    const float* other = xch + (1 - wave) * kHalf + (mb & 1) * 4 * 16 * 64;
+    const float* other = xch + ((1 - wave) * kHalfG + mb % kHalfG) * kGroupFloats;
     float v[4][16];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -229,13 +246,10 @@ __device__ __forceinline__ void moe_w13_tile_block(const MoeArgs& a, const int4v
       }
     }
   };
-  if (wave == 0) {
-    a_group(std::integral_constant<int, 0>{});
-    a_group(std::integral_constant<int, 1>{});
-  } else {
-    a_group(std::integral_constant<int, 2>{});
-    a_group(std::integral_constant<int, 3>{});
-  }
+  if (wave == 0)
+    for_groups<0, kHalfG>(a_group);
+  else
+    for_groups<kHalfG, kHalfG>(a_group);
 }
 
 template <int K>
@@ -247,19 +261,19 @@ __device__ __forceinline__ void moe_w2_tile_block(const MoeArgs& a, const int4v 
   int* pid = reinterpret_cast<int*>(lds);
   char* slots = lds + 512;
   const uint32_t a_bytes = uint32_t(a.P) * uint32_t(a.ldh) * 2u;
-  uint32_t aoff[4];
+  uint32_t aoff[kMB];
   moe_tile_rows(a, ch, pid, a.ldh, a_bytes, aoff);
   const int hb = 4 * cg + wave;
   if (hb >= a.H / kHad) return;                             // past the last 128-column block (no barrier below)
-  float16v acc[4][4];
-  moe_tile_gemm<K>(a.w2 + a.off_w2[slot], uint32_t(int64_t(a.I) * a.H * K / 8), uint32_t(a.H / 16), hb, a.ah,
-                   a_bytes, aoff, a.I / 64, slots + wave * Slot<K>::kBytes, acc);
+  float16v acc[kMB][4];
+  moe_tile_gemm<K, kMB>(a.w2 + a.off_w2[slot], uint32_t(int64_t(a.I) * a.H * K / 8), uint32_t(a.H / 16), hb, a.ah,
+                        a_bytes, aoff, a.I / 64, slots + wave * Slot<K>::kBytes, acc);
   const int col0 = hb * kHad;
   float sv[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) sv[nb] = kInvSqrt128 * f16_to_f32(a.w2_svh[int64_t(slot) * a.H + col0 + 32 * nb + c]);
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  auto o_group = [&](auto mbc) {
+    constexpr int mb = decltype(mbc)::value;
     float v[4][16];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -274,11 +288,12 @@ __device__ __forceinline__ void moe_w2_tile_block(const MoeArgs& a, const int4v 
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) dst[32 * nb] = v[nb][r] * sv[nb];
     }
-  }
+  };
+  for_groups<0, kMB>(o_group);
 }
 
 template <int KSET>
-__global__ __launch_bounds__(128, 1) void moe_w13_tile_kernel(MoeArgs a) {
+__global__ __launch_bounds__(128, kTileWavesPerSimd) void moe_w13_tile_kernel(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int c, ib;
   moe_tile(a.I / kHad, c, ib);
@@ -288,7 +303,7 @@ __global__ __launch_bounds__(128, 1) void moe_w13_tile_kernel(MoeArgs a) {
 }
 
 template <int KSET>
-__global__ __launch_bounds__(256, 1) void moe_w2_tile_kernel(MoeArgs a) {
+__global__ __launch_bounds__(256, kTileWavesPerSimd) void moe_w2_tile_kernel(MoeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int c, cg;
   moe_tile((a.H / kHad + 3) / 4, c, cg);
@@ -303,7 +318,7 @@ template <int KS>
 static void launch_tiles(const MoeArgs& a, int pass, size_t kslot, int64_t cgroups, hipStream_t stream) {
   if (pass == 0)
     hipLaunchKernelGGL(moe_w13_tile_kernel<KS>, dim3(unsigned(cgroups * (a.I / kHad))), dim3(128),
-                       512 + kXchBytes + 2 * kslot, stream, a);
+                       moe_w13_tile_lds(kslot), stream, a);
   else
     hipLaunchKernelGGL(moe_w2_tile_kernel<KS>, dim3(unsigned(cgroups * ((a.H / kHad + 3) / 4))), dim3(256),
                        512 + 4 * kslot, stream, a);

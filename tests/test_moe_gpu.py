@@ -20,8 +20,8 @@ def _setup(m):
     return bank, x, ids, w
 
 
-# the two plans: the decode-sized one (32-row chunks, streaming core) and the prefill one (128-row
-# chunks, grouped 128 x 128 tiles); by default the call picks one by the pairs per expert
+# the two plans: the decode-sized one (32-row chunks, streaming core) and the prefill one (64-row
+# chunks, grouped 64 x 128 tiles); by default the call picks one by the pairs per expert
 PLANS = {"decode_plan": exl3.FORCE_GEMV, "prefill_plan": exl3.FORCE_MFMA}
 
 
@@ -60,8 +60,8 @@ def test_moe_small_full_parity(cfg, plan):
 
 @pytest.mark.parametrize("plan", list(PLANS))
 def test_moe_many_rows_per_expert_and_empty_expert(plan):
-    """~100 rows per expert (several 32-row chunks, one partial; one partial 128-row chunk on the prefill
-    plan) and one expert with no token."""
+    """~100 rows per expert (several 32-row chunks, one partial; a full and a partial 64-row chunk on the
+    prefill plan) and one expert with no token."""
     m = synth.moe_case(711, T=200, E=5, topk=2, H=256, I=256, Ks=(2, 3, 4))
     rng = np.random.default_rng(9)
     ids = np.stack([rng.choice(4, 2, replace=False) for _ in range(m["T"])]).astype(np.int32)   # expert 4 unused
@@ -209,9 +209,9 @@ def test_moe_full_size_sampled():
 
 
 def test_moe_plan_choice_by_pairs_per_expert():
-    """Without a FORCE flag the call runs the decode-sized plan below 256 routed pairs per expert and the
+    """Without a FORCE flag the call runs the decode-sized plan below 128 routed pairs per expert and the
     prefill plan from there on (bitwise the forced calls)."""
-    for T, plan in ((510, "decode_plan"), (512, "prefill_plan")):      # 8 experts, top-4: 255 and 256 per expert
+    for T, plan in ((254, "decode_plan"), (256, "prefill_plan")):      # 8 experts, top-4: 127 and 128 per expert
         m = synth.moe_case(740 + T, T=T, E=8, topk=4, H=256, I=128)
         bank, x, ids, w = _setup(m)
         assert torch.equal(_run(bank, x, ids, w), _run(bank, x, ids, w, flags=PLANS[plan])), T
@@ -219,7 +219,7 @@ def test_moe_plan_choice_by_pairs_per_expert():
 
 def test_moe_prefill_bank_full_size_sampled():
     """The prefill-sized call on the full bank shape: T=4096 tokens, 128 experts, top-8 (32,768 pairs, ~256
-    rows per expert: two 128-row chunks each), H=2048, I=768, K in {2,3,4}; 16 tokens against the oracle,
+    rows per expert: four or five 64-row chunks each), H=2048, I=768, K in {2,3,4}; 16 tokens against the oracle,
     covering every K group and the most- and least-loaded experts."""
     cfg = synth.MOE
     T = 4096
