@@ -22,6 +22,7 @@ same step, on one thread and on all usable cores (with the host's CPU count and 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill] [--no-moe] [--no-mlp]
                     [--no-embed]
     python bench.py --pmc-ref ...     # eager launches plus a 1 GiB copy, for counter runs
+    python bench.py --pmc-moe ...     # eager MoE bank calls (T=256, T=4096) plus 1 GiB copies, for counter runs
     python bench.py --pmc-int8        # the same for the int8 embedding gather and output head
 """
 from __future__ import annotations
@@ -71,6 +72,9 @@ def parse():
                     help="counter runs: 1 GiB device copies (known bytes), then two eager calls of each prefill projection")
     ap.add_argument("--pmc-ref", action="store_true",
                     help="eager decode launches (no graph) plus a plain 1 GiB copy, for hardware-counter runs")
+    ap.add_argument("--pmc-moe", action="store_true",
+                    help="counter runs: 1 GiB device copies (known bytes), then eager MoE bank calls at T=256 and "
+                         "T=4096 (3 of each, on one bank)")
     ap.add_argument("--pmc-int8", action="store_true",
                     help="counter runs: 1 GiB device copies (known bytes), then eager int8 embedding gathers "
                          "(T=8192) and output-head calls (M=1) over the 248,320 x 5120 table")
@@ -585,6 +589,38 @@ def pmc_int8(torch, exl3, dev):
                       "head_bytes": V * H + 2 * V + 2 * H + 2 * V}), flush=True)
 
 
+def pmc_moe(torch, exl3, synth, dev):
+    """Eager launches for counter runs on the MoE bank: 1 GiB copies, then 3 calls at T=256 (the decode-sized
+    plan) and 3 at T=4096 (the prefill plan) on one bank, with the bench's inputs."""
+    from moe_exl3_pre_amd.bank import DeviceBank, pack_bank
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    del src, dst
+    cfg = synth.MOE
+    m = synth.moe_case(1003, T=cfg["T"], E=cfg["E"], topk=cfg["topk"], H=cfg["H"], I=cfg["I"], Ks=cfg["Ks"])
+    bank = DeviceBank(pack_bank(m["experts"], cfg["H"], cfg["I"]), dev)
+    rng = np.random.default_rng(1009)
+    for T in (cfg["T"], 4096):
+        if T == cfg["T"]:
+            x = torch.from_numpy(m["x_bits"].view(np.int16).copy()).to(dev).view(torch.bfloat16)
+            ids, w = m["topk_ids"], m["topk_w"]
+        else:
+            x = torch.from_numpy(synth.random_activations(rng, T, cfg["H"])[1].view(np.int16).copy()).to(dev)
+            x = x.view(torch.bfloat16)
+            ids, w = synth.routing(rng, T, cfg["E"], cfg["topk"])
+        ids = torch.from_numpy(ids.astype(np.int32)).to(dev)
+        w = torch.from_numpy(w.astype(np.float32)).to(dev)
+        out = torch.empty_like(x)
+        ws = exl3.alloc_workspace(exl3.moe_workspace_bytes(bank, T, cfg["topk"]), dev)
+        for _ in range(3):
+            exl3.moe_bank_forward(out, x, ids, w, bank, ws=ws)
+        torch.cuda.synchronize()
+        del ws
+    print(json.dumps({"pmc_moe": True, "copy_bytes": 1 << 30}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -601,6 +637,9 @@ def main():
         return
     if a.pmc_int8:
         pmc_int8(torch, exl3, dev)
+        return
+    if a.pmc_moe:
+        pmc_moe(torch, exl3, synth, dev)
         return
     if a.pmc_prefill:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

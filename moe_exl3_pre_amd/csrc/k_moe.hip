@@ -679,9 +679,9 @@ hipError_t launch_moe(const MoeLaunch& m, hipStream_t stream) {
   const int64_t rot_blocks = (rot_units + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
   hipLaunchKernelGGL(moe_route_rotate_kernel, dim3(unsigned(1 + rot_blocks)), dim3(kRouteThreads),
                      moe_route_lds_bytes(a.E, a.P), stream, a);
-  // chunk groups of 8 (moe_tile); the prefill plan's chunks of kTileRows number at most P / kTileRows + E
+  // chunk slots of the grid (moe_tile); the prefill plan's chunks of kTileRows number at most P / kTileRows + E
   const int64_t nch = prefill ? (int64_t(a.P) + kTileRows - 1) / kTileRows + a.E : a.max_chunks;
-  const int64_t cgroups = (nch + 7) / 8 * 8;
+  const int64_t cgroups = moe_chunk_slots(nch);
   const dim3 g13(unsigned(cgroups * (a.I / kHad))), g2(unsigned(cgroups * ((a.H / kHad + 1) / 2)));
   for (int pass = 0; pass < 2; ++pass) {
     // the K values of this projection, as a bit set

@@ -52,13 +52,23 @@ __device__ __forceinline__ bool moe_chunk(const MoeArgs& a, int c, int4v& ch) {
   return true;
 }
 
-// Workgroup -> (chunk, column group).  The column groups of one chunk land on one XCD (workgroups are
-// dealt to the 8 XCDs round-robin), so the chunk's gathered activations are fetched into one L2.
+// Workgroup -> (chunk, column group).  Workgroups are dealt to the 8 XCDs round-robin (block id mod 8);
+// XCD x takes the chunk runs x, x + 8, x + 16, ... of kChunkRun consecutive chunks each, with every column
+// group of each chunk.  So the column groups of a chunk share its gathered activations in one L2, and the
+// consecutive chunks of one expert mostly share its trellis words there too, while every XCD still gets
+// a mix of the K groups.  The launch covers a multiple of 8 kChunkRun chunks (moe_chunk_slots).
+constexpr int kChunkRun = 4;
+
 __device__ __forceinline__ void moe_tile(int ncg, int& c, int& cg) {
   const int id = blockIdx.x, x = id & 7, y = id >> 3;
   cg = y % ncg;
-  c = (y / ncg) * 8 + x;
+  const int i = y / ncg;                                     // this XCD's i-th chunk
+  c = ((i / kChunkRun) * 8 + x) * kChunkRun + i % kChunkRun;
 }
+
+// Chunk slots a launch covers for at most n chunks: a multiple of 8 kChunkRun, so that moe_tile maps the
+// grid onto [0, slots) one to one.
+inline int64_t moe_chunk_slots(int64_t n) { return (n + 8 * kChunkRun - 1) / (8 * kChunkRun) * (8 * kChunkRun); }
 
 // KSET 0 covers the mixed set {2, 3, 4} in one launch (one switch per workgroup); KSET k in 1..8 serves
 // the chunks of one K and skips the others, so any other mix runs as one launch per distinct K.

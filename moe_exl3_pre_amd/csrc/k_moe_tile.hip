@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, kTileWavesPerSimd) void moe_w2_tile_kernel(Moe
 }
 
 // One pass of the prefill plan (0: w13, 1: w2) for the K set KS (0: the mixed set {2, 3, 4}); the grid
-// covers `cgroups` chunks (a multiple of 8, see moe_tile) x the column groups.
+// covers `cgroups` chunk slots (moe_chunk_slots, see moe_tile) x the column groups.
 template <int KS>
 static void launch_tiles(const MoeArgs& a, int pass, size_t kslot, int64_t cgroups, hipStream_t stream) {
   if (pass == 0)
