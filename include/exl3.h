@@ -70,8 +70,8 @@ const char* exl3_last_error(void);
 /* ABI version (major * 100 + minor). */
 int exl3_version(void);
 
-/* Largest M served by the decode-phase path (launches of up to 16 rows) when no FORCE flag is given,
- * for a call whose widest shard has OC output columns: 16 * clamp(16384 / OC, 2, 8), the measured
+/* Largest M served by the decode-phase path (launches of up to 32 rows) when no FORCE flag is given,
+ * for a call whose widest shard has OC output columns: 16 * clamp(10240 / OC, 2, 8), the measured
  * crossover against the (feature-split) MFMA GEMM over a 5120/17408 decoder's projections. */
 int64_t exl3_gemv_max_rows(int64_t OC);
 
@@ -109,9 +109,9 @@ int exl3_gemm_tail_splits(int64_t M, int64_t IC, int64_t OC);
  * bf16.  M <= exl3_gemv_max_rows(OC) runs the decode-phase kernel, larger M the MFMA GEMM (the two agree
  * to rounding, not bitwise), split over the input features when the shard is small (exl3_gemm_splits).
  * For a given split count a row's result does not depend on the other rows; on the GEMM with
- * EXL3_GEMM_NO_SPLIT it does not depend on M at all.  Decode-phase launches of 5..16 rows rotate the
- * activations once per call into the workspace (16 x IC fp16 per distinct (s_in, rin)) before the
- * decode kernel; smaller ones rotate inside the kernel.  Both rotations give the same bits.
+ * EXL3_GEMM_NO_SPLIT it does not depend on M at all.  Decode-phase launches of 5..32 rows rotate the
+ * activations once per call into the workspace (16 or 32 rows x IC fp16 per distinct (s_in, rin)) before
+ * the decode kernel; smaller ones rotate inside the kernel.  Both rotations give the same bits.
  * 8-bit path (EXL3_ACT_INT8): the codes q are exact in fp16 and every q * W product is exact in fp32,
  * so the contraction is the integer dot product up to fp32 summation; the row scale is applied before
  * the output transform.
@@ -160,7 +160,7 @@ int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int
  * device array of exl3_static_scratch_bytes() (16 MiB) that the library holds on every GPU it runs on
  * until the process ends; nothing is allocated or freed per call.  A call whose workspace need
  * (exl3_linear_multi_workspace_bytes) exceeds that size launches nothing and returns EXL3_EWORKSPACE;
- * decode-phase calls of the usual shapes fit (the 4096 -> 2 x 14336 gate_up at 16 rows needs 3.8 MB),
+ * decode-phase calls of the usual shapes fit (the 4096 -> 2 x 14336 gate_up needs 3.8 MB at 16 rows, 7.6 at 32),
  * most prefill-phase calls do not.
  * The first call on a device (with that device current) looks up the array's address and clears its
  * counter head with a kernel on `stream`; make that first call outside stream capture.  Every call on a

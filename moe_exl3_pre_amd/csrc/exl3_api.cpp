@@ -54,7 +54,7 @@ constexpr unsigned kKnownFlags = EXL3_ACT_INT8 | EXL3_FORCE_GEMV | EXL3_FORCE_MF
 // up to 32 rows for 17408 and 7168 outputs and up to 48 for 5120; the threshold
 // 16 * clamp(16384 / OC, 2, 8) follows that, between two and eight launches.
 int64_t gemv_max_rows(int64_t OC) {
-  int64_t chunks = OC > 0 ? 16384 / OC : 2;
+  int64_t chunks = OC > 0 ? 10240 / OC : 2;
   chunks = chunks < 2 ? 2 : (chunks > 8 ? 8 : chunks);
   return chunks * kDecodeMaxRows;
 }
@@ -105,9 +105,11 @@ bool use_decode_path(int64_t M, unsigned flags, int64_t OC) {
   return M <= gemv_max_rows(OC);
 }
 
-// Row chunks the decode-phase path launches: full chunks of kDecodeMaxRows rows, then the remainder.
-int64_t first_chunk(int64_t M) { return M < kDecodeMaxRows ? M : kDecodeMaxRows; }
-int64_t last_chunk(int64_t M) { return M - (M - 1) / kDecodeMaxRows * kDecodeMaxRows; }
+// Row chunks the decode-phase path launches: full chunks of kDecodeLaunchRows rows, then the remainder.
+int64_t first_chunk(int64_t M) { return M < kDecodeLaunchRows ? M : kDecodeLaunchRows; }
+int64_t last_chunk(int64_t M) { return M - (M - 1) / kDecodeLaunchRows * kDecodeLaunchRows; }
+// Rows the pre-rotation region of a decode-phase call holds: its largest chunk, padded to 16-row fragments.
+int64_t pre_rows(int64_t M) { return (first_chunk(M) + kDecodeMaxRows - 1) / kDecodeMaxRows * kDecodeMaxRows; }
 
 // Slab bytes the decode-phase path needs for these shards (mixes the kernels do not cover run one
 // launch per shard); false if some chunk cannot be planned.
@@ -171,10 +173,11 @@ int check_workspace(const Layout& L, void* ws, size_t ws_bytes) {
   return EXL3_OK;
 }
 
-// The decode-phase path: one launch per chunk of <= 16 rows covering every shard.  A chunk of at least
+// The decode-phase path: one launch per chunk of <= 32 rows covering every shard.  A chunk of at least
 // kPreRotateRows rows first rotates its activations once per distinct (s_in, rin) into the workspace
-// (fragment-major, 16 rows), and the decode launch reads them from there.
-// gu (optional): the dense MLP block's gate_up output [M, 2 IC]; the pre-rotation (5..16 rows) or the decode
+// (fragment-major, 16-row blocks), and the decode launch reads them from there (a chunk of 17..32 rows
+// as two 16-row groups in one launch, so the weights are streamed once per 32 rows).
+// gu (optional): the dense MLP block's gate_up output [M, 2 IC]; the pre-rotation (5..32 rows) or the decode
 // kernel's in-block pre-pass (1..4 rows) then forms the input h = bf16(silu(g) * u) itself.
 int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n,
                const DecShardIn* in_, char* ws, const Layout& L, hipStream_t stream, const void* gu = nullptr) {
@@ -182,8 +185,8 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
   for (int i = 0; i < n; ++i) in[i] = in_[i];
   int slot[kMaxShards];
   distinct_inputs(n, in, slot);
-  for (int64_t r0 = 0; r0 < M; r0 += kDecodeMaxRows) {
-    const int64_t rows = (M - r0) < kDecodeMaxRows ? (M - r0) : kDecodeMaxRows;
+  for (int64_t r0 = 0; r0 < M; r0 += kDecodeLaunchRows) {
+    const int64_t rows = (M - r0) < kDecodeLaunchRows ? (M - r0) : kDecodeLaunchRows;
     const void* xr = static_cast<const uint16_t*>(x) + r0 * IC;
     void* orow = static_cast<uint16_t*>(out) + r0 * ldo;
     DecPlan pl;
@@ -193,7 +196,7 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
       for (int i = 0; i < n; ++i) {
         char* region = ws + L.xh_off + L.xh_bytes * size_t(slot[i]);
         if (slot[i] > done) {
-          if (L.xh_bytes < size_t(kDecodeMaxRows) * size_t(IC) * 2)
+          if (L.xh_bytes < size_t((rows + kDecodeMaxRows - 1) / kDecodeMaxRows * kDecodeMaxRows) * size_t(IC) * 2)
             return fail(EXL3_EWORKSPACE, "%s: workspace has no pre-rotation region", who);
           hipError_t e =
               gu ? launch_prepass_silu_f16(static_cast<const uint16_t*>(gu) + r0 * 2 * IC, in[i].s_in, in[i].rin,
@@ -348,7 +351,7 @@ bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsign
     if (!decode_slab_bytes(M, IC, n, in, &slab)) return false;
     int slot[kMaxShards];
     const bool pre = first_chunk(M) >= kPreRotateRows || last_chunk(M) >= kPreRotateRows;
-    *L = layout_for(slab, kDecodeMaxRows, IC, pre ? distinct_inputs(n, in, slot) : 0, false, kDecodeMaxRows);
+    *L = layout_for(slab, pre_rows(M), IC, pre ? distinct_inputs(n, in, slot) : 0, false, kDecodeMaxRows);
   } else {
     size_t slab = 0;                                      // shards run one after another: the largest split
     if (!(flags & EXL3_GEMM_NO_SPLIT))

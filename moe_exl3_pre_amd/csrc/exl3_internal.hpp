@@ -12,7 +12,8 @@ constexpr size_t kCounterBytes = kCounterSlots * sizeof(int);
 constexpr size_t kAlign = 256;
 constexpr int kMaxShards = 16;
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
-constexpr int kDecodeMaxRows = 16;      // rows one decode-phase launch covers
+constexpr int kDecodeMaxRows = 16;      // rows of one MFMA row group of the decode-phase kernel
+constexpr int kDecodeLaunchRows = 32;   // rows one decode-phase launch covers (two groups, pre-rotated)
 // Decode-phase launches of at least this many rows take activations rotated once per call by the
 // fragment-major pre-pass instead of rotating them in every block.  The separate launch costs ~4 us; the
 // in-block rotation grows with the rows (gate_up IC=4096 at M = 4 / 5: 19.0 / 20.9 us in-block against
@@ -48,7 +49,8 @@ struct DecPlan {
   int counters;             // counter slots used
 };
 
-// Plans one decode-phase launch of M <= 16 rows over n shards; false if it cannot be served.
+// Plans one decode-phase launch of M <= 32 rows over n shards (above 16 rows with pre-rotated
+// activations); false if it cannot be served.
 bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl);
 // silu: x is a dense MLP block's gate_up output [M, 2 IC] and the activation bf16(silu(g) * u) is formed in the
 // in-block pre-pass (one shard, 1..4 rows, no pre-rotation; otherwise hipErrorInvalidValue).

@@ -63,10 +63,14 @@ struct DecArgs {
 // repeats the rotation, which at M = 8 costs about as much VALU as the decode itself.
 // SILU (MR 1 or 4 only): a.x is a dense MLP block's gate_up output [M, 2 IC]; the pre-pass input is
 // h = bf16(silu(g) * u), g = a.x[m, k], u = a.x[m, IC + k], formed as the block's activation kernel forms it.
-template <int K, int SPW, int MR, bool SILU = false>
+// RG (MR == 0 only): 16-row groups of the launch.  With RG = 2 one launch covers up to 32 rows: every
+// decoded tile column feeds the MFMAs of both groups, so the weights are streamed once for 32 rows, and
+// each group is reduced exactly as a 16-row launch reduces it (the same bits per row).
+template <int K, int SPW, int MR, bool SILU = false, int RG = 1>
 __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& sh, int local, char* lds) {
   constexpr bool kPre = MR == 0;
   static_assert(!SILU || MR == 1 || MR == 4, "the folded activation is for the in-block pre-pass");
+  static_assert(RG == 1 || (RG == 2 && kPre), "two row groups need pre-rotated activations");
   using G = Geom<K>;
   // steps of trellis words in flight per wave: one.  Every block requests its first step at once, so
   // deeper prefetch only queues the first data of late waves behind the early waves' later steps.
@@ -128,12 +132,15 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   const uint32_t step_stride = 4u * tpr * G::kWords * 4u;
   const uint32_t base_blk = uint32_t(blk) * kNB * G::kWords * 4u;
   u32x4 tb[kD][K];
-  half8 ta[kD][2];   // pre-rotated A fragments of the staged steps (kPre)
-  auto load_a = [&](int st, half8 (&dst)[2]) {
+  half8 ta[kD][RG][2];   // pre-rotated A fragments of the staged steps (kPre)
+  auto load_a = [&](int st, half8 (&dst)[RG][2]) {
     const int step = 2 * ba + (cnt > 0 ? w_s0 + (st < cnt ? st : cnt - 1) : 0);
-    const uint16_t* f = sh.xf + (int64_t(step) * 2 * 512 + lane * 8);
-    dst[0] = *reinterpret_cast<const half8*>(f);
-    dst[1] = *reinterpret_cast<const half8*>(f + 512);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {   // 16-row block rg of the fragment-major buffer
+      const uint16_t* f = sh.xf + ((int64_t(rg) * (a.IC / 64) + step) * 2 * 512 + lane * 8);
+      dst[rg][0] = *reinterpret_cast<const half8*>(f);
+      dst[rg][1] = *reinterpret_cast<const half8*>(f + 512);
+    }
   };
   auto load_step = [&](int st, u32x4 (&dst)[K]) {
     // Steps past this wave's count (their results are never used) re-read a step of this block's own
@@ -184,9 +191,11 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   int woff[G::kNW], shift;
   column_word_offsets<K>(n, woff, shift);
   const CodebookRegs cb = codebook_regs();
-  float4v acc[kNB];
+  float4v acc[RG][kNB];
 #pragma unroll
-  for (int j = 0; j < kNB; ++j) acc[j] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) acc[rg][j] = (float4v){0.f, 0.f, 0.f, 0.f};
   const uint16_t* xa = xs + (n < M ? n : M) * lrow + 64 * w_s0 + 16 * g;   // row n, or the zero row
 #pragma unroll
   for (int st = 0; st < SPW; ++st) {
@@ -195,17 +204,20 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
       for (int i = 0; i < K; ++i)
         *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tb[st % kD][i];
     }
-    half8 a0, a1;
+    half8 a0[RG], a1[RG];
     if constexpr (kPre) {
-      a0 = ta[st % kD][0];
-      a1 = ta[st % kD][1];
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        a0[rg] = ta[st % kD][rg][0];
+        a1[rg] = ta[st % kD][rg][1];
+      }
       load_a(st + kD, ta[st % kD]);
     }
     load_step(st + kD, tb[st % kD]);
     if (st < cnt) {
       if constexpr (!kPre) {
-        a0 = *reinterpret_cast<const half8*>(xa + 64 * st);
-        a1 = *reinterpret_cast<const half8*>(xa + 64 * st + 8);
+        a0[0] = *reinterpret_cast<const half8*>(xa + 64 * st);
+        a1[0] = *reinterpret_cast<const half8*>(xa + 64 * st + 8);
       }
       uint32_t wv[2][G::kNW];
       auto read_col = [&](int j, uint32_t (&dst)[G::kNW]) {
@@ -219,37 +231,46 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
         if (j + 1 < kNB) read_col(j + 1, wv[(j + 1) & 1]);
         uint32_t b[8];
         decode_column<K>(wv[j & 1], shift, b, cb);
-        acc[j] = mfma16(a0, as_half8(b[0], b[1], b[2], b[3]), acc[j]);
-        acc[j] = mfma16(a1, as_half8(b[4], b[5], b[6], b[7]), acc[j]);
+        const half8 b0 = as_half8(b[0], b[1], b[2], b[3]), b1 = as_half8(b[4], b[5], b[6], b[7]);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) acc[rg][j] = mfma16(a0[rg], b0, acc[rg][j]);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) acc[rg][j] = mfma16(a1[rg], b1, acc[rg][j]);
       }
     }
   }
 
-  // ---- 5. sum the waves' partials in LDS (fixed order); wave w finishes output rows w, w + kWaves
-  __syncthreads();                                          // everyone is done reading xs
-  float* red = reinterpret_cast<float*>(lds);               // [kWaves][M][128]
-#pragma unroll
-  for (int j = 0; j < kNB; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * g + r;
-      if (row < M) red[(wave * M + row) * kHad + 16 * j + n] = acc[j][r];
-    }
-  __syncthreads();
-
+  // ---- 5. sum the waves' partials in LDS (fixed order), one 16-row group at a time; wave w finishes
+  // rows w and w + kWaves of every group
   const int64_t c0 = int64_t(blk) * kHad + 2 * lane;        // shard-local column of (v0, v1)
-  constexpr int kRW = (kDecodeMaxRows + kWaves - 1) / kWaves; // output rows per wave: wave + t * kWaves
-  float v0[kRW], v1[kRW];
+  constexpr int kRW = (kDecodeMaxRows + kWaves - 1) / kWaves; // output rows per wave and group
+  constexpr int kRT = RG * kRW;                               // output rows per wave
+  auto out_row = [&](int t) { return kDecodeMaxRows * (t / kRW) + wave + (t % kRW) * kWaves; };
+  float v0[kRT], v1[kRT];
+  float* red = reinterpret_cast<float*>(lds);               // [kWaves][rows of the group][128]
 #pragma unroll
-  for (int t = 0; t < kRW; ++t) {
-    const int row = wave + t * kWaves;
-    v0[t] = v1[t] = 0.f;
-    if (row < M) {
+  for (int rg = 0; rg < RG; ++rg) {
+    const int Mg = M - kDecodeMaxRows * rg < kDecodeMaxRows ? M - kDecodeMaxRows * rg : kDecodeMaxRows;
+    __syncthreads();                                        // xs, or the previous group's partials, are read
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float* p = red + (w * M + row) * kHad + 2 * lane;
-        v0[t] += p[0];
-        v1[t] += p[1];
+    for (int j = 0; j < kNB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        if (row < Mg) red[(wave * Mg + row) * kHad + 16 * j + n] = acc[rg][j][r];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int tg = 0; tg < kRW; ++tg) {
+      const int row = wave + tg * kWaves;                   // within the group
+      v0[rg * kRW + tg] = v1[rg * kRW + tg] = 0.f;
+      if (row < Mg) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float* p = red + (w * Mg + row) * kHad + 2 * lane;
+          v0[rg * kRW + tg] += p[0];
+          v1[rg * kRW + tg] += p[1];
+        }
       }
     }
   }
@@ -258,8 +279,8 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
     // ---- 6a. split-K hand-off: coherent partial stores, then one counter bump per block
     const int64_t OC = sh.OC;
 #pragma unroll
-    for (int t = 0; t < kRW; ++t) {
-      const int row = wave + t * kWaves;
+    for (int t = 0; t < kRT; ++t) {
+      const int row = out_row(t);
       if (row < M) {
         float* dst = sh.slab + (int64_t(s) * M + row) * OC + c0;
         __hip_atomic_store(dst, v0[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -277,8 +298,8 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
     const int old = *flag;
     if (old != sh.S - 1) return;                            // not the last split of this block
 #pragma unroll
-    for (int t = 0; t < kRW; ++t) {
-      const int row = wave + t * kWaves;
+    for (int t = 0; t < kRT; ++t) {
+      const int row = out_row(t);
       if (row < M) {
         v0[t] = v1[t] = 0.f;
         for (int sp = 0; sp < sh.S; ++sp) {
@@ -293,8 +314,8 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
 
   // ---- 6. output Hadamard-128, rout * s_out, bf16 into the slice
 #pragma unroll
-  for (int t = 0; t < kRW; ++t) {
-    const int row = wave + t * kWaves;
+  for (int t = 0; t < kRT; ++t) {
+    const int row = out_row(t);
     if (row < M) {
       float x0 = v0[t], x1 = v1[t];
       had128_wave(x0, x1, lane);
@@ -311,7 +332,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   }
 }
 
-template <int KSET, int SPW, int MR, bool SILU = false>
+template <int KSET, int SPW, int MR, bool SILU = false, int RG = 1>
 __global__ __launch_bounds__(512, 4) void decode_kernel(DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int wg = blockIdx.x;
@@ -320,12 +341,12 @@ __global__ __launch_bounds__(512, 4) void decode_kernel(DecArgs a) {
   const DecShard& sh = a.sh[i];
   const int local = wg - sh.wg_begin;
   if constexpr (KSET >= 1 && KSET <= 8) {
-    decode_block<KSET, SPW, MR, SILU>(a, sh, local, lds);
+    decode_block<KSET, SPW, MR, SILU, RG>(a, sh, local, lds);
   } else {   // KSET 0: the mixed set {2, 3, 4}
     switch (sh.K) {
-      case 2: decode_block<2, SPW, MR>(a, sh, local, lds); break;
-      case 3: decode_block<3, SPW, MR>(a, sh, local, lds); break;
-      default: decode_block<4, SPW, MR>(a, sh, local, lds); break;
+      case 2: decode_block<2, SPW, MR, false, RG>(a, sh, local, lds); break;
+      case 3: decode_block<3, SPW, MR, false, RG>(a, sh, local, lds); break;
+      default: decode_block<4, SPW, MR, false, RG>(a, sh, local, lds); break;
     }
   }
 }
@@ -349,8 +370,9 @@ size_t slot_bytes(int K) { return size_t(4) * (256 * K + 64); }
 // LDS of one block: rotated activations, then the waves' trellis staging slots; the reduction buffer
 // reuses the same space after the main loop.
 size_t lds_bytes_for(int M, int lds_row, int K) {
+  const int Mg = M < kDecodeMaxRows ? M : kDecodeMaxRows;   // the reduction runs one 16-row group at a time
   const size_t main = tr_offset(M, lds_row) + size_t(kWaves) * slot_bytes(lds_k(K));
-  const size_t red = size_t(kWaves) * M * kHad * 4;
+  const size_t red = size_t(kWaves) * Mg * kHad * 4;
   return main > red ? main : red;
 }
 
@@ -364,17 +386,19 @@ size_t lds_bytes_for(int M, int lds_row, int K) {
 constexpr int kFillBlocks = 224;
 
 int shard_splits(int64_t M, int B, int nblk, int K) {
+  // rows of one 16-row group: a launch of 17..32 rows (two groups) splits a shard exactly as 16 rows do
+  const int Mg = int(M < kDecodeMaxRows ? M : kDecodeMaxRows);
   for (int S = 1;; ++S) {
     if (S >= B) return B;
     const int nb_max = (B + S - 1) / S;
     const int spw_need = 2 * ((nb_max + kWaves - 1) / kWaves);   // whole Hadamard blocks per wave
-    const bool lds_ok = lds_bytes_for(int(M), kHad * nb_max + 8, K) <= kMaxLds;
+    const bool lds_ok = lds_bytes_for(Mg, kHad * nb_max + 8, K) <= kMaxLds;
     if (spw_need <= kMaxSpw && lds_ok && (nblk * S >= kFillBlocks || nb_max <= kWaves)) return S;
   }
 }
 
 bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl) {
-  if (M < 1 || M > 16 || n < 1 || n > kMaxShards) return false;
+  if (M < 1 || M > kDecodeLaunchRows || n < 1 || n > kMaxShards) return false;
   const int B = int(IC / kHad);
   int nb_max = 1;
   for (int i = 0; i < n; ++i) {
@@ -425,14 +449,14 @@ bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl
   return counters <= kCounterSlots;
 }
 
-template <int KSET, int MR, bool SILU = false>
+template <int KSET, int MR, bool SILU = false, int RG = 1>
 static void launch_kset_mr(const DecPlan& pl, const DecArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)pl.wg_total), block(kWaves * 64);
   const size_t lds = pl.lds_bytes;
   if (pl.spw <= 2)
-    hipLaunchKernelGGL((decode_kernel<KSET, 2, MR, SILU>), grid, block, lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<KSET, 2, MR, SILU, RG>), grid, block, lds, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<KSET, 4, MR, SILU>), grid, block, lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<KSET, 4, MR, SILU, RG>), grid, block, lds, stream, a);
 }
 
 template <int KSET>
@@ -451,7 +475,10 @@ static hipError_t launch_kset(const DecPlan& pl, const DecArgs& a, hipStream_t s
     }
   }
   // activation rows the fused pre-pass loads unconditionally: 1, 4 or 16; 0 = pre-rotated activations
-  if (pl.pre)
+  // (two 16-row groups above 16 rows)
+  if (pl.pre && a.M > kDecodeMaxRows)
+    launch_kset_mr<KSET, 0, false, 2>(pl, a, stream);
+  else if (pl.pre)
     launch_kset_mr<KSET, 0>(pl, a, stream);
   else if (a.M <= 1)
     launch_kset_mr<KSET, 1>(pl, a, stream);

@@ -303,37 +303,61 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   }
 }
 
-// K-split reduction over the launch's tiles: one wave per (32-row group, 128-column tile) sums the splits'
-// partials in split order (fixed, so the result is deterministic) and applies the output transform.
+// K-split reduction over the launch's tiles: one workgroup per (32-row group, 128-column tile).  Its four
+// waves sum contiguous quarters of the splits, in split order, with the next split's loads in flight while
+// one is added; wave 0 then adds the other waves' sums in wave order (a fixed order, so the result is
+// deterministic) and applies the output transform.
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs p) {
+  __shared__ float4v part[3][16][64];                       // waves 1..3: their sums, 48 KB
   const int lane = threadIdx.x & 63;
-  const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (unit >= int64_t(p.ntiles) * kWavesN * 4) return;
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int64_t unit = blockIdx.x;
+  if (unit >= int64_t(p.ntiles) * kWavesN * 4) return;     // uniform over the workgroup, as are the next two
   const int lt = int(unit / (kWavesN * 4)), wave = int(unit / 4) % kWavesN, mb = int(unit & 3);
   int mtile, ctile;
   tile_coords(p, p.tile0 + lt, wave, mtile, ctile);
   if (ctile * kCols >= p.OC) return;                        // past the last column block
   const int r0 = mtile * kRows + 32 * mb;
   if (r0 >= p.M) return;                                    // the whole group is past M
-  float4v sum[4][4];
+  auto first = [&](int ww) { return (ww * p.splits + 3) / 4; };
+  const int s0 = first(w), s1 = first(w + 1);
+  float4v sum[16];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sum[nb][q] = (float4v){0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < p.splits; ++sp) {
+  for (int i = 0; i < 16; ++i) sum[i] = (float4v){0.f, 0.f, 0.f, 0.f};
+  // split sp's 16 KB of partials for this group
+  auto load = [&](int sp, float4v (&dst)[16]) {
     const float4v* src = p.slab + ((int64_t(sp) * p.ntiles + lt) * kWavesN + wave) * 4096 + mb * 16 * 64 + lane;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int i = 0; i < 16; ++i) dst[i] = src[i * 64];
+  };
+  float4v buf[2][16];
+  if (s0 < s1) load(s0, buf[0]);
+  for (int sp = s0; sp < s1; sp += 2) {
+    if (sp + 1 < s1) load(sp + 1, buf[1]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sum[nb][q] += src[(nb * 4 + q) * 64];
+    for (int i = 0; i < 16; ++i) sum[i] += buf[0][i];
+    if (sp + 1 >= s1) break;
+    if (sp + 2 < s1) load(sp + 2, buf[0]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum[i] += buf[1][i];
   }
+  if (w > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[w - 1][i][lane] = sum[i];
+  }
+  __syncthreads();
+  if (w > 0) return;
+  for (int ww = 1; ww < 4; ++ww)
+    if (first(ww) < first(ww + 1))                          // a wave with no split adds nothing
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum[i] += part[ww - 1][i][lane];
   float v[4][16], sc[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[nb][4 * q + e] = sum[nb][q][e];
+      for (int e = 0; e < 4; ++e) v[nb][4 * q + e] = sum[nb * 4 + q][e];
   column_scales(p, ctile * kCols, lane & 31, sc);
   epilogue_group(p, v, sc, r0, ctile * kCols, lane);
 }
@@ -388,8 +412,8 @@ hipError_t launch_gemm(const void* xf, const int16_t* code, int K, const void* r
     }
 #undef EXL3_GEMM_CASE
     if (splits > 1) {
-      const int64_t units = int64_t(ntiles) * kWavesN * 4;
-      hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
+      const int64_t units = int64_t(ntiles) * kWavesN * 4;   // one workgroup per (32-row group, tile)
+      hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)units), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
   };

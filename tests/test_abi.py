@@ -32,8 +32,9 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_limits():
     L = exl3.lib()
     assert L.exl3_version() >= 100
-    # the measured crossover rule against the (feature-split) GEMM: 16 * clamp(16384 // OC, 2, 8)
-    for OC, rows in ((17408, 32), (14336, 32), (7168, 32), (5120, 48), (4096, 64), (256, 128), (81920, 32)):
+    # the measured crossover rule against the (feature-split) GEMM: 16 * clamp(10240 // OC, 2, 8)
+    for OC, rows in ((17408, 32), (14336, 32), (7168, 32), (5120, 32), (4096, 32), (2560, 64), (1024, 128),
+                     (256, 128), (81920, 32)):
         assert L.exl3_gemv_max_rows(OC) == rows, OC
 
 
@@ -121,15 +122,18 @@ def test_gemm_tail_split_plan():
 
 
 def test_decode_workspace_pre_rotation_region():
-    """Decode-phase launches of 5..16 rows rotate the activations once per call into the workspace
-    (fragment-major, 16 rows x IC fp16); below 5 rows each block rotates its own.  A 28672-column shard
-    over IC=2048 needs no split-K slab, so the workspace is the counter area plus that region."""
+    """Decode-phase launches of 5..32 rows rotate the activations once per call into the workspace
+    (fragment-major 16-row blocks: 16 rows x IC fp16 up to 16 rows, 32 above); below 5 rows each block
+    rotates its own.  A 28672-column shard over IC=2048 needs no split-K slab, so the workspace is the
+    counter area plus that region."""
     IC, OC = 2048, 28672
-    assert exl3.lib().exl3_gemv_max_rows(OC) >= 16
+    assert exl3.lib().exl3_gemv_max_rows(OC) >= 32
     for M in (1, 4):
         assert exl3.linear_workspace_bytes(M, IC, OC) == 16384
     for M in (5, 8, 16):
         assert exl3.linear_workspace_bytes(M, IC, OC) == 16384 + 16 * IC * 2
+    for M in (17, 32):
+        assert exl3.linear_workspace_bytes(M, IC, OC) == 16384 + 32 * IC * 2
 
 
 def test_workspace_sizes():

@@ -174,11 +174,13 @@ def test_linear_workspace_poison_counters_and_determinism():
 
 def test_linear_batch_invariance_decode_rows():
     """A row's output does not depend on the other rows of the batch (decode-phase kernel), also across
-    the switch from in-block rotation (M <= 4) to activations rotated once per call (M >= 5)."""
-    c = synth.linear_case(1006, 16, 512, 384, 2)
+    the switch from in-block rotation (M <= 4) to activations rotated once per call (M >= 5) and across
+    launches of one and of two 16-row groups (17..32 rows): M=48 runs as launches of 32 and 16 rows."""
+    c = synth.linear_case(1006, 48, 512, 384, 2)
     d = _case_to_dev(c)
+    assert exl3.lib().exl3_gemv_max_rows(384) >= 48
     full = _run_linear(c, d)
-    for M in (1, 4, 5, 9):
+    for M in (1, 4, 5, 9, 16, 17, 32, 33, 36):
         sub = dict(c, M=M)
         part = _run_linear(sub, dict(d, x=d["x"][:M].contiguous()))
         assert torch.equal(part, full[:M])
@@ -186,7 +188,7 @@ def test_linear_batch_invariance_decode_rows():
 
 # ------------------------------------------------------------------------------------------ merged shards
 
-@pytest.mark.parametrize("M", [1, 2, 4, 8])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 24])
 def test_decode_gate_up_config(M):
     """Merged gate (K=2) | up (K=3), IC=4096, 2 x 14336 columns: multi-shard call == per-shard calls
     bit for bit, and sampled 128-column blocks of both shards match the oracle."""
@@ -228,10 +230,11 @@ def test_merged_shards_with_distinct_input_vectors():
                             O.linear(case["x"], *args))
 
 
-@pytest.mark.parametrize("M", [3, 8])
+@pytest.mark.parametrize("M", [3, 8, 24, 40])
 def test_large_ic_sampled(M):
     """down_proj shape IC=17408, OC=5120, K=3 at decode M (many splits), sampled blocks; M=8 takes the
-    activations rotated once per call (a 16 x 17408 fragment-major region of the workspace)."""
+    activations rotated once per call (a 16 x 17408 fragment-major region of the workspace), M=24 one
+    launch of two 16-row groups, M=40 launches of 32 and 8 rows."""
     c = synth.linear_case(1300 + M, M, 17408, 5120, 3)
     log(f"large IC sampled M={M}")
     out = _run_linear(c, _case_to_dev(c))
