@@ -60,8 +60,19 @@ enum {
                                  Y = sc * (q . W); runs on the MFMA GEMM at every M (not with FORCE_GEMV) */
   EXL3_FORCE_GEMV = 1u << 1, /* force the decode-phase (streaming split-K) kernel whatever M is */
   EXL3_FORCE_MFMA = 1u << 2, /* force the prefill-phase (tiled MFMA GEMM) kernel whatever M is */
-  EXL3_GEMM_NO_SPLIT = 1u << 3 /* never split the GEMM's input features (exl3_gemm_splits): one fixed-order
+  EXL3_GEMM_NO_SPLIT = 1u << 3, /* never split the GEMM's input features (exl3_gemm_splits): one fixed-order
                                  reduction per output element, so a row's result does not depend on M */
+  EXL3_BATCH_INVARIANT = 1u << 4 /* a row's result depends on that row alone, at every M and across the
+                                 decode/prefill crossover ("vLLM PR #190" commit message: the fused dense
+                                 kernel's output does not change with the batch size).  The 16-bit path runs
+                                 the decode-phase kernel at every M: its reduction order per output element
+                                 (waves' feature ranges summed in wave order, then the input-feature splits
+                                 in split order) does not depend on M, since every 16-row group of a launch
+                                 is reduced alike and the split count is a function of (IC, OC, K) only.
+                                 Costs nothing up to the crossover (exl3_gemv_max_rows); above it runs at the
+                                 decode-phase kernel's rate, e.g. ~0.75 ms for a 5120 -> 7168 K=3
+                                 projection at M=128 against ~0.04 ms on the GEMM.  The 8-bit path runs the
+                                 unsplit GEMM (as EXL3_GEMM_NO_SPLIT).  Not with EXL3_FORCE_MFMA. */
 };
 
 /* Text of the last failure on the calling thread ("" if none). */

@@ -46,7 +46,10 @@ int launch_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-constexpr unsigned kKnownFlags = EXL3_ACT_INT8 | EXL3_FORCE_GEMV | EXL3_FORCE_MFMA | EXL3_GEMM_NO_SPLIT;
+constexpr unsigned kKnownFlags =
+    EXL3_ACT_INT8 | EXL3_FORCE_GEMV | EXL3_FORCE_MFMA | EXL3_GEMM_NO_SPLIT | EXL3_BATCH_INVARIANT;
+// The GEMM runs unsplit under either flag.
+constexpr unsigned kNoSplitFlags = EXL3_GEMM_NO_SPLIT | EXL3_BATCH_INVARIANT;
 // Dispatch threshold.  The decode-phase path streams every weight once per 16-row launch, so its time
 // grows with ceil(M/16) * OC; the MFMA GEMM splits the input features of a shard with few output tiles
 // so that about 1024 waves run, which keeps its time nearly flat in M up to a few hundred rows.
@@ -63,6 +66,8 @@ int check_flags(unsigned flags) {
   if (flags & ~kKnownFlags) return fail(EXL3_EINVAL, "flags: unknown bits 0x%x", flags & ~kKnownFlags);
   if ((flags & EXL3_FORCE_GEMV) && (flags & EXL3_FORCE_MFMA))
     return fail(EXL3_EINVAL, "flags: EXL3_FORCE_GEMV and EXL3_FORCE_MFMA are exclusive");
+  if ((flags & EXL3_BATCH_INVARIANT) && (flags & EXL3_FORCE_MFMA))
+    return fail(EXL3_EINVAL, "flags: EXL3_BATCH_INVARIANT selects the decode-phase kernel; EXL3_FORCE_MFMA cannot be combined with it");
   if ((flags & EXL3_ACT_INT8) && (flags & EXL3_FORCE_GEMV))
     return fail(EXL3_EUNSUPPORTED, "flags: the 8-bit path runs on the MFMA GEMM; EXL3_FORCE_GEMV cannot be combined with it");
   return EXL3_OK;
@@ -100,7 +105,7 @@ int check_shard(const char* who, int64_t IC, const int16_t* code, int64_t OC, in
 // The prefill/decode choice is made here, inside the op, by M ("radiance_escha.py", `escha_linear_into`).
 bool use_decode_path(int64_t M, unsigned flags, int64_t OC) {
   if (flags & EXL3_ACT_INT8) return false;   // the row amax needs the whole row before any product
-  if (flags & EXL3_FORCE_GEMV) return true;
+  if (flags & (EXL3_FORCE_GEMV | EXL3_BATCH_INVARIANT)) return true;
   if (flags & EXL3_FORCE_MFMA) return false;
   return M <= gemv_max_rows(OC);
 }
@@ -251,7 +256,7 @@ int run_gemm(const char* who, void* out, int64_t ldo, const void* x, int64_t M, 
       if (int rc = launch_status(e, who)) return rc;
       done = slot[i];
     }
-    const GemmSplit sp = (flags & EXL3_GEMM_NO_SPLIT) ? GemmSplit{1, int(IC / 64)} : gemm_split(M, IC, in[i].OC);
+    const GemmSplit sp = (flags & kNoSplitFlags) ? GemmSplit{1, int(IC / 64)} : gemm_split(M, IC, in[i].OC);
     hipError_t e = launch_gemm(region, in[i].code, in[i].K, in[i].rout, in[i].s_out, out, ldo, in[i].col0, M, IC,
                                in[i].OC, stream, scale, sp, reinterpret_cast<float*>(ws + L.slab_off));
     if (int rc = launch_status(e, who)) return rc;
@@ -354,7 +359,7 @@ bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsign
     *L = layout_for(slab, pre_rows(M), IC, pre ? distinct_inputs(n, in, slot) : 0, false, kDecodeMaxRows);
   } else {
     size_t slab = 0;                                      // shards run one after another: the largest split
-    if (!(flags & EXL3_GEMM_NO_SPLIT))
+    if (!(flags & kNoSplitFlags))
       for (int i = 0; i < n; ++i) {
         const size_t b = gemm_slab_bytes(M, in[i].OC, gemm_split(M, IC, in[i].OC));
         slab = b > slab ? b : slab;

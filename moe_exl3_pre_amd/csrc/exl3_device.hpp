@@ -205,6 +205,21 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {   // round to nearest 
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// A rotated activation as the MFMAs take it: the fp32 Hadamard output times 1/sqrt(128), rounded to fp32,
+// then to fp16 (nearest even).  Every rotation ends in this one sequence, so the pre-pass kernels and the
+// decode kernel's in-block rotation give the same bits.  The empty asm statement (no instruction) makes
+// the fp32 product a value the compiler cannot look through: otherwise it fuses product and conversion
+// into one mixed-precision FMA that rounds once instead of twice, in some kernels and not in others.
+__device__ __forceinline__ float rot_scale(float v) {
+  float p = v * kInvSqrt128;
+  __asm__("" : "+v"(p));
+  return p;
+}
+__device__ __forceinline__ uint16_t rot_f16(float v) { return f32_to_f16(rot_scale(v)); }
+__device__ __forceinline__ uint32_t rot_f16x2(float lo, float hi) {
+  return f32x2_to_f16x2(rot_scale(lo), rot_scale(hi));
+}
+
 // ---------------------------------------------------------------------------------------------------
 // Wave-wide orthonormal Hadamard-128: lane l holds features 2l (v0) and 2l+1 (v1) of one 128-block.
 // Radix-2 butterflies in natural (Sylvester) order; of each pair the lower feature index takes a + b,

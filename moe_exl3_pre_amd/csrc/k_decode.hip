@@ -173,8 +173,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
           float v0 = bf16_to_f32(xw & 0xFFFFu) * s0 * r0;
           float v1 = bf16_to_f32(xw >> 16) * s1 * r1;
           had128_wave_pairs8(v0, v1, lane);
-          *reinterpret_cast<uint32_t*>(xs + m * lrow + kl) =
-              uint32_t(f32_to_f16(v0 * kInvSqrt128)) | (uint32_t(f32_to_f16(v1 * kInvSqrt128)) << 16);
+          *reinterpret_cast<uint32_t*>(xs + m * lrow + kl) = rot_f16x2(v0, v1);
         }
       }
       *reinterpret_cast<uint32_t*>(xs + M * lrow + kl) = 0u;

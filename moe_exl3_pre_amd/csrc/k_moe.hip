@@ -339,8 +339,8 @@ __device__ void moe_rotate(const MoeArgs& a, int64_t unit) {
       u32x4 o0, o1;                                        // PERM16: positions (2i, 2i+1) hold features (i, i+8)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        o0[i] = f32x2_to_f16x2(v[i] * kInvSqrt128, v[i + 8] * kInvSqrt128);
-        o1[i] = f32x2_to_f16x2(v[i + 4] * kInvSqrt128, v[i + 12] * kInvSqrt128);
+        o0[i] = rot_f16x2(v[i], v[i + 8]);
+        o1[i] = rot_f16x2(v[i + 4], v[i + 12]);
       }
       dst[0] = o0;
       dst[1] = o1;
@@ -517,8 +517,7 @@ __device__ __forceinline__ void moe_w13_block(const MoeArgs& a, const int4v ch, 
     float vb = h1b / (1.0f + __expf(-h1b)) * h3b * u2b;
     had128_wave(va, vb, lane);
     uint16_t* dst = a.ah + int64_t(a.rows[row0 + r]) * a.ldh + int64_t(cb) * kHad + 2 * lane;
-    *reinterpret_cast<uint32_t*>(dst) =
-        uint32_t(f32_to_f16(va * kInvSqrt128)) | (uint32_t(f32_to_f16(vb * kInvSqrt128)) << 16);
+    *reinterpret_cast<uint32_t*>(dst) = rot_f16x2(va, vb);
   }
 }
 

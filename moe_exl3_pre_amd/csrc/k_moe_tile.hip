@@ -242,7 +242,7 @@ __device__ __forceinline__ void moe_w13_tile_block(const MoeArgs& a, const int4v
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int f = 32 * nb + c;                          // feature of the block, stored in PERM16 order
-        dst[(f & ~15) + perm16_pos(f & 15)] = f32_to_f16(v[nb][r] * kInvSqrt128);
+        dst[(f & ~15) + perm16_pos(f & 15)] = rot_f16(v[nb][r]);
       }
     }
   };

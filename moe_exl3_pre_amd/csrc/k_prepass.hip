@@ -25,8 +25,8 @@ __device__ __forceinline__ void rotate_block(const uint16_t* __restrict__ x, con
   v0 = bf16_to_f32(xb & 0xFFFFu) * f16_to_f32(sb & 0xFFFFu) * f16_to_f32(rb & 0xFFFFu);
   v1 = bf16_to_f32(xb >> 16) * f16_to_f32(sb >> 16) * f16_to_f32(rb >> 16);
   had128_wave(v0, v1, lane);
-  v0 *= kInvSqrt128;
-  v1 *= kInvSqrt128;
+  v0 = rot_scale(v0);
+  v1 = rot_scale(v1);
 }
 
 // Natural layout.  One wave per 8 rows of one 128-block: the block's s_in / rin are loaded once, every
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void prepass_f16_kernel(const uint16_t* __rest
       float v0 = bf16_to_f32(xv[r] & 0xFFFFu) * si0 * ri0;
       float v1 = bf16_to_f32(xv[r] >> 16) * si1 * ri1;
       had128_wave(v0, v1, lane);
-      packed = uint32_t(f32_to_f16(v0 * kInvSqrt128)) | (uint32_t(f32_to_f16(v1 * kInvSqrt128)) << 16);
+      packed = rot_f16x2(v0, v1);
     }
     *reinterpret_cast<uint32_t*>(xh + m * IC + k0 + 2 * lane) = packed;
   }
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void prepass_frag_f16_kernel(const uint16_t* _
       u32x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        o[j] = f32x2_to_f16x2(v[t][4 * h + j] * kInvSqrt128, v[t][4 * h + j + 8] * kInvSqrt128);
+        o[j] = rot_f16x2(v[t][4 * h + j], v[t][4 * h + j + 8]);
       *reinterpret_cast<u32x4*>(frag_addr<R32>(xf, IC, rb, q, lane, t, h)) = o;
     }
 }

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libexl3.so")
 
 OK, EINVAL, EWORKSPACE, EUNSUPPORTED, ELAUNCH = 0, -1, -2, -3, -4
-ACT_INT8, FORCE_GEMV, FORCE_MFMA, GEMM_NO_SPLIT = 1, 2, 4, 8
+ACT_INT8, FORCE_GEMV, FORCE_MFMA, GEMM_NO_SPLIT, BATCH_INVARIANT = 1, 2, 4, 8, 16
 
 _lib = None
 

@@ -68,6 +68,8 @@ def _linear(**kw):
     (dict(flags=exl3.ACT_INT8 | exl3.FORCE_GEMV), exl3.EUNSUPPORTED, "flags"),
     (dict(flags=exl3.ACT_INT8, ws=None), exl3.EWORKSPACE, "ws"),              # 8-bit path accepted
     (dict(flags=exl3.FORCE_GEMV | exl3.FORCE_MFMA), exl3.EINVAL, "flags"),
+    (dict(flags=exl3.BATCH_INVARIANT | exl3.FORCE_MFMA), exl3.EINVAL, "BATCH_INVARIANT"),
+    (dict(flags=exl3.BATCH_INVARIANT | exl3.ACT_INT8, ws=None), exl3.EWORKSPACE, "ws"),  # accepted
     (dict(ws=None), exl3.EWORKSPACE, "ws"),
     (dict(ws=FAKE, ws_bytes=1024), exl3.EWORKSPACE, "ws_bytes"),
     (dict(ws=FAKE + 16, ws_bytes=1 << 30), exl3.EINVAL, "ws"),

@@ -5,8 +5,8 @@ import torch
 
 from oracle import exl3_oracle as O
 from moe_exl3_pre_amd import exl3, synth
-from tests.helpers import (assert_close_linear, bf16_to_f64, dev, log, oracle_block_columns, rel_fro, shard_to_dev,
-                           to_dev, to_dev_x)
+from tests.helpers import (assert_close_linear, bf16_to_f64, dev, gpu_int8_codes, log, oracle_block_columns,
+                           oracle_int8_block_columns, rel_fro, shard_to_dev, to_dev, to_dev_x)
 
 pytestmark = pytest.mark.gpu
 
@@ -184,6 +184,39 @@ def test_linear_batch_invariance_decode_rows():
         sub = dict(c, M=M)
         part = _run_linear(sub, dict(d, x=d["x"][:M].contiguous()))
         assert torch.equal(part, full[:M])
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_batch_invariant_flag_across_the_crossover(int8):
+    """EXL3_BATCH_INVARIANT: at M in {1, 8, 16, 17, 32, 33, 48, 64, 300} a row's bits equal the bits of that
+    row computed alone (M=1), although the default dispatch for this 5120-column shard switches to the
+    GEMM above 32 rows (and its split count changes with M).  The 16-bit path runs the decode-phase
+    kernel (launches of 32 rows and a remainder); the 8-bit path the unsplit GEMM.  The M=300 output
+    meets the oracle on sampled column blocks (the 8-bit path on the kernel's own codes)."""
+    IC, OC, K, MMAX = 512, 5120, 3, 300
+    c = synth.linear_case(1011, MMAX, IC, OC, K)
+    d = _case_to_dev(c)
+    assert exl3.lib().exl3_gemv_max_rows(OC) == 32
+    flags = exl3.BATCH_INVARIANT | (exl3.ACT_INT8 if int8 else 0)
+    full = _run_linear(c, d, flags=flags)
+    for r in list(range(0, MMAX, 13)) + [MMAX - 1]:
+        one = _run_linear(dict(c, M=1), dict(d, x=d["x"][r:r + 1].contiguous()), flags=flags)
+        assert torch.equal(one[0], full[r]), r
+    for M in (1, 8, 16, 17, 32, 33, 48, 64):
+        part = _run_linear(dict(c, M=M), dict(d, x=d["x"][:M].contiguous()), flags=flags)
+        assert torch.equal(part, full[:M]), M
+    blocks = [0, OC // 128 - 1, 17]
+    got = bf16_to_f64(full)
+    if int8:
+        q, sc = gpu_int8_codes(d["x"], d["s_in"], d["rin"], c["x"], c["s_in"], c["rin"])
+        cols, y8 = oracle_int8_block_columns(q, sc, c["code"], K, c["rout"], c["s_out"], blocks)
+        _, y64 = oracle_block_columns(c["x"], c["code"], K, c["s_in"], c["rin"], c["rout"], c["s_out"], blocks)
+        assert_close_linear(got[:, cols], y8, y64, tol=3e-2)
+    else:
+        args = (c["x"], c["code"], K, c["s_in"], c["rin"], c["rout"], c["s_out"], blocks)
+        cols, y64 = oracle_block_columns(*args)
+        _, y16 = oracle_block_columns(*args, act="f16")
+        assert_close_linear(got[:, cols], y16, y64)
 
 
 # ------------------------------------------------------------------------------------------ merged shards

@@ -131,6 +131,25 @@ def test_mlp_equals_the_three_calls(M):
     assert torch.equal(out, ref)
 
 
+def test_mlp_batch_invariant_flag():
+    """EXL3_BATCH_INVARIANT through the block: a row of an M=70 call equals that row run alone, for a
+    block whose default dispatch switches gate_up to the GEMM above 32 rows (I = 5120)."""
+    M = 70
+    c = synth.mlp_case(97, M, 256, 5120, 2, 3, 3)
+    x, g, u, d = _to_dev_case(c)
+    assert exl3.lib().exl3_gemv_max_rows(5120) == 32
+    f = exl3.BATCH_INVARIANT
+    full = exl3.mlp_forward(x, g, u, d, flags=f)
+    for r in (0, 1, 31, 32, 33, 69):
+        one = exl3.mlp_forward(x[r:r + 1].contiguous(), g, u, d, flags=f)
+        torch.cuda.synchronize()
+        assert torch.equal(one[0], full[r]), r
+    for m in (4, 5, 40):
+        part = exl3.mlp_forward(x[:m].contiguous(), g, u, d, flags=f)
+        torch.cuda.synchronize()
+        assert torch.equal(part, full[:m]), m
+
+
 def test_mlp_rejects_mismatched_shapes():
     c = synth.mlp_case(95, 2, 512, 1024, 2, 3, 3)
     x, g, u, d = _to_dev_case(c)
