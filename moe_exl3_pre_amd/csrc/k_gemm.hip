@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   // the one before) and the read of the next step's words for that column; then park and load.  The
   // scheduling groups interleave one MFMA with kValuPerMfma VALU instructions, so the decode of the next
   // columns fills the MFMA issue gaps instead of running in bursts with the matrix core idle.
-  constexpr int kValuPerMfma = K <= 1 ? 2 : K == 2 ? 3 : K <= 4 ? 5 : 8;
+  constexpr int kValuPerMfma = K <= 1 ? 2 : K == 2 ? 3 : K == 3 ? 4 : K == 4 ? 5 : 8;
   auto step = [&](int st, const half8 (&a)[4][2][2]) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
