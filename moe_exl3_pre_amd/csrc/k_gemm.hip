@@ -303,7 +303,45 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   }
 }
 
-// K-split reduction over the launch's tiles: one workgroup per (32-row group, 128-column tile).  Its four
+// K-split reduction for a few splits (at most kFewSplits): one wave per (32-row group, 128-column tile),
+// four units per workgroup, sums the splits' partials in split order (fixed, so the result is
+// deterministic) and applies the output transform.
+constexpr int kFewSplits = 3;
+
+__global__ __launch_bounds__(256) void gemm_reduce_wave_kernel(GemmArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (unit >= int64_t(p.ntiles) * kWavesN * 4) return;
+  const int lt = int(unit / (kWavesN * 4)), wave = int(unit / 4) % kWavesN, mb = int(unit & 3);
+  int mtile, ctile;
+  tile_coords(p, p.tile0 + lt, wave, mtile, ctile);
+  if (ctile * kCols >= p.OC) return;                        // past the last column block
+  const int r0 = mtile * kRows + 32 * mb;
+  if (r0 >= p.M) return;                                    // the whole group is past M
+  float4v sum[4][4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sum[nb][q] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < p.splits; ++sp) {
+    const float4v* src = p.slab + ((int64_t(sp) * p.ntiles + lt) * kWavesN + wave) * 4096 + mb * 16 * 64 + lane;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sum[nb][q] += src[(nb * 4 + q) * 64];
+  }
+  float v[4][16], sc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[nb][4 * q + e] = sum[nb][q][e];
+  column_scales(p, ctile * kCols, lane & 31, sc);
+  epilogue_group(p, v, sc, r0, ctile * kCols, lane);
+}
+
+// K-split reduction for more than kFewSplits splits: one workgroup per (32-row group, 128-column tile).  Its four
 // waves sum contiguous quarters of the splits, in split order, with the next split's loads in flight while
 // one is added; wave 0 then adds the other waves' sums in wave order (a fixed order, so the result is
 // deterministic) and applies the output transform.
@@ -412,8 +450,11 @@ hipError_t launch_gemm(const void* xf, const int16_t* code, int K, const void* r
     }
 #undef EXL3_GEMM_CASE
     if (splits > 1) {
-      const int64_t units = int64_t(ntiles) * kWavesN * 4;   // one workgroup per (32-row group, tile)
-      hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)units), dim3(256), 0, stream, a);
+      const int64_t units = int64_t(ntiles) * kWavesN * 4;   // (32-row group, tile) units
+      if (splits <= kFewSplits)                               // a wave per unit
+        hipLaunchKernelGGL(gemm_reduce_wave_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
+      else                                                    // a workgroup per unit
+        hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)units), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
   };
