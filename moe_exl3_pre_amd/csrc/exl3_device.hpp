@@ -168,6 +168,14 @@ struct Slot {
   static constexpr int kBytes = 4 * kRowBytes;
 };
 
+// The kernels hand data between the lanes of one wave through LDS without a barrier: staged trellis
+// words, rotated activations.  The hardware executes one wave's LDS operations in order, so a lane's
+// read after the other lanes' writes sees them; but the compiler sees each lane as a thread of its own,
+// for which another lane's store does not exist, so it may reuse a value it loaded earlier from an
+// address this lane did not store to, or move this lane's store across loads of the other lanes' data.
+// This compiler fence (no instruction) between every write phase and read phase forbids both.
+__device__ __forceinline__ void lane_exchange_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
 __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4 v = {a, b, c, d};
   return __builtin_bit_cast(half8, v);

@@ -184,7 +184,8 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   // tile column (column n of tile row g), decodes them into MFMA B operands and accumulates.  Only
   // this wave touches its slot and its slice of xs, so no barrier is needed; LDS operations of one wave
   // complete in order, so the reads of a step see that step's writes and the next step's writes do
-  // not overtake this step's reads.
+  // not overtake this step's reads (lane_exchange_fence keeps the compiler to that order).
+  lane_exchange_fence();                                    // the rotated activations above are written
   char* slot = lds + a.tr_off + wave * Slot<K>::kBytes;
   char* my_row = slot + g * Slot<K>::kRowBytes;
   int woff[G::kNW], shift;
@@ -199,9 +200,11 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
 #pragma unroll
   for (int st = 0; st < SPW; ++st) {
     if (st < cnt) {
+      lane_exchange_fence();                                // the previous step's reads come first
 #pragma unroll
       for (int i = 0; i < K; ++i)
         *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tb[st % kD][i];
+      lane_exchange_fence();                                // this step's reads see these words
     }
     half8 a0[RG], a1[RG];
     if constexpr (kPre) {

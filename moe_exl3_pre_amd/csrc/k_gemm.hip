@@ -219,8 +219,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   // start, and every global load has two steps of MFMAs to arrive in.
   u32x4 tn[K];
   auto park = [&]() {
+    lane_exchange_fence();                                  // earlier reads of the slot come first
 #pragma unroll
     for (int i = 0; i < K; ++i) *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tn[i];
+    lane_exchange_fence();                                  // later reads see these words
   };
   uint32_t wv[4][2][G::kNW];
   // One step: per decoded tile column 8 MFMAs (the 4 row groups, half 0 then half 1, so no MFMA waits on

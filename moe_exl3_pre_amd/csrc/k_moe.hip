@@ -424,8 +424,10 @@ __device__ __forceinline__ void moe_accumulate(const uint16_t* code, uint32_t co
       load_a(st0 + st + 1, A[(p + 1) & 1]);
       const bool live = st < nst;
       if (live) {
+        lane_exchange_fence();                              // the previous step's reads come first
 #pragma unroll
         for (int i = 0; i < K; ++i) *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tb[p % PD][i];
+        lane_exchange_fence();                              // this step's reads see these words
       }
       load_step(st0 + st + PD, tb[p % PD]);
       if (live) {

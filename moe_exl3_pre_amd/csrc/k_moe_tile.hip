@@ -73,8 +73,10 @@ __device__ __forceinline__ void moe_tile_gemm(const uint16_t* code, uint32_t cod
   const CodebookRegs cbk = codebook_regs();
   u32x4 tn[K];
   auto park = [&]() {
+    lane_exchange_fence();                                  // earlier reads of the slot come first
 #pragma unroll
     for (int i = 0; i < K; ++i) *reinterpret_cast<u32x4*>(my_row + (i * 16 + n) * 16) = tn[i];
+    lane_exchange_fence();                                  // later reads see these words
   };
   // The slot holds the words of the step being decoded; each lane reads one tile column ahead (two waves
   // share a SIMD, so one column of decode covers the LDS latency).  At the end of step st the words of
