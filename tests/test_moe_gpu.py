@@ -47,6 +47,7 @@ def _check(m, out, tokens=None, experts=None):
     dict(T=64, E=16, topk=4, H=256, I=256, Ks=(2, 3, 4)),                        # one mixed-K launch
     dict(T=48, E=12, topk=3, H=256, I=384, Ks=(2, 3, 4), k_d_independent=True),  # k_gu != k_d
     dict(T=40, E=8, topk=2, H=384, I=128, Ks=(1, 5)),                            # one launch per K; odd H blocks
+    dict(T=56, E=12, topk=3, H=256, I=256, Ks=(6, 7, 8), k_d_independent=True),  # the widest codes, per-K launches
     dict(T=1, E=8, topk=8, H=256, I=128, Ks=(2, 3, 4)),                          # one token, every expert
 ])
 @pytest.mark.parametrize("plan", list(PLANS))
@@ -54,6 +55,9 @@ def test_moe_small_full_parity(cfg, plan):
     cfg = dict(cfg)
     log(f"moe parity {cfg} {plan}")
     m = synth.moe_case(700 + cfg["T"], **cfg)
+    # every K of the case is present in both projections, so each per-K kernel runs
+    for key in ("k_gu", "k_d"):
+        assert {e[key] for e in m["experts"]} == set(cfg["Ks"])
     bank, x, ids, w = _setup(m)
     _check(m, _run(bank, x, ids, w, flags=PLANS[plan]))
 
