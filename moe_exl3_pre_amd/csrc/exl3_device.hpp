@@ -86,19 +86,30 @@ __device__ __forceinline__ uint32_t window16(const uint32_t (&r)[Geom<K>::kNR]) 
   }
 }
 
+// A 32-bit constant in a scalar register that the compiler cannot see through.  The asm writes only
+// a scalar register: vector outputs of inline asm are avoided, because the compiler inserts no wait
+// states around inline asm for the matrix cores, and a vector register it picks for an asm output could
+// be one that an MFMA still in flight reads or writes.
+template <uint32_t V>
+__device__ __forceinline__ uint32_t opaque_sgpr() {
+  uint32_t x;
+  asm("s_mov_b32 %0, %1" : "=s"(x) : "n"(V));
+  return x;
+}
+
 // Constants of the codebook held in registers.  gfx9 VOP3 encodings cannot carry literals, so with
 // literal operands the compiler splits the mask-and-or into two instructions; opaque register values
-// let it select a single v_and_or_b32.
+// let it select a single v_and_or_b32.  That instruction reads at most one scalar register, so the bias
+// must be in a vector register: or-ing in the thread index masked by an opaque zero makes it a per-lane
+// value, which the compiler builds (once per kernel) in one of its own choosing.
 struct CodebookRegs {
   uint32_t mask;   // 0x8F808F80 (scalar register)
   uint32_t bias;   // 0x30003000 (vector register)
 };
 
 __device__ __forceinline__ CodebookRegs codebook_regs() {
-  CodebookRegs c;
-  asm("s_mov_b32 %0, 0x8f808f80" : "=s"(c.mask));
-  asm("v_mov_b32 %0, 0x30003000" : "=v"(c.bias));
-  return c;
+  const uint32_t bias = opaque_sgpr<0x30003000u>() | (__builtin_amdgcn_workitem_id_x() & opaque_sgpr<0u>());
+  return CodebookRegs{opaque_sgpr<0x8F808F80u>(), bias};
 }
 
 // State -> fp16 bit pattern for two states at once:  ((s * 0x9E37) mod 2^16) & 0x8F80 | 0x3000.
@@ -112,20 +123,37 @@ __device__ __forceinline__ uint32_t codebook2(uint32_t states, const CodebookReg
 // kernel already fills the register file (the prefill GEMM at K >= 4) the 32-bit form is kept, because the
 // aligned register pairs the 64-bit shift needs would spill.
 template <int K, int P, bool PAIR64>
-__device__ __forceinline__ uint32_t decode_pair(const uint32_t (&r)[Geom<K>::kNR], const CodebookRegs& c) {
-  // States p and p+8 start 8K bits (K bytes) apart.  When both fit one 64-bit window of the realigned
-  // stream, a single 64-bit shift brings state p to bit 0 and one byte permute picks bytes (0, 1) and
-  // (K, K+1) of the shifted pair; otherwise each state gets its own 32-bit window.
+__device__ __forceinline__ constexpr bool pair_fits64() {
   constexpr int kA = P * K, kJ = kA >> 5, kSh = kA & 31;
-  constexpr bool kFits64 = PAIR64 && kJ + 1 < Geom<K>::kNR && kSh + 8 * K + 16 <= 64;
+  return PAIR64 && K != 2 && kJ + 1 < Geom<K>::kNR && kSh + 8 * K + 16 <= 64;
+}
+
+// q >> D in one v_lshrrev_b64 (full rate on gfx950).  The amount comes from an opaque scalar register:
+// with a literal amount the compiler splits the shift into two 32-bit funnel shifts when only some bytes
+// of the result are used.
+template <int D>
+__device__ __forceinline__ uint64_t shr64(uint64_t q) {
+  if constexpr (D == 0) return q;
+  else return q >> opaque_sgpr<uint32_t(D)>();
+}
+
+// Pair P of a tile column: rows (P, P+8).  States p and p+8 start 8K bits (K bytes) apart.  When both fit
+// one 64-bit window of the realigned stream, the window q is shifted so that state p sits at bit 0 and one
+// byte permute picks bytes (0, 1) and (K, K+1); consecutive pairs of the same window continue from the
+// previous pair's shifted q (a shift by K), so every pair costs one shift.  Otherwise each state gets its
+// own 32-bit window.
+template <int K, int P, bool PAIR64>
+__device__ __forceinline__ uint32_t decode_pair(const uint32_t (&r)[Geom<K>::kNR], uint64_t& q, const CodebookRegs& c) {
+  constexpr int kA = P * K, kJ = kA >> 5, kSh = kA & 31;
   if constexpr (K == 2) {
     // state p at bit 2p, state p+8 at bit 2p+16: one 32-bit window holds both.
     return codebook2(P == 0 ? r[0] : __builtin_amdgcn_alignbit(r[1], r[0], 2 * P), c);
-  } else if constexpr (kFits64) {
-    uint64_t q = (uint64_t(r[kJ + 1]) << 32) | r[kJ];
-    // One v_lshrrev_b64 (full rate on gfx950).  Written out because the compiler otherwise splits the
-    // shift into two 32-bit funnel shifts when only some bytes of the result are used.
-    if constexpr (kSh != 0) asm("v_lshrrev_b64 %0, %2, %1" : "=v"(q) : "v"(q), "n"(kSh));
+  } else if constexpr (pair_fits64<K, P, PAIR64>()) {
+    constexpr int kAp = (P - 1) * K;
+    if constexpr (P > 0 && pair_fits64<K, P - 1, PAIR64>() && (kAp >> 5) == kJ)
+      q = shr64<kSh - (kAp & 31)>(q);
+    else
+      q = shr64<kSh>((uint64_t(r[kJ + 1]) << 32) | r[kJ]);
     constexpr uint32_t kSel = 0x0100u | (uint32_t(K) << 16) | (uint32_t(K + 1) << 24);
     return codebook2(__builtin_amdgcn_perm(uint32_t(q >> 32), uint32_t(q), kSel), c);
   } else {
@@ -147,14 +175,15 @@ __device__ __forceinline__ void decode_column(const uint32_t (&w)[Geom<K>::kNW],
 #pragma unroll
     for (int j = 0; j < Geom<K>::kNR; ++j) r[j] = w[j];
   }
-  out[0] = decode_pair<K, 0, PAIR64>(r, c);
-  out[1] = decode_pair<K, 1, PAIR64>(r, c);
-  out[2] = decode_pair<K, 2, PAIR64>(r, c);
-  out[3] = decode_pair<K, 3, PAIR64>(r, c);
-  out[4] = decode_pair<K, 4, PAIR64>(r, c);
-  out[5] = decode_pair<K, 5, PAIR64>(r, c);
-  out[6] = decode_pair<K, 6, PAIR64>(r, c);
-  out[7] = decode_pair<K, 7, PAIR64>(r, c);
+  uint64_t q = 0;   // the current 64-bit window, carried from pair to pair
+  out[0] = decode_pair<K, 0, PAIR64>(r, q, c);
+  out[1] = decode_pair<K, 1, PAIR64>(r, q, c);
+  out[2] = decode_pair<K, 2, PAIR64>(r, q, c);
+  out[3] = decode_pair<K, 3, PAIR64>(r, q, c);
+  out[4] = decode_pair<K, 4, PAIR64>(r, q, c);
+  out[5] = decode_pair<K, 5, PAIR64>(r, q, c);
+  out[6] = decode_pair<K, 6, PAIR64>(r, q, c);
+  out[7] = decode_pair<K, 7, PAIR64>(r, q, c);
 }
 
 // Staging of trellis words.  The words of one 64-feature step of a 128-column block are 4 tile rows x
