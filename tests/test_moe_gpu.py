@@ -1,5 +1,7 @@
 """GPU parity of the MoE expert-bank forward against the fp64 oracle's dense per-expert loop, through
 the C ABI."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -113,6 +115,36 @@ def test_moe_out_of_range_ids_are_ignored(plan):
         w0[t, j] = 0.0
     out0 = _run(bank, x, to_dev(ids0.astype(np.int32)), to_dev(w0.astype(np.float32)), flags=f)
     assert torch.equal(out_bad, out0)
+
+
+@pytest.mark.parametrize("plan", list(PLANS))
+def test_moe_every_id_dropped_gives_zeros(plan):
+    """No pair reaches an expert (ids negative or >= E): the route yields no chunk, the expert launches find
+    no work, and every output element is an exact zero, as in the oracle's per-expert loop."""
+    m = synth.moe_case(716, T=24, E=8, topk=3, H=256, I=128)
+    ids = np.full_like(m["topk_ids"], -1)
+    ids[::2, 1] = m["E"]
+    ids[1::3, 2] = 1 << 20
+    m_bad = dict(m, topk_ids=ids)
+    log(f"moe all ids dropped {plan}")
+    bank, x, dids, w = _setup(m_bad)
+    out = _run(bank, x, dids, w, flags=PLANS[plan])
+    assert torch.equal(out, torch.zeros_like(out))
+    assert not np.any(O.moe_forward(m_bad["x"], ids, m_bad["topk_w"], m_bad["experts"]))
+
+
+def test_moe_zero_tokens_is_a_no_op():
+    """T = 0 through the C ABI returns OK and leaves the output buffer untouched."""
+    m = synth.moe_case(717, T=4, E=8, topk=2, H=256, I=128)
+    bank, x, ids, w = _setup(m)
+    out = torch.full(x.shape, -1000.0, dtype=torch.bfloat16, device=dev())
+    ws = exl3.alloc_workspace(exl3.moe_workspace_bytes(bank, 4, 2), dev())
+    rc = exl3.lib().exl3_moe_bank_forward(exl3._ptr(out), exl3._ptr(x), 0, exl3._ptr(ids), exl3._ptr(w), 2,
+                                           ctypes.byref(bank.struct), 0, exl3._ptr(ws), ws.numel(),
+                                           exl3._stream(dev()))
+    torch.cuda.synchronize()
+    assert rc == exl3.OK
+    assert torch.equal(out, torch.full_like(out, -1000.0))
 
 
 @pytest.mark.parametrize("plan", list(PLANS))
