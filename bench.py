@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--no-mlp", action="store_true", help="skip the dense MLP block measurement")
     ap.add_argument("--no-embed", action="store_true", help="skip the int8 embedding gather and output-head measurements")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured streaming-read and MFMA peaks")
+    ap.add_argument("--no-int8-decode", action="store_true",
+                    help="skip the 8-bit activation path at decode sizes (gate_up at M = 1 and 8)")
     ap.add_argument("--sweep", action="store_true",
                     help="the M sweep over a 64-layer projection set on both paths (prints its own report)")
     ap.add_argument("--sweep-ms", default="1,4,8,16,24,32,48,64,128,512,8192")
@@ -176,10 +178,11 @@ def stats_us(t):
             "calls_per_replay": t.get("calls_per_replay", 1)}
 
 
-def time_decode(torch, exl3, dev, x, out, sets, steps, warmup):
+def time_decode(torch, exl3, dev, x, out, sets, steps, warmup, flags=0):
     M, IC = x.shape
-    ws = exl3.alloc_workspace(max(exl3.linear_multi_workspace_bytes(M, IC, s) for s in sets), dev)
-    return graph_time(torch, lambda i: exl3.linear_multi_into(out, x, sets[i % len(sets)], ws=ws), steps, warmup)
+    ws = exl3.alloc_workspace(max(exl3.linear_multi_workspace_bytes(M, IC, s, flags) for s in sets), dev)
+    return graph_time(torch, lambda i: exl3.linear_multi_into(out, x, sets[i % len(sets)], flags=flags, ws=ws),
+                      steps, warmup)
 
 
 def time_mlp(torch, exl3, synth, dev, copies=8, steps=64):
@@ -668,6 +671,16 @@ def main():
         print(f"# decode gate_up M={M}: {t['mean'] * 1e6:.2f} us/step (median {t['median'] * 1e6:.2f}, p10 "
               f"{t['p10'] * 1e6:.2f}, p90 {t['p90'] * 1e6:.2f}), {trellis_bytes / t['mean'] / 1e9:.1f} GB/s trellis",
               file=sys.stderr, flush=True)
+    # the 8-bit activation path at decode sizes: the pre-pass (row maxima, scales, codes) plus the decode kernel
+    results_i8 = {}
+    for M in () if a.no_int8_decode else (1, 8):
+        _, xb = synth.random_activations(rng, M, IC)
+        x = torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        out = torch.empty((M, ldo), dtype=torch.bfloat16, device=dev)
+        t = time_decode(torch, exl3, dev, x, out, sets, max(a.steps // 4, 2 * COPIES), COPIES, flags=exl3.ACT_INT8)
+        results_i8[M] = t
+        print(f"# decode gate_up 8-bit M={M}: {t['mean'] * 1e6:.2f} us/step (median {t['median'] * 1e6:.2f})",
+              file=sys.stderr, flush=True)
 
     peaks = None if a.no_peaks else measured_peaks(torch, exl3, dev)
     prefill = {} if a.no_prefill else time_prefill(torch, exl3, synth, dev)
@@ -704,6 +717,10 @@ def main():
         line["extra"][f"decode_M{M}"] = dict(stats_us(t), us_per_step=round(t["mean"] * 1e6, 3), trellis_GBps=round(g, 1),
                                              frac_hbm=round(g / HBM_PEAK_GBS, 4),
                                              frac_of_measured_read=vs_measured(g, "hbm_read_GBps"))
+    for M, t in results_i8.items():
+        g = trellis_bytes / t["mean"] / 1e9
+        line["extra"][f"decode_int8_M{M}"] = dict(stats_us(t), us_per_step=round(t["mean"] * 1e6, 3),
+                                                  trellis_GBps=round(g, 1), frac_hbm=round(g / HBM_PEAK_GBS, 4))
     for name, (t, flop) in prefill.items():
         tf = flop / t["median"] / 1e12
         e = dict(stats_us(t), ms_per_call=round(t["median"] * 1e3, 4), TFLOPs=round(tf, 1),

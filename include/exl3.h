@@ -57,7 +57,8 @@ typedef enum {
 /* flags */
 enum {
   EXL3_ACT_INT8 = 1u << 0,   /* per-row 8-bit activations: sc = max|xh| / 127, q = clamp(rne(xh / sc), +-127),
-                                 Y = sc * (q . W); runs on the MFMA GEMM at every M (not with FORCE_GEMV) */
+                                 Y = sc * (q . W); dispatched by M like the 16-bit path (the codes and scales
+                                 are written by a pre-pass in either phase) */
   EXL3_FORCE_GEMV = 1u << 1, /* force the decode-phase (streaming split-K) kernel whatever M is */
   EXL3_FORCE_MFMA = 1u << 2, /* force the prefill-phase (tiled MFMA GEMM) kernel whatever M is */
   EXL3_GEMM_NO_SPLIT = 1u << 3, /* never split the GEMM's input features (exl3_gemm_splits): one fixed-order
@@ -123,11 +124,13 @@ int exl3_gemm_tail_splits(int64_t M, int64_t IC, int64_t OC);
  * EXL3_GEMM_NO_SPLIT it does not depend on M at all.  Decode-phase launches of 5..32 rows rotate the
  * activations once per call into the workspace (16 or 32 rows x IC fp16 per distinct (s_in, rin)) before
  * the decode kernel; smaller ones rotate inside the kernel.  Both rotations give the same bits.
- * 8-bit path (EXL3_ACT_INT8): the codes q are exact in fp16 and every q * W product is exact in fp32,
- * so the contraction is the integer dot product up to fp32 summation; the row scale is applied before
- * the output transform.
- * Returns EXL3_OK, EXL3_EINVAL, EXL3_EWORKSPACE, EXL3_EUNSUPPORTED (EXL3_ACT_INT8 with EXL3_FORCE_GEMV),
- * EXL3_ELAUNCH.
+ * 8-bit path (EXL3_ACT_INT8): a pre-pass (three launches: row maxima, row scales, codes) writes the codes q
+ * as fp16 numbers, exact, in the operand layout of the phase that runs, so the decode-phase kernel serves
+ * small M here too; every q * W product is exact in fp32, so the contraction is the integer dot product up
+ * to fp32 summation; in both phases the row scale multiplies the result after the output Hadamard and
+ * before rout * s_out.  The decode-phase path needs 16 or 32 rows x IC fp16 of codes, the row scales and
+ * the row maxima (rows x IC/128 fp32) in the workspace per distinct (s_in, rin).
+ * Returns EXL3_OK, EXL3_EINVAL, EXL3_EWORKSPACE, EXL3_EUNSUPPORTED, EXL3_ELAUNCH.
  * ------------------------------------------------------------------------------------------------ */
 size_t exl3_linear_workspace_bytes(int64_t M, int64_t IC, int64_t OC, unsigned flags);
 

@@ -68,8 +68,6 @@ int check_flags(unsigned flags) {
     return fail(EXL3_EINVAL, "flags: EXL3_FORCE_GEMV and EXL3_FORCE_MFMA are exclusive");
   if ((flags & EXL3_BATCH_INVARIANT) && (flags & EXL3_FORCE_MFMA))
     return fail(EXL3_EINVAL, "flags: EXL3_BATCH_INVARIANT selects the decode-phase kernel; EXL3_FORCE_MFMA cannot be combined with it");
-  if ((flags & EXL3_ACT_INT8) && (flags & EXL3_FORCE_GEMV))
-    return fail(EXL3_EUNSUPPORTED, "flags: the 8-bit path runs on the MFMA GEMM; EXL3_FORCE_GEMV cannot be combined with it");
   return EXL3_OK;
 }
 
@@ -102,9 +100,11 @@ int check_shard(const char* who, int64_t IC, const int16_t* code, int64_t OC, in
   return EXL3_OK;
 }
 
-// The prefill/decode choice is made here, inside the op, by M ("radiance_escha.py", `escha_linear_into`).
+// The prefill/decode choice is made here, inside the op, by M ("radiance_escha.py", `escha_linear_into`: the
+// 8-bit staging buffers serve either phase).  With EXL3_BATCH_INVARIANT the 8-bit path keeps the unsplit GEMM,
+// whose order per output does not depend on M.
 bool use_decode_path(int64_t M, unsigned flags, int64_t OC) {
-  if (flags & EXL3_ACT_INT8) return false;   // the row amax needs the whole row before any product
+  if ((flags & EXL3_ACT_INT8) && (flags & EXL3_BATCH_INVARIANT)) return false;
   if (flags & (EXL3_FORCE_GEMV | EXL3_BATCH_INVARIANT)) return true;
   if (flags & EXL3_FORCE_MFMA) return false;
   return M <= gemv_max_rows(OC);
@@ -118,15 +118,15 @@ int64_t pre_rows(int64_t M) { return (first_chunk(M) + kDecodeMaxRows - 1) / kDe
 
 // Slab bytes the decode-phase path needs for these shards (mixes the kernels do not cover run one
 // launch per shard); false if some chunk cannot be planned.
-bool decode_slab_bytes(int64_t M, int64_t IC, int n, const DecShardIn* in, size_t* need) {
+bool decode_slab_bytes(int64_t M, int64_t IC, int n, const DecShardIn* in, size_t* need, bool pre) {
   *need = 0;
   for (int64_t rows : {first_chunk(M), last_chunk(M)}) {
     DecPlan pl;
-    if (!plan_decode(rows, IC, n, in, &pl)) return false;
+    if (!plan_decode(rows, IC, n, in, &pl, pre)) return false;
     if (pl.kset < 0) {
       for (int i = 0; i < n; ++i) {
         DecPlan p1;
-        if (!plan_decode(rows, IC, 1, in + i, &p1)) return false;
+        if (!plan_decode(rows, IC, 1, in + i, &p1, pre)) return false;
         *need = p1.slab_bytes > *need ? p1.slab_bytes : *need;
       }
     } else {
@@ -184,8 +184,13 @@ int check_workspace(const Layout& L, void* ws, size_t ws_bytes) {
 // as two 16-row groups in one launch, so the weights are streamed once per 32 rows).
 // gu (optional): the dense MLP block's gate_up output [M, 2 IC]; the pre-rotation (5..32 rows) or the decode
 // kernel's in-block pre-pass (1..4 rows) then forms the input h = bf16(silu(g) * u) itself.
+// int8: the 8-bit path.  Every chunk, of any size, first writes its integer codes (as fp16 numbers) and row
+// scales with the fragment-major 8-bit pre-pass; the decode launch multiplies the codes and applies each
+// row's scale after its output Hadamard, as the GEMM's epilogue does.
 int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n,
-               const DecShardIn* in_, char* ws, const Layout& L, hipStream_t stream, const void* gu = nullptr) {
+               const DecShardIn* in_, char* ws, const Layout& L, hipStream_t stream, const void* gu = nullptr,
+               bool int8 = false) {
+  if (int8 && gu) return fail(EXL3_EUNSUPPORTED, "%s: the folded activation is for the 16-bit path", who);
   DecShardIn in[kMaxShards];
   for (int i = 0; i < n; ++i) in[i] = in_[i];
   int slot[kMaxShards];
@@ -195,22 +200,28 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
     const void* xr = static_cast<const uint16_t*>(x) + r0 * IC;
     void* orow = static_cast<uint16_t*>(out) + r0 * ldo;
     DecPlan pl;
-    if (!plan_decode(rows, IC, n, in, &pl)) return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
+    if (!plan_decode(rows, IC, n, in, &pl, int8)) return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
     if (pl.pre) {
       int done = -1;
       for (int i = 0; i < n; ++i) {
         char* region = ws + L.xh_off + L.xh_bytes * size_t(slot[i]);
+        float* scale = int8 ? reinterpret_cast<float*>(region + L.scale_off) : nullptr;
         if (slot[i] > done) {
-          if (L.xh_bytes < size_t((rows + kDecodeMaxRows - 1) / kDecodeMaxRows * kDecodeMaxRows) * size_t(IC) * 2)
+          const size_t codes = size_t((rows + kDecodeMaxRows - 1) / kDecodeMaxRows * kDecodeMaxRows) * size_t(IC) * 2;
+          if (L.xh_bytes < codes || (int8 && (L.scale_off < codes || L.part_off < L.scale_off + size_t(rows) * 4 ||
+                                              L.xh_bytes < L.part_off + size_t(rows) * size_t(IC / 128) * 4)))
             return fail(EXL3_EWORKSPACE, "%s: workspace has no pre-rotation region", who);
           hipError_t e =
-              gu ? launch_prepass_silu_f16(static_cast<const uint16_t*>(gu) + r0 * 2 * IC, in[i].s_in, in[i].rin,
-                                           region, rows, IC, stream)
-                 : launch_prepass_f16(xr, in[i].s_in, in[i].rin, region, rows, IC, true, stream, kDecodeMaxRows);
+              int8 ? launch_prepass_i8(xr, in[i].s_in, in[i].rin, region, scale, rows, IC, true, stream, true,
+                                       reinterpret_cast<float*>(region + L.part_off), false)
+              : gu ? launch_prepass_silu_f16(static_cast<const uint16_t*>(gu) + r0 * 2 * IC, in[i].s_in, in[i].rin,
+                                             region, rows, IC, stream)
+                   : launch_prepass_f16(xr, in[i].s_in, in[i].rin, region, rows, IC, true, stream, kDecodeMaxRows);
           if (int rc = launch_status(e, who)) return rc;
           done = slot[i];
         }
         in[i].xf = region;
+        in[i].sc = scale;
       }
     }
     if (gu && !pl.pre) {   // the folded activation in the in-block pre-pass (down is one shard)
@@ -225,7 +236,7 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
     } else {
       for (int i = 0; i < n; ++i) {
         DecPlan p1;
-        if (!plan_decode(rows, IC, 1, in + i, &p1)) return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
+        if (!plan_decode(rows, IC, 1, in + i, &p1, int8)) return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
         hipError_t e = launch_decode(p1, xr, rows, IC, 1, in + i, orow, ldo,
                                      reinterpret_cast<float*>(ws + L.slab_off), reinterpret_cast<int*>(ws), stream);
         if (int rc = launch_status(e, who)) return rc;
@@ -352,11 +363,12 @@ int64_t max_oc(int n, const DecShardIn* in) {
 // Workspace of either path for these shards (host descriptors; only OC, K and the s_in/rin pointers are read).
 bool workspace_layout(int64_t M, int64_t IC, int n, const DecShardIn* in, unsigned flags, Layout* L) {
   if (use_decode_path(M, flags, max_oc(n, in))) {
+    const bool int8 = (flags & EXL3_ACT_INT8) != 0;
     size_t slab = 0;
-    if (!decode_slab_bytes(M, IC, n, in, &slab)) return false;
+    if (!decode_slab_bytes(M, IC, n, in, &slab, int8)) return false;
     int slot[kMaxShards];
-    const bool pre = first_chunk(M) >= kPreRotateRows || last_chunk(M) >= kPreRotateRows;
-    *L = layout_for(slab, pre_rows(M), IC, pre ? distinct_inputs(n, in, slot) : 0, false, kDecodeMaxRows);
+    const bool pre = int8 || first_chunk(M) >= kPreRotateRows || last_chunk(M) >= kPreRotateRows;
+    *L = layout_for(slab, pre_rows(M), IC, pre ? distinct_inputs(n, in, slot) : 0, int8, kDecodeMaxRows);
   } else {
     size_t slab = 0;                                      // shards run one after another: the largest split
     if (!(flags & kNoSplitFlags))
@@ -430,7 +442,8 @@ int linear_into_impl(void* out, int64_t ldo, int64_t col0, const void* x, int64_
   if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rc = use_decode_path(M, flags, OC)
-                     ? run_decode("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, st, gu)
+                     ? run_decode("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, st, gu,
+                                  (flags & EXL3_ACT_INT8) != 0)
                      : run_gemm("exl3_linear_into", out, ldo, x, M, IC, 1, &in, static_cast<char*>(ws), L, flags, st, gu);
   if (rc) return rc;
   return ok();
@@ -481,7 +494,8 @@ int exl3_linear_multi_into(void* out, int64_t ldo, const void* x, int64_t M, int
   if (int rc = check_workspace(L, ws, ws_bytes)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rc = use_decode_path(M, flags, max_oc(n_shards, in))
-                     ? run_decode("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L, st)
+                     ? run_decode("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L, st,
+                                  nullptr, (flags & EXL3_ACT_INT8) != 0)
                      : run_gemm("exl3_linear_multi_into", out, ldo, x, M, IC, n_shards, in, static_cast<char*>(ws), L, flags,
                                 st);
   if (rc) return rc;

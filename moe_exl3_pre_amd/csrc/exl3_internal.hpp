@@ -30,6 +30,7 @@ struct DecShardIn {
   int64_t col0;
   const void *s_in, *rin, *rout, *s_out;
   const void* xf = nullptr;   // decode phase, pre-rotated launches: this shard's fragment-major activations
+  const float* sc = nullptr;  // decode phase, 8-bit path: the launch rows' scales (xf then holds the codes)
 };
 
 struct DecPlan {
@@ -39,7 +40,7 @@ struct DecPlan {
   int tr_off;               // LDS byte offset of the trellis staging slots
   size_t lds_bytes;         // dynamic LDS per block
   int kset;                 // kernel K set: 1..8 single K, 0 mixed {2,3,4}, -1 unsupported mix
-  bool pre;                 // activations pre-rotated once per launch (M >= kPreRotateRows)
+  bool pre;                 // activations pre-rotated once per launch (M >= kPreRotateRows, or forced)
   int order[kMaxShards];    // shard processed in grid position r
   int wg_begin[kMaxShards];
   size_t slab_off[kMaxShards];
@@ -50,8 +51,9 @@ struct DecPlan {
 };
 
 // Plans one decode-phase launch of M <= 32 rows over n shards (above 16 rows with pre-rotated
-// activations); false if it cannot be served.
-bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl);
+// activations); false if it cannot be served.  pre: read pre-rotated activations at any M (the 8-bit
+// path, whose codes need the row's maximum over all input features first).
+bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl, bool pre = false);
 // silu: x is a dense MLP block's gate_up output [M, 2 IC] and the activation bf16(silu(g) * u) is formed in the
 // in-block pre-pass (one shard, 1..4 rows, no pre-rotation; otherwise hipErrorInvalidValue).
 hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,

@@ -36,6 +36,7 @@ constexpr int kNB = 8;           // tile columns per wave = one 128-column block
 struct DecShard {
   const uint32_t* code;
   const uint16_t* xf;            // pre-rotated activations, fragment-major (MR == 0 only)
+  const float* sc;               // 8-bit path: row scales of the integer codes in xf (else null)
   const uint16_t* s_in;
   const uint16_t* rin;
   const uint16_t* rout;
@@ -314,13 +315,18 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
     if (threadIdx.x == 0) __hip_atomic_store(sh.counters + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- 6. output Hadamard-128, rout * s_out, bf16 into the slice
+  // ---- 6. output Hadamard-128, (the row scale on the 8-bit path,) rout * s_out, bf16 into the slice
 #pragma unroll
   for (int t = 0; t < kRT; ++t) {
     const int row = out_row(t);
     if (row < M) {
       float x0 = v0[t], x1 = v1[t];
       had128_wave(x0, x1, lane);
+      if (sh.sc) {
+        const float rs = sh.sc[row];
+        x0 *= rs;
+        x1 *= rs;
+      }
       x0 = x0 * kInvSqrt128 * f16_to_f32(sh.rout[c0]) * f16_to_f32(sh.s_out[c0]);
       x1 = x1 * kInvSqrt128 * f16_to_f32(sh.rout[c0 + 1]) * f16_to_f32(sh.s_out[c0 + 1]);
       uint16_t* dst = a.out + int64_t(row) * a.ldo + sh.col0 + c0;
@@ -399,7 +405,7 @@ int shard_splits(int64_t M, int B, int nblk, int K) {
   }
 }
 
-bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl) {
+bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl, bool pre) {
   if (M < 1 || M > kDecodeLaunchRows || n < 1 || n > kMaxShards) return false;
   const int B = int(IC / kHad);
   int nb_max = 1;
@@ -411,7 +417,7 @@ bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl
   pl->spw = spw_variant(2 * ((nb_max + kWaves - 1) / kWaves));
   int kmax = 1;
   for (int i = 0; i < n; ++i) kmax = in[i].K > kmax ? in[i].K : kmax;
-  pl->pre = M >= kPreRotateRows;
+  pl->pre = pre || M >= kPreRotateRows;
   pl->lds_row = pl->pre ? 0 : kHad * nb_max + 8;
   pl->tr_off = int(tr_offset(int(M), pl->lds_row));
   pl->lds_bytes = lds_bytes_for(int(M), pl->lds_row, kmax);
@@ -508,6 +514,7 @@ hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC
     DecShard& d = a.sh[r];
     d.code = (const uint32_t*)s.code;
     d.xf = (const uint16_t*)s.xf;
+    d.sc = s.sc;
     d.s_in = (const uint16_t*)s.s_in;
     d.rin = (const uint16_t*)s.rin;
     d.rout = (const uint16_t*)s.rout;

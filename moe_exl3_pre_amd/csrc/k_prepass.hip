@@ -235,21 +235,48 @@ __global__ __launch_bounds__(256) void prepass_row_scale_kernel(const float* __r
   if (lane == 0) scale[row] = __fdiv_rn(a, 127.0f);
 }
 
-template <bool R32>
+// FOLD: the row scale is not read from `scale` but formed here from the per-(row, block) maxima in `part`
+// (max over the row's blocks, then / 127, the operations of prepass_row_scale_kernel, so the same value); the
+// unit of block 0 writes it to `scale`.  This saves the row-scale launch where launches dominate (a few rows).
+template <bool R32, bool FOLD = false>
 __global__ __launch_bounds__(256) void prepass_frag_codes_kernel(const uint16_t* __restrict__ x,
                                                                  const uint16_t* __restrict__ s_in,
                                                                  const uint16_t* __restrict__ rin,
-                                                                 const float* __restrict__ scale,
+                                                                 float* __restrict__ scale,
+                                                                 const float* __restrict__ part,
                                                                  uint16_t* __restrict__ xf, int64_t M, int64_t IC) {
   const int lane = threadIdx.x & 63;
   const int64_t nq = IC / kHad;
   const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (unit >= frag_row_units(M, R32) * nq) return;
   const int64_t rb = unit / nq, q = unit % nq;
+  const int64_t row = rb * 16 + (lane & 15);
+  // FOLD: the four lanes of row n take every fourth block's maximum.  The first eight loads per lane are
+  // issued before the transform's own loads, so both wait out one memory latency together.
+  const float* pr = part + (row < M ? row : 0) * (FOLD ? nq : 0);
+  const int64_t b0 = lane >> 4;
+  float pm[8];
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) pm[k] = b0 + 4 * k < nq ? pr[b0 + 4 * k] : 0.f;
+  }
   float v[2][16];
   frag_transform(x, s_in, rin, M, IC, rb, q, lane, v);
-  const int64_t row = rb * 16 + (lane & 15);
-  const float sc = row < M ? scale[row] : 0.f;
+  float sc = 0.f;
+  if constexpr (FOLD) {
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, pm[k]);
+    for (int64_t bb = b0 + 32; bb < nq; bb += 4) m = fmaxf(m, pr[bb]);
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (row < M) {
+      sc = __fdiv_rn(m, 127.0f);
+      if (q == 0 && lane < 16) scale[row] = sc;
+    }
+  } else {
+    sc = row < M ? scale[row] : 0.f;
+  }
   auto code = [&](float xv) -> float {
     return sc > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(xv * kInvSqrt128, sc)), -127.f), 127.f) : 0.f;
   };
@@ -345,22 +372,23 @@ hipError_t launch_prepass_silu_f16(const void* gu, const void* s_in, const void*
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
                              int64_t IC, bool permuted, hipStream_t stream, bool f16_codes, float* part, bool rows32) {
   if (M <= 0) return hipSuccess;
-  if (permuted && f16_codes) {                            // fragment-major fp16 codes (the GEMM operand)
+  if (permuted && f16_codes) {                            // fragment-major fp16 codes (the MFMA operand)
     if (!part) return hipErrorInvalidValue;
     const int64_t units = (M + 15) / 16 * (IC / kHad);
     const dim3 ug((unsigned)((units + 3) / 4)), blk(256);
     const uint16_t *xx = (const uint16_t*)x, *si = (const uint16_t*)s_in, *ri = (const uint16_t*)rin;
     hipLaunchKernelGGL(prepass_frag_amax_kernel, ug, blk, 0, stream, xx, si, ri, part, M, IC);
-    hipLaunchKernelGGL(prepass_row_scale_kernel, dim3((unsigned)((M + 3) / 4)), blk, 0, stream, (const float*)part,
-                       scale, M, IC / kHad);
     const int64_t cunits = frag_row_units(M, rows32) * (IC / kHad);
     const dim3 cg((unsigned)((cunits + 3) / 4));
-    if (rows32)
-      hipLaunchKernelGGL(prepass_frag_codes_kernel<true>, cg, blk, 0, stream, xx, si, ri, (const float*)scale,
+    if (rows32) {                                         // the prefill GEMM's operand: many rows, a scale launch
+      hipLaunchKernelGGL(prepass_row_scale_kernel, dim3((unsigned)((M + 3) / 4)), blk, 0, stream, (const float*)part,
+                         scale, M, IC / kHad);
+      hipLaunchKernelGGL((prepass_frag_codes_kernel<true>), cg, blk, 0, stream, xx, si, ri, scale, (const float*)part,
                          (uint16_t*)q, M, IC);
-    else
-      hipLaunchKernelGGL(prepass_frag_codes_kernel<false>, cg, blk, 0, stream, xx, si, ri, (const float*)scale,
-                         (uint16_t*)q, M, IC);
+    } else {                                              // the decode-phase operand (<= 32 rows): scales folded in
+      hipLaunchKernelGGL((prepass_frag_codes_kernel<false, true>), cg, blk, 0, stream, xx, si, ri, scale,
+                         (const float*)part, (uint16_t*)q, M, IC);
+    }
     return hipGetLastError();
   }
   if (permuted || f16_codes) return hipErrorInvalidValue;  // natural layout: int8 codes only

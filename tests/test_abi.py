@@ -65,7 +65,7 @@ def _linear(**kw):
     (dict(x=FAKE + 4), exl3.EINVAL, "x"),
     (dict(out=None), exl3.EINVAL, "out"),
     (dict(flags=1 << 7), exl3.EINVAL, "flags"),
-    (dict(flags=exl3.ACT_INT8 | exl3.FORCE_GEMV), exl3.EUNSUPPORTED, "flags"),
+    (dict(flags=exl3.ACT_INT8 | exl3.FORCE_GEMV, ws=None), exl3.EWORKSPACE, "ws"),  # 8-bit decode phase accepted
     (dict(flags=exl3.ACT_INT8, ws=None), exl3.EWORKSPACE, "ws"),              # 8-bit path accepted
     (dict(flags=exl3.FORCE_GEMV | exl3.FORCE_MFMA), exl3.EINVAL, "flags"),
     (dict(flags=exl3.BATCH_INVARIANT | exl3.FORCE_MFMA), exl3.EINVAL, "BATCH_INVARIANT"),
@@ -121,6 +121,19 @@ def test_gemm_tail_split_plan():
     ws = exl3.linear_workspace_bytes(8192, 17408, 5120)
     assert ws >= 16384 + 2 * 128 * 4 * 65536 + 8192 * 17408 * 2
     assert exl3.linear_workspace_bytes(8192, 17408, 5120, exl3.GEMM_NO_SPLIT) < ws
+
+
+def test_int8_decode_workspace_holds_codes_scales_and_maxima():
+    """The 8-bit path on the decode-phase kernel writes its codes at every M: 16 (32) rows x IC fp16, plus the
+    row scales and the per-(row, 128-block) maxima, per distinct (s_in, rin); the 16-bit path needs no region
+    below 5 rows."""
+    IC, OC = 2048, 28672
+    for M, rows in ((1, 16), (4, 16), (16, 16), (17, 32), (32, 32)):
+        f16 = exl3.linear_workspace_bytes(M, IC, OC)
+        i8 = exl3.linear_workspace_bytes(M, IC, OC, exl3.ACT_INT8)
+        assert i8 >= 16384 + rows * IC * 2 + rows * 4 + rows * (IC // 128) * 4, (M, i8)
+        assert i8 > f16, (M, i8, f16)
+        assert exl3.linear_workspace_bytes(M, IC, OC, exl3.ACT_INT8 | exl3.FORCE_GEMV) == i8
 
 
 def test_decode_workspace_pre_rotation_region():

@@ -90,11 +90,17 @@ def test_int8_zero_rows_and_scale_invariance():
 
 
 def test_int8_dispatch_and_merged():
-    """The 8-bit path runs on the MFMA GEMM at every M (bitwise equal to forcing it); merged shards equal
-    separate calls bit for bit."""
+    """The 8-bit path is dispatched by M like the 16-bit one: up to exl3_gemv_max_rows(OC) it runs the
+    decode-phase kernel (bitwise equal to forcing it), above it the MFMA GEMM; merged shards equal separate
+    calls bit for bit."""
     c = synth.linear_case(8500, 5, 512, 256, 2)
     d = _dev_case(c)
-    assert torch.equal(_run(c, d), _run(c, d, flags=exl3.ACT_INT8 | exl3.FORCE_MFMA))
+    assert 5 <= exl3.lib().exl3_gemv_max_rows(256)
+    assert torch.equal(_run(c, d), _run(c, d, flags=exl3.ACT_INT8 | exl3.FORCE_GEMV))
+    big = synth.linear_case(8502, 300, 512, 256, 2)
+    assert 300 > exl3.lib().exl3_gemv_max_rows(256)
+    db = _dev_case(big)
+    assert torch.equal(_run(big, db), _run(big, db, flags=exl3.ACT_INT8 | exl3.FORCE_MFMA))
     case = synth.merged_case(8501, 9, 512, [(256, 2), (384, 3)])
     x = to_dev_x(case["x_bits"])
     s_in, rin = to_dev(case["shards"][0]["s_in"]), to_dev(case["shards"][0]["rin"])
@@ -107,6 +113,56 @@ def test_int8_dispatch_and_merged():
                          flags=exl3.ACT_INT8)
     torch.cuda.synchronize()
     assert torch.equal(merged, sep)
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 32, 40])
+@pytest.mark.parametrize("K", [2, 3])
+def test_int8_decode_phase_against_the_oracle(M, K):
+    """The decode-phase kernel on the 8-bit path (EXL3_FORCE_GEMV): one 16-row group, two groups in one
+    launch (17..32 rows) and two launches (40 rows), element by element on the kernel's own codes; the
+    forced GEMM gives the same values to rounding."""
+    c = synth.linear_case(8600 + 10 * M + K, M, 1024, 384, K)
+    d = _dev_case(c)
+    out = _run(c, d, flags=exl3.ACT_INT8 | exl3.FORCE_GEMV)
+    ref8, ref = _refs(c, d)
+    e = assert_close_linear(bf16_to_f64(out), ref8, ref, tol=TOL_INT8)
+    gemm = bf16_to_f64(_run(c, d, flags=exl3.ACT_INT8 | exl3.FORCE_MFMA))
+    assert_close_linear(bf16_to_f64(out), gemm, ref, tol=TOL_INT8)
+    log(f"  M={M} K={K}: rel err vs exact {e:.3e}")
+
+
+def test_int8_decode_phase_other_k_split_and_slice():
+    """K outside {2, 3, 4} (one launch per shard), a shard wide enough in IC to split along the input
+    features (partials summed before the row scale), and a slice of a wider output."""
+    for K, IC, OC in ((1, 512, 256), (6, 512, 256), (3, 8192, 256)):
+        c = synth.linear_case(8700 + K + IC, 4, IC, OC, K)
+        d = _dev_case(c)
+        out = _run(c, d, flags=exl3.ACT_INT8 | exl3.FORCE_GEMV, ldo=OC + 256, col0=128)
+        o = bf16_to_f64(out)
+        assert np.all(o[:, :128] == SENTINEL) and np.all(o[:, 128 + OC:] == SENTINEL)
+        ref8, ref = _refs(c, d)
+        assert_close_linear(o[:, 128:128 + OC], ref8, ref, tol=TOL_INT8)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_int8_decode_gate_up_config_sampled(M):
+    """The decode-phase gate_up shape (IC=4096, 2 x 14336, K=2 | K=3) on the 8-bit path: one merged launch
+    per chunk, equal to per-shard calls bit for bit; sampled 128-column blocks of both shards against the
+    oracle on the kernel's own codes."""
+    cfg = synth.DECODE_GATE_UP
+    case = synth.merged_case(8800 + M, M, cfg["IC"], [(cfg["OC_gate"], cfg["K_gate"]), (cfg["OC_up"], cfg["K_up"])])
+    x = to_dev_x(case["x_bits"])
+    s_in, rin = to_dev(case["shards"][0]["s_in"]), to_dev(case["shards"][0]["rin"])
+    shards = [shard_to_dev(s, s_in, rin) for s in case["shards"]]
+    out = torch.full((M, case["ldo"]), SENTINEL, dtype=torch.bfloat16, device=dev())
+    exl3.linear_multi_into(out, x, shards, flags=exl3.ACT_INT8)
+    sep = torch.full_like(out, SENTINEL)
+    for s in shards:
+        exl3.linear_into(sep, x, s["code"], s["K"], s["s_in"], s["rin"], s["rout"], s["s_out"], col0=s["col0"],
+                         flags=exl3.ACT_INT8)
+    torch.cuda.synchronize()
+    assert torch.equal(out, sep)
+    _sampled(case["x"], x, case["shards"], shards, out, np.arange(M), 11 + M)
 
 
 def _sampled(case_x, x_dev, shards, dev_shards, out, rows, seed):
