@@ -124,9 +124,9 @@ int exl3_gemm_tail_splits(int64_t M, int64_t IC, int64_t OC);
  * EXL3_GEMM_NO_SPLIT it does not depend on M at all.  Decode-phase launches of 5..32 rows rotate the
  * activations once per call into the workspace (16 or 32 rows x IC fp16 per distinct (s_in, rin)) before
  * the decode kernel; smaller ones rotate inside the kernel.  Both rotations give the same bits.
- * 8-bit path (EXL3_ACT_INT8): a pre-pass (three launches: row maxima, row scales, codes) writes the codes q
- * as fp16 numbers, exact, in the operand layout of the phase that runs, so the decode-phase kernel serves
- * small M here too; every q * W product is exact in fp32, so the contraction is the integer dot product up
+ * 8-bit path (EXL3_ACT_INT8): a pre-pass writes the row maxima and then the codes q as fp16 numbers, exact,
+ * in the operand layout of the phase that runs (decode-phase launches of 1..4 rows form the same codes in
+ * the kernel's own pre-pass from the row maxima), so the decode-phase kernel serves small M here too; every q * W product is exact in fp32, so the contraction is the integer dot product up
  * to fp32 summation; in both phases the row scale multiplies the result after the output Hadamard and
  * before rout * s_out.  The decode-phase path needs 16 or 32 rows x IC fp16 of codes, the row scales and
  * the row maxima (rows x IC/128 fp32) in the workspace per distinct (s_in, rin).

@@ -184,9 +184,10 @@ int check_workspace(const Layout& L, void* ws, size_t ws_bytes) {
 // as two 16-row groups in one launch, so the weights are streamed once per 32 rows).
 // gu (optional): the dense MLP block's gate_up output [M, 2 IC]; the pre-rotation (5..32 rows) or the decode
 // kernel's in-block pre-pass (1..4 rows) then forms the input h = bf16(silu(g) * u) itself.
-// int8: the 8-bit path.  Every chunk, of any size, first writes its integer codes (as fp16 numbers) and row
-// scales with the fragment-major 8-bit pre-pass; the decode launch multiplies the codes and applies each
-// row's scale after its output Hadamard, as the GEMM's epilogue does.
+// int8: the 8-bit path.  A chunk of 5..32 rows first writes its integer codes (as fp16 numbers) and row
+// scales with the fragment-major 8-bit pre-pass; a chunk of 1..4 rows only the per-(row, block) maxima, and
+// the decode kernel's in-block pre-pass forms the same codes.  The decode launch multiplies the codes and
+// applies each row's scale after its output Hadamard, as the GEMM's epilogue does.
 int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M, int64_t IC, int n,
                const DecShardIn* in_, char* ws, const Layout& L, hipStream_t stream, const void* gu = nullptr,
                bool int8 = false) {
@@ -200,7 +201,24 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
     const void* xr = static_cast<const uint16_t*>(x) + r0 * IC;
     void* orow = static_cast<uint16_t*>(out) + r0 * ldo;
     DecPlan pl;
-    if (!plan_decode(rows, IC, n, in, &pl, int8)) return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
+    const bool i8_inblock = int8 && rows <= 4;
+    if (!plan_decode(rows, IC, n, in, &pl, int8 && !i8_inblock))
+      return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
+    if (i8_inblock) {
+      int done = -1;
+      for (int i = 0; i < n; ++i) {
+        char* region = ws + L.xh_off + L.xh_bytes * size_t(slot[i]);
+        float* part = reinterpret_cast<float*>(region + L.part_off);
+        if (slot[i] > done) {
+          if (L.xh_bytes < L.part_off + size_t(rows) * size_t(IC / 128) * 4)
+            return fail(EXL3_EWORKSPACE, "%s: workspace has no 8-bit region", who);
+          if (int rc = launch_status(launch_prepass_amax(xr, in[i].s_in, in[i].rin, part, rows, IC, stream), who))
+            return rc;
+          done = slot[i];
+        }
+        in[i].part = part;
+      }
+    }
     if (pl.pre) {
       int done = -1;
       for (int i = 0; i < n; ++i) {
@@ -231,14 +249,16 @@ int run_decode(const char* who, void* out, int64_t ldo, const void* x, int64_t M
       if (int rc = launch_status(e, who)) return rc;
     } else if (pl.kset >= 0) {
       hipError_t e = launch_decode(pl, xr, rows, IC, n, in, orow, ldo, reinterpret_cast<float*>(ws + L.slab_off),
-                                   reinterpret_cast<int*>(ws), stream);
+                                   reinterpret_cast<int*>(ws), stream, false, i8_inblock);
       if (int rc = launch_status(e, who)) return rc;
     } else {
       for (int i = 0; i < n; ++i) {
         DecPlan p1;
-        if (!plan_decode(rows, IC, 1, in + i, &p1, int8)) return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
+        if (!plan_decode(rows, IC, 1, in + i, &p1, int8 && !i8_inblock))
+          return fail(EXL3_EUNSUPPORTED, "%s: no decode-phase plan", who);
         hipError_t e = launch_decode(p1, xr, rows, IC, 1, in + i, orow, ldo,
-                                     reinterpret_cast<float*>(ws + L.slab_off), reinterpret_cast<int*>(ws), stream);
+                                     reinterpret_cast<float*>(ws + L.slab_off), reinterpret_cast<int*>(ws), stream,
+                                     false, i8_inblock);
         if (int rc = launch_status(e, who)) return rc;
       }
     }

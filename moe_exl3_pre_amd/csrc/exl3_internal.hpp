@@ -31,6 +31,7 @@ struct DecShardIn {
   const void *s_in, *rin, *rout, *s_out;
   const void* xf = nullptr;   // decode phase, pre-rotated launches: this shard's fragment-major activations
   const float* sc = nullptr;  // decode phase, 8-bit path: the launch rows' scales (xf then holds the codes)
+  const float* part = nullptr;  // decode phase, 8-bit path with in-block codes (1..4 rows): the rows' block maxima
 };
 
 struct DecPlan {
@@ -56,8 +57,10 @@ struct DecPlan {
 bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl, bool pre = false);
 // silu: x is a dense MLP block's gate_up output [M, 2 IC] and the activation bf16(silu(g) * u) is formed in the
 // in-block pre-pass (one shard, 1..4 rows, no pre-rotation; otherwise hipErrorInvalidValue).
+// i8: the 8-bit path with in-block codes (1..4 rows, no pre-rotation; every shard's `part` set).
 hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,
-                         void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream, bool silu = false);
+                         void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream, bool silu = false,
+                         bool i8 = false);
 
 // permuted: fragment-major, with 16-row fragments (the decode-phase kernel's operand) or with rows32 the
 // 32-row fragments of the prefill GEMM (k_gemm.hip), rows past M written as zeros up to the next multiple
@@ -67,6 +70,10 @@ hipError_t launch_prepass_f16(const void* x, const void* s_in, const void* rin, 
 // Natural layout: q receives int8 codes.  permuted with f16_codes: the same codes as fp16 numbers in the
 // fragment-major layout (16- or, with rows32, 32-row fragments), which needs part, M * (IC / 128) floats of
 // scratch.  Other combinations are rejected.
+// The per-(row, 128-block) max |xh| of the fragment-major 8-bit pre-pass alone, into part [M, IC / 128]
+// (the decode-phase kernel forms the codes of 1..4 rows itself).
+hipError_t launch_prepass_amax(const void* x, const void* s_in, const void* rin, float* part, int64_t M, int64_t IC,
+                               hipStream_t stream);
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
                              int64_t IC, bool permuted, hipStream_t stream, bool f16_codes = false,
                              float* part = nullptr, bool rows32 = false);

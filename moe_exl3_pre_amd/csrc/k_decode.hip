@@ -37,6 +37,7 @@ struct DecShard {
   const uint32_t* code;
   const uint16_t* xf;            // pre-rotated activations, fragment-major (MR == 0 only)
   const float* sc;               // 8-bit path: row scales of the integer codes in xf (else null)
+  const float* part;             // 8-bit path, in-block codes (I8): per-(row, 128-block) max |xh|, [M, IC / 128]
   const uint16_t* s_in;
   const uint16_t* rin;
   const uint16_t* rout;
@@ -67,10 +68,15 @@ struct DecArgs {
 // RG (MR == 0 only): 16-row groups of the launch.  With RG = 2 one launch covers up to 32 rows: every
 // decoded tile column feeds the MFMAs of both groups, so the weights are streamed once for 32 rows, and
 // each group is reduced exactly as a 16-row launch reduces it (the same bits per row).
-template <int K, int SPW, int MR, bool SILU = false, int RG = 1>
+// I8 (MR 1 or 4 only): the 8-bit path with the codes formed in the in-block pre-pass.  Each row's scale
+// sc = max / 127 comes from the per-(row, block) maxima of sh.part (the values the fragment-major pre-pass
+// forms, by the same max and division), the rotated values are quantised as that pre-pass quantises them,
+// q = clamp(rne(xh / sc), +-127) in fp32, and stored as fp16 numbers; the epilogue applies the row scale.
+template <int K, int SPW, int MR, bool SILU = false, int RG = 1, bool I8 = false>
 __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& sh, int local, char* lds) {
   constexpr bool kPre = MR == 0;
   static_assert(!SILU || MR == 1 || MR == 4, "the folded activation is for the in-block pre-pass");
+  static_assert(!I8 || ((MR == 1 || MR == 4) && !SILU && RG == 1), "in-block codes: 1..4 rows, 16-bit input");
   static_assert(RG == 1 || (RG == 2 && kPre), "two row groups need pre-rotated activations");
   using G = Geom<K>;
   // steps of trellis words in flight per wave: one.  Every block requests its first step at once, so
@@ -122,6 +128,15 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
       }
     }
   }
+  // I8: the rows' block maxima (reduced over the wave once the weight stream is requested)
+  const int nq = a.IC / kHad;
+  float pmax[I8 ? kMR : 1];
+#pragma unroll
+  for (int m = 0; m < (I8 ? kMR : 0); ++m) {
+    const float* pr = sh.part + int64_t(m < M ? m : M - 1) * nq;
+    pmax[m] = 0.f;
+    for (int b = lane; b < nq; b += 64) pmax[m] = fmaxf(pmax[m], pr[b]);
+  }
   __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the weight stream
 
   // ---- 2. the first kD steps of the weight stream, as coalesced 16-byte loads.  One step of this
@@ -159,7 +174,16 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
     load_step(d, tb[d]);
   }
 
-  // ---- 3. this wave's rotated activations into LDS (PERM16 order); its part of row M stays zero
+  // ---- 3. this wave's rotated activations (I8: their codes) into LDS (PERM16 order); its part of row M
+  // stays zero
+  float rsc[I8 ? kMR : 1];   // I8: the rows' scales (wave-uniform)
+#pragma unroll
+  for (int m = 0; m < (I8 ? kMR : 0); ++m) {
+    float mx = pmax[m];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+    rsc[m] = __fdiv_rn(mx, 127.0f);
+  }
 #pragma unroll
   for (int pb = 0; pb < (kPre ? 0 : kPB); ++pb) {
     if (hb0 + pb < hb1) {
@@ -174,7 +198,15 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
           float v0 = bf16_to_f32(xw & 0xFFFFu) * s0 * r0;
           float v1 = bf16_to_f32(xw >> 16) * s1 * r1;
           had128_wave_pairs8(v0, v1, lane);
-          *reinterpret_cast<uint32_t*>(xs + m * lrow + kl) = rot_f16x2(v0, v1);
+          if constexpr (I8) {
+            const float sc = rsc[m];
+            auto code = [&](float xv) -> float {
+              return sc > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(xv * kInvSqrt128, sc)), -127.f), 127.f) : 0.f;
+            };
+            *reinterpret_cast<uint32_t*>(xs + m * lrow + kl) = f32x2_to_f16x2(code(v0), code(v1));
+          } else {
+            *reinterpret_cast<uint32_t*>(xs + m * lrow + kl) = rot_f16x2(v0, v1);
+          }
         }
       }
       *reinterpret_cast<uint32_t*>(xs + M * lrow + kl) = 0u;
@@ -322,7 +354,13 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
     if (row < M) {
       float x0 = v0[t], x1 = v1[t];
       had128_wave(x0, x1, lane);
-      if (sh.sc) {
+      if constexpr (I8) {
+        float rs = rsc[0];
+#pragma unroll
+        for (int m = 1; m < kMR; ++m) rs = row == m ? rsc[m] : rs;
+        x0 *= rs;
+        x1 *= rs;
+      } else if (sh.sc) {
         const float rs = sh.sc[row];
         x0 *= rs;
         x1 *= rs;
@@ -340,7 +378,7 @@ __device__ __forceinline__ void decode_block(const DecArgs& a, const DecShard& s
   }
 }
 
-template <int KSET, int SPW, int MR, bool SILU = false, int RG = 1>
+template <int KSET, int SPW, int MR, bool SILU = false, int RG = 1, bool I8 = false>
 __global__ __launch_bounds__(512, 4) void decode_kernel(DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int wg = blockIdx.x;
@@ -349,12 +387,12 @@ __global__ __launch_bounds__(512, 4) void decode_kernel(DecArgs a) {
   const DecShard& sh = a.sh[i];
   const int local = wg - sh.wg_begin;
   if constexpr (KSET >= 1 && KSET <= 8) {
-    decode_block<KSET, SPW, MR, SILU, RG>(a, sh, local, lds);
+    decode_block<KSET, SPW, MR, SILU, RG, I8>(a, sh, local, lds);
   } else {   // KSET 0: the mixed set {2, 3, 4}
     switch (sh.K) {
-      case 2: decode_block<2, SPW, MR, false, RG>(a, sh, local, lds); break;
-      case 3: decode_block<3, SPW, MR, false, RG>(a, sh, local, lds); break;
-      default: decode_block<4, SPW, MR, false, RG>(a, sh, local, lds); break;
+      case 2: decode_block<2, SPW, MR, false, RG, I8>(a, sh, local, lds); break;
+      case 3: decode_block<3, SPW, MR, false, RG, I8>(a, sh, local, lds); break;
+      default: decode_block<4, SPW, MR, false, RG, I8>(a, sh, local, lds); break;
     }
   }
 }
@@ -457,18 +495,27 @@ bool plan_decode(int64_t M, int64_t IC, int n, const DecShardIn* in, DecPlan* pl
   return counters <= kCounterSlots;
 }
 
-template <int KSET, int MR, bool SILU = false, int RG = 1>
+template <int KSET, int MR, bool SILU = false, int RG = 1, bool I8 = false>
 static void launch_kset_mr(const DecPlan& pl, const DecArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)pl.wg_total), block(kWaves * 64);
   const size_t lds = pl.lds_bytes;
   if (pl.spw <= 2)
-    hipLaunchKernelGGL((decode_kernel<KSET, 2, MR, SILU, RG>), grid, block, lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<KSET, 2, MR, SILU, RG, I8>), grid, block, lds, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<KSET, 4, MR, SILU, RG>), grid, block, lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<KSET, 4, MR, SILU, RG, I8>), grid, block, lds, stream, a);
 }
 
 template <int KSET>
-static hipError_t launch_kset(const DecPlan& pl, const DecArgs& a, hipStream_t stream, bool silu) {
+static hipError_t launch_kset(const DecPlan& pl, const DecArgs& a, hipStream_t stream, bool silu, bool i8) {
+  // the 8-bit path with in-block codes: launches of 1..4 rows without pre-rotation
+  if (i8) {
+    if (silu || pl.pre || a.M > 4) return hipErrorInvalidValue;
+    if (a.M <= 1)
+      launch_kset_mr<KSET, 1, false, 1, true>(pl, a, stream);
+    else
+      launch_kset_mr<KSET, 4, false, 1, true>(pl, a, stream);
+    return hipGetLastError();
+  }
   // the folded MLP activation: single-shard launches of 1..4 rows with in-block rotation only
   if (silu) {
     if constexpr (KSET >= 1 && KSET <= 8) {
@@ -498,7 +545,7 @@ static hipError_t launch_kset(const DecPlan& pl, const DecArgs& a, hipStream_t s
 }
 
 hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC, int n, const DecShardIn* in,
-                         void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream, bool silu) {
+                         void* out, int64_t ldo, float* slab, int* counters, hipStream_t stream, bool silu, bool i8) {
   if (pl.kset < 0) return hipErrorInvalidValue;
   DecArgs a;
   a.x = (const uint16_t*)x;
@@ -515,6 +562,8 @@ hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC
     d.code = (const uint32_t*)s.code;
     d.xf = (const uint16_t*)s.xf;
     d.sc = s.sc;
+    d.part = s.part;
+    if (i8 && !s.part) return hipErrorInvalidValue;
     d.s_in = (const uint16_t*)s.s_in;
     d.rin = (const uint16_t*)s.rin;
     d.rout = (const uint16_t*)s.rout;
@@ -529,15 +578,15 @@ hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC
     d.wg_begin = pl.wg_begin[r];
   }
   switch (pl.kset) {
-    case 0: return launch_kset<0>(pl, a, stream, silu);
-    case 1: return launch_kset<1>(pl, a, stream, silu);
-    case 2: return launch_kset<2>(pl, a, stream, silu);
-    case 3: return launch_kset<3>(pl, a, stream, silu);
-    case 4: return launch_kset<4>(pl, a, stream, silu);
-    case 5: return launch_kset<5>(pl, a, stream, silu);
-    case 6: return launch_kset<6>(pl, a, stream, silu);
-    case 7: return launch_kset<7>(pl, a, stream, silu);
-    case 8: return launch_kset<8>(pl, a, stream, silu);
+    case 0: return launch_kset<0>(pl, a, stream, silu, i8);
+    case 1: return launch_kset<1>(pl, a, stream, silu, i8);
+    case 2: return launch_kset<2>(pl, a, stream, silu, i8);
+    case 3: return launch_kset<3>(pl, a, stream, silu, i8);
+    case 4: return launch_kset<4>(pl, a, stream, silu, i8);
+    case 5: return launch_kset<5>(pl, a, stream, silu, i8);
+    case 6: return launch_kset<6>(pl, a, stream, silu, i8);
+    case 7: return launch_kset<7>(pl, a, stream, silu, i8);
+    case 8: return launch_kset<8>(pl, a, stream, silu, i8);
   }
   return hipErrorInvalidValue;
 }

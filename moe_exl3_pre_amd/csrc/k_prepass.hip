@@ -369,6 +369,15 @@ hipError_t launch_prepass_silu_f16(const void* gu, const void* s_in, const void*
   return hipGetLastError();
 }
 
+hipError_t launch_prepass_amax(const void* x, const void* s_in, const void* rin, float* part, int64_t M, int64_t IC,
+                               hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  const int64_t units = (M + 15) / 16 * (IC / kHad);
+  hipLaunchKernelGGL(prepass_frag_amax_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream,
+                     (const uint16_t*)x, (const uint16_t*)s_in, (const uint16_t*)rin, part, M, IC);
+  return hipGetLastError();
+}
+
 hipError_t launch_prepass_i8(const void* x, const void* s_in, const void* rin, void* q, float* scale, int64_t M,
                              int64_t IC, bool permuted, hipStream_t stream, bool f16_codes, float* part, bool rows32) {
   if (M <= 0) return hipSuccess;

@@ -131,6 +131,23 @@ def test_int8_decode_phase_against_the_oracle(M, K):
     log(f"  M={M} K={K}: rel err vs exact {e:.3e}")
 
 
+@pytest.mark.parametrize("K", [2, 3, 5])
+def test_int8_inblock_codes_equal_the_codes_launch(K):
+    """Launches of 1..4 rows form the codes in the decode kernel's in-block pre-pass (from the row maxima the
+    first launch writes); launches of 5..32 rows read them from the codes launch.  Both quantise the same fp32
+    rotated values with the same division, so a row's output is the same bits whichever path ran (a shard
+    whose input-feature split is 1 at every M: IC = 1024, at most one Hadamard block per wave)."""
+    c = synth.linear_case(8750 + K, 17, 1024, 2048, K)
+    d = _dev_case(c)
+    flags = exl3.ACT_INT8 | exl3.FORCE_GEMV
+    full = _run(c, d, flags=flags)
+    for M in (1, 2, 4, 5):
+        part = _run(c, d, flags=flags, x=d["x"][:M].contiguous())
+        assert torch.equal(part, full[:M]), M
+    ref8, ref = _refs(c, d)
+    assert_close_linear(bf16_to_f64(full), ref8, ref, tol=TOL_INT8)
+
+
 def test_int8_decode_phase_other_k_split_and_slice():
     """K outside {2, 3, 4} (one launch per shard), a shard wide enough in IC to split along the input
     features (partials summed before the row scale), and a slice of a wider output."""
