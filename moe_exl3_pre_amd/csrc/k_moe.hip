@@ -33,6 +33,8 @@ constexpr int kMoeRows = 32;          // rows of one chunk: two 16-row MFMA grou
 constexpr int kMoeWaves = 4;          // waves per w13 / w2 workgroup: two per half
 constexpr int kRedStride = kHad + 4;  // padded fp32 row of the reduction buffers (spreads LDS banks)
 constexpr int kRouteThreads = 1024;
+static_assert(kMoeMaxExperts <= kRouteThreads && kMoeMaxGroups <= kRouteThreads,
+              "the route keeps one slot and one K group per thread");
 // w13 / w2 workgroups: the reduction buffer [2 halves][32 rows][kRedStride] and, before it is used, the
 // four waves' trellis staging slots share one LDS array
 constexpr int kMoeRedFloats = 2 * kMoeRows * kRedStride;
@@ -168,95 +170,160 @@ __device__ void moe_route_general(const MoeArgs& a, int* lds) {
   }
 }
 
-// Fast path of the route when one bit per (slot, pair) fits in LDS (E * ceil(P/32) <= kBitmapWords): the
-// pairs set bits of a [slot][P/32] bitmap, one wave per slot turns its row into exclusive popcount prefixes,
-// and a pair's position in its slot's list is the number of set bits before it -- the same stable order
-// (pair ids ascending inside a slot) without any serial pass.
+// Fast path of the route when one bit per (slot, pair) and every pair's slot fit in LDS (bitmap_route_fits):
+// the pairs set bits of a [slot][P/32] bitmap, one wave per slot turns its row into exclusive popcount
+// prefixes, and a pair's position in its slot's list is the number of set bits before it -- the same stable
+// order (pair ids ascending inside a slot) without any serial pass.
 constexpr int kBitmapWords = 8192;
 constexpr int kBitmapSlotCache = 8192;   // pairs whose slots the bitmap route keeps in LDS
+static_assert(kBitmapSlotCache % kRouteThreads == 0, "whole batches of expert ids per thread");
+
+__host__ __device__ inline bool bitmap_route_fits(int E, int P) {
+  return int64_t(E) * ((P + 31) / 32) <= kBitmapWords && P <= kBitmapSlotCache;
+}
 
 __device__ void moe_route_bitmap(const MoeArgs& a, int* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kW = kRouteThreads / 64;
-  const int E = a.E, W = (a.P + 31) / 32;
+  // Every kernel argument the route reads is requested here, together: the first read of each argument
+  // line is a memory round trip, and requested at first use they would cost one per phase.
+  const int* ids = a.ids;
+  const int* perm = a.perm;
+  int *pslot = a.pslot, *offs = a.offs, *rows = a.rows, *n_chunks = a.n_chunks;
+  int4v* chunks = a.chunks;
+  const int P = a.P, E = a.E, chunk_rows = a.chunk_rows, n_groups = a.n_groups;
+  asm volatile("" ::"s"(ids), "s"(perm), "s"(pslot), "s"(offs), "s"(rows), "s"(n_chunks), "s"(chunks), "s"(P),
+               "s"(E), "s"(chunk_rows), "s"(n_groups));
+  const int W = (P + 31) / 32;
   uint32_t* bm = reinterpret_cast<uint32_t*>(lds);   // [E][W]
   int* pre = lds + E * W;                             // [E][W] exclusive prefix of popcounts
   int* cnt = pre + E * W;                             // [E]
   int* tmp = cnt + E;                                 // [48]
   int* perm_l = tmp + 48;                             // [E] the slot of each logical expert
-  int* slot_of = perm_l + E;                          // [P] when it fits (see moe_route_lds_bytes), else null
-  if (a.P > kBitmapSlotCache) slot_of = nullptr;
-  if (slot_of) {
-    // every expert id and the slot table are loaded at once (no load waits for another), the slots are
-    // then LDS lookups
-    for (int q = tid; q < a.P; q += kRouteThreads) slot_of[q] = a.ids[q];
-    for (int e = tid; e < E; e += kRouteThreads) perm_l[e] = a.perm[e];
+  int* grp = perm_l + E;                              // [2][kMoeMaxGroups] the K groups' end slots and K
+  int* slot_of = grp + 2 * kMoeMaxGroups;             // [P] (P <= kBitmapSlotCache on this path)
+  // The slot table, the group table and (when they fit in LDS) every expert id are requested before the
+  // first of them is stored, so the phase waits out one memory latency (E <= kRouteThreads).  The loads
+  // are unconditional, with clamped indices: a load under a branch makes the compiler wait for it before
+  // the next batch.
+  const int pv = perm[tid < E ? tid : E - 1];
+  const int gt = tid < kMoeMaxGroups ? tid : kMoeMaxGroups - 1;
+  const int gh = a.g_hi[gt], gkv = a.g_k[gt];
+  {                                                   // P <= kBitmapSlotCache: one batch, no loop
+    constexpr int kIds = kBitmapSlotCache / kRouteThreads;
+    int v[kIds];
+#pragma unroll
+    for (int k = 0; k < kIds; ++k) {
+      const int q = k * kRouteThreads + tid;
+      v[k] = ids[q < P ? q : P - 1];
+    }
+#pragma unroll
+    for (int k = 0; k < kIds; ++k) {
+      const int q = k * kRouteThreads + tid;
+      if (q < P) slot_of[q] = v[k];
+    }
+    if (tid < E) perm_l[tid] = pv;
+  }
+  if (tid < n_groups) {
+    grp[tid] = gh;
+    grp[kMoeMaxGroups + tid] = gkv;
   }
   for (int i = tid; i < E * W; i += kRouteThreads) bm[i] = 0u;
   __syncthreads();
-  for (int q = tid; q < a.P; q += kRouteThreads) {
-    int s;
-    if (slot_of) {
-      const int e = slot_of[q];
-      s = (e >= 0 && e < E) ? perm_l[e] : -1;
-      s = (s >= 0 && s < E) ? s : -1;
-      slot_of[q] = s;
-    } else {
-      s = pair_slot(a, q);
-    }
-    a.pslot[q] = s;
+  for (int q = tid; q < P; q += kRouteThreads) {
+    const int e = slot_of[q];
+    int s = (e >= 0 && e < E) ? perm_l[e] : -1;
+    s = (s >= 0 && s < E) ? s : -1;
+    slot_of[q] = s;
     if (s >= 0) atomicOr(&bm[s * W + (q >> 5)], 1u << (q & 31));
   }
   __syncthreads();
-  for (int s = wave; s < E; s += kW) {
-    int carry = 0;
-    for (int j0 = 0; j0 < W; j0 += 64) {
-      const int j = j0 + lane;
-      const int v = j < W ? __popc(bm[s * W + j]) : 0;
-      const int inc = wave_incl_scan(v);
-      if (j < W) pre[s * W + j] = carry + inc - v;
-      carry += __builtin_amdgcn_readlane(inc, 63);
+  if (W <= 64) {
+    // Rows of up to 64 words: 8 lanes per slot, 8 consecutive words per lane, 8 slots per wave in one
+    // pass.  A lane's words take local popcount prefixes; the lane totals are scanned inside each 8-lane
+    // segment (DPP shifts by 1, 2 and 4 within the row of 16 lanes, added only from lanes of the same
+    // segment).  The prefixes are those of the per-slot scan below.
+    const int seg = lane & 7;
+    for (int s0 = 8 * wave; s0 < E; s0 += 8 * kW) {
+      const int s = s0 + (lane >> 3);
+      const int j0 = 8 * seg;
+      int pc[8], tot = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pc[i] = tot;
+        tot += (s < E && j0 + i < W) ? __popc(bm[s * W + j0 + i]) : 0;
+      }
+      int inc = tot;
+      int t = __builtin_amdgcn_update_dpp(0, inc, 0x111, 0xF, 0xF, false);   // row_shr:1
+      inc += seg >= 1 ? t : 0;
+      t = __builtin_amdgcn_update_dpp(0, inc, 0x112, 0xF, 0xF, false);       // row_shr:2
+      inc += seg >= 2 ? t : 0;
+      t = __builtin_amdgcn_update_dpp(0, inc, 0x114, 0xF, 0xF, false);       // row_shr:4
+      inc += seg >= 4 ? t : 0;
+      const int ex = inc - tot;
+      if (s < E) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (j0 + i < W) pre[s * W + j0 + i] = ex + pc[i];
+        if (seg == 7) cnt[s] = inc;
+      }
     }
-    if (lane == 0) cnt[s] = carry;
+  } else {
+    for (int s = wave; s < E; s += kW) {
+      int carry = 0;
+      for (int j0 = 0; j0 < W; j0 += 64) {
+        const int j = j0 + lane;
+        const int v = j < W ? __popc(bm[s * W + j]) : 0;
+        const int inc = wave_incl_scan(v);
+        if (j < W) pre[s * W + j] = carry + inc - v;
+        carry += __builtin_amdgcn_readlane(inc, 63);
+      }
+      if (lane == 0) cnt[s] = carry;
+    }
   }
   __syncthreads();
   const int s = tid;
   const int c = s < E ? cnt[s] : 0;
   int total = 0, chunk_total = 0;
   const int off = block_excl_scan(c, tmp, &total);
-  const int nch = (c + a.chunk_rows - 1) / a.chunk_rows;
+  const int nch = (c + chunk_rows - 1) / chunk_rows;
   const int coff = block_excl_scan(nch, tmp, &chunk_total);
+  int gk = 0;
   if (s < E) {
-    a.offs[s] = off;
     cnt[s] = off;                                     // from here on: first row of the slot
-    int gk = 0;
-    for (int g = 0; g < a.n_groups; ++g)
-      if (s < a.g_hi[g]) {
-        gk = a.g_k[g];
+    for (int g = 0; g < n_groups; ++g)
+      if (s < grp[g]) {
+        gk = grp[kMoeMaxGroups + g];
         break;
       }
+  }
+  __syncthreads();
+  // The route's global stores all come after its last barrier: a store still in flight at a barrier makes
+  // the compiler wait for it there as soon as a register it reads is reused.
+  for (int q = tid; q < P; q += kRouteThreads) {
+    const int sl = slot_of[q];                       // this thread wrote it above
+    pslot[q] = sl;
+    if (sl >= 0) {
+      const int w = sl * W + (q >> 5);
+      rows[cnt[sl] + pre[w] + __popc(bm[w] & ((1u << (q & 31)) - 1u))] = q;
+    }
+  }
+  if (s < E) {
+    offs[s] = off;
     for (int i = 0; i < nch; ++i) {
-      const int r0 = off + i * a.chunk_rows;
-      const int nr = c - i * a.chunk_rows < a.chunk_rows ? c - i * a.chunk_rows : a.chunk_rows;
-      a.chunks[coff + i] = (int4v){s, r0, nr, gk};
+      const int r0 = off + i * chunk_rows;
+      const int nr = c - i * chunk_rows < chunk_rows ? c - i * chunk_rows : chunk_rows;
+      chunks[coff + i] = (int4v){s, r0, nr, gk};
     }
   }
   if (s == 0) {
-    a.offs[E] = total;
-    a.n_chunks[0] = chunk_total;
-  }
-  __syncthreads();
-  for (int q = tid; q < a.P; q += kRouteThreads) {
-    const int sl = slot_of ? slot_of[q] : a.pslot[q];   // this thread wrote both above
-    if (sl >= 0) {
-      const int w = sl * W + (q >> 5);
-      a.rows[cnt[sl] + pre[w] + __popc(bm[w] & ((1u << (q & 31)) - 1u))] = q;
-    }
+    offs[E] = total;
+    n_chunks[0] = chunk_total;
   }
 }
 
 __device__ void moe_route(const MoeArgs& a, int* lds) {
-  if (a.E * ((a.P + 31) / 32) <= kBitmapWords)
+  if (bitmap_route_fits(a.E, a.P))
     moe_route_bitmap(a, lds);
   else
     moe_route_general(a, lds);
@@ -632,7 +699,7 @@ static size_t moe_slot_bytes(unsigned ks) {   // staging slot of the largest K i
 
 static size_t moe_route_lds_bytes(int E, int P) {
   const size_t words = size_t(E) * ((P + 31) / 32);
-  if (words <= size_t(kBitmapWords)) return (2 * words + 2 * E + 48 + (P <= kBitmapSlotCache ? P : 0)) * sizeof(int);
+  if (bitmap_route_fits(E, P)) return (2 * words + 2 * E + 48 + 2 * kMoeMaxGroups + size_t(P)) * sizeof(int);
   return size_t(3 * E + 48 + (P <= kSlotCache ? P : 0)) * sizeof(int);
 }
 
