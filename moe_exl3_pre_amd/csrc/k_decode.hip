@@ -22,6 +22,7 @@
 //     finishes the block and resets the counter for the next launch or graph replay.  The slab and the
 //     counters live in the caller's workspace ("radiance_escha.py", `_ensure_scratch`: split-K partial
 //     slab plus block counter, allocated once, never inside the launch).
+#include <climits>
 #include <utility>
 
 #include "exl3_device.hpp"
@@ -55,6 +56,7 @@ struct DecArgs {
   int64_t ldo;
   int M, IC, n_shards, lds_row;  // lds_row: halves per activation row in LDS (padded)
   int tr_off;                    // byte offset of the per-wave trellis staging slots in LDS
+  int wgb[kMaxShards];           // first workgroup of each shard in grid order; INT_MAX past n_shards
   DecShard sh[kMaxShards];
 };
 
@@ -382,9 +384,17 @@ template <int KSET, int SPW, int MR, bool SILU = false, int RG = 1, bool I8 = fa
 __global__ __launch_bounds__(512, 4) void decode_kernel(DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int wg = blockIdx.x;
+  // The block's shard, and every kernel argument the block reads, in two batches of scalar loads: the
+  // first read of an argument line is a memory round trip, and requested at first use (or through a
+  // search loop) they form a chain of them before the first weight load.
   int i = 0;
-  while (i + 1 < a.n_shards && wg >= a.sh[i + 1].wg_begin) ++i;     // shards are in wg_begin order
+#pragma unroll
+  for (int j = 1; j < kMaxShards; ++j) i += wg >= a.wgb[j] ? 1 : 0;   // shards are in grid order
   const DecShard& sh = a.sh[i];
+  asm volatile("" ::"s"(a.x), "s"(a.out), "s"(a.ldo), "s"(a.M), "s"(a.IC), "s"(a.lds_row), "s"(a.tr_off));
+  asm volatile("" ::"s"(sh.code), "s"(sh.xf), "s"(sh.sc), "s"(sh.part), "s"(sh.s_in), "s"(sh.rin), "s"(sh.rout),
+               "s"(sh.s_out), "s"(sh.slab), "s"(sh.counters), "s"(sh.col0), "s"(sh.code_bytes), "s"(sh.OC),
+               "s"(sh.K), "s"(sh.S), "s"(sh.wg_begin));
   const int local = wg - sh.wg_begin;
   if constexpr (KSET >= 1 && KSET <= 8) {
     decode_block<KSET, SPW, MR, SILU, RG, I8>(a, sh, local, lds);
@@ -556,6 +566,7 @@ hipError_t launch_decode(const DecPlan& pl, const void* x, int64_t M, int64_t IC
   a.n_shards = n;
   a.lds_row = pl.lds_row;
   a.tr_off = pl.tr_off;
+  for (int r = 0; r < kMaxShards; ++r) a.wgb[r] = r < n ? pl.wg_begin[r] : INT_MAX;
   for (int r = 0; r < n; ++r) {
     const DecShardIn& s = in[pl.order[r]];
     DecShard& d = a.sh[r];
