@@ -144,7 +144,7 @@ __device__ void moe_route_general(const MoeArgs& a, int* lds) {
     for (int i = 0; i < nch; ++i) {
       const int r0 = off + i * a.chunk_rows;
       const int nr = c - i * a.chunk_rows < a.chunk_rows ? c - i * a.chunk_rows : a.chunk_rows;
-      a.chunks[coff + i] = (int4v){s, r0, nr, gk};
+      a.chunks[chunk_total - 1 - (coff + i)] = (int4v){s, r0, nr, gk};   // heaviest first (moe_chunk)
     }
   }
   if (s == 0) {
@@ -313,7 +313,7 @@ __device__ void moe_route_bitmap(const MoeArgs& a, int* lds) {
     for (int i = 0; i < nch; ++i) {
       const int r0 = off + i * chunk_rows;
       const int nr = c - i * chunk_rows < chunk_rows ? c - i * chunk_rows : chunk_rows;
-      chunks[coff + i] = (int4v){s, r0, nr, gk};
+      chunks[chunk_total - 1 - (coff + i)] = (int4v){s, r0, nr, gk};   // heaviest first (moe_chunk)
     }
   }
   if (s == 0) {

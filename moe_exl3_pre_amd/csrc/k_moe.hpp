@@ -44,12 +44,13 @@ struct MoeArgs {
   int g_k[kMoeMaxGroups];   // k_gu | k_d << 8
 };
 
-// Chunk c of the launch (heavier K groups sit at the end of the slot order, so they go first).
+// Chunk c of the launch.  The route stores the table heaviest K group first (heavier groups sit at the end
+// of the slot order, so entry 0 is the last slot's last chunk): the entry is requested together with the
+// chunk count instead of after it.  Entries from the count up to max_chunks are stale and never used.
 __device__ __forceinline__ bool moe_chunk(const MoeArgs& a, int c, int4v& ch) {
   const int n = a.n_chunks[0];
-  if (c >= n) return false;
-  ch = a.chunks[n - 1 - c];
-  return true;
+  ch = a.chunks[c < a.max_chunks ? c : a.max_chunks - 1];
+  return c < n;
 }
 
 // Workgroup -> (chunk, column group).  Workgroups are dealt to the 8 XCDs round-robin (block id mod 8);
