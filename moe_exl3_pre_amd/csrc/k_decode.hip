@@ -389,7 +389,8 @@ __global__ __launch_bounds__(512, 4) void decode_kernel(DecArgs a) {
   // search loop) they form a chain of them before the first weight load.
   int i = 0;
 #pragma unroll
-  for (int j = 1; j < kMaxShards; ++j) i += wg >= a.wgb[j] ? 1 : 0;   // shards are in grid order
+  for (int j = 1; j < kMaxShards; ++j)   // shards are in grid order; +1 when wgb[j] <= wg (scalar ALU only)
+    i += int(uint32_t(a.wgb[j] - wg - 1) >> 31);
   const DecShard& sh = a.sh[i];
   asm volatile("" ::"s"(a.x), "s"(a.out), "s"(a.ldo), "s"(a.M), "s"(a.IC), "s"(a.lds_row), "s"(a.tr_off));
   asm volatile("" ::"s"(sh.code), "s"(sh.xf), "s"(sh.sc), "s"(sh.part), "s"(sh.s_in), "s"(sh.rin), "s"(sh.rout),
