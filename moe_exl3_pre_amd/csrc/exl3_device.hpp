@@ -86,6 +86,23 @@ __device__ __forceinline__ uint32_t window16(const uint32_t (&r)[Geom<K>::kNR]) 
   }
 }
 
+// A pointer or size that is the same in every lane of the wave, moved to scalar registers where the
+// compiler can see that.  A buffer resource built from a value it must treat as varying across lanes
+// (one derived from the wave index, threadIdx.x / 64) is otherwise wrapped, at every buffer access, in a
+// loop over the distinct values of the active lanes (four readfirstlane, two compares, an exec-mask loop).
+// The builtin takes and returns a signed int: each half goes back through uint32_t before it is widened,
+// or a low half with bit 31 set would sign-extend into the high half of the address.
+template <class T>
+__device__ __forceinline__ T* wave_uniform(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v))));
+  const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v >> 32))));
+  return reinterpret_cast<T*>(lo | (hi << 32));
+}
+__device__ __forceinline__ uint32_t wave_uniform(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_readfirstlane(int(x)));
+}
+
 // A 32-bit constant in a scalar register that the compiler cannot see through.  The asm writes only
 // a scalar register: vector outputs of inline asm are avoided, because the compiler inserts no wait
 // states around inline asm for the matrix cores, and a vector register it picks for an asm output could

@@ -447,7 +447,8 @@ __device__ __forceinline__ void moe_accumulate(const uint16_t* code, uint32_t co
   int woff[G::kNW], shift;
   column_word_offsets<K>(n, woff, shift);
   const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(code), (short)0, (int)code_bytes, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wave_uniform(code)), (short)0,
+                                        (int)wave_uniform(code_bytes), kBufferFlags);
   const uint32_t lane_off = uint32_t(g) * uint32_t(tpr) * G::kWords * 4u + uint32_t(n) * 16u;
   const uint32_t step_stride = 4u * uint32_t(tpr) * G::kWords * 4u;
   const uint32_t base_blk = uint32_t(blk) * 8u * G::kWords * 4u;
