@@ -656,16 +656,25 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
   for (int j0 = 0; j0 < a.topk; j0 += kB) {
     float w[kB];
     float4 v[kB];
+    // Every term's row, slot and weight are requested before any is used: the loads are unconditional
+    // (q < P, always inside the workspace and the weight array), and the selections come after them.  A
+    // dropped pair's row was never written and is replaced by exact zeros.
+    float4 raw[kB];
+    int sl[kB];
+    float wv[kB];
 #pragma unroll
     for (int r = 0; r < kB; ++r) {
       const int j = j0 + r < a.topk ? j0 + r : a.topk - 1;
       const int q = t * a.topk + j;
-      // the row is loaded whatever the pair's slot (q < P: always inside the workspace), so this load does
-      // not wait for the slot's; a dropped pair's row was never written and is replaced by exact zeros
-      const float4 raw = *reinterpret_cast<const float4*>(a.o + int64_t(q) * a.H + c);
-      const bool use = j0 + r < a.topk && a.pslot[q] >= 0;
-      w[r] = use ? a.wts[q] : 0.f;
-      v[r] = use ? raw : make_float4(0.f, 0.f, 0.f, 0.f);
+      raw[r] = *reinterpret_cast<const float4*>(a.o + int64_t(q) * a.H + c);
+      sl[r] = a.pslot[q];
+      wv[r] = a.wts[q];
+    }
+#pragma unroll
+    for (int r = 0; r < kB; ++r) {
+      const bool use = j0 + r < a.topk && sl[r] >= 0;
+      w[r] = use ? wv[r] : 0.f;
+      v[r] = use ? raw[r] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int r = 0; r < kB; ++r) {   // top-k order; a dropped term adds exactly zero
